@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the indexer top-k path.
+
+This module only draws and quantizes inputs; it holds none of the method's
+arithmetic.  Both the oracle-side tests and the HIP-side tests / benchmark use
+it, so the two sides always see byte-identical operands.
+
+Shapes and value distributions follow the FlashTopK README "Quick start"
+example (a causal chunk of 4096 queries over 128K FP8 keys, 32 heads x 128,
+per-key fp32 scales, per-head fp32 weights, topk 2048) and the packed-sequence
+window helper of its "Usage" section.  Every array is produced on the host with
+``numpy.random.default_rng(seed)`` and quantized on the CPU with torch's
+round-to-nearest-even casts to ``float8_e4m3fn`` / ``bfloat16``.
+
+A workload is a plain dict:
+    q        uint8 [T,32,128] (FP8 E4M3FN codes) or uint16 (BF16 codes)
+    kv       uint8 [S,128] / uint16 [S,128]
+    dtype    "fp8" | "bf16"
+    kv_scales float32 [S] or None (all ones)
+    weights  float32 [T,32]
+    ks, ke   int32 [T]
+    topk     int
+    name     str
+"""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+
+HEADS = 32
+DIM = 128
+
+
+def _quantize(x: np.ndarray, dtype: str) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "fp8":
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    if dtype == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    raise ValueError(dtype)
+
+
+def causal_windows(T: int, S: int):
+    """Query i of a chunk of the last T tokens sees keys [0, S - T + i + 1)
+    (README "Quick start": causal prefill chunk)."""
+    ke = np.arange(S - T + 1, S + 1, dtype=np.int64)
+    ks = np.zeros(T, dtype=np.int64)
+    return ks.astype(np.int32), ke.astype(np.int32)
+
+
+def packed_windows(cu_seqlens_q, cu_seqlens_k):
+    """Causal windows of packed sequences (README "Usage": windows_from_cu_seqlens).
+
+    Document j holds queries [cu_q[j], cu_q[j+1]) and keys [cu_k[j], cu_k[j+1]).
+    Reading: bottom-right aligned, as in the causal-chunk example, so query i of
+    a document with Lq queries and Lk keys sees keys
+    [cu_k[j], cu_k[j] + Lk - Lq + i + 1).
+    """
+    cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
+    cu_k = np.asarray(cu_seqlens_k, dtype=np.int64)
+    T = int(cu_q[-1])
+    ks = np.zeros(T, dtype=np.int64)
+    ke = np.zeros(T, dtype=np.int64)
+    for j in range(len(cu_q) - 1):
+        lq = cu_q[j + 1] - cu_q[j]
+        lk = cu_k[j + 1] - cu_k[j]
+        i = np.arange(lq)
+        ks[cu_q[j]: cu_q[j + 1]] = cu_k[j]
+        ke[cu_q[j]: cu_q[j + 1]] = np.clip(cu_k[j] + lk - lq + i + 1, cu_k[j], cu_k[j + 1])
+    return ks.astype(np.int32), ke.astype(np.int32)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def gaussian(T, S, topk, dtype, seed, *, weight_scale=1.0, scales="uniform01",
+             windows="causal", docs=None, name=None):
+    """q, kv ~ N(0,1); weights ~ N(0,1) * weight_scale; kv_scales per ``scales``.
+
+    Draw order: q, kv, weights, kv_scales."""
+    rng = np.random.default_rng(seed)
+    q = _quantize(_normal(rng, (T, HEADS, DIM)), dtype)
+    kv = _quantize(_normal(rng, (S, DIM)), dtype)
+    w = (_normal(rng, (T, HEADS)) * np.float32(weight_scale)).astype(np.float32)
+    if scales == "ones":
+        sc = None
+    elif scales == "uniform01":
+        sc = rng.random(S, dtype=np.float32)
+    else:
+        raise ValueError(scales)
+    ks, ke = _windows(T, S, windows, docs)
+    return dict(q=q, kv=kv, dtype=dtype, kv_scales=sc, weights=w, ks=ks, ke=ke, topk=int(topk),
+                name=name or f"gaussian_{dtype}_{T}x{S}_k{topk}")
+
+
+def integer(T, S, topk, dtype, seed, *, windows="causal", docs=None, name=None):
+    """Tie-heavy exact data: q, kv integers uniform in [-4, 4]; weights uniform in
+    {+-1/4, +-1/2, +-1}; kv_scales uniform in {1/2, 1, 2}.  Every partial sum of
+    the score is a multiple of 1/8 below 2^18, so binary32 arithmetic is exact.
+
+    Draw order: q, kv, weights, kv_scales."""
+    rng = np.random.default_rng(seed)
+    q = _quantize(rng.integers(-4, 5, size=(T, HEADS, DIM)).astype(np.float32), dtype)
+    kv = _quantize(rng.integers(-4, 5, size=(S, DIM)).astype(np.float32), dtype)
+    wv = np.array([-1.0, -0.5, -0.25, 0.25, 0.5, 1.0], dtype=np.float32)
+    w = wv[rng.integers(0, 6, size=(T, HEADS))]
+    sv = np.array([0.5, 1.0, 2.0], dtype=np.float32)
+    sc = sv[rng.integers(0, 3, size=S)]
+    ks, ke = _windows(T, S, windows, docs)
+    return dict(q=q, kv=kv, dtype=dtype, kv_scales=sc, weights=w, ks=ks, ke=ke, topk=int(topk),
+                name=name or f"integer_{dtype}_{T}x{S}_k{topk}")
+
+
+def trained_shaped(T, S, topk, dtype, seed, *, heavy_frac=0.03, windows="causal", docs=None,
+                   name=None):
+    """Heavy-tailed rows, shaped like a trained indexer.
+
+    u = normalize(N(0, I_128)); per head c_h ~ U(0.5, 1.5) (shared by all
+    queries); q[t,h] = c_h u + 0.5 N(0, I); each key is heavy with probability
+    heavy_frac, g ~ N(4, 1) if heavy else N(0, 1); kv[s] = g_s u + 0.5 N(0, I);
+    kv_scales ~ U(0.5, 1); weights ~ |N(0, 1)|.
+
+    Draw order: u, c, heavy, g, q noise, kv noise, weights, kv_scales."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(DIM)
+    u = (u / np.linalg.norm(u)).astype(np.float32)
+    c = rng.uniform(0.5, 1.5, size=HEADS).astype(np.float32)
+    heavy = rng.random(S) < heavy_frac
+    g = np.where(heavy, rng.normal(4.0, 1.0, size=S), rng.normal(0.0, 1.0, size=S)).astype(np.float32)
+    qf = c[None, :, None] * u[None, None, :] + np.float32(0.5) * _normal(rng, (T, HEADS, DIM))
+    q = _quantize(qf, dtype)
+    del qf
+    kf = g[:, None] * u[None, :] + np.float32(0.5) * _normal(rng, (S, DIM))
+    kv = _quantize(kf, dtype)
+    del kf
+    w = np.abs(_normal(rng, (T, HEADS))).astype(np.float32)
+    sc = rng.uniform(0.5, 1.0, size=S).astype(np.float32)
+    ks, ke = _windows(T, S, windows, docs)
+    return dict(q=q, kv=kv, dtype=dtype, kv_scales=sc, weights=w, ks=ks, ke=ke, topk=int(topk),
+                name=name or f"trained_{dtype}_{T}x{S}_k{topk}")
+
+
+def _windows(T, S, windows, docs):
+    if windows == "causal":
+        return causal_windows(T, S)
+    if windows == "packed":
+        cu = np.concatenate([[0], np.cumsum(np.asarray(docs, dtype=np.int64))])
+        if cu[-1] != T or T != S:
+            raise ValueError("packed windows need T == S == sum(docs)")
+        return packed_windows(cu, cu)
+    if windows == "full":
+        return np.zeros(T, np.int32), np.full(T, S, np.int32)
+    raise ValueError(windows)
+
+
+# The five named workloads and their exact-arithmetic twins.
+PACKED_DOCS = (8192, 16384, 24576, 16384)
+
+
+def config(n: int, *, integer_twin: bool = False):
+    """Named workloads 1..5 (integer twins for 3..5 with integer_twin=True)."""
+    if integer_twin:
+        if n == 3:
+            return integer(4096, 131072, 4096, "fp8", 13, name="untrained_int_fp8_4096x131072_k4096")
+        if n == 4:
+            return integer(4096, 131072, 2048, "fp8", 14, name="trained_int_fp8_4096x131072_k2048")
+        if n == 5:
+            return integer(65536, 65536, 512, "bf16", 15, windows="packed", docs=PACKED_DOCS,
+                           name="packed_int_bf16_65536_k512")
+        raise ValueError(n)
+    if n == 1:
+        return gaussian(64, 2048, 64, "bf16", 1, weight_scale=32 ** -0.5, scales="ones",
+                        name="smallest_bf16_64x2048_k64")
+    if n == 2:
+        return integer(256, 8192, 512, "fp8", 2, name="tieheavy_fp8_256x8192_k512")
+    if n == 3:
+        return gaussian(4096, 131072, 4096, "fp8", 3, name="untrained_fp8_4096x131072_k4096")
+    if n == 4:
+        return trained_shaped(4096, 131072, 2048, "fp8", 4, name="trained_fp8_4096x131072_k2048")
+    if n == 5:
+        return gaussian(65536, 65536, 512, "bf16", 5, weight_scale=32 ** -0.5, scales="ones",
+                        windows="packed", docs=PACKED_DOCS, name="packed_bf16_65536_k512")
+    raise ValueError(n)
+
+
+def digest(wl) -> str:
+    """SHA-256 over every operand byte, in a fixed order."""
+    h = hashlib.sha256()
+    for k in ("q", "kv", "kv_scales", "weights", "ks", "ke"):
+        a = wl[k]
+        if a is not None:
+            h.update(np.ascontiguousarray(a).tobytes())
+    h.update(str(wl["topk"]).encode())
+    h.update(wl["dtype"].encode())
+    return h.hexdigest()
+
+
+def window_sum(wl) -> int:
+    return int(np.maximum(wl["ke"].astype(np.int64) - wl["ks"].astype(np.int64), 0).sum())
