@@ -1,0 +1,147 @@
+/*
+ * flashtopk.h -- C ABI of the MI355X (gfx950) fused indexer top-k library.
+ *
+ * One call scores every key of each query row's window with the lightning
+ * indexer and returns the row's exact top-k keys:
+ *
+ *     I[t,s] = sigma[s] * sum_{h<32} w[t,h] * ReLU( q[t,h,:] . kv[s,:] )
+ *
+ * for s in the half-open window [ks[t], ke[t])  (FlashTopK README, section
+ * "Quick start": the indexer-score equation, the window, the causal-chunk
+ * example and its shapes).  Selection is exact and deterministic: row t lists
+ * min(topk, ke[t]-ks[t]) absolute key indices ordered by score descending, and
+ * among equal scores the smaller key index comes first (README, "What you can
+ * do": "Exact" and "Deterministic").  Slots beyond the window length are padded
+ * with index -1 and value -inf (DeepSelect README, "Variable-length rows": rows
+ * shorter than topk are padded with fill values; -1 / -inf are this library's
+ * fill values).  +0 and -0 scores compare equal and are returned as +0.
+ *
+ * Operand layouts (all row-major, contiguous, device memory):
+ *   q          [num_q, 32, 128]  FP8 E4M3FN (OCP, finite-only) or BF16
+ *   kv         [num_kv, 128]     same dtype as q; one key per token, shared by
+ *                                all 32 heads
+ *   kv_scales  [num_kv] float32  per-key scale sigma >= 0, or NULL for all ones
+ *   weights    [num_q, 32] float32 per-head weights (any sign)
+ *   ks, ke     [num_q] int32     window bounds, 0 <= ks[t] <= ke[t] <= num_kv
+ *   out_idx    [num_q, topk] int32
+ *   out_val    [num_q, topk] float32 (the score of out_idx), or NULL to skip
+ *
+ * Ownership: the caller allocates and owns every operand and output.  The
+ * library owns only scratch memory: a grow-only workspace per (device,
+ * stream) that it keeps between calls and frees in flashtopk_release().
+ * Operands must stay unmodified until the stream has finished the call.
+ *
+ * Synchronisation: work is enqueued on `stream` (a hipStream_t; NULL is the
+ * device's null stream).  The call returns after the stream has finished its
+ * own work, so out_idx / out_val are valid when it returns 0.
+ *
+ * Errors: every entry point returns 0 (FLASHTOPK_OK) or a positive status;
+ * nothing is thrown across the ABI and nothing is printed.  Preconditions
+ * that cost a device read (window bounds inside [0, num_kv], finite operands)
+ * are not checked; violating them is undefined behaviour.
+ */
+#ifndef FLASHTOPK_H
+#define FLASHTOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Operand dtypes (README, "Support": FP8 or BF16 operands). */
+#define FLASHTOPK_FP8_E4M3 0
+#define FLASHTOPK_BF16 1
+
+/* Fixed indexer geometry (README, "Support": indexers of 32 heads x 128). */
+#define FLASHTOPK_HEADS 32
+#define FLASHTOPK_DIM 128
+/* Largest supported topk (README, "Support": topk up to 4096). */
+#define FLASHTOPK_MAX_TOPK 4096
+
+/* Status codes. */
+#define FLASHTOPK_OK 0
+#define FLASHTOPK_ERR_INVALID_ARGUMENT 1 /* null required pointer, bad size, topk outside [1, 4096] */
+#define FLASHTOPK_ERR_UNSUPPORTED 2      /* dtype other than FP8 E4M3 / BF16 */
+#define FLASHTOPK_ERR_OUT_OF_MEMORY 3    /* workspace allocation failed */
+#define FLASHTOPK_ERR_HIP 4              /* a HIP runtime or launch error */
+
+/* Execution paths.  Every path returns bit-identical results; they differ only
+ * in speed.  Used by tests and benchmarks to force a path. */
+#define FLASHTOPK_PATH_AUTO 0     /* the planner decides per call */
+#define FLASHTOPK_PATH_SCAN 1     /* sampled threshold + full scan, no pruning */
+#define FLASHTOPK_PATH_PRUNE 2    /* sampled threshold + score-bound key pruning */
+#define FLASHTOPK_PATH_RECOVER 3  /* dense rescoring + exact select for every row */
+
+/* Knobs for flashtopk_select_ex.  Zero-initialise for defaults. */
+typedef struct flashtopk_options {
+    int path;                 /* FLASHTOPK_PATH_* */
+    int cand_capacity;        /* candidates kept per row before a row is
+                                 rescored densely; 0 = default min(16384, 4*topk),
+                                 otherwise clamped to [topk, 16384] */
+    float sample_rank_scale;  /* multiplies the rank of the sampled threshold;
+                                 0 = 1.  Below 1 raises the threshold (fewer
+                                 candidates), above 1 lowers it */
+    int sample_target;        /* keys sampled per row for the threshold;
+                                 0 = 2048 */
+    int64_t recover_budget_bytes; /* scratch for dense rescoring; 0 = 1 GiB */
+} flashtopk_options;
+
+/* What the last call on a stream did (README, "Usage": last_info). */
+typedef struct flashtopk_info {
+    int32_t status;             /* status of that call */
+    int32_t path;               /* FLASHTOPK_PATH_SCAN / _PRUNE / _RECOVER */
+    int64_t rows;               /* num_q */
+    int64_t rows_empty;         /* ks == ke */
+    int64_t rows_take_all;      /* window no longer than the candidate capacity:
+                                   every key is a candidate */
+    int64_t rows_sampled;       /* rows filtered by a sampled threshold */
+    int64_t rows_underflow;     /* sampled rows left with fewer than topk candidates */
+    int64_t rows_overflow;      /* sampled rows with more candidates than capacity */
+    int64_t rows_recovered;     /* rows rescored densely (underflow + overflow,
+                                   or every row on the recover path) */
+    int64_t max_candidates;     /* largest candidate count of a sampled row */
+    int64_t window_keys;        /* sum of window lengths */
+    int64_t pruned_keys;        /* (row, key) pairs skipped by the score bound */
+    int32_t cand_capacity;      /* capacity used */
+    int32_t sample_target;      /* sample size used */
+} flashtopk_info;
+
+/* Exact top-k of the indexer score for every query row (see the file comment
+ * for operand layouts and semantics).  num_q >= 0, 0 <= num_kv < 2^31,
+ * 1 <= topk <= 4096, dtype FLASHTOPK_FP8_E4M3 or FLASHTOPK_BF16.  num_q == 0
+ * is a no-op. */
+int flashtopk_select(const void *q, const void *kv, const float *kv_scales,
+                     const float *weights, const int32_t *ks, const int32_t *ke,
+                     int64_t num_q, int64_t num_kv, int dtype, int topk,
+                     int32_t *out_idx, float *out_val, void *stream);
+
+/* flashtopk_select with options (opt may be NULL = defaults). */
+int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales,
+                        const float *weights, const int32_t *ks, const int32_t *ke,
+                        int64_t num_q, int64_t num_kv, int dtype, int topk,
+                        int32_t *out_idx, float *out_val, void *stream,
+                        const flashtopk_options *opt);
+
+/* Pre-allocate the workspace of (current device, stream) for calls up to the
+ * given sizes, so later calls allocate nothing (README, "Usage": the
+ * Selector's plan() owns the workspace and prepares up front). */
+int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream);
+
+/* Statistics of the last call issued on `stream` from this process. */
+int flashtopk_get_last_info(void *stream, flashtopk_info *out);
+
+/* Frees every cached workspace.  No call may be in flight. */
+void flashtopk_release(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *flashtopk_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int flashtopk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHTOPK_H */

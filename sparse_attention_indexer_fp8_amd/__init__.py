@@ -1,0 +1,228 @@
+"""Python binding of the gfx950 fused indexer top-k library (libflashtopk.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/flashtopk.h.  torch supplies
+device memory and the stream.  The functions below carry the C entry points'
+names; ``select`` mirrors the FlashTopK README "Usage" signature
+``select(q, kv, weights, ks, ke, kv_scales=None, topk=2048, ...)``.
+
+There is no fallback: if the HIP library is missing or no GPU is present the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashtopk.so")
+
+FLASHTOPK_FP8_E4M3 = 0
+FLASHTOPK_BF16 = 1
+HEADS = 32
+DIM = 128
+MAX_TOPK = 4096
+
+PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER = 0, 1, 2, 3
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "out of device memory",
+          4: "HIP runtime error"}
+
+
+class FlashTopKError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {status} ({STATUS.get(status, 'unknown')})")
+
+
+class Options(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int),
+        ("cand_capacity", ctypes.c_int),
+        ("sample_rank_scale", ctypes.c_float),
+        ("sample_target", ctypes.c_int),
+        ("recover_budget_bytes", ctypes.c_int64),
+    ]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [
+        ("status", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+        ("rows", ctypes.c_int64),
+        ("rows_empty", ctypes.c_int64),
+        ("rows_take_all", ctypes.c_int64),
+        ("rows_sampled", ctypes.c_int64),
+        ("rows_underflow", ctypes.c_int64),
+        ("rows_overflow", ctypes.c_int64),
+        ("rows_recovered", ctypes.c_int64),
+        ("max_candidates", ctypes.c_int64),
+        ("window_keys", ctypes.c_int64),
+        ("pruned_keys", ctypes.c_int64),
+        ("cand_capacity", ctypes.c_int32),
+        ("sample_target", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+# Every symbol include/flashtopk.h declares.
+EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_reserve", "flashtopk_get_last_info",
+           "flashtopk_release", "flashtopk_status_string", "flashtopk_version")
+
+_lib = None
+
+
+def load_library():
+    """Loads libflashtopk.so (no GPU needed to load it)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sel = [P, P, P, P, P, P, I64, I64, I, I, P, P, P]
+    lib.flashtopk_select.argtypes = sel
+    lib.flashtopk_select.restype = I
+    lib.flashtopk_select_ex.argtypes = sel + [ctypes.POINTER(Options)]
+    lib.flashtopk_select_ex.restype = I
+    lib.flashtopk_reserve.argtypes = [I64, I64, I, I, P]
+    lib.flashtopk_reserve.restype = I
+    lib.flashtopk_get_last_info.argtypes = [P, ctypes.POINTER(Info)]
+    lib.flashtopk_get_last_info.restype = I
+    lib.flashtopk_release.argtypes = []
+    lib.flashtopk_release.restype = None
+    lib.flashtopk_status_string.argtypes = [I]
+    lib.flashtopk_status_string.restype = ctypes.c_char_p
+    lib.flashtopk_version.argtypes = []
+    lib.flashtopk_version.restype = I
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FLASHTOPK_FP8_E4M3
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return FLASHTOPK_BF16
+    raise TypeError(f"q/kv must be float8_e4m3fn or bfloat16 (or their uint8/int16 codes), got {t.dtype}")
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, dtypes=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=None, stream=None,
+                        options: Options | None = None) -> None:
+    """Fills out_idx [T, topk] int32 (and out_val [T, topk] float32 if given)."""
+    torch = _torch()
+    lib = load_library()
+    T, S = q.shape[0], kv.shape[0]
+    code = _dtype_code(q)
+    if _dtype_code(kv) != code:
+        raise TypeError("q and kv must have the same dtype")
+    if tuple(q.shape[1:]) != (HEADS, DIM) or tuple(kv.shape[1:]) != (DIM,):
+        raise ValueError("q must be [T, 32, 128] and kv [S, 128]")
+    _check_dev("q", q)
+    _check_dev("kv", kv)
+    _check_dev("kv_scales", kv_scales, (torch.float32,), (S,))
+    _check_dev("weights", weights, (torch.float32,), (T, HEADS))
+    _check_dev("ks", ks, (torch.int32,), (T,))
+    _check_dev("ke", ke, (torch.int32,), (T,))
+    _check_dev("out_idx", out_idx, (torch.int32,), (T, topk))
+    _check_dev("out_val", out_val, (torch.float32,), (T, topk))
+    opt = ctypes.byref(options) if options is not None else None
+    st = lib.flashtopk_select_ex(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(weights), _ptr(ks), _ptr(ke),
+                                 T, S, code, int(topk), _ptr(out_idx), _ptr(out_val),
+                                 ctypes.c_void_p(_stream_handle(stream)), opt)
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_select_ex")
+
+
+def flashtopk_select(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=None, stream=None) -> None:
+    flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val, stream, None)
+
+
+def flashtopk_reserve(max_q, max_kv, max_topk, dtype=FLASHTOPK_FP8_E4M3, stream=None) -> None:
+    st = load_library().flashtopk_reserve(int(max_q), int(max_kv), int(max_topk), int(dtype),
+                                          ctypes.c_void_p(_stream_handle(stream)))
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_reserve")
+
+
+def flashtopk_get_last_info(stream=None) -> dict:
+    info = Info()
+    st = load_library().flashtopk_get_last_info(ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(info))
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_get_last_info")
+    return info.as_dict()
+
+
+def flashtopk_release() -> None:
+    load_library().flashtopk_release()
+
+
+def flashtopk_status_string(status: int) -> str:
+    return load_library().flashtopk_status_string(int(status)).decode()
+
+
+def flashtopk_version() -> int:
+    return int(load_library().flashtopk_version())
+
+
+def select(q, kv, weights, ks, ke, kv_scales=None, topk=2048, return_scores=False, options=None, stream=None):
+    """indices [T, topk] int32 (and scores [T, topk] float32 with return_scores)."""
+    torch = _torch()
+    T = q.shape[0]
+    idx = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    val = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, idx, val, stream, options)
+    return (idx, val) if return_scores else idx
+
+
+def windows_from_cu_seqlens(cu_seqlens_q, cu_seqlens_k):
+    """Causal windows of packed sequences (README "Usage"), bottom-right
+    aligned: query i of a document with Lq queries and Lk keys sees keys
+    [cu_k[j], cu_k[j] + Lk - Lq + i + 1).  Returns int32 (ks, ke)."""
+    torch = _torch()
+    cq = cu_seqlens_q.to(torch.int64)
+    ck = cu_seqlens_k.to(torch.int64)
+    lq = cq[1:] - cq[:-1]
+    lk = ck[1:] - ck[:-1]
+    T = int(cq[-1].item())
+    doc = torch.repeat_interleave(torch.arange(lq.numel(), device=cq.device), lq)
+    pos = torch.arange(T, device=cq.device) - cq[doc]
+    ks = ck[doc]
+    ke = torch.minimum(torch.maximum(ck[doc] + lk[doc] - lq[doc] + pos + 1, ks), ck[doc + 1])
+    return ks.to(torch.int32), ke.to(torch.int32)

@@ -1,0 +1,387 @@
+// C ABI of the fused indexer top-k library (declared in include/flashtopk.h).
+//
+// Launch sequence of one call, all on the caller's stream:
+//   1. k_score<sample>  strided-sample scores of every long row     (MFMA)
+//   2. k_tau            per-row threshold = r-th largest sample score
+//   3. k_score<filter>  fused score + threshold filter -> candidates (MFMA, hot)
+//   4. k_triage         flag rows whose candidates under/overflowed
+//   5. k_select         exact top-k of every unflagged row
+//   6. (flagged rows)   k_score<dense> + k_select<dense> in batches
+// The count of flagged rows is read back once (a stream synchronisation)
+// to size step 6; the call returns with the stream drained.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "flashtopk.h"
+#include "ftk_score.hpp"
+#include "ftk_select.hpp"
+
+using namespace ftk;
+
+namespace {
+
+constexpr int kMaxCap = 16384;
+constexpr int kDefaultSampleTarget = 2048;
+constexpr int64_t kDefaultRecoverBudget = int64_t(1) << 30;
+
+// Grow-only device buffer.
+struct DevBuf {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+struct Workspace {
+    int device = -1;
+    hipStream_t stream = nullptr;
+    DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch;
+    unsigned long long *host_stats = nullptr;  // pinned
+    flashtopk_info last{};
+    bool has_last = false;
+};
+
+std::mutex g_mu;
+std::vector<Workspace *> g_ws;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return FLASHTOPK_OK;
+    if (e == hipErrorOutOfMemory) return FLASHTOPK_ERR_OUT_OF_MEMORY;
+    return FLASHTOPK_ERR_HIP;
+}
+
+// Ensures `b` holds at least `bytes`; on growth the stream is drained first so
+// no pending kernel still uses the old buffer.
+int ensure(Workspace &w, DevBuf &b, size_t bytes)
+{
+    if (b.bytes >= bytes && b.ptr) return FLASHTOPK_OK;
+    size_t want = std::max(bytes, b.bytes + b.bytes / 4);
+    if (b.ptr) {
+        hipError_t e = hipStreamSynchronize(w.stream);
+        if (e != hipSuccess) return hip_status(e);
+        (void)hipFree(b.ptr);
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+    hipError_t e = hipMalloc(&b.ptr, std::max<size_t>(want, 256));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        b.ptr = nullptr;
+        return hip_status(e);
+    }
+    b.bytes = std::max<size_t>(want, 256);
+    return FLASHTOPK_OK;
+}
+
+Workspace *get_ws(hipStream_t stream, int *status)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *status = hip_status(e);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (Workspace *w : g_ws)
+        if (w->device == dev && w->stream == stream) return w;
+    Workspace *w = new Workspace();
+    w->device = dev;
+    w->stream = stream;
+    e = hipHostMalloc((void **)&w->host_stats, sizeof(unsigned long long) * kStCount, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        delete w;
+        *status = hip_status(e);
+        return nullptr;
+    }
+    g_ws.push_back(w);
+    return w;
+}
+
+struct Plan {
+    int64_t T, S;
+    int dtype, topk, cap, sample_target, path;
+    float rank_scale;
+    int64_t recover_budget;
+};
+
+int resolve(Plan &p, const flashtopk_options *opt)
+{
+    p.path = opt ? opt->path : FLASHTOPK_PATH_AUTO;
+    if (p.path < FLASHTOPK_PATH_AUTO || p.path > FLASHTOPK_PATH_RECOVER) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    int cap = (opt && opt->cand_capacity > 0) ? opt->cand_capacity : std::min(kMaxCap, 4 * p.topk);
+    p.cap = std::min(kMaxCap, std::max(cap, p.topk));
+    p.sample_target = (opt && opt->sample_target > 0) ? opt->sample_target : kDefaultSampleTarget;
+    p.rank_scale = (opt && opt->sample_rank_scale > 0.0f) ? opt->sample_rank_scale : 1.0f;
+    p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
+    if (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE) p.path = FLASHTOPK_PATH_SCAN;
+    return FLASHTOPK_OK;
+}
+
+template <int DT>
+void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
+{
+    if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, kThreads, 0, st>>>(a);
+    else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, kThreads, 0, st>>>(a);
+    else k_score<DT, kModeDense><<<grid, kThreads, 0, st>>>(a);
+}
+
+void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
+{
+    if (dtype == FLASHTOPK_FP8_E4M3) launch_score<kFP8>(mode, grid, st, a);
+    else launch_score<kBF16>(mode, grid, st, a);
+}
+
+int run(const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
+        const int32_t *ke, int32_t *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+{
+    int st = FLASHTOPK_OK;
+    Workspace *w = get_ws(stream, &st);
+    if (!w) return st;
+    const int64_t T = p.T, S = p.S;
+    if ((st = ensure(*w, w->tau, sizeof(float) * T))) return st;
+    if ((st = ensure(*w, w->cnt, sizeof(uint32_t) * T))) return st;
+    if ((st = ensure(*w, w->rowflag, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(*w, w->rowlist, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(*w, w->nflagged, sizeof(int32_t)))) return st;
+    if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
+    const bool recover_all = p.path == FLASHTOPK_PATH_RECOVER;
+    if (!recover_all) {
+        if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * p.cap))) return st;
+        if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * p.sample_target))) return st;
+    }
+
+    const int ntiles = (int)((T + kTileQ - 1) / kTileQ);
+    const int nchunks = (int)std::max<int64_t>(1, (S + kChunkKeys - 1) / kChunkKeys);
+
+    ScoreArgs sa{};
+    sa.q = (const uint8_t *)q;
+    sa.kv = (const uint8_t *)kv;
+    sa.sigma = kv_scales;
+    sa.w = weights;
+    sa.ks = ks;
+    sa.ke = ke;
+    sa.num_q = T;
+    sa.num_kv = S;
+    sa.ntiles = ntiles;
+    sa.cap = p.cap;
+    sa.tau = (const float *)w->tau.ptr;
+    sa.cnt = (uint32_t *)w->cnt.ptr;
+    sa.cand = (uint64_t *)w->cand.ptr;
+    sa.samp = (uint32_t *)w->samp.ptr;
+    sa.sample_target = p.sample_target;
+
+    if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3(ntiles), stream, sa);
+
+    TauArgs ta{};
+    ta.ks = ks;
+    ta.ke = ke;
+    ta.topk = p.topk;
+    ta.cap = p.cap;
+    ta.samp = (const uint32_t *)w->samp.ptr;
+    ta.sample_target = p.sample_target;
+    ta.rank_scale = p.rank_scale;
+    ta.recover_all = recover_all ? 1 : 0;
+    ta.tau = (float *)w->tau.ptr;
+    ta.cnt = (uint32_t *)w->cnt.ptr;
+    k_tau<<<dim3((unsigned)T), kSelThreads, 0, stream>>>(ta);
+
+    if (!recover_all) launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
+
+    TriageArgs tr{};
+    tr.ks = ks;
+    tr.ke = ke;
+    tr.num_q = T;
+    tr.topk = p.topk;
+    tr.cap = p.cap;
+    tr.cnt = (const uint32_t *)w->cnt.ptr;
+    tr.recover_all = recover_all ? 1 : 0;
+    tr.rowflag = (int32_t *)w->rowflag.ptr;
+    tr.rowlist = (int32_t *)w->rowlist.ptr;
+    tr.nflagged = (int32_t *)w->nflagged.ptr;
+    tr.stats = (unsigned long long *)w->stats.ptr;
+    k_triage<<<1, 1024, 0, stream>>>(tr);
+
+    SelectArgs se{};
+    se.ks = ks;
+    se.ke = ke;
+    se.topk = p.topk;
+    se.cap = p.cap;
+    se.cnt = (const uint32_t *)w->cnt.ptr;
+    se.rowflag = (const int32_t *)w->rowflag.ptr;
+    se.cand = (const uint64_t *)w->cand.ptr;
+    se.rowlist = (const int32_t *)w->rowlist.ptr;
+    se.nrows = (const int32_t *)w->nflagged.ptr;
+    se.out_idx = out_idx;
+    se.out_val = out_val;
+    k_select<false><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
+
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    e = hipMemcpyAsync(w->host_stats, w->stats.ptr, sizeof(unsigned long long) * kStCount,
+                       hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+
+    const int64_t R = (int64_t)w->host_stats[kStFlagged];
+    if (R > 0) {
+        // Dense rescoring of flagged rows, in batches that fit the budget.
+        const int64_t stride = std::max<int64_t>(S, 1);
+        int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(uint64_t) * stride));
+        rcap = std::min<int64_t>(rcap, (R + kTileQ - 1) / kTileQ * kTileQ);
+        rcap = (rcap + kTileQ - 1) / kTileQ * kTileQ;
+        if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)rcap * stride))) return st;
+        sa.rowlist = (const int32_t *)w->rowlist.ptr;
+        sa.nrows = (const int32_t *)w->nflagged.ptr;
+        sa.row_limit = (int)rcap;
+        sa.scratch = (uint64_t *)w->scratch.ptr;
+        sa.scratch_stride = stride;
+        sa.ntiles = (int)(rcap / kTileQ);
+        se.row_limit = (int)rcap;
+        se.scratch = (const uint64_t *)w->scratch.ptr;
+        se.scratch_stride = stride;
+        for (int64_t rb = 0; rb < R; rb += rcap) {
+            sa.row_base = (int)rb;
+            se.row_base = (int)rb;
+            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * nchunks)), stream, sa);
+            k_select<true><<<dim3((unsigned)rcap), kSelThreads, 0, stream>>>(se);
+        }
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
+
+    flashtopk_info &info = w->last;
+    std::memset(&info, 0, sizeof(info));
+    const unsigned long long *hs = w->host_stats;
+    info.status = FLASHTOPK_OK;
+    info.path = p.path;
+    info.rows = (int64_t)hs[kStRows];
+    info.rows_empty = (int64_t)hs[kStEmpty];
+    info.rows_take_all = (int64_t)hs[kStTakeAll];
+    info.rows_sampled = (int64_t)hs[kStSampled];
+    info.rows_underflow = (int64_t)hs[kStUnder];
+    info.rows_overflow = (int64_t)hs[kStOver];
+    info.rows_recovered = R;
+    info.max_candidates = (int64_t)hs[kStMaxCand];
+    info.window_keys = (int64_t)hs[kStWindow];
+    info.pruned_keys = 0;
+    info.cand_capacity = p.cap;
+    info.sample_target = p.sample_target;
+    w->has_last = true;
+    return FLASHTOPK_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, const float *weights,
+                        const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype,
+                        int topk, int32_t *out_idx, float *out_val, void *stream,
+                        const flashtopk_options *opt)
+{
+    if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
+    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 31))
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (topk < 1 || topk > FLASHTOPK_MAX_TOPK) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (num_q == 0) return FLASHTOPK_OK;
+    if (!q || !weights || !ks || !ke || !out_idx || (!kv && num_kv > 0)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || (kv && !aligned16(kv))) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    Plan p{};
+    p.T = num_q;
+    p.S = num_kv;
+    p.dtype = dtype;
+    p.topk = topk;
+    int st = resolve(p, opt);
+    if (st) return st;
+    return run(q, kv, kv_scales, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
+}
+
+int flashtopk_select(const void *q, const void *kv, const float *kv_scales, const float *weights,
+                     const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype, int topk,
+                     int32_t *out_idx, float *out_val, void *stream)
+{
+    return flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, num_q, num_kv, dtype, topk, out_idx, out_val,
+                               stream, nullptr);
+}
+
+int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream)
+{
+    if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
+    if (max_q < 0 || max_kv < 0 || max_topk < 1 || max_topk > FLASHTOPK_MAX_TOPK)
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    int st = FLASHTOPK_OK;
+    Workspace *w = get_ws((hipStream_t)stream, &st);
+    if (!w) return st;
+    const int64_t T = std::max<int64_t>(max_q, 1);
+    const int cap = std::min(kMaxCap, std::max(4 * max_topk, max_topk));
+    if ((st = ensure(*w, w->tau, sizeof(float) * T))) return st;
+    if ((st = ensure(*w, w->cnt, sizeof(uint32_t) * T))) return st;
+    if ((st = ensure(*w, w->rowflag, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(*w, w->rowlist, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(*w, w->nflagged, sizeof(int32_t)))) return st;
+    if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
+    if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * cap))) return st;
+    if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * kDefaultSampleTarget))) return st;
+    (void)max_kv;
+    return FLASHTOPK_OK;
+}
+
+int flashtopk_get_last_info(void *stream, flashtopk_info *out)
+{
+    if (!out) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (Workspace *w : g_ws) {
+        if (w->device == dev && w->stream == (hipStream_t)stream && w->has_last) {
+            *out = w->last;
+            return FLASHTOPK_OK;
+        }
+    }
+    std::memset(out, 0, sizeof(*out));
+    return FLASHTOPK_ERR_INVALID_ARGUMENT;
+}
+
+void flashtopk_release(void)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (Workspace *w : g_ws) {
+        int prev = 0;
+        (void)hipGetDevice(&prev);
+        (void)hipSetDevice(w->device);
+        (void)hipStreamSynchronize(w->stream);
+        DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowflag, &w->rowlist, &w->nflagged, &w->stats,
+                          &w->cand, &w->samp, &w->scratch};
+        for (DevBuf *b : bufs)
+            if (b->ptr) (void)hipFree(b->ptr);
+        if (w->host_stats) (void)hipHostFree(w->host_stats);
+        (void)hipSetDevice(prev);
+        delete w;
+    }
+    g_ws.clear();
+}
+
+const char *flashtopk_status_string(int status)
+{
+    switch (status) {
+    case FLASHTOPK_OK: return "ok";
+    case FLASHTOPK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FLASHTOPK_ERR_UNSUPPORTED: return "unsupported dtype";
+    case FLASHTOPK_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case FLASHTOPK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int flashtopk_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Shared device definitions of the gfx950 indexer top-k kernels: geometry,
+// operand vector types and the 64-bit selection key.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ftk {
+
+// Indexer geometry: 32 heads of 128 dimensions sharing one key per token
+// (FlashTopK README, "Support": indexers of 32 heads x 128).
+constexpr int kHeads = 32;
+constexpr int kDim = 128;
+
+// Work decomposition.  A tile is 16 query rows: the N = 16 columns of a
+// 16x16 MFMA output.  A wave scores kSub 16-key subtiles per step (the M = 16
+// rows), eight waves share a tile, and a work item covers kChunkKeys keys.
+constexpr int kTileQ = 16;
+constexpr int kSub = 4;
+constexpr int kStepKeys = 16 * kSub;      // 64 keys per wave step
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;     // 512
+constexpr int kChunkKeys = 4096;          // keys per work item
+
+constexpr int kFP8 = 0;
+constexpr int kBF16 = 1;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Bytes of one key row (or one query head row) per dtype.
+template <int DT> struct RowBytes { static constexpr int value = DT == kFP8 ? 128 : 256; };
+
+// Order-preserving map of a binary32 score onto uint32: a larger score gives
+// a larger code, and -0 folds into +0 so the two compare equal.
+__device__ __forceinline__ uint32_t ord_of(float f)
+{
+    uint32_t b = __float_as_uint(f);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float float_of_ord(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// 64-bit selection key: score code in the high word, the complement of the
+// key index in the low word.  Ordering keys descending gives score
+// descending and, among equal scores, the smaller key index first -- the tie
+// rule of the README ("What you can do": ties at the k-th score keep the
+// smallest key indices).  Keys of distinct indices are distinct.
+__device__ __forceinline__ uint64_t sel_key(float score, int32_t s)
+{
+    return ((uint64_t)ord_of(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
+}
+
+__device__ __forceinline__ int32_t key_index(uint64_t k)
+{
+    return (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+__device__ __forceinline__ float key_score(uint64_t k)
+{
+    return float_of_ord((uint32_t)(k >> 32));
+}
+
+// ReLU as an integer max on the bit pattern: non-negative floats have
+// non-negative int32 patterns, negative floats negative ones.  Exact for every
+// finite input (and -0 becomes +0); one VALU op with no NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Smallest power of two d with len <= target * d: the stride of the row's
+// strided sample, so the sample holds at most `target` keys.
+__device__ __host__ __forceinline__ int sample_stride(int64_t len, int target)
+{
+    int d = 1;
+    while (len > (int64_t)target * d) d <<= 1;
+    return d;
+}
+
+// Number of multiples of d (a power of two) in [lo, hi).
+__device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi, int d)
+{
+    if (hi <= lo) return 0;
+    int64_t first = (lo + d - 1) / d * d;
+    if (first >= hi) return 0;
+    return (hi - 1 - first) / d + 1;
+}
+
+}  // namespace ftk

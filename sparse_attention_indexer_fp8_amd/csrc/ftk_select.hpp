@@ -1,0 +1,320 @@
+// Per-row threshold, triage and exact selection kernels.
+//
+// Threshold ("gate"): FlashTopK README, "Highlights": each row's threshold
+// comes from a strided sample of its own window.  The sample is the lattice of
+// multiples of a power-of-two stride d inside [ks, ke) (at most
+// `sample_target` keys); the threshold is the r-th largest sample score with
+// r = ceil(alpha * topk * n_sample / L), alpha = 2, so about alpha * topk keys
+// of the window are expected to reach it.
+//
+// Exactness ("What you can do": exact; rows the sampled threshold misses are
+// rescored on the GPU): a row whose candidate count is below min(topk, L)
+// (the threshold was too high) or above the candidate capacity (too low) is
+// flagged by triage and rescored densely; every other row's candidates
+// contain its whole top-k, because every key outside them scores below the
+// threshold.
+//
+// Selection: the k-th largest 64-bit key (score code, complemented index) is
+// found by an MSB-first radix select with 8-bit digits; keys at or above it --
+// exactly k, since keys are distinct -- are gathered into LDS and sorted
+// descending by a bitonic network.  Descending key order is score descending
+// with the smaller index first on ties ("What you can do": deterministic).
+#pragma once
+
+#include "ftk_common.hpp"
+
+namespace ftk {
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kMaxTopk = 4096;
+
+// ---------------------------------------------------------------------------
+// Block-wide radix select.  `fetch(i)` returns element i (i < n).  Returns the
+// smallest key T such that exactly k elements are >= T (the k-th largest key,
+// or a lower bound with the same count).  All threads of the block must call
+// it; k must satisfy 1 <= k <= n.  Uses the caller's LDS scratch.
+
+struct RadixLds {
+    uint32_t hist[kSelWaves][256];
+    uint32_t tot[256];
+    uint32_t suf[257];
+    uint32_t digit;
+};
+
+template <typename KeyT, int NDIGITS, typename Fetch>
+__device__ KeyT radix_select_kth(RadixLds &L, Fetch fetch, int64_t n, uint32_t k)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int BITS = 8 * sizeof(KeyT);
+    KeyT prefix = 0;
+    uint32_t remaining = k;
+    for (int p = 0; p < NDIGITS; ++p) {
+        const int shift = BITS - 8 * (p + 1);
+        for (int i = tid; i < kSelWaves * 256; i += blockDim.x) (&L.hist[0][0])[i] = 0;
+        __syncthreads();
+        for (int64_t i = tid; i < n; i += blockDim.x) {
+            KeyT e = fetch(i);
+            bool match = (p == 0) || (((e ^ prefix) >> (shift + 8)) == 0);
+            if (match) atomicAdd(&L.hist[wave][(uint32_t)(e >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t s = 0;
+#pragma unroll
+            for (int w = 0; w < kSelWaves; ++w) s += L.hist[w][tid];
+            L.tot[tid] = s;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // Suffix sums over bins, highest digit first: lane handles 4 bins.
+            uint32_t v0 = L.tot[255 - 4 * lane], v1 = L.tot[254 - 4 * lane];
+            uint32_t v2 = L.tot[253 - 4 * lane], v3 = L.tot[252 - 4 * lane];
+            uint32_t c0 = v0, c1 = c0 + v1, c2 = c1 + v2, c3 = c2 + v3;
+            uint32_t x = c3;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                uint32_t y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            uint32_t ex = x - c3;
+            L.suf[255 - 4 * lane] = ex + c0;
+            L.suf[254 - 4 * lane] = ex + c1;
+            L.suf[253 - 4 * lane] = ex + c2;
+            L.suf[252 - 4 * lane] = ex + c3;
+            if (lane == 0) L.suf[256] = 0;
+        }
+        __syncthreads();
+        if (tid < 256 && L.suf[tid] >= remaining && L.suf[tid + 1] < remaining) L.digit = tid;
+        __syncthreads();
+        const uint32_t d = L.digit;
+        const uint32_t above = L.suf[d + 1];
+        const uint32_t inbin = L.tot[d];
+        __syncthreads();
+        remaining -= above;
+        prefix |= (KeyT)d << shift;
+        if (inbin == remaining) break;  // the whole bin is selected
+    }
+    return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row threshold from the row's strided sample.
+
+struct TauArgs {
+    const int32_t *ks;
+    const int32_t *ke;
+    int topk;
+    int cap;
+    const uint32_t *samp;
+    int sample_target;
+    float rank_scale;
+    int recover_all;
+    float *tau;
+    uint32_t *cnt;
+};
+
+__global__ __launch_bounds__(kSelThreads) void k_tau(TauArgs a)
+{
+    __shared__ RadixLds L;
+    const int t = blockIdx.x;
+    const int64_t lo = a.ks[t], hi = a.ke[t];
+    const int64_t len = hi > lo ? hi - lo : 0;
+    if (threadIdx.x == 0) a.cnt[t] = 0;
+    if (a.recover_all || len <= a.cap) {
+        if (threadIdx.x == 0) a.tau[t] = a.recover_all ? __builtin_inff() : -__builtin_inff();
+        return;
+    }
+    const int d = sample_stride(len, a.sample_target);
+    const int64_t ns = lattice_count(lo, hi, d);
+    double want = ceil(2.0 * (double)a.topk * (double)ns / (double)len * (double)a.rank_scale);
+    uint32_t r = (uint32_t)min(max(want, 1.0), (double)ns);
+    const uint32_t *row = a.samp + (int64_t)t * a.sample_target;
+    uint32_t kth = radix_select_kth<uint32_t, 4>(L, [&](int64_t i) { return row[i]; }, ns, r);
+    if (threadIdx.x == 0) a.tau[t] = float_of_ord(kth);
+}
+
+// ---------------------------------------------------------------------------
+// Triage: one block classifies every row, lists the flagged rows in row
+// order and gathers the statistics.
+
+enum Stat {
+    kStRows = 0, kStEmpty, kStTakeAll, kStSampled, kStUnder, kStOver, kStFlagged, kStMaxCand,
+    kStWindow, kStCount
+};
+
+struct TriageArgs {
+    const int32_t *ks;
+    const int32_t *ke;
+    int64_t num_q;
+    int topk;
+    int cap;
+    const uint32_t *cnt;
+    int recover_all;
+    int32_t *rowflag;
+    int32_t *rowlist;
+    int32_t *nflagged;
+    unsigned long long *stats;
+};
+
+__global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
+{
+    __shared__ unsigned long long s_st[kStCount];
+    __shared__ uint32_t s_wave[16];
+    __shared__ uint32_t s_base;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < kStCount) s_st[tid] = 0;
+    if (tid == 0) s_base = 0;
+    __syncthreads();
+    for (int64_t b0 = 0; b0 < a.num_q; b0 += 1024) {
+        const int64_t t = b0 + tid;
+        bool flag = false;
+        if (t < a.num_q) {
+            const int64_t lo = a.ks[t], hi = a.ke[t];
+            const int64_t len = hi > lo ? hi - lo : 0;
+            const uint32_t c = a.cnt[t];
+            if (len == 0) {
+                atomicAdd(&s_st[kStEmpty], 1ull);
+            } else if (a.recover_all) {
+                flag = true;
+            } else {
+                const int64_t need = min((int64_t)a.topk, len);
+                const bool under = (int64_t)c < need;
+                const bool over = (int64_t)c > a.cap;
+                flag = under || over;
+                if (len <= a.cap) {
+                    atomicAdd(&s_st[kStTakeAll], 1ull);
+                } else {
+                    atomicAdd(&s_st[kStSampled], 1ull);
+                    atomicMax(&s_st[kStMaxCand], (unsigned long long)c);
+                }
+                if (under) atomicAdd(&s_st[kStUnder], 1ull);
+                if (over) atomicAdd(&s_st[kStOver], 1ull);
+            }
+            atomicAdd(&s_st[kStWindow], (unsigned long long)len);
+            a.rowflag[t] = flag ? 1 : 0;
+        }
+        // Order-preserving compaction of the flagged rows.
+        const uint64_t bal = __ballot(flag);
+        const uint32_t below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) s_wave[wave] = __builtin_popcountll(bal);
+        __syncthreads();
+        uint32_t off = s_base;
+        for (int w = 0; w < wave; ++w) off += s_wave[w];
+        if (flag) a.rowlist[off + below] = (int32_t)t;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t s = 0;
+            for (int w = 0; w < 16; ++w) s += s_wave[w];
+            s_base += s;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        *a.nflagged = (int32_t)s_base;
+        s_st[kStRows] = (unsigned long long)a.num_q;
+        s_st[kStFlagged] = s_base;
+    }
+    __syncthreads();
+    if (tid < kStCount) a.stats[tid] = s_st[tid];
+}
+
+// ---------------------------------------------------------------------------
+// Exact selection of one row per block.
+
+struct SelectArgs {
+    const int32_t *ks;
+    const int32_t *ke;
+    int topk;
+    int cap;
+    // candidate rows
+    const uint32_t *cnt;
+    const int32_t *rowflag;
+    const uint64_t *cand;
+    // dense (recovered) rows
+    const int32_t *rowlist;
+    const int32_t *nrows;
+    int row_base;
+    int row_limit;
+    const uint64_t *scratch;
+    int64_t scratch_stride;
+    int32_t *out_idx;
+    float *out_val;
+};
+
+template <bool DENSE>
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
+{
+    __shared__ RadixLds L;
+    __shared__ uint64_t s_sel[kMaxTopk];
+    __shared__ uint32_t s_n;
+    const int tid = threadIdx.x;
+    int t;
+    const uint64_t *src;
+    int64_t n;
+    if (DENSE) {
+        const int e = blockIdx.x;
+        if (e >= a.row_limit || a.row_base + e >= *a.nrows) return;
+        t = a.rowlist[a.row_base + e];
+        src = a.scratch + (int64_t)e * a.scratch_stride;
+        const int64_t lo = a.ks[t], hi = a.ke[t];
+        n = hi > lo ? hi - lo : 0;
+    } else {
+        t = blockIdx.x;
+        if (a.rowflag[t]) return;
+        src = a.cand + (int64_t)t * a.cap;
+        n = min((int64_t)a.cnt[t], (int64_t)a.cap);
+    }
+    const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
+    int32_t *oi = a.out_idx + (int64_t)t * a.topk;
+    float *ov = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
+
+    uint64_t thr = 0;
+    if (k > 0 && (int64_t)k < n)
+        thr = radix_select_kth<uint64_t, 8>(L, [&](int64_t i) { return src[i]; }, n, k);
+
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    if (k > 0) {
+        for (int64_t i = tid; i < n; i += blockDim.x) {
+            uint64_t e = src[i];
+            if (e >= thr) {
+                const uint32_t pos = atomicAdd(&s_n, 1u);
+                if (pos < (uint32_t)kMaxTopk) s_sel[pos] = e;
+            }
+        }
+    }
+    uint32_t P = 1;
+    while (P < k) P <<= 1;
+    __syncthreads();
+    for (uint32_t i = k + tid; i < P; i += blockDim.x) s_sel[i] = 0;  // below every real key
+    __syncthreads();
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = tid; i < P / 2; i += blockDim.x) {
+                uint32_t lo = 2 * i - (i & (stride - 1));
+                uint32_t hi = lo + stride;
+                bool desc = (lo & size) == 0;
+                uint64_t x = s_sel[lo], y = s_sel[hi];
+                if (desc ? (x < y) : (x > y)) {
+                    s_sel[lo] = y;
+                    s_sel[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int j = tid; j < a.topk; j += blockDim.x) {
+        int32_t idx = -1;
+        float v = -__builtin_inff();
+        if ((uint32_t)j < k) {
+            uint64_t e = s_sel[j];
+            idx = key_index(e);
+            v = key_score(e);
+        }
+        oi[j] = idx;
+        if (ov) ov[j] = v;
+    }
+}
+
+}  // namespace ftk

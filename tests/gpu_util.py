@@ -1,0 +1,68 @@
+"""Helpers of the GPU tests: move a workload to the device, run the HIP path
+through the C ABI, run the oracle, check parity."""
+import numpy as np
+
+import oracle
+import workloads
+
+import checker
+
+
+def to_device(wl, dev="cuda:0"):
+    import torch
+
+    if wl["dtype"] == "fp8":
+        q = torch.from_numpy(wl["q"]).to(dev).view(torch.float8_e4m3fn)
+        kv = torch.from_numpy(wl["kv"]).to(dev).view(torch.float8_e4m3fn)
+    else:
+        q = torch.from_numpy(wl["q"].view(np.int16)).to(dev).view(torch.bfloat16)
+        kv = torch.from_numpy(wl["kv"].view(np.int16)).to(dev).view(torch.bfloat16)
+    sc = None if wl["kv_scales"] is None else torch.from_numpy(wl["kv_scales"]).to(dev)
+    return dict(q=q, kv=kv, kv_scales=sc, weights=torch.from_numpy(wl["weights"]).to(dev),
+                ks=torch.from_numpy(wl["ks"]).to(dev), ke=torch.from_numpy(wl["ke"]).to(dev))
+
+
+def run_gpu(wl, d=None, options=None, topk=None):
+    import torch
+
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    d = d or to_device(wl)
+    k = topk or wl["topk"]
+    idx, val = ftk.select(d["q"], d["kv"], d["weights"], d["ks"], d["ke"], d["kv_scales"], topk=k,
+                          return_scores=True, options=options)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def run_oracle(wl, rows=None, topk=None):
+    k = topk or wl["topk"]
+    return oracle.select(wl["q"], wl["kv"], wl["dtype"], wl["kv_scales"], wl["weights"], wl["ks"], wl["ke"],
+                         k, rows=rows, all_scores=True)
+
+
+def parity(wl, idx, val, mode, rows=None, ref=None, topk=None):
+    k = topk or wl["topk"]
+    o = ref if ref is not None else run_oracle(wl, rows=rows, topk=k)
+    if rows is not None:
+        idx, val = idx[rows], val[rows]
+    rep = checker.check(idx, val, wl["ks"], wl["ke"], k, o_idx=o[0], o_val=o[1], o_score=o[2],
+                        all_scores=o[3], rows=rows, mode=mode)
+    return rep
+
+
+def opts(**kw):
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    o = ftk.Options()
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def sample_rows(T, n_mid=24, edge=8, seed=0):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(edge, max(edge + 1, T - edge)), size=min(n_mid, max(0, T - 2 * edge)),
+                     replace=False)
+    rows = np.unique(np.concatenate([np.arange(min(edge, T)), np.arange(max(0, T - edge), T), mid]))
+    return rows.astype(np.int64)

@@ -1,0 +1,91 @@
+"""The C-ABI library loads and exports every entry point include/flashtopk.h
+declares; argument checks that need no device memory (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_fp8_amd as ftk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashtopk.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flashtopk_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ftk.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return ftk.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(ftk.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version(lib):
+    assert ftk.flashtopk_status_string(0) == "ok"
+    assert ftk.flashtopk_status_string(1) == "invalid argument"
+    assert ftk.flashtopk_status_string(2) == "unsupported dtype"
+    assert ftk.flashtopk_status_string(999) == "unknown status"
+    assert ftk.flashtopk_version() >= 100
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (FLASHTOPK_\w+) (-?\d+)", text))
+    assert int(consts["FLASHTOPK_FP8_E4M3"]) == ftk.FLASHTOPK_FP8_E4M3
+    assert int(consts["FLASHTOPK_BF16"]) == ftk.FLASHTOPK_BF16
+    assert int(consts["FLASHTOPK_MAX_TOPK"]) == ftk.MAX_TOPK
+    assert int(consts["FLASHTOPK_PATH_RECOVER"]) == ftk.PATH_RECOVER
+
+
+def test_options_and_info_layout_match_header():
+    # sizes of the C structs as laid out by the platform ABI
+    assert ctypes.sizeof(ftk.Options) == 24
+    assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4
+
+
+def _call(lib, **kw):
+    args = dict(q=None, kv=None, kv_scales=None, weights=None, ks=None, ke=None, num_q=0, num_kv=0,
+                dtype=0, topk=1, out_idx=None, out_val=None, stream=None)
+    args.update(kw)
+    return lib.flashtopk_select(*[args[k] for k in ("q", "kv", "kv_scales", "weights", "ks", "ke", "num_q",
+                                                    "num_kv", "dtype", "topk", "out_idx", "out_val",
+                                                    "stream")])
+
+
+def test_argument_errors_without_device(lib):
+    # these return before any device work
+    assert _call(lib, dtype=7) == 2
+    assert _call(lib, topk=0) == 1
+    assert _call(lib, topk=4097) == 1
+    assert _call(lib, num_q=-1) == 1
+    assert _call(lib, num_kv=1 << 31) == 1
+    assert _call(lib, num_q=0, topk=5) == 0                  # empty call is a no-op
+    assert _call(lib, num_q=3, topk=5) == 1                  # null required pointers
+    assert lib.flashtopk_reserve(-1, 0, 1, 0, None) == 1
+    assert lib.flashtopk_reserve(1, 1, 1, 3, None) == 2
+
+
+def test_misaligned_operands_rejected(lib):
+    buf = (ctypes.c_uint8 * 64)()
+    base = ctypes.addressof(buf)
+    odd = base + (1 if base % 16 else 1)
+    p = ctypes.c_void_p(odd)
+    ok = ctypes.c_void_p(base + (-base) % 16)
+    assert _call(lib, q=p, kv=ok, weights=ok, ks=ok, ke=ok, out_idx=ok, num_q=1, num_kv=1) == 1

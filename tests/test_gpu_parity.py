@@ -1,0 +1,214 @@
+"""HIP path against the oracle, through the C ABI (MI355X only).
+
+Bit-exact where binary32 arithmetic is exact (integer-valued inputs); within
+|dI| <= 1e-3 * max|I_row| elsewhere, with any differing index scoring within
+that tolerance of the oracle's k-th score.  Sizes span several 16-row tiles,
+several 4096-key chunks and ragged tails.
+"""
+import numpy as np
+import pytest
+
+import workloads
+
+import golden_cases
+from gpu_util import opts, parity, run_gpu, run_oracle, sample_rows, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("cid,ex,case,dtype", list(golden_cases.all_cases()),
+                         ids=[c[0] for c in golden_cases.all_cases()])
+def test_hand_worked_examples(cid, ex, case, dtype):
+    _say("case", cid)
+    wl, exp_idx, exp_val = golden_cases.build(ex, case, dtype)
+    idx, val = run_gpu(wl)
+    assert np.array_equal(idx, exp_idx)
+    assert np.array_equal(val.view(np.uint32), exp_val.view(np.uint32))
+
+
+SMALL_EXACT = [
+    ("int_fp8_37x5000_k64", lambda: workloads.integer(37, 5000, 64, "fp8", 101)),
+    ("int_bf16_50x4500_k200", lambda: workloads.integer(50, 4500, 200, "bf16", 102)),
+    ("int_fp8_33x9000_k1", lambda: workloads.integer(33, 9000, 1, "fp8", 103)),
+    ("int_fp8_20x700_k4096", lambda: workloads.integer(20, 700, 4096, "fp8", 104)),
+    ("int_bf16_packed_96", lambda: workloads.integer(96, 96, 16, "bf16", 105, windows="packed",
+                                                     docs=(5, 40, 3, 48))),
+    ("int_fp8_full_17x12345_k300", lambda: workloads.integer(17, 12345, 300, "fp8", 106, windows="full")),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL_EXACT, ids=[n for n, _ in SMALL_EXACT])
+def test_integer_inputs_bit_exact(name, make):
+    _say("case", name)
+    wl = make()
+    idx, val = run_gpu(wl)
+    rep = parity(wl, idx, val, "exact")
+    assert rep["ok"], rep
+
+
+SMALL_TOL = [
+    ("gauss_fp8_100x6000_k128", lambda: workloads.gaussian(100, 6000, 128, "fp8", 201)),
+    ("gauss_bf16_64x5000_k100", lambda: workloads.gaussian(64, 5000, 100, "bf16", 202, weight_scale=0.2)),
+    ("trained_fp8_48x9000_k256", lambda: workloads.trained_shaped(48, 9000, 256, "fp8", 203)),
+    ("gauss_fp8_ones_31x4097_k33", lambda: workloads.gaussian(31, 4097, 33, "fp8", 204, scales="ones")),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL_TOL, ids=[n for n, _ in SMALL_TOL])
+def test_random_inputs_within_tolerance(name, make):
+    _say("case", name)
+    wl = make()
+    idx, val = run_gpu(wl)
+    rep = parity(wl, idx, val, "tolerance")
+    assert rep["ok"], rep
+    assert rep["precision"] > 0.99
+
+
+def test_config_smallest_full():
+    wl = workloads.config(1)
+    _say("case", wl["name"])
+    idx, val = run_gpu(wl)
+    rep = parity(wl, idx, val, "tolerance")
+    assert rep["ok"], rep
+
+
+def test_config_tie_heavy_full_bit_exact():
+    wl = workloads.config(2)
+    _say("case", wl["name"])
+    idx, val = run_gpu(wl)
+    rep = parity(wl, idx, val, "exact")
+    assert rep["ok"], rep
+
+
+# ---------------------------------------------------------------- paths ----
+
+@pytest.fixture(scope="module")
+def path_case():
+    wl = workloads.gaussian(64, 9000, 256, "fp8", 301)
+    d = to_device(wl)
+    base = run_gpu(wl, d)
+    return wl, d, base
+
+
+@pytest.mark.parametrize("label,kw", [
+    ("recover_all", dict(path=3)),
+    ("tiny_capacity_overflow", dict(cand_capacity=256)),
+    ("high_threshold_underflow", dict(sample_rank_scale=0.02)),
+    ("low_threshold", dict(sample_rank_scale=1.7)),
+    ("small_sample", dict(sample_target=64)),
+    ("tiny_recover_budget", dict(cand_capacity=256, recover_budget_bytes=1)),
+])
+def test_paths_give_identical_bits(path_case, label, kw):
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    wl, d, base = path_case
+    _say("case", label)
+    idx, val = run_gpu(wl, d, options=opts(**kw))
+    assert np.array_equal(idx, base[0])
+    assert np.array_equal(val.view(np.uint32), base[1].view(np.uint32))
+    info = ftk.flashtopk_get_last_info()
+    if label in ("recover_all", "tiny_capacity_overflow", "high_threshold_underflow", "tiny_recover_budget"):
+        assert info["rows_recovered"] > 0, info
+
+
+def test_default_path_recovers_nothing_on_random_rows(path_case):
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    wl, d, base = path_case
+    run_gpu(wl, d)
+    info = ftk.flashtopk_get_last_info()
+    assert info["rows_recovered"] == 0, info
+    assert info["rows_sampled"] == 64
+
+
+def test_repeat_runs_identical(path_case):
+    wl, d, base = path_case
+    for _ in range(5):
+        idx, val = run_gpu(wl, d)
+        assert np.array_equal(idx, base[0])
+        assert np.array_equal(val.view(np.uint32), base[1].view(np.uint32))
+
+
+def test_recovered_rows_match_oracle(path_case):
+    wl, d, base = path_case
+    idx, val = run_gpu(wl, d, options=opts(path=3))
+    rep = parity(wl, idx, val, "tolerance")
+    assert rep["ok"], rep
+
+
+# ------------------------------------------------------------ edge cases ---
+
+def test_empty_short_and_degenerate_windows():
+    wl = workloads.integer(40, 3000, 50, "fp8", 401)
+    ks = np.zeros(40, np.int32)
+    ke = np.zeros(40, np.int32)
+    ks[:10], ke[:10] = 7, 7                       # empty
+    ks[10:20], ke[10:20] = 100, 100 + np.arange(10, 20)   # shorter than topk
+    ks[20:30], ke[20:30] = 2999, 3000             # one key
+    ks[30:], ke[30:] = np.arange(10) * 250, 3000  # long
+    wl = dict(wl, ks=ks, ke=ke)
+    idx, val = run_gpu(wl)
+    rep = parity(wl, idx, val, "exact")
+    assert rep["ok"], rep
+    assert np.all(idx[:10] == -1)
+
+
+def test_zero_scales_signed_zero_ties():
+    wl = workloads.integer(20, 1000, 30, "bf16", 402)
+    wl = dict(wl, kv_scales=np.zeros(1000, np.float32))
+    idx, val = run_gpu(wl)
+    rep = parity(wl, idx, val, "exact")
+    assert rep["ok"], rep
+    # all scores are +-0: the smallest indices of each window win
+    for t in range(20):
+        assert idx[t, 0] == wl["ks"][t]
+
+
+def test_no_scales_means_ones():
+    wl = workloads.integer(24, 2000, 40, "fp8", 403)
+    wl1 = dict(wl, kv_scales=None)
+    wl2 = dict(wl, kv_scales=np.ones(2000, np.float32))
+    a = run_gpu(wl1)
+    b = run_gpu(wl2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    rep = parity(wl1, a[0], a[1], "exact")
+    assert rep["ok"], rep
+
+
+def test_scale_doubling_metamorphic():
+    wl = workloads.gaussian(32, 5000, 77, "fp8", 404)
+    a = run_gpu(wl)
+    b = run_gpu(dict(wl, kv_scales=wl["kv_scales"] * np.float32(2)))
+    assert np.array_equal(a[0], b[0])
+    fin = a[0] >= 0
+    assert np.array_equal(b[1][fin], a[1][fin] * np.float32(2))
+
+
+def test_without_values_output():
+    import torch
+
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    wl = workloads.integer(30, 3000, 64, "fp8", 405)
+    d = to_device(wl)
+    idx = ftk.select(d["q"], d["kv"], d["weights"], d["ks"], d["ke"], d["kv_scales"], topk=64)
+    torch.cuda.synchronize()
+    o = run_oracle(wl)
+    assert np.array_equal(idx.cpu().numpy(), o[0])
+
+
+def test_bad_arguments_raise():
+    import torch
+
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    wl = workloads.integer(4, 100, 8, "fp8", 406)
+    d = to_device(wl)
+    with pytest.raises(ValueError):
+        ftk.select(d["q"].cpu(), d["kv"], d["weights"], d["ks"], d["ke"], topk=8)
+    with pytest.raises(ftk.FlashTopKError):
+        ftk.select(d["q"], d["kv"], d["weights"], d["ks"], d["ke"], topk=5000)
