@@ -1,0 +1,199 @@
+"""Benchmark of the fused indexer scoring + exact top-k path on one MI355X.
+
+One step = one flashtopk_select call over one causal prefill chunk: every
+query row is scored against every key of its window and its exact top-k is
+returned (FlashTopK README, "Quick start": 4096 queries over 128K FP8 keys,
+32 heads x 128, topk 2048).  Inputs are synthetic, seeded, and resident in
+HBM before the timed region starts.
+
+Prints one JSON line.  Besides the headline time it carries:
+  roofline      the fused score + filter kernel against the FP8 (or BF16)
+                dense MFMA peak: dense-equivalent FLOPs 2*32*128 per
+                (row, key) of every window, divided by that kernel's average
+                device time, measured with HIP events on the call's stream;
+  cpu_baseline  the CPU oracle (binary64, plain sort) on a bounded row sample
+                of the same workload, scaled to the whole chunk.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense MFMA peaks
+FLOP_PER_PAIR = 2 * 32 * 128
+METRIC = "ms per 4096-query x 128K-key FP8 top-2048 chunk; % of FP8 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, help="named workload 1..5 (4 is the headline)")
+    ap.add_argument("--integer-twin", action="store_true")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scan, 2 prune, 3 recover all")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--profile-steps", type=int, default=5)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, target_s):
+    """Times the oracle on an evenly spaced row sample; returns ms per chunk."""
+    import oracle
+
+    T = wl["q"].shape[0]
+    win = np.maximum(wl["ke"].astype(np.int64) - wl["ks"], 0)
+    total = float(win.sum())
+    threads = oracle.max_threads()
+    # calibrate on a few rows, then size the sample to the target time
+    probe = np.linspace(0, T - 1, num=min(T, max(2, threads)), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.select(wl["q"], wl["kv"], wl["dtype"], wl["kv_scales"], wl["weights"], wl["ks"], wl["ke"],
+                  wl["topk"], rows=probe)
+    dt = time.perf_counter() - t0
+    per_pair = dt / max(1.0, float(win[probe].sum()))
+    want_pairs = target_s / max(per_pair, 1e-12)
+    n = int(min(T, max(len(probe), want_pairs / max(1.0, total / T))))
+    rows = np.linspace(0, T - 1, num=n, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.select(wl["q"], wl["kv"], wl["dtype"], wl["kv_scales"], wl["weights"], wl["ks"], wl["ke"],
+                  wl["topk"], rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = float(win[rows].sum())
+    ms_chunk = dt * 1e3 * total / max(pairs, 1.0)
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": ms_chunk, "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {T} rows (evenly spaced), {pairs:.3g} of {total:.3g} (row, key) pairs, "
+                      f"{dt:.1f} s wall, scaled by pairs; {cpu}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is design-only",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    import sparse_attention_indexer_fp8_amd as ftk
+    from sparse_attention_indexer_fp8_amd import Options
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = workloads.config(args.workload, integer_twin=args.integer_twin)
+    T, S, topk, dt = wl["q"].shape[0], wl["kv"].shape[0], wl["topk"], wl["dtype"]
+    pairs = workloads.window_sum(wl)
+    print(f"bench: workload {wl['name']} T={T} S={S} topk={topk} dtype={dt} pairs={pairs}", file=sys.stderr,
+          flush=True)
+
+    if dt == "fp8":
+        q = torch.from_numpy(wl["q"]).to(dev).view(torch.float8_e4m3fn)
+        kv = torch.from_numpy(wl["kv"]).to(dev).view(torch.float8_e4m3fn)
+    else:
+        q = torch.from_numpy(wl["q"].view(np.int16)).to(dev).view(torch.bfloat16)
+        kv = torch.from_numpy(wl["kv"].view(np.int16)).to(dev).view(torch.bfloat16)
+    sc = None if wl["kv_scales"] is None else torch.from_numpy(wl["kv_scales"]).to(dev)
+    w = torch.from_numpy(wl["weights"]).to(dev)
+    ks = torch.from_numpy(wl["ks"]).to(dev)
+    ke = torch.from_numpy(wl["ke"]).to(dev)
+    idx = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    ftk.flashtopk_reserve(T, S, topk, ftk.FLASHTOPK_FP8_E4M3 if dt == "fp8" else ftk.FLASHTOPK_BF16)
+
+    opt = Options()
+    opt.path = args.path
+
+    def step(o=opt):
+        ftk.flashtopk_select_ex(q, kv, sc, w, ks, ke, topk, idx, val, options=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("bench: warmup done", file=sys.stderr, flush=True)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = start.elapsed_time(end) / args.steps
+    info = ftk.flashtopk_get_last_info()
+    print(f"bench: {ms:.3f} ms/step (wall {wall_ms:.3f})", file=sys.stderr, flush=True)
+
+    # Per-phase device times with HIP events on the library's stream.
+    popt = Options()
+    popt.path = args.path
+    popt.profile = 1
+    phases = {k: [] for k in ("ms_sample", "ms_tau", "ms_filter", "ms_triage", "ms_select", "ms_recover")}
+    for _ in range(args.profile_steps):
+        step(popt)
+        pi = ftk.flashtopk_get_last_info()
+        for k in phases:
+            phases[k].append(pi[k])
+    kern = {k[3:]: float(np.mean(v)) for k, v in phases.items()}
+    filt_ms = kern["filter"]
+    flops = float(FLOP_PER_PAIR) * pairs
+    peak = PEAK_TFLOPS[dt]
+    achieved = flops / (filt_ms * 1e-3) / 1e12 if filt_ms > 0 else 0.0
+    whole = flops / (ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "num_q": T, "num_kv": S, "topk": topk, "heads": 32, "dim": 128,
+                   "windows": "packed" if args.workload == 5 else "causal", "window_pairs": pairs,
+                   "path": {0: "auto", 1: "scan", 2: "prune", 3: "recover"}[args.path]},
+        "rows_per_s": round(T / (ms * 1e-3), 1),
+        "pct_mfma_peak": round(100.0 * whole / peak, 2),
+        "dense_equiv_tflops": round(whole, 1),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "pruned_key_fraction": info["pruned_keys"] / max(1, info["window_keys"]),
+        "rows_recovered": info["rows_recovered"],
+        "max_candidates": info["max_candidates"],
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "roofline": {"bound": "mfma", "kernel": "k_score<filter>", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "flops_per_launch": flops},
+    }
+    if not args.no_cpu:
+        print("bench: cpu oracle leg", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

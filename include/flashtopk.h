@@ -85,6 +85,9 @@ typedef struct flashtopk_options {
     int sample_target;        /* keys sampled per row for the threshold;
                                  0 = 2048 */
     int64_t recover_budget_bytes; /* scratch for dense rescoring; 0 = 1 GiB */
+    int profile;              /* nonzero: time each kernel phase with HIP
+                                 events on the call's stream (ms_* of
+                                 flashtopk_info); adds a few microseconds */
 } flashtopk_options;
 
 /* What the last call on a stream did (README, "Usage": last_info). */
@@ -105,6 +108,10 @@ typedef struct flashtopk_info {
     int64_t pruned_keys;        /* (row, key) pairs skipped by the score bound */
     int32_t cand_capacity;      /* capacity used */
     int32_t sample_target;      /* sample size used */
+    /* Device time of each phase in milliseconds when the call ran with
+     * options.profile set, else 0: strided-sample scoring, per-row threshold,
+     * fused score + filter, triage, candidate selection, dense recovery. */
+    float ms_sample, ms_tau, ms_filter, ms_triage, ms_select, ms_recover;
 } flashtopk_info;
 
 /* Exact top-k of the indexer score for every query row (see the file comment

@@ -42,6 +42,7 @@ class Options(ctypes.Structure):
         ("sample_rank_scale", ctypes.c_float),
         ("sample_target", ctypes.c_int),
         ("recover_budget_bytes", ctypes.c_int64),
+        ("profile", ctypes.c_int),
     ]
 
 
@@ -61,6 +62,12 @@ class Info(ctypes.Structure):
         ("pruned_keys", ctypes.c_int64),
         ("cand_capacity", ctypes.c_int32),
         ("sample_target", ctypes.c_int32),
+        ("ms_sample", ctypes.c_float),
+        ("ms_tau", ctypes.c_float),
+        ("ms_filter", ctypes.c_float),
+        ("ms_triage", ctypes.c_float),
+        ("ms_select", ctypes.c_float),
+        ("ms_recover", ctypes.c_float),
     ]
 
     def as_dict(self):

@@ -41,6 +41,7 @@ struct Workspace {
     hipStream_t stream = nullptr;
     DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch;
     unsigned long long *host_stats = nullptr;  // pinned
+    hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     flashtopk_info last{};
     bool has_last = false;
 };
@@ -107,6 +108,7 @@ struct Plan {
     int dtype, topk, cap, sample_target, path;
     float rank_scale;
     int64_t recover_budget;
+    int profile;
 };
 
 int resolve(Plan &p, const flashtopk_options *opt)
@@ -118,6 +120,7 @@ int resolve(Plan &p, const flashtopk_options *opt)
     p.sample_target = (opt && opt->sample_target > 0) ? opt->sample_target : kDefaultSampleTarget;
     p.rank_scale = (opt && opt->sample_rank_scale > 0.0f) ? opt->sample_rank_scale : 1.0f;
     p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
+    p.profile = (opt && opt->profile) ? 1 : 0;
     if (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE) p.path = FLASHTOPK_PATH_SCAN;
     return FLASHTOPK_OK;
 }
@@ -134,6 +137,24 @@ void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const Score
 {
     if (dtype == FLASHTOPK_FP8_E4M3) launch_score<kFP8>(mode, grid, st, a);
     else launch_score<kBF16>(mode, grid, st, a);
+}
+
+// Phase boundary i of a profiled call (no-op otherwise).
+void mark(Workspace &w, const Plan &p, int i, hipStream_t stream)
+{
+    if (!p.profile) return;
+    if (!w.ev[i]) (void)hipEventCreate(&w.ev[i]);
+    (void)hipEventRecord(w.ev[i], stream);
+}
+
+float phase_ms(Workspace &w, const Plan &p, int i)
+{
+    float ms = 0.0f;
+    if (p.profile && w.ev[i] && w.ev[i + 1] && hipEventElapsedTime(&ms, w.ev[i], w.ev[i + 1]) != hipSuccess) {
+        (void)hipGetLastError();
+        ms = 0.0f;
+    }
+    return ms;
 }
 
 int run(const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
@@ -175,7 +196,9 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.samp = (uint32_t *)w->samp.ptr;
     sa.sample_target = p.sample_target;
 
+    mark(*w, p, 0, stream);
     if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3(ntiles), stream, sa);
+    mark(*w, p, 1, stream);
 
     TauArgs ta{};
     ta.ks = ks;
@@ -189,8 +212,10 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     ta.tau = (float *)w->tau.ptr;
     ta.cnt = (uint32_t *)w->cnt.ptr;
     k_tau<<<dim3((unsigned)T), kSelThreads, 0, stream>>>(ta);
+    mark(*w, p, 2, stream);
 
     if (!recover_all) launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
+    mark(*w, p, 3, stream);
 
     TriageArgs tr{};
     tr.ks = ks;
@@ -205,6 +230,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     tr.nflagged = (int32_t *)w->nflagged.ptr;
     tr.stats = (unsigned long long *)w->stats.ptr;
     k_triage<<<1, 1024, 0, stream>>>(tr);
+    mark(*w, p, 4, stream);
 
     SelectArgs se{};
     se.ks = ks;
@@ -219,6 +245,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     se.out_idx = out_idx;
     se.out_val = out_val;
     k_select<false><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
+    mark(*w, p, 5, stream);
 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_status(e);
@@ -228,6 +255,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     if (e != hipSuccess) return hip_status(e);
 
     const int64_t R = (int64_t)w->host_stats[kStFlagged];
+    mark(*w, p, 6, stream);  // recovery timed from here (0 when nothing is flagged)
     if (R > 0) {
         // Dense rescoring of flagged rows, in batches that fit the budget.
         const int64_t stride = std::max<int64_t>(S, 1);
@@ -251,7 +279,22 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             k_select<true><<<dim3((unsigned)rcap), kSelThreads, 0, stream>>>(se);
         }
         e = hipGetLastError();
-        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    float ms_rec = 0.0f;
+    if (p.profile) {
+        hipEvent_t end = nullptr;
+        (void)hipEventCreate(&end);
+        (void)hipEventRecord(end, stream);
+        (void)hipEventSynchronize(end);
+        if (hipEventElapsedTime(&ms_rec, w->ev[6], end) != hipSuccess) {
+            (void)hipGetLastError();
+            ms_rec = 0.0f;
+        }
+        (void)hipEventDestroy(end);
+    }
+    if (R > 0) {
+        e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_status(e);
     }
 
@@ -272,6 +315,12 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     info.pruned_keys = 0;
     info.cand_capacity = p.cap;
     info.sample_target = p.sample_target;
+    info.ms_sample = phase_ms(*w, p, 0);
+    info.ms_tau = phase_ms(*w, p, 1);
+    info.ms_filter = phase_ms(*w, p, 2);
+    info.ms_triage = phase_ms(*w, p, 3);
+    info.ms_select = phase_ms(*w, p, 4);
+    info.ms_recover = R > 0 ? ms_rec : 0.0f;
     w->has_last = true;
     return FLASHTOPK_OK;
 }
@@ -364,6 +413,8 @@ void flashtopk_release(void)
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);
+        for (hipEvent_t &ev : w->ev)
+            if (ev) (void)hipEventDestroy(ev);
         (void)hipSetDevice(prev);
         delete w;
     }

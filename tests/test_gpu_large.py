@@ -1,0 +1,67 @@
+"""Full-size workloads on the GPU, in the launch configuration bench.py times,
+checked against the oracle on sampled rows (MI355X only).
+
+* 4096 queries x 128K FP8 keys, causal, topk 4096 (flat Gaussian rows) and
+  topk 2048 (heavy-tailed rows);
+* 64K x 64K BF16 packed sequence of four documents, topk 512, rows shorter
+  than topk padded;
+* the integer-valued twins of all three, checked bit-exact.
+Sampled rows: the first and last rows, random rows, and (packed) rows at
+every document start and in the short-window region.
+"""
+import numpy as np
+import pytest
+
+import workloads
+
+from gpu_util import parity, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(wl, extra=()):
+    T = wl["q"].shape[0]
+    rows = sample_rows(T, n_mid=20, edge=6, seed=T)
+    return np.unique(np.concatenate([rows, np.asarray(extra, np.int64)])).astype(np.int64)
+
+
+def _packed_extra():
+    starts = np.cumsum((0,) + workloads.PACKED_DOCS[:-1])
+    extra = []
+    for s in starts:
+        extra += [s, s + 1, s + 255, s + 510, s + 511, s + 512, s + 2047, s + 2048, s + 2049]
+    return extra
+
+
+CASES = [
+    ("untrained_fp8_k4096", 3, False, "tolerance"),
+    ("trained_fp8_k2048", 4, False, "tolerance"),
+    ("packed_bf16_k512", 5, False, "tolerance"),
+    ("untrained_int_fp8_k4096", 3, True, "exact"),
+    ("trained_int_fp8_k2048", 4, True, "exact"),
+    ("packed_int_bf16_k512", 5, True, "exact"),
+]
+
+
+@pytest.mark.parametrize("name,n,twin,mode", CASES, ids=[c[0] for c in CASES])
+def test_full_size_sampled_rows(name, n, twin, mode):
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    print("case", name, flush=True)
+    wl = workloads.config(n, integer_twin=twin)
+    idx, val = run_gpu(wl)
+    info = ftk.flashtopk_get_last_info()
+    print("info", info, flush=True)
+    rows = _rows(wl, _packed_extra() if n == 5 else ())
+    rep = parity(wl, idx, val, mode, rows=rows)
+    assert rep["ok"], rep
+    # every row, sampled or not, has the right structure
+    import checker
+
+    T = wl["q"].shape[0]
+    for t in range(0, T, max(1, T // 512)):
+        assert not checker.structure_failures(idx[t], val[t], wl["ks"][t], wl["ke"][t], wl["topk"]), t
+    if n == 5:
+        short = (wl["ke"] - wl["ks"]) < wl["topk"]
+        assert short.sum() == 4 * 511
+        assert np.all(idx[short][:, -1] == -1)
