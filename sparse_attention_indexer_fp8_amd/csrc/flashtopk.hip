@@ -1,6 +1,7 @@
 // C ABI of the fused indexer top-k library (declared in include/flashtopk.h).
 //
 // Launch sequence of one call, all on the caller's stream:
+//   0. k_qbar           (FP8) head-weighted query sums, split into FP8 parts
 //   1. k_score<sample>  strided-sample scores of every long row     (MFMA)
 //   2. k_tau            per-row threshold = r-th largest sample score
 //   3. k_score<filter>  fused score + threshold filter -> candidates (MFMA, hot)
@@ -39,7 +40,7 @@ struct DevBuf {
 struct Workspace {
     int device = -1;
     hipStream_t stream = nullptr;
-    DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch;
+    DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch, qbar, qscale, sigh;
     unsigned long long *host_stats = nullptr;  // pinned
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     flashtopk_info last{};
@@ -171,6 +172,12 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     if ((st = ensure(*w, w->nflagged, sizeof(int32_t)))) return st;
     if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
     const bool recover_all = p.path == FLASHTOPK_PATH_RECOVER;
+    const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
+    if (fp8) {
+        if ((st = ensure(*w, w->qbar, (size_t)T * kQbarParts * kDim))) return st;
+        if ((st = ensure(*w, w->qscale, sizeof(float) * T))) return st;
+    }
+    if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(S + 64)))) return st;
     if (!recover_all) {
         if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * p.cap))) return st;
         if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * p.sample_target))) return st;
@@ -183,11 +190,14 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.q = (const uint8_t *)q;
     sa.kv = (const uint8_t *)kv;
     sa.sigma = kv_scales;
+    sa.sigh = (const float *)w->sigh.ptr;
     sa.w = weights;
     sa.ks = ks;
     sa.ke = ke;
-    sa.num_q = T;
-    sa.num_kv = S;
+    sa.num_q = (int)T;
+    sa.num_kv = (int)S;
+    sa.qbar = (const uint8_t *)w->qbar.ptr;
+    sa.qscale = (const float *)w->qscale.ptr;
     sa.ntiles = ntiles;
     sa.cap = p.cap;
     sa.tau = (const float *)w->tau.ptr;
@@ -197,6 +207,14 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.sample_target = p.sample_target;
 
     mark(*w, p, 0, stream);
+    {
+        const unsigned nb = (unsigned)std::min<int64_t>(1024, (S + 64 + 255) / 256);
+        if (fp8) k_sigh<kFP8><<<nb, 256, 0, stream>>>(kv_scales, (int)S, (float *)w->sigh.ptr);
+        else k_sigh<kBF16><<<nb, 256, 0, stream>>>(kv_scales, (int)S, (float *)w->sigh.ptr);
+    }
+    if (fp8)
+        k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T, (uint8_t *)w->qbar.ptr,
+                                                                 (float *)w->qscale.ptr);
     if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3(ntiles), stream, sa);
     mark(*w, p, 1, stream);
 
@@ -379,6 +397,10 @@ int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, vo
     if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
     if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * cap))) return st;
     if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * kDefaultSampleTarget))) return st;
+    if (dtype == FLASHTOPK_FP8_E4M3) {
+        if ((st = ensure(*w, w->qbar, (size_t)T * kQbarParts * kDim))) return st;
+        if ((st = ensure(*w, w->qscale, sizeof(float) * T))) return st;
+    }
     (void)max_kv;
     return FLASHTOPK_OK;
 }
@@ -409,7 +431,7 @@ void flashtopk_release(void)
         (void)hipSetDevice(w->device);
         (void)hipStreamSynchronize(w->stream);
         DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowflag, &w->rowlist, &w->nflagged, &w->stats,
-                          &w->cand, &w->samp, &w->scratch};
+                          &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh};
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);

@@ -20,7 +20,7 @@ constexpr int kSub = 4;
 constexpr int kStepKeys = 16 * kSub;      // 64 keys per wave step
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;     // 512
-constexpr int kChunkKeys = 4096;          // keys per work item
+constexpr int kChunkKeys = 8192;          // keys per work item
 
 constexpr int kFP8 = 0;
 constexpr int kBF16 = 1;
@@ -55,6 +55,19 @@ __device__ __forceinline__ float float_of_ord(uint32_t u)
 __device__ __forceinline__ uint64_t sel_key(float score, int32_t s)
 {
     return ((uint64_t)ord_of(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
+}
+
+// Raw candidate as the scoring kernels write it: the binary32 score bits in
+// the low word, the key index in the high word.  The selection kernels turn
+// it into the ordered key above when they load it.
+__device__ __forceinline__ uint64_t raw_cand(float score, int32_t s)
+{
+    return ((uint64_t)(uint32_t)s << 32) | (uint64_t)__float_as_uint(score);
+}
+
+__device__ __forceinline__ uint64_t key_of_raw(uint64_t r)
+{
+    return sel_key(__uint_as_float((uint32_t)r), (int32_t)(r >> 32));
 }
 
 __device__ __forceinline__ int32_t key_index(uint64_t k)

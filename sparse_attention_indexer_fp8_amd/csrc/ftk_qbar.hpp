@@ -1,0 +1,80 @@
+// Head-weighted query sum for the FP8 score path.
+//
+// With ReLU(x) = (x + |x|) / 2 the indexer score (FlashTopK README, "Quick
+// start", indexer-score equation) splits into
+//     sum_h w[t,h] ReLU(x_h) = ( sum_h w[t,h] |x_h|  +  qbar[t] . kv[s] ) / 2,
+//     qbar[t] = sum_h w[t,h] q[t,h,:],
+// an identity of real numbers.  The |x_h| half costs one fused multiply-add
+// per (row, head, key) in the vector ALUs, half of max + multiply-add; the
+// linear half is one more dot product per (row, key), done on the matrix
+// cores.  The FP8 MFMA takes 8-bit operands only, so qbar (binary32) is
+// scaled by a per-row power of two 2^e (largest component in [128, 256)) and
+// written as the sum of three FP8 E4M3 parts, each the truncation of what the
+// previous parts left over; the matrix cores then accumulate
+// sum_p part_p . kv[s] and the kernel multiplies by 2^-e.  Three parts carry
+// 12 significant bits of every component: exact whenever qbar's components
+// have at most 12 (integer-valued operands with dyadic weights), and about
+// 2^-12 relative to the row's largest component otherwise.
+#pragma once
+
+#include "ftk_common.hpp"
+
+namespace ftk {
+
+constexpr int kQbarParts = 3;
+
+// OCP E4M3 ("fn") code -> binary32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+{
+    const uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 0xFu, m = c & 0x7u;
+    if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));  // m * 2^-9
+    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// binary32 with |v| <= 448 -> E4M3 code, truncating toward zero.
+__device__ __forceinline__ uint32_t f32_to_e4m3_trunc(float v)
+{
+    const uint32_t b = __float_as_uint(v), s = (b >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a < 0.001953125f) return s;                        // below the smallest subnormal
+    const int E = (int)((b >> 23) & 0xFFu) - 127;
+    if (E < -6) return s | (uint32_t)(a * 512.0f);         // subnormal: trunc(a / 2^-9)
+    return s | ((uint32_t)(E + 7) << 3) | ((b >> 20) & 7u);  // normal: top 3 mantissa bits
+}
+
+// One wave per query row; lane l owns dimensions 2l and 2l+1.  Writes
+// parts[t][p][d] (E4M3 codes) and qscale[t] = 2^-e.
+__global__ __launch_bounds__(256) void k_qbar(const uint8_t *q, const float *w, int64_t num_q, uint8_t *parts,
+                                              float *qscale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= num_q) return;
+    const uint8_t *qr = q + t * kHeads * kDim + 2 * lane;
+    float v0 = 0.0f, v1 = 0.0f;
+    for (int h = 0; h < kHeads; ++h) {
+        const float wh = w[t * kHeads + h];
+        const uint32_t c = *reinterpret_cast<const uint16_t *>(qr + h * kDim);
+        v0 = __builtin_fmaf(wh, e4m3_to_f32(c & 0xFFu), v0);
+        v1 = __builtin_fmaf(wh, e4m3_to_f32(c >> 8), v1);
+    }
+    float m = fmaxf(fabsf(v0), fabsf(v1));
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    int k = 0;
+    if (m > 0.0f) {
+        int E;
+        frexpf(m, &E);  // m = f * 2^E, f in [0.5, 1)
+        k = 8 - E;      // m * 2^k in [128, 256)
+    }
+    float r0 = ldexpf(v0, k), r1 = ldexpf(v1, k);
+    uint8_t *out = parts + t * kQbarParts * kDim + 2 * lane;
+    for (int p = 0; p < kQbarParts; ++p) {
+        const uint32_t c0 = f32_to_e4m3_trunc(r0), c1 = f32_to_e4m3_trunc(r1);
+        r0 -= e4m3_to_f32(c0);  // exact: the part holds the leading bits of r0
+        r1 -= e4m3_to_f32(c1);
+        *reinterpret_cast<uint16_t *>(out + p * kDim) = (uint16_t)(c0 | (c1 << 8));
+    }
+    if (lane == 0) qscale[t] = ldexpf(1.0f, -k);
+}
+
+}  // namespace ftk

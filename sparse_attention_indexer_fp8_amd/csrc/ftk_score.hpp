@@ -18,17 +18,26 @@
 // one 16x16 MFMA per 16-key subtile with A = 16 keys (M rows, read straight
 // from HBM/L2 into registers) and B = the 16 queries' head-h vectors (N
 // columns, read from LDS).  The 16x16 fp32 output leaves each lane four keys
-// of ONE query, so the ReLU, the w[t,h] weighting and the sum over heads all
-// stay inside the lane: acc = fma(w[t,h], ReLU(x), acc) for h = 0..31 in
-// order, then I = sigma[s] * acc.  The [T, S] score matrix never reaches HBM.
-//   FP8:  v_mfma_f32_16x16x128_f8f6f4, one MFMA covers the full d = 128.
-//   BF16: v_mfma_f32_16x16x32_bf16, four chained MFMAs cover d = 128.
+// of ONE query, so the nonlinearity, the w[t,h] weighting and the sum over
+// heads all stay inside the lane.  The [T, S] score matrix never reaches HBM.
+//
+//   FP8 (v_mfma_f32_16x16x128_f8f6f4, one MFMA per 128-dim dot product): the
+//   score is evaluated as sigma/2 * (sum_h w |x_h| + qbar . k) (see
+//   ftk_qbar.hpp), one vector FMA per (row, head, key) plus three MFMAs per
+//   (row, key) on the FP8 parts of qbar, staged in LDS as three extra heads.
+//   FP8 MFMAs are fast enough that the vector ALUs would otherwise bound the
+//   loop.
+//   BF16 (v_mfma_f32_16x16x32_bf16, four chained MFMAs per dot product): the
+//   matrix cores are the bound, so the plain form sigma * sum_h w ReLU(x_h)
+//   is kept (ReLU as an integer max on the bit pattern, then an FMA).
+//
 // Both operands of an MFMA use the same assignment of the 128 dimensions to
 // (lane group, byte) slots -- lane group g holds dimensions [32g, 32g+32) --
 // so the contraction covers every dimension exactly once.
 #pragma once
 
 #include "ftk_common.hpp"
+#include "ftk_qbar.hpp"
 
 namespace ftk {
 
@@ -36,19 +45,28 @@ constexpr int kModeFilter = 0;
 constexpr int kModeSample = 1;
 constexpr int kModeDense = 2;
 
+// q-tile "heads" in LDS: the 32 heads, plus the qbar parts on the FP8 path.
+template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? kHeads + kQbarParts : kHeads; };
+
 // Candidate ring per (wave, query) in filter mode: survivors are staged in LDS
-// and flushed to the row's candidate list with one atomic per query.
-template <int DT> struct RingEntries { static constexpr int value = DT == kFP8 ? 88 : 24; };
+// and flushed to the row's candidate list with one atomic per query.  The
+// stride between the 16 rings of a wave is odd in 8-byte entries (RING + 1),
+// so the rings start on distinct LDS banks.
+template <int DT> struct RingEntries { static constexpr int value = DT == kFP8 ? 80 : 24; };
+template <int DT> struct RingStride { static constexpr int value = RingEntries<DT>::value + 1; };
 
 struct ScoreArgs {
     const uint8_t *q;          // [num_q, 32, 128] codes
     const uint8_t *kv;         // [num_kv, 128] codes
     const float *sigma;        // [num_kv] or null
+    const float *sigh;         // [num_kv + 64]: sigma (BF16) or sigma / 2 (FP8), zero padded
     const float *w;            // [num_q, 32]
     const int32_t *ks;         // [num_q]
     const int32_t *ke;         // [num_q]
-    int64_t num_q;
-    int64_t num_kv;
+    const uint8_t *qbar;       // [num_q, 3, 128] FP8 parts (FP8 path)
+    const float *qscale;       // [num_q] 2^-e of the parts (FP8 path)
+    int num_q;
+    int num_kv;
     int ntiles;                // tiles along the grid's fast index
     int cap;                   // candidate capacity per row
     // filter mode
@@ -75,17 +93,16 @@ template <> struct KFrag<kFP8> { v8i a; };
 template <> struct KFrag<kBF16> { v4i a[4]; };
 
 // Key row p, lane group g: dimensions [32g, 32g+32).
-__device__ __forceinline__ void load_kfrag(KFrag<kFP8> &f, const uint8_t *kv, int64_t p, int g)
+__device__ __forceinline__ void load_kfrag(KFrag<kFP8> &f, const uint8_t *kv, int p, int g)
 {
-    const v4i *src = reinterpret_cast<const v4i *>(kv + p * 128 + 32 * g);
-    v4i lo = src[0];
-    v4i hi = src[1];
+    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 128 + 32 * g);
+    const v4i lo = src[0], hi = src[1];
     f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, int64_t p, int g)
+__device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, int p, int g)
 {
-    const v4i *src = reinterpret_cast<const v4i *>(kv + p * 256 + 64 * g);
+    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 256 + 64 * g);
 #pragma unroll
     for (int m = 0; m < 4; ++m) f.a[m] = src[m];
 }
@@ -94,37 +111,57 @@ __device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, i
 // consecutive 16-byte slots, slot (h, sub, lane) at ((h*SUB + sub)*64 + lane)*16
 // where lane = n + 16 g (query n, lane group g) and sub indexes the 16-byte
 // pieces of the lane's 32 (FP8) or 64 (BF16) bytes.  Each ds_read_b128 of a
-// head reads 1 KiB of consecutive LDS, free of bank conflicts.
+// head reads 1 KiB of consecutive LDS, free of bank conflicts.  On the FP8
+// path heads 32..34 hold the qbar parts.
 template <int DT>
-__device__ __forceinline__ void stage_q_tile(uint8_t *s_q, const uint8_t *q, const int *s_row)
+__device__ __forceinline__ void stage_q_tile(uint8_t *s_q, const ScoreArgs &a, const int *s_row)
 {
     constexpr int RB = RowBytes<DT>::value;
     constexpr int CPR = RB / 16;    // 16-byte pieces per head row
     constexpr int SUB = CPR / 4;    // pieces per lane group
-    constexpr int NCH = kTileQ * kHeads * CPR;
-    for (int id = threadIdx.x; id < NCH; id += kThreads) {
-        int n = id / (kHeads * CPR);
-        int h = (id / CPR) % kHeads;
-        int c = id % CPR;
-        int t = s_row[n];
+    constexpr int TH = TileHeads<DT>::value;
+    constexpr int NCH = kTileQ * TH * CPR;
+    for (int id = threadIdx.x; id < NCH; id += blockDim.x) {
+        const int n = id / (TH * CPR);
+        const int h = (id / CPR) % TH;
+        const int c = id % CPR;
+        const int t = s_row[n];
         v4i v = {0, 0, 0, 0};
-        if (t >= 0) v = *reinterpret_cast<const v4i *>(q + ((int64_t)t * kHeads + h) * RB + c * 16);
-        int sub = c % SUB, g = c / SUB;
+        if (t >= 0) {
+            const uint8_t *src = (h < kHeads) ? a.q + ((int64_t)t * kHeads + h) * RB
+                                              : a.qbar + ((int64_t)t * kQbarParts + (h - kHeads)) * RB;
+            v = *reinterpret_cast<const v4i *>(src + c * 16);
+        }
+        const int sub = c % SUB, g = c / SUB;
         *reinterpret_cast<v4i *>(s_q + ((h * SUB + sub) * 64 + n + 16 * g) * 16) = v;
     }
 }
 
-// Scores of kSub subtiles x 4 keys for the lane's query, accumulated over all
-// heads.  kf: the lane's key fragments; s_w: the tile's weights in LDS,
-// s_w[h * 16 + n] = w[row n, h].
+// ---------------------------------------------------------------------------
+// One 64-key step of one wave: score kSub subtiles x 4 keys for the lane's
+// query.  s_w holds the tile's weights, s_w[h * 16 + n] = w[row n, h].
 //
-// Software pipeline over heads: the MFMAs of head h are issued while the VALU
-// epilogue (ReLU, weight, sum) of head h-1 runs, so the matrix cores and the
-// vector ALUs work at the same time; the q fragment and weight of head h+1 are
-// read from LDS one head ahead.  The head loop is kept rolled so each head is
-// its own scheduling region: the compiler cannot hoist every head's operands
-// (or sink every epilogue), which would need far more than 256 registers.
-__device__ __forceinline__ void head_epilogue(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
+// Software pipeline over heads: the MFMAs of a head are issued while the VALU
+// epilogue of an earlier head runs, so the matrix cores and the vector ALUs
+// work at the same time; result sets rotate so no copies are needed.  The
+// head loop stays rolled so each group of heads is its own scheduling region:
+// the compiler cannot hoist every head's operands (or sink every epilogue),
+// which would need far more than 256 registers.
+
+struct StepOut {
+    float acc[kSub][4];   // FP8: sum_h w |x|;  BF16: sum_h w ReLU(x)
+    v4f lin[kSub];        // FP8: sum_p part_p . k (unscaled qbar . k)
+};
+
+__device__ __forceinline__ void epi_abs(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
+{
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[kt][i] = __builtin_fmaf(w, __builtin_fabsf(x[kt][i]), acc[kt][i]);
+}
+
+__device__ __forceinline__ void epi_relu(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
 {
 #pragma unroll
     for (int kt = 0; kt < kSub; ++kt)
@@ -133,43 +170,53 @@ __device__ __forceinline__ void head_epilogue(float (&acc)[kSub][4], const v4f (
 }
 
 // qp points at the lane's slot of head 0 (s_q + lane * 16); head h adds h * 2 KiB.
-__device__ __forceinline__ void mfma_fp8_heads(v4f (&x)[kSub], const KFrag<kFP8> (&kf)[kSub], const uint8_t *qp)
+__device__ __forceinline__ void mfma_fp8_head(v4f (&x)[kSub], const KFrag<kFP8> (&kf)[kSub], const uint8_t *qp,
+                                              const v4f (&c)[kSub])
 {
-    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
     const v4i lo = *reinterpret_cast<const v4i *>(qp);
     const v4i hi = *reinterpret_cast<const v4i *>(qp + 1024);
     const v8i qf = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
     for (int kt = 0; kt < kSub; ++kt)
-        x[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt].a, qf, z, 0, 0, 0, 0, 0, 0);
+        x[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt].a, qf, c[kt], 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ void score_step(float (&acc)[kSub][4], const KFrag<kFP8> (&kf)[kSub],
-                                           const uint8_t *s_q, const float *s_w, int lane)
+__device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[kSub], const uint8_t *s_q,
+                                           const float *s_w, int lane)
 {
     constexpr int HB = 2048;  // LDS bytes per head of the q tile
+    const v4f z[kSub] = {};
 #pragma unroll
     for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[kt][i] = 0.0f;
+        for (int i = 0; i < 4; ++i) o.acc[kt][i] = 0.0f;
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
-    // Two result sets alternate so no copies are needed between heads.
-    v4f xa[kSub], xb[kSub];
-    mfma_fp8_heads(xa, kf, qp);
+    // Three result sets rotate: the epilogue of head h-2 runs while the MFMAs
+    // of head h execute, so no epilogue waits on an MFMA still in flight.
+    v4f xa[kSub], xb[kSub], xc[kSub];
+    mfma_fp8_head(xa, kf, qp, z);
+    mfma_fp8_head(xb, kf, qp + HB, z);
 #pragma unroll 1
-    for (int h = 1; h < kHeads - 1; h += 2) {
-        const float w0 = wp[0], w1 = wp[kTileQ];
-        mfma_fp8_heads(xb, kf, qp + HB);
-        head_epilogue(acc, xa, w0);
-        mfma_fp8_heads(xa, kf, qp + 2 * HB);
-        head_epilogue(acc, xb, w1);
-        qp += 2 * HB;
-        wp += 2 * kTileQ;
+    for (int h = 2; h + 2 < kHeads; h += 3) {
+        const float w0 = wp[0], w1 = wp[kTileQ], w2 = wp[2 * kTileQ];
+        mfma_fp8_head(xc, kf, qp + 2 * HB, z);
+        epi_abs(o.acc, xa, w0);
+        mfma_fp8_head(xa, kf, qp + 3 * HB, z);
+        epi_abs(o.acc, xb, w1);
+        mfma_fp8_head(xb, kf, qp + 4 * HB, z);
+        epi_abs(o.acc, xc, w2);
+        qp += 3 * HB;
+        wp += 3 * kTileQ;
     }
-    mfma_fp8_heads(xb, kf, qp + HB);
-    head_epilogue(acc, xa, wp[0]);
-    head_epilogue(acc, xb, wp[kTileQ]);
+    // Heads 30 and 31 remain in xa and xb.  The linear half: qbar parts are
+    // heads 32..34, accumulated in the MFMA.
+    const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
+    mfma_fp8_head(o.lin, kf, pp, z);
+    epi_abs(o.acc, xa, wp[0]);
+    mfma_fp8_head(o.lin, kf, pp + HB, o.lin);
+    epi_abs(o.acc, xb, wp[kTileQ]);
+    mfma_fp8_head(o.lin, kf, pp + 2 * HB, o.lin);
 }
 
 __device__ __forceinline__ v4f mfma_bf16_d128(const KFrag<kBF16> &k, const v4i (&qf)[4])
@@ -183,7 +230,7 @@ __device__ __forceinline__ v4f mfma_bf16_d128(const KFrag<kBF16> &k, const v4i (
 }
 
 // qp points at the lane's slot of head 0 (s_q + lane * 16); head h adds h * 4 KiB.
-__device__ __forceinline__ void mfma_bf16_heads(v4f (&x)[kSub], const KFrag<kBF16> (&kf)[kSub], const uint8_t *qp)
+__device__ __forceinline__ void mfma_bf16_head(v4f (&x)[kSub], const KFrag<kBF16> (&kf)[kSub], const uint8_t *qp)
 {
     v4i qf[4];
 #pragma unroll
@@ -192,32 +239,63 @@ __device__ __forceinline__ void mfma_bf16_heads(v4f (&x)[kSub], const KFrag<kBF1
     for (int kt = 0; kt < kSub; ++kt) x[kt] = mfma_bf16_d128(kf[kt], qf);
 }
 
-__device__ __forceinline__ void score_step(float (&acc)[kSub][4], const KFrag<kBF16> (&kf)[kSub],
-                                           const uint8_t *s_q, const float *s_w, int lane)
+__device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[kSub], const uint8_t *s_q,
+                                           const float *s_w, int lane)
 {
+    // One head is 16 MFMAs here, so a one-head lag already covers the MFMA
+    // latency and two result sets suffice (the key fragments take 128
+    // registers on this path).
     constexpr int HB = 4096;
 #pragma unroll
     for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[kt][i] = 0.0f;
+        for (int i = 0; i < 4; ++i) o.acc[kt][i] = 0.0f;
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
     v4f xa[kSub], xb[kSub];
-    mfma_bf16_heads(xa, kf, qp);
+    mfma_bf16_head(xa, kf, qp);
 #pragma unroll 1
     for (int h = 1; h < kHeads - 1; h += 2) {
         const float w0 = wp[0], w1 = wp[kTileQ];
-        mfma_bf16_heads(xb, kf, qp + HB);
-        head_epilogue(acc, xa, w0);
-        mfma_bf16_heads(xa, kf, qp + 2 * HB);
-        head_epilogue(acc, xb, w1);
+        mfma_bf16_head(xb, kf, qp + HB);
+        epi_relu(o.acc, xa, w0);
+        mfma_bf16_head(xa, kf, qp + 2 * HB);
+        epi_relu(o.acc, xb, w1);
         qp += 2 * HB;
         wp += 2 * kTileQ;
     }
-    mfma_bf16_heads(xb, kf, qp + HB);
-    head_epilogue(acc, xa, wp[0]);
-    head_epilogue(acc, xb, wp[kTileQ]);
+    mfma_bf16_head(xb, kf, qp + HB);
+    epi_relu(o.acc, xa, wp[0]);
+    epi_relu(o.acc, xb, wp[kTileQ]);
 }
+
+// The score of output element (kt, i) from the step accumulators; sh is the
+// key's scale factor as stored in sigh (sigma / 2 on the FP8 path).
+// FP8: sigma/2 * (qbar . k + sum_h w |x|) with qbar . k = lin * qscale.
+template <int DT>
+__device__ __forceinline__ float score_of(const StepOut &o, int kt, int i, float qsc, float sh)
+{
+    if (DT == kFP8) return __builtin_fmaf(o.lin[kt][i], qsc, o.acc[kt][i]) * sh;
+    return o.acc[kt][i] * sh;
+}
+
+// Scale factor of key p as stored in sigh, from the caller's kv_scales.
+template <int DT>
+__device__ __forceinline__ float sigh_of(const float *sigma, int p)
+{
+    const float sg = sigma ? sigma[p] : 1.0f;
+    return DT == kFP8 ? sg * 0.5f : sg;
+}
+
+// Fills sigh[0, num_kv + 64): the per-key factor of score_of, zero past the end.
+template <int DT>
+__global__ __launch_bounds__(256) void k_sigh(const float *sigma, int num_kv, float *sigh)
+{
+    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < num_kv + 64; p += gridDim.x * blockDim.x)
+        sigh[p] = p < num_kv ? sigh_of<DT>(sigma, p) : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
 
 // Wave-local LDS ordering: wait for this wave's LDS operations to finish
 // before other lanes of the wave read what they wrote.
@@ -230,7 +308,7 @@ __device__ __forceinline__ void wave_lds_sync()
 // Moves a wave's staged candidates to the rows' candidate lists: one atomic
 // per query reserves the slots, then the wave copies.  Slots past the
 // capacity are dropped; the counter still counts them (overflow triage).
-template <int RING>
+template <int RS>
 __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_cnt, int n, int g, int t,
                                            uint32_t *cnt, uint64_t *cand, int cap)
 {
@@ -240,7 +318,7 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
     base = __shfl(base, n);
     if (t >= 0) {
         for (uint32_t k = g; k < ring_cnt; k += 4) {
-            uint64_t v = ring[n * RING + k];
+            const uint64_t v = ring[n * RS + k];
             if (base + k < (uint32_t)cap) cand[(int64_t)t * cap + base + k] = v;
         }
     }
@@ -253,17 +331,20 @@ template <int DT, int MODE>
 __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
 {
     constexpr int RB = RowBytes<DT>::value;
+    constexpr int TH = TileHeads<DT>::value;
     constexpr int RING = (MODE == kModeFilter) ? RingEntries<DT>::value : 1;
-    // One LDS block carved by hand so the q tile sits at offset 0 and every
-    // q-fragment read fits the 16-bit immediate offset of ds_read.
-    constexpr int QB = kTileQ * kHeads * RB;
+    constexpr int RS = (MODE == kModeFilter) ? RingStride<DT>::value : 1;
+    // One LDS block carved by hand: weights (2 KiB) then the q tile, so the
+    // weight and q-fragment reads of the head loop fit the 16-bit immediate
+    // offset of ds_read; the candidate rings last.
+    constexpr int QB = kTileQ * TH * RB;
     constexpr int WB = kHeads * kTileQ * 4;
-    constexpr int RGB = (MODE == kModeFilter) ? kWaves * kTileQ * RING * 8 : 0;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[QB + WB + RGB];
+    constexpr int RGB = (MODE == kModeFilter) ? kWaves * kTileQ * RS * 8 : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[WB + QB + RGB];
     __shared__ int s_row[kTileQ], s_ks[kTileQ], s_ke[kTileQ], s_d[kTileQ];
-    uint8_t *s_q = smem;
-    float *s_w = reinterpret_cast<float *>(smem + QB);
-    uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + QB + WB);
+    float *s_w = reinterpret_cast<float *>(smem);
+    uint8_t *s_q = smem + WB;
+    uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + WB + QB);
 
     int tile, chunk;
     if (MODE == kModeSample) {
@@ -275,12 +356,13 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
     }
 
     if (threadIdx.x < kTileQ) {
-        int n = threadIdx.x, t = -1;
+        const int n = threadIdx.x;
+        int t = -1;
         if (MODE == kModeDense) {
-            int e = tile * kTileQ + n;
+            const int e = tile * kTileQ + n;
             if (e < a.row_limit && a.row_base + e < *a.nrows) t = a.rowlist[a.row_base + e];
         } else {
-            int64_t tt = (int64_t)tile * kTileQ + n;
+            const int64_t tt = (int64_t)tile * kTileQ + n;
             if (tt < a.num_q) t = (int)tt;
         }
         int lo = 0, hi = 0, d = 1;
@@ -304,13 +386,16 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
     }
     __syncthreads();
 
-    // Union of the tile's windows; the lattice stride of the tile's samples.
-    int lo = 0x7fffffff, hi = 0, dmin = 0x40000000;
+    // Union (lo, hi) and intersection (ilo, ihi) of the tile's windows; the
+    // lattice stride of the tile's samples.
+    int lo = 0x7fffffff, hi = 0, ilo = 0, ihi = 0x7fffffff, dmin = 0x40000000;
 #pragma unroll
     for (int n = 0; n < kTileQ; ++n) {
         if (s_row[n] >= 0 && s_ke[n] > s_ks[n]) {
             lo = min(lo, s_ks[n]);
             hi = max(hi, s_ke[n]);
+            ilo = max(ilo, s_ks[n]);
+            ihi = min(ihi, s_ke[n]);
             dmin = min(dmin, s_d[n]);
         }
     }
@@ -318,22 +403,22 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
 
     // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode the
     // steps index the lattice first_b + e * dmin, e < nlat.
-    int64_t jlo, jhi, first_b = 0, nlat = 0;
+    int jlo, jhi, first_b = 0, nlat = 0;
     if (MODE == kModeSample) {
-        first_b = ((int64_t)lo + dmin - 1) / dmin * dmin;
-        nlat = lattice_count(lo, hi, dmin);
+        first_b = (lo + dmin - 1) / dmin * dmin;
+        nlat = (int)lattice_count(lo, hi, dmin);
         jlo = 0;
         jhi = (nlat + kStepKeys - 1) / kStepKeys;
     } else {
-        int64_t c0 = (int64_t)chunk * kChunkKeys;
-        int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + kChunkKeys);
+        const int64_t c0 = (int64_t)chunk * kChunkKeys;
+        const int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + kChunkKeys);
         if (khi <= klo) return;
-        jlo = klo / kStepKeys;
-        jhi = (khi + kStepKeys - 1) / kStepKeys;
+        jlo = (int)(klo / kStepKeys);
+        jhi = (int)((khi + kStepKeys - 1) / kStepKeys);
     }
 
-    stage_q_tile<DT>(s_q, a.q, s_row);
-    for (int i = threadIdx.x; i < kHeads * kTileQ; i += kThreads) {
+    stage_q_tile<DT>(s_q, a, s_row);
+    for (int i = threadIdx.x; i < kHeads * kTileQ; i += blockDim.x) {
         const int rn = i & (kTileQ - 1), h = i / kTileQ;
         const int rt = s_row[rn];
         s_w[i] = rt >= 0 ? a.w[(int64_t)rt * kHeads + h] : 0.0f;
@@ -344,103 +429,110 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
     const int n = lane & 15, g = lane >> 4;
     const int t = s_row[n];
     const int rks = s_ks[n], rke = s_ke[n];
+    const int S = a.num_kv;
+    const float qsc = (DT == kFP8 && t >= 0) ? a.qscale[t] : 1.0f;
 
     float tau = __builtin_inff();
     if (MODE == kModeFilter && t >= 0) tau = a.tau[t];
-    int dn = s_d[n];
-    int64_t first_n = ((int64_t)rks + dn - 1) / dn * dn;
-    uint64_t *ring = s_ring + (MODE == kModeFilter ? wave * kTileQ * RING : 0);
+    const int dn = s_d[n];
+    const int first_n = (rks + dn - 1) / dn * dn;
+    uint64_t *ring = s_ring + (MODE == kModeFilter ? wave * kTileQ * RS : 0);
     uint32_t ring_cnt = 0;
-    const int64_t S = a.num_kv;
 
     // Key fragments of step j: this lane loads key row 16 kt + n of the step.
-    auto load_step = [&](KFrag<DT>(&f)[kSub], int64_t j) {
+    auto load_step = [&](KFrag<DT>(&f)[kSub], int j) {
 #pragma unroll
         for (int kt = 0; kt < kSub; ++kt) {
-            int64_t e = j * kStepKeys + 16 * kt + n;
-            int64_t p = (MODE == kModeSample) ? first_b + e * dmin : e;
+            const int e = j * kStepKeys + 16 * kt + n;
+            int p = (MODE == kModeSample) ? first_b + e * dmin : e;
             p = min(p, S - 1);
             load_kfrag(f[kt], a.kv, p, g);
         }
     };
-    KFrag<DT> kf[kSub];
-    if (jlo + wave < jhi) load_step(kf, jlo + wave);
-    for (int64_t j = jlo + wave; j < jhi; j += kWaves) {
-        KFrag<DT> kn[kSub];
-        if (j + kWaves < jhi) load_step(kn, j + kWaves);  // prefetch the wave's next step
-        float acc[kSub][4];
-        score_step(acc, kf, s_q, s_w, lane);
 
-        // Output element (kt, i) of this lane: key row 16 kt + 4 g + i, query n.
+    // Scores one step and hands its 16 outputs per lane to the mode's sink.
+    auto process = [&](const KFrag<DT>(&kf)[kSub], int j) {
+        const int sb = j * kStepKeys + 4 * g;  // key of element (kt, i) is sb + 16 kt + i
+        // Scale factors of the step's outputs (4 consecutive keys per
+        // subtile), loaded before the MFMA work so their latency hides.
+        v4f shv[kSub];
+        if (MODE != kModeSample) {
+#pragma unroll
+            for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
+        }
+        StepOut o;
+        score_step(o, kf, s_q, s_w, lane);
         if (MODE == kModeFilter) {
             // Keep (row, key) when the key is in the row's window and its
             // score reaches the row's threshold (take-all rows: -inf).
-            uint32_t mask = 0;
+            // Elements outside the window become NaN, which fails every test.
             float sc[kSub * 4];
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    int64_t s = j * kStepKeys + 16 * kt + 4 * g + i;
-                    float sg = a.sigma ? a.sigma[min(s, S - 1)] : 1.0f;
-                    float I = sg * acc[kt][i];
-                    sc[kt * 4 + i] = I;
-                    bool ok = (s >= rks) && (s < rke) && (I >= tau);
-                    mask |= (uint32_t)ok << (kt * 4 + i);
+                for (int i = 0; i < 4; ++i) sc[kt * 4 + i] = score_of<DT>(o, kt, i, qsc, shv[kt][i]);
+            const bool inside = j * kStepKeys >= ilo && (j + 1) * kStepKeys <= ihi;  // wave-uniform
+            if (!inside) {
+#pragma unroll
+                for (int b = 0; b < kSub * 4; ++b) {
+                    const int s = sb + 16 * (b >> 2) + (b & 3);
+                    if (s < rks || s >= rke) sc[b] = __builtin_nanf("");
                 }
-            const int64_t sbase = j * kStepKeys + 4 * g;
+            }
+            uint32_t m = 0;
+#pragma unroll
+            for (int b = 0; b < kSub * 4; ++b) m += (sc[b] >= tau) ? 1u : 0u;
             // Survivors of the 4 lanes that hold query n: total and this lane's offset.
-            uint32_t m = __builtin_popcount(mask);
-            uint32_t c0 = __shfl(m, n), c1 = __shfl(m, n + 16), c2 = __shfl(m, n + 32), c3 = __shfl(m, n + 48);
+            const uint32_t c0 = __shfl(m, n), c1 = __shfl(m, n + 16), c2 = __shfl(m, n + 32),
+                           c3 = __shfl(m, n + 48);
             uint32_t tot = c0 + c1 + c2 + c3;
-            uint32_t pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+            const uint32_t pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
             if (__any(ring_cnt + tot > (uint32_t)RING)) {
-                ring_flush<RING>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
+                ring_flush<RS>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
                 ring_cnt = 0;
             }
+            bool direct = false;
             if (__any(tot > (uint32_t)RING)) {
                 // More than a ring holds: reserve slots in the row's list directly.
                 uint32_t base = 0;
-                bool direct = tot > (uint32_t)RING;
+                direct = tot > (uint32_t)RING;
                 if (direct && g == 0 && t >= 0) base = atomicAdd(a.cnt + t, tot);
                 base = __shfl(base, n);
                 uint32_t pos = base + pre;
                 if (direct && t >= 0) {
 #pragma unroll
                     for (int b = 0; b < kSub * 4; ++b) {
-                        if (mask & (1u << b)) {
-                            int64_t s = sbase + 16 * (b >> 2) + (b & 3);
-                            if (pos < (uint32_t)a.cap) a.cand[(int64_t)t * a.cap + pos] = sel_key(sc[b], (int32_t)s);
+                        if (sc[b] >= tau) {
+                            if (pos < (uint32_t)a.cap)
+                                a.cand[(int64_t)t * a.cap + pos] = raw_cand(sc[b], sb + 16 * (b >> 2) + (b & 3));
                             ++pos;
                         }
                     }
-                    mask = 0;
-                    tot = 0;
                 }
             }
-            uint32_t pos = ring_cnt + pre;
+            if (!direct && __any(m != 0)) {
+                uint64_t *rp = ring + n * RS + ring_cnt + pre;
 #pragma unroll
-            for (int b = 0; b < kSub * 4; ++b) {
-                if (mask & (1u << b)) {
-                    int64_t s = sbase + 16 * (b >> 2) + (b & 3);
-                    ring[n * RING + pos] = sel_key(sc[b], (int32_t)s);
-                    ++pos;
+                for (int b = 0; b < kSub * 4; ++b) {
+                    if (sc[b] >= tau) {
+                        *rp = raw_cand(sc[b], sb + 16 * (b >> 2) + (b & 3));
+                        ++rp;
+                    }
                 }
             }
-            ring_cnt += tot;
+            ring_cnt += direct ? 0u : tot;
         } else if (MODE == kModeSample) {
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    int64_t e = j * kStepKeys + 16 * kt + 4 * g + i;
+                    const int e = sb + 16 * kt + i;
                     if (t < 0 || e >= nlat) continue;
-                    int64_t p = first_b + e * dmin;
+                    const int p = first_b + e * dmin;
                     if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
-                    float sg = a.sigma ? a.sigma[p] : 1.0f;
-                    float I = sg * acc[kt][i];
-                    int64_t idx = (p - first_n) / dn;
-                    a.samp[(int64_t)t * a.sample_target + idx] = ord_of(I);
+                    const int idx = (p - first_n) / dn;
+                    a.samp[(int64_t)t * a.sample_target + idx] =
+                        ord_of(score_of<DT>(o, kt, i, qsc, sigh_of<DT>(a.sigma, p)));
                 }
         } else {
             const int slot = tile * kTileQ + n;
@@ -448,18 +540,28 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
             for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    int64_t s = j * kStepKeys + 16 * kt + 4 * g + i;
+                    const int s = sb + 16 * kt + i;
                     if (t < 0 || s < rks || s >= rke) continue;
-                    float sg = a.sigma ? a.sigma[s] : 1.0f;
-                    float I = sg * acc[kt][i];
-                    a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] = sel_key(I, (int32_t)s);
+                    a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] =
+                        raw_cand(score_of<DT>(o, kt, i, qsc, shv[kt][i]), s);
                 }
         }
-#pragma unroll
-        for (int kt = 0; kt < kSub; ++kt) kf[kt] = kn[kt];
+    };
+
+    // Steps of this wave: jlo + wave, + kWaves, ...; two fragment sets
+    // alternate so the next step's keys load while this step computes.
+    KFrag<DT> ka[kSub], kb[kSub];
+    int j = jlo + wave;
+    if (j < jhi) load_step(ka, j);
+    for (; j < jhi; j += 2 * kWaves) {
+        if (j + kWaves < jhi) load_step(kb, j + kWaves);
+        process(ka, j);
+        if (j + kWaves >= jhi) break;
+        if (j + 2 * kWaves < jhi) load_step(ka, j + 2 * kWaves);
+        process(kb, j + kWaves);
     }
     if (MODE == kModeFilter) {
-        if (__any(ring_cnt > 0)) ring_flush<RING>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
+        if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
     }
 }
 

@@ -271,13 +271,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
 
     uint64_t thr = 0;
     if (k > 0 && (int64_t)k < n)
-        thr = radix_select_kth<uint64_t, 8>(L, [&](int64_t i) { return src[i]; }, n, k);
+        thr = radix_select_kth<uint64_t, 8>(L, [&](int64_t i) { return key_of_raw(src[i]); }, n, k);
 
     if (tid == 0) s_n = 0;
     __syncthreads();
     if (k > 0) {
         for (int64_t i = tid; i < n; i += blockDim.x) {
-            uint64_t e = src[i];
+            uint64_t e = key_of_raw(src[i]);
             if (e >= thr) {
                 const uint32_t pos = atomicAdd(&s_n, 1u);
                 if (pos < (uint32_t)kMaxTopk) s_sel[pos] = e;
