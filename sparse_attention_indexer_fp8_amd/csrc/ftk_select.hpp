@@ -54,9 +54,21 @@ __device__ KeyT radix_select_kth(RadixLds &L, Fetch fetch, int64_t n, uint32_t k
         for (int i = tid; i < kSelWaves * 256; i += blockDim.x) (&L.hist[0][0])[i] = 0;
         __syncthreads();
         for (int64_t i = tid; i < n; i += blockDim.x) {
-            KeyT e = fetch(i);
-            bool match = (p == 0) || (((e ^ prefix) >> (shift + 8)) == 0);
-            if (match) atomicAdd(&L.hist[wave][(uint32_t)(e >> shift) & 255u], 1u);
+            const KeyT e = fetch(i);
+            const bool match = (p == 0) || (((e ^ prefix) >> (shift + 8)) == 0);
+            const uint32_t dig = (uint32_t)(e >> shift) & 255u;
+            // Lanes that share the first active lane's digit add once: the
+            // candidates of a row crowd into few digits, and same-address LDS
+            // atomics would serialise.
+            const uint64_t act = __ballot(match);
+            if (act) {
+                const int leader = __builtin_ctzll(act);
+                const uint32_t ld = __shfl(dig, leader);
+                const bool same = match && dig == ld;
+                const uint64_t sm = __ballot(same);
+                if (lane == leader) atomicAdd(&L.hist[wave][ld], (uint32_t)__builtin_popcountll(sm));
+                if (match && !same) atomicAdd(&L.hist[wave][dig], 1u);
+            }
         }
         __syncthreads();
         if (tid < 256) {
@@ -242,13 +254,36 @@ struct SelectArgs {
     float *out_val;
 };
 
+// Bucketed selection.  The row's candidates are spread over kBuckets
+// buckets linear in score between their minimum and maximum, highest scores
+// in bucket 0.  The bucket function is monotone (a larger score never lands
+// in a later bucket, equal scores share a bucket), so after one histogram and
+// one prefix sum the bucket holding the k-th key is known, every key of an
+// earlier bucket is selected, and a counting-sort scatter followed by a sort
+// of each (small) bucket by full key yields the top k in order.  Rows whose
+// buckets are too crowded (massive ties) use the radix select + bitonic sort.
+constexpr int kBuckets = 4096;
+constexpr int kSegMax = 48;
+constexpr int kBinsPerThread = kBuckets / kSelThreads;
+
+struct SelectLds {
+    union {
+        RadixLds radix;
+        uint32_t bucket[kBuckets];
+    };
+    uint64_t sel[kMaxTopk + kSegMax];
+    float redf[2 * kSelWaves];
+    uint32_t redu[kSelWaves];
+    uint32_t misc[4];
+};
+
+__device__ __forceinline__ float raw_score(uint64_t r) { return __uint_as_float((uint32_t)r); }
+
 template <bool DENSE>
 __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
 {
-    __shared__ RadixLds L;
-    __shared__ uint64_t s_sel[kMaxTopk];
-    __shared__ uint32_t s_n;
-    const int tid = threadIdx.x;
+    __shared__ SelectLds S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int t;
     const uint64_t *src;
     int64_t n;
@@ -269,46 +304,144 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
     int32_t *oi = a.out_idx + (int64_t)t * a.topk;
     float *ov = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
 
-    uint64_t thr = 0;
-    if (k > 0 && (int64_t)k < n)
-        thr = radix_select_kth<uint64_t, 8>(L, [&](int64_t i) { return key_of_raw(src[i]); }, n, k);
-
-    if (tid == 0) s_n = 0;
-    __syncthreads();
+    bool fast = false;
+    float mx = 0.0f, scale = 0.0f;
+    uint32_t kb = 0;
     if (k > 0) {
+        // Score range of the candidates.
+        float lo = __builtin_inff(), hi = -__builtin_inff();
         for (int64_t i = tid; i < n; i += blockDim.x) {
-            uint64_t e = key_of_raw(src[i]);
-            if (e >= thr) {
-                const uint32_t pos = atomicAdd(&s_n, 1u);
-                if (pos < (uint32_t)kMaxTopk) s_sel[pos] = e;
-            }
+            const float f = raw_score(src[i]);
+            lo = fminf(lo, f);
+            hi = fmaxf(hi, f);
         }
+        for (int off = 32; off > 0; off >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, off));
+            hi = fmaxf(hi, __shfl_xor(hi, off));
+        }
+        if (lane == 0) {
+            S.redf[wave] = lo;
+            S.redf[kSelWaves + wave] = hi;
+        }
+        for (int i = tid; i < kBuckets; i += blockDim.x) S.bucket[i] = 0;
+        __syncthreads();
+        lo = S.redf[0];
+        hi = S.redf[kSelWaves];
+        for (int w = 1; w < kSelWaves; ++w) {
+            lo = fminf(lo, S.redf[w]);
+            hi = fmaxf(hi, S.redf[kSelWaves + w]);
+        }
+        mx = hi;
+        scale = (float)kBuckets / (hi - lo);
+        fast = hi > lo && __builtin_isfinite(scale) && __builtin_isfinite(hi - lo);
     }
-    uint32_t P = 1;
-    while (P < k) P <<= 1;
-    __syncthreads();
-    for (uint32_t i = k + tid; i < P; i += blockDim.x) s_sel[i] = 0;  // below every real key
-    __syncthreads();
-    for (uint32_t size = 2; size <= P; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t i = tid; i < P / 2; i += blockDim.x) {
-                uint32_t lo = 2 * i - (i & (stride - 1));
-                uint32_t hi = lo + stride;
-                bool desc = (lo & size) == 0;
-                uint64_t x = s_sel[lo], y = s_sel[hi];
-                if (desc ? (x < y) : (x > y)) {
-                    s_sel[lo] = y;
-                    s_sel[hi] = x;
+    auto bucket_of = [&](float f) -> uint32_t {
+        const float x = (mx - f) * scale;
+        return x < (float)(kBuckets - 1) ? (uint32_t)x : (uint32_t)(kBuckets - 1);
+    };
+    if (fast) {
+        for (int64_t i = tid; i < n; i += blockDim.x) atomicAdd(&S.bucket[bucket_of(raw_score(src[i]))], 1u);
+        __syncthreads();
+        // Exclusive prefix over buckets; each thread owns kBinsPerThread
+        // consecutive buckets and keeps their counts.
+        uint32_t cntv[kBinsPerThread], run = 0;
+#pragma unroll
+        for (int q = 0; q < kBinsPerThread; ++q) {
+            cntv[q] = S.bucket[tid * kBinsPerThread + q];
+            run += cntv[q];
+        }
+        uint32_t x = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) S.redu[wave] = x;
+        __syncthreads();
+        uint32_t base = x - run;
+        for (int w = 0; w < wave; ++w) base += S.redu[w];
+#pragma unroll
+        for (int q = 0; q < kBinsPerThread; ++q) {
+            const uint32_t b = tid * kBinsPerThread + q;
+            S.bucket[b] = base;
+            if (base <= k - 1 && k - 1 < base + cntv[q]) S.misc[0] = b;  // bucket of the k-th key
+            base += cntv[q];
+        }
+        __syncthreads();
+        kb = S.misc[0];
+        uint32_t seg = 0;
+#pragma unroll
+        for (int q = 0; q < kBinsPerThread; ++q)
+            if ((uint32_t)(tid * kBinsPerThread + q) <= kb) seg = max(seg, cntv[q]);
+        for (int off = 32; off > 0; off >>= 1) seg = max(seg, (uint32_t)__shfl_xor(seg, off));
+        if (lane == 0) S.redu[wave] = seg;
+        __syncthreads();
+        for (int w = 0; w < kSelWaves; ++w) seg = max(seg, S.redu[w]);
+        fast = seg <= (uint32_t)kSegMax;
+        if (fast) {
+            for (int64_t i = tid; i < n; i += blockDim.x) {
+                const uint64_t r = src[i];
+                const uint32_t b = bucket_of(raw_score(r));
+                if (b <= kb) S.sel[atomicAdd(&S.bucket[b], 1u)] = key_of_raw(r);
+            }
+            __syncthreads();
+            // Bucket b now spans [bucket[b-1], bucket[b]); sort it descending.
+            for (uint32_t b = tid; b <= kb; b += blockDim.x) {
+                const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
+                for (uint32_t i = s0 + 1; i < s1; ++i) {
+                    const uint64_t v = S.sel[i];
+                    uint32_t j = i;
+                    while (j > s0 && S.sel[j - 1] < v) {
+                        S.sel[j] = S.sel[j - 1];
+                        --j;
+                    }
+                    S.sel[j] = v;
                 }
             }
             __syncthreads();
+        } else {
+            __syncthreads();  // everyone has read the buckets before the radix scratch reuses them
+        }
+    }
+    if (k > 0 && !fast) {
+        uint64_t thr = 0;
+        if ((int64_t)k < n)
+            thr = radix_select_kth<uint64_t, 8>(S.radix, [&](int64_t i) { return key_of_raw(src[i]); }, n, k);
+        if (tid == 0) S.misc[1] = 0;
+        __syncthreads();
+        for (int64_t i = tid; i < n; i += blockDim.x) {
+            const uint64_t e = key_of_raw(src[i]);
+            if (e >= thr) {
+                const uint32_t pos = atomicAdd(&S.misc[1], 1u);
+                if (pos < (uint32_t)kMaxTopk) S.sel[pos] = e;
+            }
+        }
+        uint32_t P = 1;
+        while (P < k) P <<= 1;
+        __syncthreads();
+        for (uint32_t i = k + tid; i < P; i += blockDim.x) S.sel[i] = 0;  // below every real key
+        __syncthreads();
+        for (uint32_t size = 2; size <= P; size <<= 1) {
+            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                for (uint32_t i = tid; i < P / 2; i += blockDim.x) {
+                    const uint32_t l0 = 2 * i - (i & (stride - 1));
+                    const uint32_t l1 = l0 + stride;
+                    const bool desc = (l0 & size) == 0;
+                    const uint64_t x = S.sel[l0], y = S.sel[l1];
+                    if (desc ? (x < y) : (x > y)) {
+                        S.sel[l0] = y;
+                        S.sel[l1] = x;
+                    }
+                }
+                __syncthreads();
+            }
         }
     }
     for (int j = tid; j < a.topk; j += blockDim.x) {
         int32_t idx = -1;
         float v = -__builtin_inff();
         if ((uint32_t)j < k) {
-            uint64_t e = s_sel[j];
+            const uint64_t e = S.sel[j];
             idx = key_index(e);
             v = key_score(e);
         }
