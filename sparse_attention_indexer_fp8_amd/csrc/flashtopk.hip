@@ -129,9 +129,10 @@ int resolve(Plan &p, const flashtopk_options *opt)
 template <int DT>
 void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
 {
-    if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, kThreads, 0, st>>>(a);
-    else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, kThreads, 0, st>>>(a);
-    else k_score<DT, kModeDense><<<grid, kThreads, 0, st>>>(a);
+    constexpr int nt = 64 * ScoreCfg<DT>::waves;
+    if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, nt, 0, st>>>(a);
+    else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, nt, 0, st>>>(a);
+    else k_score<DT, kModeDense><<<grid, nt, 0, st>>>(a);
 }
 
 void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)

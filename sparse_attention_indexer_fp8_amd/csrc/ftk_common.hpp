@@ -14,12 +14,11 @@ constexpr int kDim = 128;
 
 // Work decomposition.  A tile is 16 query rows: the N = 16 columns of a
 // 16x16 MFMA output.  A wave scores kSub 16-key subtiles per step (the M = 16
-// rows), eight waves share a tile, and a work item covers kChunkKeys keys.
+// rows), the waves of a workgroup share a tile, and a work item covers
+// kChunkKeys keys.
 constexpr int kTileQ = 16;
 constexpr int kSub = 4;
 constexpr int kStepKeys = 16 * kSub;      // 64 keys per wave step
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;     // 512
 constexpr int kChunkKeys = 8192;          // keys per work item
 
 constexpr int kFP8 = 0;

@@ -48,11 +48,26 @@ constexpr int kModeDense = 2;
 // q-tile "heads" in LDS: the 32 heads, plus the qbar parts on the FP8 path.
 template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? kHeads + kQbarParts : kHeads; };
 
+// Per-dtype launch shape.
+//   FP8: 16 waves per workgroup (4 per SIMD, at most 128 VGPRs each) so that
+//   while one wave waits on LDS or memory three others keep the matrix cores
+//   and vector ALUs busy; each wave loads its step's keys when it starts it.
+//   BF16: the q tile takes 128 KiB of LDS and each wave's key fragments 64
+//   VGPRs, so 8 waves (2 per SIMD) with the next step's keys prefetched.
 // Candidate ring per (wave, query) in filter mode: survivors are staged in LDS
 // and flushed to the row's candidate list with one atomic per query.  The
-// stride between the 16 rings of a wave is odd in 8-byte entries (RING + 1),
+// stride between the 16 rings of a wave is odd in 8-byte entries (ring + 1),
 // so the rings start on distinct LDS banks.
-template <int DT> struct RingEntries { static constexpr int value = DT == kFP8 ? 80 : 24; };
+template <int DT> struct ScoreCfg;
+template <> struct ScoreCfg<kFP8> {
+    static constexpr int waves = 16, ring = 40;
+    static constexpr bool prefetch = false;
+};
+template <> struct ScoreCfg<kBF16> {
+    static constexpr int waves = 8, ring = 24;
+    static constexpr bool prefetch = true;
+};
+template <int DT> struct RingEntries { static constexpr int value = ScoreCfg<DT>::ring; };
 template <int DT> struct RingStride { static constexpr int value = RingEntries<DT>::value + 1; };
 
 struct ScoreArgs {
@@ -192,25 +207,22 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
         for (int i = 0; i < 4; ++i) o.acc[kt][i] = 0.0f;
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
-    // Three result sets rotate: the epilogue of head h-2 runs while the MFMAs
-    // of head h execute, so no epilogue waits on an MFMA still in flight.
-    v4f xa[kSub], xb[kSub], xc[kSub];
+    // Two result sets alternate: the epilogue of head h-1 runs while the
+    // MFMAs of head h execute.
+    v4f xa[kSub], xb[kSub];
     mfma_fp8_head(xa, kf, qp, z);
-    mfma_fp8_head(xb, kf, qp + HB, z);
 #pragma unroll 1
-    for (int h = 2; h + 2 < kHeads; h += 3) {
-        const float w0 = wp[0], w1 = wp[kTileQ], w2 = wp[2 * kTileQ];
-        mfma_fp8_head(xc, kf, qp + 2 * HB, z);
+    for (int h = 1; h < kHeads - 1; h += 2) {
+        const float w0 = wp[0], w1 = wp[kTileQ];
+        mfma_fp8_head(xb, kf, qp + HB, z);
         epi_abs(o.acc, xa, w0);
-        mfma_fp8_head(xa, kf, qp + 3 * HB, z);
+        mfma_fp8_head(xa, kf, qp + 2 * HB, z);
         epi_abs(o.acc, xb, w1);
-        mfma_fp8_head(xb, kf, qp + 4 * HB, z);
-        epi_abs(o.acc, xc, w2);
-        qp += 3 * HB;
-        wp += 3 * kTileQ;
+        qp += 2 * HB;
+        wp += 2 * kTileQ;
     }
-    // Heads 30 and 31 remain in xa and xb.  The linear half: qbar parts are
-    // heads 32..34, accumulated in the MFMA.
+    mfma_fp8_head(xb, kf, qp + HB, z);
+    // The linear half: qbar parts are heads 32..34, accumulated in the MFMA.
     const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
     mfma_fp8_head(o.lin, kf, pp, z);
     epi_abs(o.acc, xa, wp[0]);
@@ -328,8 +340,9 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
 // ---------------------------------------------------------------------------
 
 template <int DT, int MODE>
-__global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
+__global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
 {
+    constexpr int kWaves = ScoreCfg<DT>::waves;
     constexpr int RB = RowBytes<DT>::value;
     constexpr int TH = TileHeads<DT>::value;
     constexpr int RING = (MODE == kModeFilter) ? RingEntries<DT>::value : 1;
@@ -455,13 +468,20 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
         const int sb = j * kStepKeys + 4 * g;  // key of element (kt, i) is sb + 16 kt + i
         // Scale factors of the step's outputs (4 consecutive keys per
         // subtile), loaded before the MFMA work so their latency hides.
+        // With the prefetching (2-wave) shape they load before the MFMA work
+        // so their latency hides; with 4 waves per SIMD other waves hide it
+        // and the registers are kept free.
         v4f shv[kSub];
-        if (MODE != kModeSample) {
+        auto load_sh = [&]() {
+            if (MODE != kModeSample) {
 #pragma unroll
-            for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
-        }
+                for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
+            }
+        };
+        if (ScoreCfg<DT>::prefetch) load_sh();
         StepOut o;
         score_step(o, kf, s_q, s_w, lane);
+        if (!ScoreCfg<DT>::prefetch) load_sh();
         if (MODE == kModeFilter) {
             // Keep (row, key) when the key is in the row's window and its
             // score reaches the row's threshold (take-all rows: -inf).
@@ -548,17 +568,26 @@ __global__ __launch_bounds__(kThreads) void k_score(ScoreArgs a)
         }
     };
 
-    // Steps of this wave: jlo + wave, + kWaves, ...; two fragment sets
-    // alternate so the next step's keys load while this step computes.
-    KFrag<DT> ka[kSub], kb[kSub];
-    int j = jlo + wave;
-    if (j < jhi) load_step(ka, j);
-    for (; j < jhi; j += 2 * kWaves) {
-        if (j + kWaves < jhi) load_step(kb, j + kWaves);
-        process(ka, j);
-        if (j + kWaves >= jhi) break;
-        if (j + 2 * kWaves < jhi) load_step(ka, j + 2 * kWaves);
-        process(kb, j + kWaves);
+    // Steps of this wave: jlo + wave, + kWaves, ...
+    if (ScoreCfg<DT>::prefetch) {
+        // Two fragment sets alternate so the next step's keys load while this
+        // step computes.
+        KFrag<DT> ka[kSub], kb[kSub];
+        int j = jlo + wave;
+        if (j < jhi) load_step(ka, j);
+        for (; j < jhi; j += 2 * kWaves) {
+            if (j + kWaves < jhi) load_step(kb, j + kWaves);
+            process(ka, j);
+            if (j + kWaves >= jhi) break;
+            if (j + 2 * kWaves < jhi) load_step(ka, j + 2 * kWaves);
+            process(kb, j + kWaves);
+        }
+    } else {
+        for (int j = jlo + wave; j < jhi; j += kWaves) {
+            KFrag<DT> kf[kSub];
+            load_step(kf, j);
+            process(kf, j);
+        }
     }
     if (MODE == kModeFilter) {
         if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
