@@ -32,8 +32,12 @@
  * Operands must stay unmodified until the stream has finished the call.
  *
  * Synchronisation: work is enqueued on `stream` (a hipStream_t; NULL is the
- * device's null stream).  The call returns after the stream has finished its
- * own work, so out_idx / out_val are valid when it returns 0.
+ * device's null stream) and is stream-ordered: out_idx / out_val are complete
+ * once the stream has reached the end of the call's work (synchronise the
+ * stream, or wait on an event recorded after the call).  The call itself
+ * blocks the calling thread until the GPU has classified the rows (it reads
+ * back how many rows need dense rescoring), but not until the selection is
+ * done.
  *
  * Errors: every entry point returns 0 (FLASHTOPK_OK) or a positive status;
  * nothing is thrown across the ABI and nothing is printed.  Preconditions

@@ -8,8 +8,10 @@
 //   4. k_triage         flag rows whose candidates under/overflowed
 //   5. k_select         exact top-k of every unflagged row
 //   6. (flagged rows)   k_score<dense> + k_select<dense> in batches
-// The count of flagged rows is read back once (a stream synchronisation)
-// to size step 6; the call returns with the stream drained.
+// The triage counts are copied to pinned host memory behind step 4; the host
+// waits for that copy (an event, while step 5 runs on the GPU) to size step
+// 6, then returns.  Outputs are complete when the stream reaches the end of
+// the call's work.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,6 +45,7 @@ struct Workspace {
     DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch, qbar, qscale, sigh;
     unsigned long long *host_stats = nullptr;  // pinned
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
+    hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
     flashtopk_info last{};
     bool has_last = false;
 };
@@ -129,10 +132,9 @@ int resolve(Plan &p, const flashtopk_options *opt)
 template <int DT>
 void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
 {
-    constexpr int nt = 64 * ScoreCfg<DT>::waves;
-    if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, nt, 0, st>>>(a);
-    else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, nt, 0, st>>>(a);
-    else k_score<DT, kModeDense><<<grid, nt, 0, st>>>(a);
+    if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
+    else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
+    else k_score<DT, kModeDense><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
 }
 
 void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
@@ -216,7 +218,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     if (fp8)
         k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T, (uint8_t *)w->qbar.ptr,
                                                                  (float *)w->qscale.ptr);
-    if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3(ntiles), stream, sa);
+    if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * kSampleSplit)), stream, sa);
     mark(*w, p, 1, stream);
 
     TauArgs ta{};
@@ -230,7 +232,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     ta.recover_all = recover_all ? 1 : 0;
     ta.tau = (float *)w->tau.ptr;
     ta.cnt = (uint32_t *)w->cnt.ptr;
-    k_tau<<<dim3((unsigned)T), kSelThreads, 0, stream>>>(ta);
+    k_tau<<<dim3((unsigned)T), kTauThreads, 0, stream>>>(ta);
     mark(*w, p, 2, stream);
 
     if (!recover_all) launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
@@ -249,6 +251,15 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     tr.nflagged = (int32_t *)w->nflagged.ptr;
     tr.stats = (unsigned long long *)w->stats.ptr;
     k_triage<<<1, 1024, 0, stream>>>(tr);
+    // The triage counts go to pinned host memory right away; the host waits
+    // for them (not for the stream) while the select kernel runs, so the GPU
+    // never idles on the host between calls.
+    hipError_t e = hipMemcpyAsync(w->host_stats, w->stats.ptr, sizeof(unsigned long long) * kStCount,
+                                  hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (!w->stats_ev && (e = hipEventCreateWithFlags(&w->stats_ev, hipEventDisableTiming)) != hipSuccess)
+        return hip_status(e);
+    if ((e = hipEventRecord(w->stats_ev, stream)) != hipSuccess) return hip_status(e);
     mark(*w, p, 4, stream);
 
     SelectArgs se{};
@@ -263,14 +274,13 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     se.nrows = (const int32_t *)w->nflagged.ptr;
     se.out_idx = out_idx;
     se.out_val = out_val;
-    k_select<false><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
+    if (p.cap <= 8 * kSelThreads) k_select<8><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
+    else if (p.cap <= 16 * kSelThreads) k_select<16><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
+    else k_select<32><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
     mark(*w, p, 5, stream);
 
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_status(e);
-    e = hipMemcpyAsync(w->host_stats, w->stats.ptr, sizeof(unsigned long long) * kStCount,
-                       hipMemcpyDeviceToHost, stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventSynchronize(w->stats_ev);
     if (e != hipSuccess) return hip_status(e);
 
     const int64_t R = (int64_t)w->host_stats[kStFlagged];
@@ -295,7 +305,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             sa.row_base = (int)rb;
             se.row_base = (int)rb;
             launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * nchunks)), stream, sa);
-            k_select<true><<<dim3((unsigned)rcap), kSelThreads, 0, stream>>>(se);
+            k_select<0><<<dim3((unsigned)rcap), kSelThreads, 0, stream>>>(se);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e);
@@ -311,10 +321,6 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             ms_rec = 0.0f;
         }
         (void)hipEventDestroy(end);
-    }
-    if (R > 0) {
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return hip_status(e);
     }
 
     flashtopk_info &info = w->last;
@@ -438,6 +444,7 @@ void flashtopk_release(void)
         if (w->host_stats) (void)hipHostFree(w->host_stats);
         for (hipEvent_t &ev : w->ev)
             if (ev) (void)hipEventDestroy(ev);
+        if (w->stats_ev) (void)hipEventDestroy(w->stats_ev);
         (void)hipSetDevice(prev);
         delete w;
     }

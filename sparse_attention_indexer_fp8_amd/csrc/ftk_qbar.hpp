@@ -51,12 +51,18 @@ __global__ __launch_bounds__(256) void k_qbar(const uint8_t *q, const float *w, 
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= num_q) return;
     const uint8_t *qr = q + t * kHeads * kDim + 2 * lane;
+    uint32_t c[kHeads];
+    float wv[kHeads];
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) {  // every load in flight before the FMAs
+        c[h] = *reinterpret_cast<const uint16_t *>(qr + h * kDim);
+        wv[h] = w[t * kHeads + h];
+    }
     float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
     for (int h = 0; h < kHeads; ++h) {
-        const float wh = w[t * kHeads + h];
-        const uint32_t c = *reinterpret_cast<const uint16_t *>(qr + h * kDim);
-        v0 = __builtin_fmaf(wh, e4m3_to_f32(c & 0xFFu), v0);
-        v1 = __builtin_fmaf(wh, e4m3_to_f32(c >> 8), v1);
+        v0 = __builtin_fmaf(wv[h], e4m3_to_f32(c[h] & 0xFFu), v0);
+        v1 = __builtin_fmaf(wv[h], e4m3_to_f32(c[h] >> 8), v1);
     }
     float m = fmaxf(fabsf(v0), fabsf(v1));
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));

@@ -45,6 +45,9 @@ constexpr int kModeFilter = 0;
 constexpr int kModeSample = 1;
 constexpr int kModeDense = 2;
 
+// Workgroups per tile in sample mode (each scores a part of the lattice).
+constexpr int kSampleSplit = 1;
+
 // q-tile "heads" in LDS: the 32 heads, plus the qbar parts on the FP8 path.
 template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? kHeads + kQbarParts : kHeads; };
 
@@ -58,16 +61,15 @@ template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? k
 // and flushed to the row's candidate list with one atomic per query.  The
 // stride between the 16 rings of a wave is odd in 8-byte entries (ring + 1),
 // so the rings start on distinct LDS banks.
-template <int DT> struct ScoreCfg;
-template <> struct ScoreCfg<kFP8> {
-    static constexpr int waves = 16, ring = 40;
-    static constexpr bool prefetch = false;
+//   Sample and dense modes (no candidate rings, more bookkeeping registers)
+//   use the 8-wave prefetching shape for both dtypes.
+template <int DT, int MODE> struct ScoreCfg {
+    static constexpr bool wide = DT == kFP8 && MODE == 0;  // 0: filter mode
+    static constexpr int waves = wide ? 16 : 8;
+    static constexpr int ring = DT == kFP8 ? 40 : 24;
+    static constexpr bool prefetch = !wide;
 };
-template <> struct ScoreCfg<kBF16> {
-    static constexpr int waves = 8, ring = 24;
-    static constexpr bool prefetch = true;
-};
-template <int DT> struct RingEntries { static constexpr int value = ScoreCfg<DT>::ring; };
+template <int DT> struct RingEntries { static constexpr int value = ScoreCfg<DT, 0>::ring; };
 template <int DT> struct RingStride { static constexpr int value = RingEntries<DT>::value + 1; };
 
 struct ScoreArgs {
@@ -340,9 +342,10 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
 // ---------------------------------------------------------------------------
 
 template <int DT, int MODE>
-__global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
+__global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(ScoreArgs a)
 {
-    constexpr int kWaves = ScoreCfg<DT>::waves;
+    using Cfg = ScoreCfg<DT, MODE>;
+    constexpr int kWaves = Cfg::waves;
     constexpr int RB = RowBytes<DT>::value;
     constexpr int TH = TileHeads<DT>::value;
     constexpr int RING = (MODE == kModeFilter) ? RingEntries<DT>::value : 1;
@@ -359,14 +362,10 @@ __global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
     uint8_t *s_q = smem + WB;
     uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + WB + QB);
 
-    int tile, chunk;
-    if (MODE == kModeSample) {
-        tile = blockIdx.x;
-        chunk = 0;
-    } else {
-        chunk = blockIdx.x / a.ntiles;
-        tile = blockIdx.x - chunk * a.ntiles;
-    }
+    // Work item: tile (fast index) x chunk; in sample mode the "chunk" is the
+    // part of the tile's sample lattice (kSampleSplit parts).
+    const int chunk = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x - chunk * a.ntiles;
 
     if (threadIdx.x < kTileQ) {
         const int n = threadIdx.x;
@@ -418,10 +417,14 @@ __global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
     // steps index the lattice first_b + e * dmin, e < nlat.
     int jlo, jhi, first_b = 0, nlat = 0;
     if (MODE == kModeSample) {
-        first_b = (lo + dmin - 1) / dmin * dmin;
+        const int msh = __builtin_ctz((unsigned)dmin);  // power of two
+        first_b = ((lo + dmin - 1) >> msh) << msh;
         nlat = (int)lattice_count(lo, hi, dmin);
-        jlo = 0;
-        jhi = (nlat + kStepKeys - 1) / kStepKeys;
+        const int nsteps = (nlat + kStepKeys - 1) / kStepKeys;
+        const int per = (nsteps + kSampleSplit - 1) / kSampleSplit;
+        jlo = chunk * per;
+        jhi = min(nsteps, jlo + per);
+        if (jhi <= jlo) return;
     } else {
         const int64_t c0 = (int64_t)chunk * kChunkKeys;
         const int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + kChunkKeys);
@@ -447,8 +450,9 @@ __global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
 
     float tau = __builtin_inff();
     if (MODE == kModeFilter && t >= 0) tau = a.tau[t];
-    const int dn = s_d[n];
-    const int first_n = (rks + dn - 1) / dn * dn;
+    const int dn = s_d[n];                       // power of two
+    const int dsh = __builtin_ctz((unsigned)dn);
+    const int first_n = ((rks + dn - 1) >> dsh) << dsh;
     uint64_t *ring = s_ring + (MODE == kModeFilter ? wave * kTileQ * RS : 0);
     uint32_t ring_cnt = 0;
 
@@ -478,10 +482,10 @@ __global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
                 for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
             }
         };
-        if (ScoreCfg<DT>::prefetch) load_sh();
+        if (Cfg::prefetch) load_sh();
         StepOut o;
         score_step(o, kf, s_q, s_w, lane);
-        if (!ScoreCfg<DT>::prefetch) load_sh();
+        if (!Cfg::prefetch) load_sh();
         if (MODE == kModeFilter) {
             // Keep (row, key) when the key is in the row's window and its
             // score reaches the row's threshold (take-all rows: -inf).
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
                     if (t < 0 || e >= nlat) continue;
                     const int p = first_b + e * dmin;
                     if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
-                    const int idx = (p - first_n) / dn;
+                    const int idx = (p - first_n) >> dsh;
                     a.samp[(int64_t)t * a.sample_target + idx] =
                         ord_of(score_of<DT>(o, kt, i, qsc, sigh_of<DT>(a.sigma, p)));
                 }
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(64 * ScoreCfg<DT>::waves) void k_score(ScoreArgs a)
     };
 
     // Steps of this wave: jlo + wave, + kWaves, ...
-    if (ScoreCfg<DT>::prefetch) {
+    if (Cfg::prefetch) {
         // Two fragment sets alternate so the next step's keys load while this
         // step computes.
         KFrag<DT> ka[kSub], kb[kSub];

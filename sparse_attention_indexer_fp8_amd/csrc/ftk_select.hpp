@@ -30,10 +30,10 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxTopk = 4096;
 
 // ---------------------------------------------------------------------------
-// Block-wide radix select.  `fetch(i)` returns element i (i < n).  Returns the
-// smallest key T such that exactly k elements are >= T (the k-th largest key,
-// or a lower bound with the same count).  All threads of the block must call
-// it; k must satisfy 1 <= k <= n.  Uses the caller's LDS scratch.
+// Block-wide radix select.  `each(f)` calls f(key) for every element this
+// thread owns.  Returns the smallest key T such that exactly k elements are
+// >= T (the k-th largest key, or a lower bound with the same count).  All
+// threads of the block must call it; k must satisfy 1 <= k <= n.
 
 struct RadixLds {
     uint32_t hist[kSelWaves][256];
@@ -42,8 +42,8 @@ struct RadixLds {
     uint32_t digit;
 };
 
-template <typename KeyT, int NDIGITS, typename Fetch>
-__device__ KeyT radix_select_kth(RadixLds &L, Fetch fetch, int64_t n, uint32_t k)
+template <typename KeyT, int NDIGITS, typename Each>
+__device__ KeyT radix_select_kth(RadixLds &L, Each each, uint32_t k)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int BITS = 8 * sizeof(KeyT);
@@ -53,12 +53,11 @@ __device__ KeyT radix_select_kth(RadixLds &L, Fetch fetch, int64_t n, uint32_t k
         const int shift = BITS - 8 * (p + 1);
         for (int i = tid; i < kSelWaves * 256; i += blockDim.x) (&L.hist[0][0])[i] = 0;
         __syncthreads();
-        for (int64_t i = tid; i < n; i += blockDim.x) {
-            const KeyT e = fetch(i);
-            const bool match = (p == 0) || (((e ^ prefix) >> (shift + 8)) == 0);
+        each([&](KeyT e, bool valid) {
+            const bool match = valid && ((p == 0) || (((e ^ prefix) >> (shift + 8)) == 0));
             const uint32_t dig = (uint32_t)(e >> shift) & 255u;
             // Lanes that share the first active lane's digit add once: the
-            // candidates of a row crowd into few digits, and same-address LDS
+            // keys of a row crowd into few digits, and same-address LDS
             // atomics would serialise.
             const uint64_t act = __ballot(match);
             if (act) {
@@ -69,7 +68,7 @@ __device__ KeyT radix_select_kth(RadixLds &L, Fetch fetch, int64_t n, uint32_t k
                 if (lane == leader) atomicAdd(&L.hist[wave][ld], (uint32_t)__builtin_popcountll(sm));
                 if (match && !same) atomicAdd(&L.hist[wave][dig], 1u);
             }
-        }
+        });
         __syncthreads();
         if (tid < 256) {
             uint32_t s = 0;
@@ -110,6 +109,50 @@ __device__ KeyT radix_select_kth(RadixLds &L, Fetch fetch, int64_t n, uint32_t k
     return prefix;
 }
 
+// Elements of a row, as a visitor over the calling thread's share: either
+// held in registers (NREG > 0: at most NREG per thread, all loads in flight
+// at once) or streamed from memory on every visit (NREG == 0).
+template <int NREG>
+struct RowElems {
+    static constexpr bool REG = NREG > 0;
+    static constexpr int kRegPer = REG ? NREG : 1;
+    const uint64_t *src;
+    int64_t n;
+    uint64_t r[kRegPer];
+
+    __device__ __forceinline__ void load(const uint64_t *p, int64_t cnt)
+    {
+        src = p;
+        n = cnt;
+        if (REG) {
+#pragma unroll
+            for (int q = 0; q < kRegPer; ++q) {
+                const int64_t i = threadIdx.x + (int64_t)q * blockDim.x;
+                r[q] = i < n ? p[i] : 0ull;
+            }
+        }
+    }
+    // f(raw, valid): visits this thread's elements; REG visits every slot so
+    // wave-wide operations inside f see all lanes.
+    template <typename F>
+    __device__ __forceinline__ void each(F f) const
+    {
+        if (REG) {
+#pragma unroll
+            for (int q = 0; q < kRegPer; ++q) {
+                const int64_t i = threadIdx.x + (int64_t)q * blockDim.x;
+                if (__any(i < n)) f(r[q], i < n);
+            }
+        } else {
+            const int64_t rounds = (n + blockDim.x - 1) / blockDim.x;
+            for (int64_t q = 0; q < rounds; ++q) {
+                const int64_t i = threadIdx.x + q * blockDim.x;
+                f(i < n ? src[i] : 0ull, i < n);
+            }
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Per-row threshold from the row's strided sample.
 
@@ -126,24 +169,109 @@ struct TauArgs {
     uint32_t *cnt;
 };
 
-__global__ __launch_bounds__(kSelThreads) void k_tau(TauArgs a)
+// The threshold needs no exact rank -- only the candidate count it admits
+// matters, and triage catches any row it misjudges -- so the sample is
+// bucketed linearly in score (kTauBuckets buckets between the sample's
+// minimum and maximum, highest first) and the threshold is the lower edge of
+// the bucket that holds the r-th largest sample.  At least r samples reach it.
+constexpr int kTauThreads = 256;
+constexpr int kTauBuckets = 2048;
+
+__global__ __launch_bounds__(kTauThreads) void k_tau(TauArgs a)
 {
-    __shared__ RadixLds L;
-    const int t = blockIdx.x;
+    __shared__ uint32_t s_b[kTauBuckets];
+    __shared__ float s_red[2 * (kTauThreads / 64)];
+    __shared__ uint32_t s_tot[kTauThreads / 64];
+    __shared__ float s_tau;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = kTauThreads / 64, PER = kTauBuckets / kTauThreads;
     const int64_t lo = a.ks[t], hi = a.ke[t];
     const int64_t len = hi > lo ? hi - lo : 0;
-    if (threadIdx.x == 0) a.cnt[t] = 0;
+    if (tid == 0) a.cnt[t] = 0;
     if (a.recover_all || len <= a.cap) {
-        if (threadIdx.x == 0) a.tau[t] = a.recover_all ? __builtin_inff() : -__builtin_inff();
+        if (tid == 0) a.tau[t] = a.recover_all ? __builtin_inff() : -__builtin_inff();
         return;
     }
     const int d = sample_stride(len, a.sample_target);
-    const int64_t ns = lattice_count(lo, hi, d);
-    double want = ceil(2.0 * (double)a.topk * (double)ns / (double)len * (double)a.rank_scale);
-    uint32_t r = (uint32_t)min(max(want, 1.0), (double)ns);
+    const int ns = (int)lattice_count(lo, hi, d);
+    const double want = ceil(2.0 * (double)a.topk * (double)ns / (double)len * (double)a.rank_scale);
+    const uint32_t r = (uint32_t)min(max(want, 1.0), (double)ns);
     const uint32_t *row = a.samp + (int64_t)t * a.sample_target;
-    uint32_t kth = radix_select_kth<uint32_t, 4>(L, [&](int64_t i) { return row[i]; }, ns, r);
-    if (threadIdx.x == 0) a.tau[t] = float_of_ord(kth);
+    // Visits this thread's samples in register chunks of 8 (loads in flight
+    // together); one chunk covers the default sample size.
+    constexpr int CH = 8;
+    auto each = [&](auto f) {
+        for (int base = 0; base < ns; base += CH * kTauThreads) {
+            float v[CH];
+#pragma unroll
+            for (int q = 0; q < CH; ++q) {
+                const int i = base + tid + q * kTauThreads;
+                v[q] = i < ns ? float_of_ord(row[i]) : __builtin_nanf("");
+            }
+#pragma unroll
+            for (int q = 0; q < CH; ++q)
+                if (base + tid + q * kTauThreads < ns) f(v[q]);
+        }
+    };
+    float vmin = __builtin_inff(), vmax = -__builtin_inff();
+    each([&](float f) {
+        vmin = fminf(vmin, f);
+        vmax = fmaxf(vmax, f);
+    });
+    for (int off = 32; off > 0; off >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, off));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    }
+    if (lane == 0) {
+        s_red[wave] = vmin;
+        s_red[NW + wave] = vmax;
+    }
+    for (int i = tid; i < kTauBuckets; i += kTauThreads) s_b[i] = 0;
+    __syncthreads();
+    vmin = s_red[0];
+    vmax = s_red[NW];
+    for (int w = 1; w < NW; ++w) {
+        vmin = fminf(vmin, s_red[w]);
+        vmax = fmaxf(vmax, s_red[NW + w]);
+    }
+    const float scale = (float)kTauBuckets / (vmax - vmin);
+    if (!(vmax > vmin) || !__builtin_isfinite(scale)) {
+        if (tid == 0) a.tau[t] = vmin;  // all samples equal: admit them all
+        return;
+    }
+    each([&](float f) {
+        const float x = (vmax - f) * scale;
+        atomicAdd(&s_b[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
+    });
+    __syncthreads();
+    uint32_t c[PER], run = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        c[q] = s_b[tid * PER + q];
+        run += c[q];
+    }
+    uint32_t x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tot[wave] = x;
+    __syncthreads();
+    uint32_t base = x - run;
+    for (int w = 0; w < wave; ++w) base += s_tot[w];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (base < r && r <= base + c[q]) {
+            // One bucket below the lower edge of bucket b, so rounding cannot
+            // leave a sample of buckets 0..b under the threshold.
+            const int b = tid * PER + q;
+            s_tau = vmax - (float)(b + 2) / scale;
+        }
+        base += c[q];
+    }
+    __syncthreads();
+    if (tid == 0) a.tau[t] = s_tau;
 }
 
 // ---------------------------------------------------------------------------
@@ -178,6 +306,9 @@ __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
     if (tid < kStCount) s_st[tid] = 0;
     if (tid == 0) s_base = 0;
     __syncthreads();
+    // Per-thread tallies, reduced per wave at the end (no per-row atomics).
+    uint32_t n_empty = 0, n_take = 0, n_samp = 0, n_under = 0, n_over = 0, maxc = 0;
+    unsigned long long win = 0;
     for (int64_t b0 = 0; b0 < a.num_q; b0 += 1024) {
         const int64_t t = b0 + tid;
         bool flag = false;
@@ -186,7 +317,7 @@ __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
             const int64_t len = hi > lo ? hi - lo : 0;
             const uint32_t c = a.cnt[t];
             if (len == 0) {
-                atomicAdd(&s_st[kStEmpty], 1ull);
+                ++n_empty;
             } else if (a.recover_all) {
                 flag = true;
             } else {
@@ -195,15 +326,15 @@ __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
                 const bool over = (int64_t)c > a.cap;
                 flag = under || over;
                 if (len <= a.cap) {
-                    atomicAdd(&s_st[kStTakeAll], 1ull);
+                    ++n_take;
                 } else {
-                    atomicAdd(&s_st[kStSampled], 1ull);
-                    atomicMax(&s_st[kStMaxCand], (unsigned long long)c);
+                    ++n_samp;
+                    maxc = max(maxc, c);
                 }
-                if (under) atomicAdd(&s_st[kStUnder], 1ull);
-                if (over) atomicAdd(&s_st[kStOver], 1ull);
+                n_under += under;
+                n_over += over;
             }
-            atomicAdd(&s_st[kStWindow], (unsigned long long)len);
+            win += (unsigned long long)len;
             a.rowflag[t] = flag ? 1 : 0;
         }
         // Order-preserving compaction of the flagged rows.
@@ -216,12 +347,31 @@ __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
         if (flag) a.rowlist[off + below] = (int32_t)t;
         __syncthreads();
         if (tid == 0) {
-            uint32_t s = 0;
-            for (int w = 0; w < 16; ++w) s += s_wave[w];
-            s_base += s;
+            uint32_t sum = 0;
+            for (int w = 0; w < 16; ++w) sum += s_wave[w];
+            s_base += sum;
         }
         __syncthreads();
     }
+    for (int off = 32; off > 0; off >>= 1) {
+        n_empty += __shfl_xor(n_empty, off);
+        n_take += __shfl_xor(n_take, off);
+        n_samp += __shfl_xor(n_samp, off);
+        n_under += __shfl_xor(n_under, off);
+        n_over += __shfl_xor(n_over, off);
+        maxc = max(maxc, (uint32_t)__shfl_xor(maxc, off));
+        win += __shfl_xor(win, off);
+    }
+    if (lane == 0) {
+        atomicAdd(&s_st[kStEmpty], (unsigned long long)n_empty);
+        atomicAdd(&s_st[kStTakeAll], (unsigned long long)n_take);
+        atomicAdd(&s_st[kStSampled], (unsigned long long)n_samp);
+        atomicAdd(&s_st[kStUnder], (unsigned long long)n_under);
+        atomicAdd(&s_st[kStOver], (unsigned long long)n_over);
+        atomicMax(&s_st[kStMaxCand], (unsigned long long)maxc);
+        atomicAdd(&s_st[kStWindow], win);
+    }
+    __syncthreads();
     if (tid == 0) {
         *a.nflagged = (int32_t)s_base;
         s_st[kStRows] = (unsigned long long)a.num_q;
@@ -279,9 +429,12 @@ struct SelectLds {
 
 __device__ __forceinline__ float raw_score(uint64_t r) { return __uint_as_float((uint32_t)r); }
 
-template <bool DENSE>
+// NREG == 0: dense (recovered) rows streamed from scratch; otherwise the
+// row's candidates (count <= NREG * kSelThreads) are held in registers.
+template <int NREG>
 __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
 {
+    constexpr bool DENSE = NREG == 0;
     __shared__ SelectLds S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int t;
@@ -298,11 +451,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
         t = blockIdx.x;
         if (a.rowflag[t]) return;
         src = a.cand + (int64_t)t * a.cap;
-        n = min((int64_t)a.cnt[t], (int64_t)a.cap);
+        n = min((int64_t)a.cnt[t], (int64_t)a.cap);  // a.cap <= NREG * kSelThreads
     }
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
     int32_t *oi = a.out_idx + (int64_t)t * a.topk;
     float *ov = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
+    RowElems<NREG> el;
+    el.load(src, n);
 
     bool fast = false;
     float mx = 0.0f, scale = 0.0f;
@@ -310,11 +465,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
     if (k > 0) {
         // Score range of the candidates.
         float lo = __builtin_inff(), hi = -__builtin_inff();
-        for (int64_t i = tid; i < n; i += blockDim.x) {
-            const float f = raw_score(src[i]);
-            lo = fminf(lo, f);
-            hi = fmaxf(hi, f);
-        }
+        el.each([&](uint64_t r, bool v) {
+            if (v) {
+                const float f = raw_score(r);
+                lo = fminf(lo, f);
+                hi = fmaxf(hi, f);
+            }
+        });
         for (int off = 32; off > 0; off >>= 1) {
             lo = fminf(lo, __shfl_xor(lo, off));
             hi = fmaxf(hi, __shfl_xor(hi, off));
@@ -340,7 +497,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
         return x < (float)(kBuckets - 1) ? (uint32_t)x : (uint32_t)(kBuckets - 1);
     };
     if (fast) {
-        for (int64_t i = tid; i < n; i += blockDim.x) atomicAdd(&S.bucket[bucket_of(raw_score(src[i]))], 1u);
+        el.each([&](uint64_t r, bool v) {
+            if (v) atomicAdd(&S.bucket[bucket_of(raw_score(r))], 1u);
+        });
         __syncthreads();
         // Exclusive prefix over buckets; each thread owns kBinsPerThread
         // consecutive buckets and keeps their counts.
@@ -379,11 +538,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
         for (int w = 0; w < kSelWaves; ++w) seg = max(seg, S.redu[w]);
         fast = seg <= (uint32_t)kSegMax;
         if (fast) {
-            for (int64_t i = tid; i < n; i += blockDim.x) {
-                const uint64_t r = src[i];
-                const uint32_t b = bucket_of(raw_score(r));
-                if (b <= kb) S.sel[atomicAdd(&S.bucket[b], 1u)] = key_of_raw(r);
-            }
+            el.each([&](uint64_t r, bool v) {
+                if (v) {
+                    const uint32_t b = bucket_of(raw_score(r));
+                    if (b <= kb) S.sel[atomicAdd(&S.bucket[b], 1u)] = key_of_raw(r);
+                }
+            });
             __syncthreads();
             // Bucket b now spans [bucket[b-1], bucket[b]); sort it descending.
             for (uint32_t b = tid; b <= kb; b += blockDim.x) {
@@ -406,16 +566,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
     if (k > 0 && !fast) {
         uint64_t thr = 0;
         if ((int64_t)k < n)
-            thr = radix_select_kth<uint64_t, 8>(S.radix, [&](int64_t i) { return key_of_raw(src[i]); }, n, k);
+            thr = radix_select_kth<uint64_t, 8>(
+                S.radix, [&](auto f) { el.each([&](uint64_t r, bool v) { f(key_of_raw(r), v); }); }, k);
         if (tid == 0) S.misc[1] = 0;
         __syncthreads();
-        for (int64_t i = tid; i < n; i += blockDim.x) {
-            const uint64_t e = key_of_raw(src[i]);
-            if (e >= thr) {
+        el.each([&](uint64_t r, bool v) {
+            const uint64_t e = key_of_raw(r);
+            if (v && e >= thr) {
                 const uint32_t pos = atomicAdd(&S.misc[1], 1u);
                 if (pos < (uint32_t)kMaxTopk) S.sel[pos] = e;
             }
-        }
+        });
         uint32_t P = 1;
         while (P < k) P <<= 1;
         __syncthreads();
