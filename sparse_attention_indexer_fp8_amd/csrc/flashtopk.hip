@@ -129,6 +129,25 @@ int resolve(Plan &p, const flashtopk_options *opt)
     return FLASHTOPK_OK;
 }
 
+// Keys per work item: large chunks amortise a work item's fixed costs
+// (staging the q tile, flushing candidates), but there must be enough items
+// (about four per compute unit) to fill the GPU.
+int chunk_keys(int ntiles, int64_t S)
+{
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop{};
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            n_cu = std::max(1, prop.multiProcessorCount);
+        else
+            n_cu = 256;
+    }
+    int chunk = kMaxChunk;
+    while (chunk > kMinChunk && (int64_t)ntiles * ((S + chunk - 1) / chunk) < 4 * (int64_t)n_cu) chunk >>= 1;
+    return chunk;
+}
+
 template <int DT>
 void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
 {
@@ -187,7 +206,8 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
 
     const int ntiles = (int)((T + kTileQ - 1) / kTileQ);
-    const int nchunks = (int)std::max<int64_t>(1, (S + kChunkKeys - 1) / kChunkKeys);
+    const int chunk = chunk_keys(ntiles, S);
+    const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
 
     ScoreArgs sa{};
     sa.q = (const uint8_t *)q;
@@ -202,6 +222,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.qbar = (const uint8_t *)w->qbar.ptr;
     sa.qscale = (const float *)w->qscale.ptr;
     sa.ntiles = ntiles;
+    sa.chunk = chunk;
     sa.cap = p.cap;
     sa.tau = (const float *)w->tau.ptr;
     sa.cnt = (uint32_t *)w->cnt.ptr;
@@ -298,13 +319,15 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         sa.scratch = (uint64_t *)w->scratch.ptr;
         sa.scratch_stride = stride;
         sa.ntiles = (int)(rcap / kTileQ);
+        sa.chunk = chunk_keys(sa.ntiles, S);
+        const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
         se.row_limit = (int)rcap;
         se.scratch = (const uint64_t *)w->scratch.ptr;
         se.scratch_stride = stride;
         for (int64_t rb = 0; rb < R; rb += rcap) {
             sa.row_base = (int)rb;
             se.row_base = (int)rb;
-            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * nchunks)), stream, sa);
+            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
             k_select<0><<<dim3((unsigned)rcap), kSelThreads, 0, stream>>>(se);
         }
         e = hipGetLastError();

@@ -14,12 +14,14 @@ constexpr int kDim = 128;
 
 // Work decomposition.  A tile is 16 query rows: the N = 16 columns of a
 // 16x16 MFMA output.  A wave scores kSub 16-key subtiles per step (the M = 16
-// rows), the waves of a workgroup share a tile, and a work item covers
-// kChunkKeys keys.
+// rows), the waves of a workgroup share a tile, and a work item covers one
+// chunk of keys (a power of two between kMinChunk and kMaxChunk, chosen per
+// call so there are enough work items to fill the GPU).
 constexpr int kTileQ = 16;
 constexpr int kSub = 4;
 constexpr int kStepKeys = 16 * kSub;      // 64 keys per wave step
-constexpr int kChunkKeys = 8192;          // keys per work item
+constexpr int kMinChunk = 1024;
+constexpr int kMaxChunk = 32768;
 
 constexpr int kFP8 = 0;
 constexpr int kBF16 = 1;

@@ -85,6 +85,7 @@ struct ScoreArgs {
     int num_q;
     int num_kv;
     int ntiles;                // tiles along the grid's fast index
+    int chunk;                 // keys per work item (filter and dense modes)
     int cap;                   // candidate capacity per row
     // filter mode
     const float *tau;          // [num_q] per-row threshold (-inf: take all)
@@ -170,6 +171,15 @@ struct StepOut {
     v4f lin[kSub];        // FP8: sum_p part_p . k (unscaled qbar . k)
 };
 
+// First head of a step: acc = w |x| (no zeroing pass).
+__device__ __forceinline__ void epi_abs_first(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
+{
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[kt][i] = w * __builtin_fabsf(x[kt][i]);
+}
+
 __device__ __forceinline__ void epi_abs(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
 {
 #pragma unroll
@@ -198,23 +208,26 @@ __device__ __forceinline__ void mfma_fp8_head(v4f (&x)[kSub], const KFrag<kFP8> 
         x[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt].a, qf, c[kt], 0, 0, 0, 0, 0, 0);
 }
 
+template <typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[kSub], const uint8_t *s_q,
-                                           const float *s_w, int lane)
+                                           const float *s_w, int lane, AfterMfma after_mfma)
 {
     constexpr int HB = 2048;  // LDS bytes per head of the q tile
     const v4f z[kSub] = {};
-#pragma unroll
-    for (int kt = 0; kt < kSub; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.acc[kt][i] = 0.0f;
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
     // Two result sets alternate: the epilogue of head h-1 runs while the
-    // MFMAs of head h execute.
+    // MFMAs of head h execute.  The first epilogue initialises acc.
     v4f xa[kSub], xb[kSub];
     mfma_fp8_head(xa, kf, qp, z);
+    mfma_fp8_head(xb, kf, qp + HB, z);
+    epi_abs_first(o.acc, xa, wp[0]);
+    mfma_fp8_head(xa, kf, qp + 2 * HB, z);
+    epi_abs(o.acc, xb, wp[kTileQ]);
+    qp += 2 * HB;
+    wp += 2 * kTileQ;
 #pragma unroll 1
-    for (int h = 1; h < kHeads - 1; h += 2) {
+    for (int h = 3; h < kHeads - 1; h += 2) {
         const float w0 = wp[0], w1 = wp[kTileQ];
         mfma_fp8_head(xb, kf, qp + HB, z);
         epi_abs(o.acc, xa, w0);
@@ -231,6 +244,7 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     mfma_fp8_head(o.lin, kf, pp + HB, o.lin);
     epi_abs(o.acc, xb, wp[kTileQ]);
     mfma_fp8_head(o.lin, kf, pp + 2 * HB, o.lin);
+    after_mfma();  // the key fragments are free from here on
 }
 
 __device__ __forceinline__ v4f mfma_bf16_d128(const KFrag<kBF16> &k, const v4i (&qf)[4])
@@ -253,8 +267,9 @@ __device__ __forceinline__ void mfma_bf16_head(v4f (&x)[kSub], const KFrag<kBF16
     for (int kt = 0; kt < kSub; ++kt) x[kt] = mfma_bf16_d128(kf[kt], qf);
 }
 
+template <typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[kSub], const uint8_t *s_q,
-                                           const float *s_w, int lane)
+                                           const float *s_w, int lane, AfterMfma after_mfma)
 {
     // One head is 16 MFMAs here, so a one-head lag already covers the MFMA
     // latency and two result sets suffice (the key fragments take 128
@@ -279,6 +294,7 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[
         wp += 2 * kTileQ;
     }
     mfma_bf16_head(xb, kf, qp + HB);
+    after_mfma();
     epi_relu(o.acc, xa, wp[0]);
     epi_relu(o.acc, xb, wp[kTileQ]);
 }
@@ -426,8 +442,8 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         jhi = min(nsteps, jlo + per);
         if (jhi <= jlo) return;
     } else {
-        const int64_t c0 = (int64_t)chunk * kChunkKeys;
-        const int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + kChunkKeys);
+        const int64_t c0 = (int64_t)chunk * a.chunk;
+        const int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + a.chunk);
         if (khi <= klo) return;
         jlo = (int)(klo / kStepKeys);
         jhi = (int)((khi + kStepKeys - 1) / kStepKeys);
@@ -467,8 +483,10 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         }
     };
 
-    // Scores one step and hands its 16 outputs per lane to the mode's sink.
-    auto process = [&](const KFrag<DT>(&kf)[kSub], int j) {
+    // Scores one step and hands its 16 outputs per lane to the mode's sink;
+    // `next` runs as soon as the step's MFMAs no longer need the key
+    // fragments (it issues the next step's key loads).
+    auto process = [&](KFrag<DT>(&kf)[kSub], int j, auto next) {
         const int sb = j * kStepKeys + 4 * g;  // key of element (kt, i) is sb + 16 kt + i
         // Scale factors of the step's outputs (4 consecutive keys per
         // subtile), loaded before the MFMA work so their latency hides.
@@ -484,7 +502,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         };
         if (Cfg::prefetch) load_sh();
         StepOut o;
-        score_step(o, kf, s_q, s_w, lane);
+        score_step(o, kf, s_q, s_w, lane, next);
         if (!Cfg::prefetch) load_sh();
         if (MODE == kModeFilter) {
             // Keep (row, key) when the key is in the row's window and its
@@ -573,6 +591,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     };
 
     // Steps of this wave: jlo + wave, + kWaves, ...
+    auto nop = []() {};
     if (Cfg::prefetch) {
         // Two fragment sets alternate so the next step's keys load while this
         // step computes.
@@ -581,16 +600,22 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         if (j < jhi) load_step(ka, j);
         for (; j < jhi; j += 2 * kWaves) {
             if (j + kWaves < jhi) load_step(kb, j + kWaves);
-            process(ka, j);
+            process(ka, j, nop);
             if (j + kWaves >= jhi) break;
             if (j + 2 * kWaves < jhi) load_step(ka, j + 2 * kWaves);
-            process(kb, j + kWaves);
+            process(kb, j + kWaves, nop);
         }
     } else {
-        for (int j = jlo + wave; j < jhi; j += kWaves) {
-            KFrag<DT> kf[kSub];
-            load_step(kf, j);
-            process(kf, j);
+        // One fragment set: the next step's keys load into it as soon as this
+        // step's last MFMA is issued, so the sink hides their latency.
+        KFrag<DT> kf[kSub];
+        int j = jlo + wave;
+        if (j < jhi) load_step(kf, j);
+        for (; j < jhi; j += kWaves) {
+            const int jn = j + kWaves;
+            process(kf, j, [&]() {
+                if (jn < jhi) load_step(kf, jn);
+            });
         }
     }
     if (MODE == kModeFilter) {
