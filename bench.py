@@ -20,6 +20,7 @@ import argparse
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -44,7 +45,54 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device-to-device (3 times), the reference for HBM counters")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("ftk_common.hpp", "ftk_qbar.hpp", "ftk_score.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_score_filter_fp8_trained_4096x131072_k2048.md")
+
+
+def kernel_digest():
+    """SHA-256 of the fused filter kernel's sources (the traffic figure is
+    only valid for the sources it was measured on)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_indexer_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the filter kernel from the committed rocprofv3
+    counter summary, or None if it is missing or was taken on other sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^- (\w+): (\S+)", text, re.M))
+    if vals.get("kernel_digest") != kernel_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes):
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes}), flush=True)
 
 
 def cpu_baseline(wl, target_s):
@@ -91,6 +139,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is design-only",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
 
@@ -155,6 +207,7 @@ def main():
         for k in phases:
             phases[k].append(pi[k])
     kern = {k[3:]: float(np.mean(v)) for k, v in phases.items()}
+    traffic = recorded_traffic() if (args.workload == 4 and not args.integer_twin and dt == "fp8") else None
     filt_ms = kern["filter"]
     flops = float(FLOP_PER_PAIR) * pairs
     peak = PEAK_TFLOPS[dt]
@@ -186,8 +239,8 @@ def main():
         "max_candidates": info["max_candidates"],
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "roofline": {"bound": "mfma", "kernel": "k_score<filter>", "achieved": round(achieved, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "flops_per_launch": flops},
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "flops_per_launch": flops},
     }
     if not args.no_cpu:
         print("bench: cpu oracle leg", file=sys.stderr, flush=True)
