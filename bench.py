@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=4, help="named workload 1..5 (4 is the headline)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="named workload 1..6 (4 is the headline; 6 has block-local keys for pruning)")
     ap.add_argument("--integer-twin", action="store_true")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scan, 2 prune, 3 recover all")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
@@ -235,6 +236,7 @@ def main():
         "dense_equiv_tflops": round(whole, 1),
         "wall_ms_per_step": round(wall_ms, 4),
         "pruned_key_fraction": info["pruned_keys"] / max(1, info["window_keys"]),
+        "path_taken": {1: "scan", 2: "prune", 3: "recover"}.get(info["path"], "?"),
         "rows_recovered": info["rows_recovered"],
         "max_candidates": info["max_candidates"],
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},

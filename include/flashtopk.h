@@ -113,8 +113,10 @@ typedef struct flashtopk_info {
     int32_t cand_capacity;      /* capacity used */
     int32_t sample_target;      /* sample size used */
     /* Device time of each phase in milliseconds when the call ran with
-     * options.profile set, else 0: strided-sample scoring, per-row threshold,
-     * fused score + filter, triage, candidate selection, dense recovery. */
+     * options.profile set, else 0: strided-sample scoring (with the per-key
+     * and per-row preparation passes), per-row threshold, fused score +
+     * filter (with the score bound), triage, candidate selection, dense
+     * recovery. */
     float ms_sample, ms_tau, ms_filter, ms_triage, ms_select, ms_recover;
 } flashtopk_info;
 

@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "flashtopk.h"
+#include "ftk_bound.hpp"
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
 
@@ -43,6 +44,7 @@ struct Workspace {
     int device = -1;
     hipStream_t stream = nullptr;
     DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch, qbar, qscale, sigh;
+    DevBuf kb, kmeta, vplan, plan, q1;         // score-bound pruning
     unsigned long long *host_stats = nullptr;  // pinned
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
@@ -125,7 +127,6 @@ int resolve(Plan &p, const flashtopk_options *opt)
     p.rank_scale = (opt && opt->sample_rank_scale > 0.0f) ? opt->sample_rank_scale : 1.0f;
     p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
     p.profile = (opt && opt->profile) ? 1 : 0;
-    if (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE) p.path = FLASHTOPK_PATH_SCAN;
     return FLASHTOPK_OK;
 }
 
@@ -206,6 +207,17 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
 
     const int ntiles = (int)((T + kTileQ - 1) / kTileQ);
+    // Score-bound pruning: on the auto path (each scan work item decides from
+    // its tile's planner sample) and the forced prune path.
+    const bool bounds = S > 0 && (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE);
+    const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
+    if (bounds) {
+        if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
+        if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)nblocks))) return st;
+        if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
+        if ((st = ensure(*w, w->plan, sizeof(unsigned long long) * kPlanCount))) return st;
+        if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
+    }
     const int chunk = chunk_keys(ntiles, S);
     const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
 
@@ -229,16 +241,36 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.cand = (uint64_t *)w->cand.ptr;
     sa.samp = (uint32_t *)w->samp.ptr;
     sa.sample_target = p.sample_target;
+    if (bounds) {
+        sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
+        sa.kb = (const uint8_t *)w->kb.ptr;
+        sa.meta = (const float2 *)w->kmeta.ptr;
+        sa.q1 = (const float *)w->q1.ptr;
+        sa.nblocks = nblocks;
+        sa.vplan = (float *)w->vplan.ptr;
+        sa.plan = (unsigned long long *)w->plan.ptr;
+    }
 
     mark(*w, p, 0, stream);
     {
-        const unsigned nb = (unsigned)std::min<int64_t>(1024, (S + 64 + 255) / 256);
-        if (fp8) k_sigh<kFP8><<<nb, 256, 0, stream>>>(kv_scales, (int)S, (float *)w->sigh.ptr);
-        else k_sigh<kBF16><<<nb, 256, 0, stream>>>(kv_scales, (int)S, (float *)w->sigh.ptr);
+        // Per-key scale factors (and block extremes for the bound).
+        const unsigned nwg = (unsigned)((S + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
+        uint8_t *kbp = bounds ? (uint8_t *)w->kb.ptr : nullptr;
+        float2 *kmp = bounds ? (float2 *)w->kmeta.ptr : nullptr;
+        unsigned long long *plp = bounds ? (unsigned long long *)w->plan.ptr : nullptr;
+        if (fp8)
+            k_keyprep<kFP8><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)S, nblocks,
+                                                     (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, plp);
+        else
+            k_keyprep<kBF16><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)S, nblocks,
+                                                      (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, plp);
     }
+    const dim3 rgrid((unsigned)((T + 3) / 4));
     if (fp8)
-        k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T, (uint8_t *)w->qbar.ptr,
-                                                                 (float *)w->qscale.ptr);
+        k_qbar<<<rgrid, 256, 0, stream>>>((const uint8_t *)q, weights, T, (uint8_t *)w->qbar.ptr,
+                                          (float *)w->qscale.ptr, bounds ? (float *)w->q1.ptr : nullptr);
+    else if (bounds)
+        k_qnorm_bf16<<<rgrid, 256, 0, stream>>>((const uint8_t *)q, weights, T, (float *)w->q1.ptr);
     if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * kSampleSplit)), stream, sa);
     mark(*w, p, 1, stream);
 
@@ -271,6 +303,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     tr.rowlist = (int32_t *)w->rowlist.ptr;
     tr.nflagged = (int32_t *)w->nflagged.ptr;
     tr.stats = (unsigned long long *)w->stats.ptr;
+    tr.plan = bounds ? (const unsigned long long *)w->plan.ptr : nullptr;
     k_triage<<<1, 1024, 0, stream>>>(tr);
     // The triage counts go to pinned host memory right away; the host waits
     // for them (not for the stream) while the select kernel runs, so the GPU
@@ -350,7 +383,8 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     std::memset(&info, 0, sizeof(info));
     const unsigned long long *hs = w->host_stats;
     info.status = FLASHTOPK_OK;
-    info.path = p.path;
+    info.path = recover_all ? FLASHTOPK_PATH_RECOVER
+                            : (hs[kStPruneOn] ? FLASHTOPK_PATH_PRUNE : FLASHTOPK_PATH_SCAN);
     info.rows = (int64_t)hs[kStRows];
     info.rows_empty = (int64_t)hs[kStEmpty];
     info.rows_take_all = (int64_t)hs[kStTakeAll];
@@ -360,7 +394,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     info.rows_recovered = R;
     info.max_candidates = (int64_t)hs[kStMaxCand];
     info.window_keys = (int64_t)hs[kStWindow];
-    info.pruned_keys = 0;
+    info.pruned_keys = (int64_t)hs[kStPruned];
     info.cand_capacity = p.cap;
     info.sample_target = p.sample_target;
     info.ms_sample = phase_ms(*w, p, 0);
@@ -461,7 +495,8 @@ void flashtopk_release(void)
         (void)hipSetDevice(w->device);
         (void)hipStreamSynchronize(w->stream);
         DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowflag, &w->rowlist, &w->nflagged, &w->stats,
-                          &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh};
+                          &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh,
+                          &w->kb, &w->kmeta, &w->vplan, &w->plan, &w->q1};
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);

@@ -107,4 +107,9 @@ __device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi
     return (hi - 1 - first) / d + 1;
 }
 
+// Counters of the score-bound pruning (zeroed by the per-key pass, written
+// by the scan, read by triage): (row, key) pairs skipped, and work items
+// that evaluated the bound.
+enum PlanCounter { kPlanPruned = 0, kPlanItems, kPlanCount };
+
 }  // namespace ftk

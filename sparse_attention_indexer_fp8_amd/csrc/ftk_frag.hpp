@@ -1,0 +1,62 @@
+// MFMA operand fragments of the scoring and bound kernels, and the per-key
+// scale factor they apply.
+//
+// Both operands of an MFMA use the same assignment of the 128 dimensions to
+// (lane group, byte) slots -- lane group g = lane / 16 holds dimensions
+// [32g, 32g+32) -- so a contraction covers every dimension exactly once.
+//   A (keys, M = 16 rows): lane (n, g) holds row n's slice, read from global.
+//   B (queries, N = 16 columns): lane (n, g) holds column n's slice, read
+//   from the q tile in LDS (slot layout: see stage_q_heads).
+#pragma once
+
+#include "ftk_common.hpp"
+
+namespace ftk {
+
+template <int DT> struct KFrag;
+template <> struct KFrag<kFP8> { v8i a; };
+template <> struct KFrag<kBF16> { v4i a[4]; };
+
+// Key row p, lane group g: dimensions [32g, 32g+32).
+__device__ __forceinline__ void load_kfrag(KFrag<kFP8> &f, const uint8_t *kv, int p, int g)
+{
+    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 128 + 32 * g);
+    const v4i lo = src[0], hi = src[1];
+    f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, int p, int g)
+{
+    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 256 + 64 * g);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) f.a[m] = src[m];
+}
+
+template <int DT> struct BFrag;
+template <> struct BFrag<kFP8> { v8i a; };
+template <> struct BFrag<kBF16> { v4i a[4]; };
+
+// A query fragment of the LDS q tile; qp points at the lane's slot of the head.
+__device__ __forceinline__ void load_bfrag(BFrag<kFP8> &f, const uint8_t *qp)
+{
+    const v4i lo = *reinterpret_cast<const v4i *>(qp);
+    const v4i hi = *reinterpret_cast<const v4i *>(qp + 1024);
+    f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ void load_bfrag(BFrag<kBF16> &f, const uint8_t *qp)
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m) f.a[m] = *reinterpret_cast<const v4i *>(qp + m * 1024);
+}
+
+// Scale factor of key p as the scoring kernels apply it (sigh): sigma on the
+// BF16 path, sigma / 2 on the FP8 path (its score is sigma/2 * (...)).
+template <int DT>
+__device__ __forceinline__ float sigh_of(const float *sigma, int p)
+{
+    const float sg = sigma ? sigma[p] : 1.0f;
+    return DT == kFP8 ? sg * 0.5f : sg;
+}
+
+}  // namespace ftk

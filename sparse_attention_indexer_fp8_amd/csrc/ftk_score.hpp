@@ -36,7 +36,9 @@
 // so the contraction covers every dimension exactly once.
 #pragma once
 
+#include "ftk_bound.hpp"
 #include "ftk_common.hpp"
+#include "ftk_frag.hpp"
 #include "ftk_qbar.hpp"
 
 namespace ftk {
@@ -101,29 +103,15 @@ struct ScoreArgs {
     int row_limit;             // entries per batch
     uint64_t *scratch;         // [row_limit, scratch_stride] keys
     int64_t scratch_stride;
+    // score-bound pruning (sample and filter modes)
+    int prune;                 // 0: off; 1: per tile, from its planner sample; 2: always
+    const uint8_t *kb;         // [nblocks, 2, 128] block extremes
+    const float2 *meta;        // [nblocks] (sigmax, kabs)
+    const float *q1;           // [num_q] sum_h |w| ||q_h||_1
+    int nblocks;
+    float *vplan;              // [ntiles, kPlanGroups, 16 blocks, 16 rows] planner sample
+    unsigned long long *plan;  // PlanCounter
 };
-
-// ---------------------------------------------------------------------------
-// Operand fragments.
-
-template <int DT> struct KFrag;
-template <> struct KFrag<kFP8> { v8i a; };
-template <> struct KFrag<kBF16> { v4i a[4]; };
-
-// Key row p, lane group g: dimensions [32g, 32g+32).
-__device__ __forceinline__ void load_kfrag(KFrag<kFP8> &f, const uint8_t *kv, int p, int g)
-{
-    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 128 + 32 * g);
-    const v4i lo = src[0], hi = src[1];
-    f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-__device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, int p, int g)
-{
-    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 256 + 64 * g);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) f.a[m] = src[m];
-}
 
 // LDS layout of the q tile: for head h, the 64 lanes' fragments are stored as
 // consecutive 16-byte slots, slot (h, sub, lane) at ((h*SUB + sub)*64 + lane)*16
@@ -131,28 +119,55 @@ __device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, i
 // pieces of the lane's 32 (FP8) or 64 (BF16) bytes.  Each ds_read_b128 of a
 // head reads 1 KiB of consecutive LDS, free of bank conflicts.  On the FP8
 // path heads 32..34 hold the qbar parts.
-template <int DT>
-__device__ __forceinline__ void stage_q_tile(uint8_t *s_q, const ScoreArgs &a, const int *s_row)
+// NT threads (the whole workgroup) stage NH heads; each thread's global loads
+// are issued in batches of up to 8 before their LDS stores, so the latency
+// of the tile's reads is paid a few times, not once per piece.
+template <int DT, int NH, int NT>
+__device__ __forceinline__ void stage_q_heads(uint8_t *s_q, const uint8_t *q, const uint8_t *qbar, const int *s_row)
 {
     constexpr int RB = RowBytes<DT>::value;
     constexpr int CPR = RB / 16;    // 16-byte pieces per head row
     constexpr int SUB = CPR / 4;    // pieces per lane group
-    constexpr int TH = TileHeads<DT>::value;
-    constexpr int NCH = kTileQ * TH * CPR;
-    for (int id = threadIdx.x; id < NCH; id += blockDim.x) {
-        const int n = id / (TH * CPR);
-        const int h = (id / CPR) % TH;
-        const int c = id % CPR;
-        const int t = s_row[n];
-        v4i v = {0, 0, 0, 0};
-        if (t >= 0) {
-            const uint8_t *src = (h < kHeads) ? a.q + ((int64_t)t * kHeads + h) * RB
-                                              : a.qbar + ((int64_t)t * kQbarParts + (h - kHeads)) * RB;
-            v = *reinterpret_cast<const v4i *>(src + c * 16);
+    constexpr int NCH = kTileQ * NH * CPR;
+    constexpr int ITER = (NCH + NT - 1) / NT;
+    constexpr int BATCH = ITER < 8 ? ITER : 8;
+#pragma unroll
+    for (int base = 0; base < ITER; base += BATCH) {
+        v4i v[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int id = threadIdx.x + (base + u) * NT;
+            v[u] = (v4i){0, 0, 0, 0};
+            if (base + u < ITER && id < NCH) {
+                const int n = id / (NH * CPR);
+                const int h = (id / CPR) % NH;
+                const int c = id % CPR;
+                const int t = s_row[n];
+                if (t >= 0) {
+                    const uint8_t *src = (h < kHeads) ? q + ((int64_t)t * kHeads + h) * RB
+                                                      : qbar + ((int64_t)t * kQbarParts + (h - kHeads)) * RB;
+                    v[u] = *reinterpret_cast<const v4i *>(src + c * 16);
+                }
+            }
         }
-        const int sub = c % SUB, g = c / SUB;
-        *reinterpret_cast<v4i *>(s_q + ((h * SUB + sub) * 64 + n + 16 * g) * 16) = v;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int id = threadIdx.x + (base + u) * NT;
+            if (base + u < ITER && id < NCH) {
+                const int n = id / (NH * CPR);
+                const int h = (id / CPR) % NH;
+                const int c = id % CPR;
+                const int sub = c % SUB, g = c / SUB;
+                *reinterpret_cast<v4i *>(s_q + ((h * SUB + sub) * 64 + n + 16 * g) * 16) = v[u];
+            }
+        }
     }
+}
+
+template <int DT, int NT>
+__device__ __forceinline__ void stage_q_tile(uint8_t *s_q, const ScoreArgs &a, const int *s_row)
+{
+    stage_q_heads<DT, TileHeads<DT>::value, NT>(s_q, a.q, a.qbar, s_row);
 }
 
 // ---------------------------------------------------------------------------
@@ -309,22 +324,6 @@ __device__ __forceinline__ float score_of(const StepOut &o, int kt, int i, float
     return o.acc[kt][i] * sh;
 }
 
-// Scale factor of key p as stored in sigh, from the caller's kv_scales.
-template <int DT>
-__device__ __forceinline__ float sigh_of(const float *sigma, int p)
-{
-    const float sg = sigma ? sigma[p] : 1.0f;
-    return DT == kFP8 ? sg * 0.5f : sg;
-}
-
-// Fills sigh[0, num_kv + 64): the per-key factor of score_of, zero past the end.
-template <int DT>
-__global__ __launch_bounds__(256) void k_sigh(const float *sigma, int num_kv, float *sigh)
-{
-    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < num_kv + 64; p += gridDim.x * blockDim.x)
-        sigh[p] = p < num_kv ? sigh_of<DT>(sigma, p) : 0.0f;
-}
-
 // ---------------------------------------------------------------------------
 
 // Wave-local LDS ordering: wait for this wave's LDS operations to finish
@@ -374,6 +373,15 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     constexpr int RGB = (MODE == kModeFilter) ? kWaves * kTileQ * RS * 8 : 0;
     __shared__ __attribute__((aligned(16))) uint8_t smem[WB + QB + RGB];
     __shared__ int s_row[kTileQ], s_ks[kTileQ], s_ke[kTileQ], s_d[kTileQ];
+    // Filter mode with pruning: offsets (from jlo) of the steps whose block
+    // is not skipped, in order.
+    constexpr int kMaxSteps = kMaxChunk / kStepKeys;
+    static_assert(MODE != kModeFilter || 64 * kWaves >= kMaxSteps, "one thread per step");
+    __shared__ uint16_t s_steps[MODE == kModeFilter ? kMaxSteps : 1];
+    __shared__ uint16_t s_skip[MODE == kModeFilter ? kMaxSteps / 16 + 1 : 1];  // per 16-block group
+    __shared__ int s_wcnt[kWaves];
+    __shared__ float s_tau[kTileQ], s_q1[kTileQ];
+    __shared__ unsigned long long s_pp[2];  // planner sample: pairs, prunable pairs
     float *s_w = reinterpret_cast<float *>(smem);
     uint8_t *s_q = smem + WB;
     uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + WB + QB);
@@ -411,6 +419,9 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         s_ks[n] = lo;
         s_ke[n] = hi;
         s_d[n] = d;
+        if (MODE == kModeFilter) s_tau[n] = t >= 0 ? a.tau[t] : __builtin_inff();
+        if (MODE != kModeDense && a.prune) s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
+        if (n < 2) s_pp[n] = 0ull;
     }
     __syncthreads();
 
@@ -449,13 +460,125 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         jhi = (int)((khi + kStepKeys - 1) / kStepKeys);
     }
 
-    stage_q_tile<DT>(s_q, a, s_row);
+    stage_q_tile<DT, 64 * kWaves>(s_q, a, s_row);
     for (int i = threadIdx.x; i < kHeads * kTileQ; i += blockDim.x) {
         const int rn = i & (kTileQ - 1), h = i / kTileQ;
         const int rt = s_row[rn];
         s_w[i] = rt >= 0 ? a.w[(int64_t)rt * kHeads + h] : 0.0f;
     }
     __syncthreads();
+
+    int nstep = jhi - jlo;
+    bool use_skip = false;  // workgroup-uniform
+    if (MODE == kModeSample && a.prune == 1 && threadIdx.x < 64 * kPlanGroups) {
+        // Planner sample: the skip test's left side for kPlanGroups groups
+        // spread over the union of ALL the tile's windows (take-all rows
+        // included: they can never be skipped, value +inf).
+        const int ln = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int n = ln & 15, g = ln >> 4;
+        const int64_t tt = (int64_t)tile * kTileQ + n;
+        int rlo = 0, rhi = 0;
+        if (tt < a.num_q) {
+            rlo = a.ks[tt];
+            rhi = max(a.ke[tt], rlo);
+        }
+        int ulo = rhi > rlo ? rlo : 0x7fffffff, uhi = rhi > rlo ? rhi : 0;
+        for (int off = 1; off < 16; off <<= 1) {
+            ulo = min(ulo, __shfl_xor(ulo, off));
+            uhi = max(uhi, __shfl_xor(uhi, off));
+        }
+        const int g0 = ulo / (16 * kBlockKeys), g1 = (uhi + 16 * kBlockKeys - 1) / (16 * kBlockKeys);
+        const int gs = g0 + ((2 * wv + 1) * (g1 - g0)) / (2 * kPlanGroups);
+        const v4f u = bound_group<DT>(a.kb, a.nblocks, gs, s_q + ln * 16, 16 * RB, s_w, ln);
+        const bool sampled = s_row[n] >= 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = gs * 16 + 4 * g + i;
+            const int ov = (b < a.nblocks) ? block_overlap(rlo, rhi, b) : 0;
+            const float v = ov == 0 ? -__builtin_inff()
+                                    : (sampled ? bound_value(u[i], a.meta[min(b, a.nblocks - 1)], s_q1[n])
+                                               : __builtin_inff());
+            a.vplan[(((int64_t)tile * kPlanGroups + wv) * 16 + 4 * g + i) * 16 + n] = v;
+        }
+    }
+    if (MODE == kModeFilter && a.prune) {
+        bool any_sampled = false;
+#pragma unroll
+        for (int n = 0; n < kTileQ; ++n) any_sampled |= s_row[n] >= 0 && s_tau[n] > -__builtin_inff();
+        if (a.prune == 2) {
+            use_skip = true;
+        } else if (any_sampled) {
+            // Read the tile's planner sample: (group, block, row) per thread.
+            const int id = threadIdx.x;
+            if (id < kPlanGroups * 256) {
+                const int k = id >> 8, blk = (id >> 4) & 15, rn = id & 15;
+                const int g0 = lo / (16 * kBlockKeys), g1 = (hi + 16 * kBlockKeys - 1) / (16 * kBlockKeys);
+                const int gs = g0 + ((2 * k + 1) * (g1 - g0)) / (2 * kPlanGroups);
+                const int b = gs * 16 + blk;
+                const int ov = (s_row[rn] >= 0 && b < a.nblocks) ? block_overlap(s_ks[rn], s_ke[rn], b) : 0;
+                const float v = a.vplan[(((int64_t)tile * kPlanGroups + k) * 16 + blk) * 16 + rn];
+                const bool ok = ov == 0 || v < s_tau[rn];
+                const unsigned long long bal = __ballot(ok);
+                const bool all = ((bal >> (threadIdx.x & 48)) & 0xFFFFull) == 0xFFFFull;
+                int sov = ov;
+                for (int off = 1; off < 16; off <<= 1) sov += __shfl_xor(sov, off);
+                if (rn == 0 && sov > 0) {
+                    atomicAdd(&s_pp[0], (unsigned long long)sov);
+                    if (all) atomicAdd(&s_pp[1], (unsigned long long)sov);
+                }
+            }
+            __syncthreads();
+            use_skip = s_pp[1] > 0 && s_pp[1] * 8ull >= s_pp[0];
+        }
+    }
+    if (MODE == kModeFilter && use_skip) {
+        // The bound of this work item's blocks, one 16-block group per wave
+        // at a time; s_skip[c - c0] bit e = block 16 c + e is skipped.
+        const int ln = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int n = ln & 15, g = ln >> 4;
+        const int c0 = jlo >> 4, c1 = (jhi + 15) >> 4;
+        const int rt = s_row[n], rks = s_ks[n], rke = s_ke[n];
+        const float rtau = s_tau[n], rq1 = s_q1[n];
+        unsigned long long pr = 0;
+        for (int c = c0 + wv; c < c1; c += kWaves) {
+            const v4f u = bound_group<DT>(a.kb, a.nblocks, c, s_q + ln * 16, 16 * RB, s_w, ln);
+            uint32_t bits = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = c * 16 + 4 * g + i;
+                const int ov = (rt >= 0 && b >= jlo && b < jhi) ? block_overlap(rks, rke, b) : 0;
+                const bool ok = ov == 0 || bound_value(u[i], a.meta[min(b, a.nblocks - 1)], rq1) < rtau;
+                const unsigned long long bal = __ballot(ok);
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg)
+                    if (((bal >> (16 * gg)) & 0xFFFFull) == 0xFFFFull) bits |= 1u << (4 * gg + i);
+                if ((bits >> (4 * g + i)) & 1u) pr += (unsigned long long)ov;
+            }
+            if (ln == 0) s_skip[c - c0] = (uint16_t)bits;
+        }
+        for (int off = 32; off > 0; off >>= 1) pr += __shfl_xor(pr, off);
+        if (ln == 0 && pr) atomicAdd(a.plan + kPlanPruned, pr);
+        if (threadIdx.x == 0) atomicAdd(a.plan + kPlanItems, 1ull);
+        __syncthreads();
+        // Order-preserving compaction of the steps that are not skipped.
+        const int i = threadIdx.x;
+        bool keep = false;
+        if (i < nstep) {
+            const int j = jlo + i;
+            keep = !((s_skip[(j >> 4) - c0] >> (j & 15)) & 1u);
+        }
+        const unsigned long long bal = __ballot(keep);
+        if (ln == 0) s_wcnt[wv] = __popcll(bal);
+        __syncthreads();
+        int base = 0, total = 0;
+        for (int v = 0; v < kWaves; ++v) {
+            base += v < wv ? s_wcnt[v] : 0;
+            total += s_wcnt[v];
+        }
+        if (keep) s_steps[base + __popcll(bal & ((1ull << ln) - 1ull))] = (uint16_t)i;
+        nstep = total;
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -590,31 +713,33 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         }
     };
 
-    // Steps of this wave: jlo + wave, + kWaves, ...
+    // Steps of this wave: the wave-th, (wave + kWaves)-th, ... step of the
+    // work item (all of [jlo, jhi), or the ones not skipped).
+    auto step_of = [&](int i) { return use_skip ? jlo + (int)s_steps[i] : jlo + i; };
     auto nop = []() {};
     if (Cfg::prefetch) {
         // Two fragment sets alternate so the next step's keys load while this
         // step computes.
         KFrag<DT> ka[kSub], kb[kSub];
-        int j = jlo + wave;
-        if (j < jhi) load_step(ka, j);
-        for (; j < jhi; j += 2 * kWaves) {
-            if (j + kWaves < jhi) load_step(kb, j + kWaves);
-            process(ka, j, nop);
-            if (j + kWaves >= jhi) break;
-            if (j + 2 * kWaves < jhi) load_step(ka, j + 2 * kWaves);
-            process(kb, j + kWaves, nop);
+        int i = wave;
+        if (i < nstep) load_step(ka, step_of(i));
+        for (; i < nstep; i += 2 * kWaves) {
+            if (i + kWaves < nstep) load_step(kb, step_of(i + kWaves));
+            process(ka, step_of(i), nop);
+            if (i + kWaves >= nstep) break;
+            if (i + 2 * kWaves < nstep) load_step(ka, step_of(i + 2 * kWaves));
+            process(kb, step_of(i + kWaves), nop);
         }
     } else {
         // One fragment set: the next step's keys load into it as soon as this
         // step's last MFMA is issued, so the sink hides their latency.
         KFrag<DT> kf[kSub];
-        int j = jlo + wave;
-        if (j < jhi) load_step(kf, j);
-        for (; j < jhi; j += kWaves) {
-            const int jn = j + kWaves;
-            process(kf, j, [&]() {
-                if (jn < jhi) load_step(kf, jn);
+        int i = wave;
+        if (i < nstep) load_step(kf, step_of(i));
+        for (; i < nstep; i += kWaves) {
+            const int in = i + kWaves;
+            process(kf, step_of(i), [&]() {
+                if (in < nstep) load_step(kf, step_of(in));
             });
         }
     }

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kTauThreads) void k_tau(TauArgs a)
 
 enum Stat {
     kStRows = 0, kStEmpty, kStTakeAll, kStSampled, kStUnder, kStOver, kStFlagged, kStMaxCand,
-    kStWindow, kStCount
+    kStWindow, kStPruned, kStPruneOn, kStCount
 };
 
 struct TriageArgs {
@@ -295,6 +295,7 @@ struct TriageArgs {
     int32_t *rowlist;
     int32_t *nflagged;
     unsigned long long *stats;
+    const unsigned long long *plan;  // pruning counters, or null (pruning off)
 };
 
 __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
@@ -376,6 +377,8 @@ __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
         *a.nflagged = (int32_t)s_base;
         s_st[kStRows] = (unsigned long long)a.num_q;
         s_st[kStFlagged] = s_base;
+        s_st[kStPruneOn] = (a.plan && a.plan[kPlanItems] > 0) ? 1ull : 0ull;
+        s_st[kStPruned] = a.plan ? a.plan[kPlanPruned] : 0ull;
     }
     __syncthreads();
     if (tid < kStCount) a.stats[tid] = s_st[tid];

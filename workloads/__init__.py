@@ -143,6 +143,59 @@ def trained_shaped(T, S, topk, dtype, seed, *, heavy_frac=0.03, windows="causal"
                 name=name or f"trained_{dtype}_{T}x{S}_k{topk}")
 
 
+def blocky(T, S, topk, dtype, seed, *, hot_frac=0.1, exact=False, windows="causal", docs=None, name=None):
+    """Keys with block locality, for the score-bound pruning path.
+
+    Keys come in aligned blocks of 64; a block is hot with probability
+    hot_frac.  Hot blocks hold independent keys; a quiet block's keys are one
+    per-block centroid plus small noise, so its per-dimension key range is
+    narrow and its scores are low.
+
+    exact=False: q ~ N(0,1); hot keys ~ N(0,1); quiet keys = 0.1 N(0,1)
+    (centroid) + 0.01 N(0,1) (per key); weights ~ |N(0,1)|; kv_scales ~ U(0.5, 1).
+    exact=True (integer-valued, exact in binary32): q, hot keys ~ U{-4..4};
+    a quiet block's centroid is +-1 on 2 random dimensions and 0 elsewhere,
+    and each quiet key adds, on each dimension with probability 1/512, a
+    step of +-1; weights ~ U{1/4, 1/2, 1}; kv_scales ~ U{1/2, 1, 2}.
+
+    Draw order: q, hot flags, hot keys, centroids, noise, weights, kv_scales."""
+    rng = np.random.default_rng(seed)
+    nb = (S + 63) // 64
+    if exact:
+        qf = rng.integers(-4, 5, size=(T, HEADS, DIM)).astype(np.float32)
+    else:
+        qf = _normal(rng, (T, HEADS, DIM))
+    q = _quantize(qf, dtype)
+    del qf
+    hot = np.repeat(rng.random(nb) < hot_frac, 64)[:S]
+    if exact:
+        hk = rng.integers(-4, 5, size=(S, DIM)).astype(np.float32)
+        sup = np.argsort(rng.random((nb, DIM)), axis=1)[:, :2]
+        c = np.zeros((nb, DIM), np.float32)
+        np.put_along_axis(c, sup, rng.choice(np.array([-1.0, 1.0], np.float32), size=(nb, 2)), axis=1)
+        cen = np.repeat(c, 64, axis=0)[:S]
+        step = rng.integers(-1, 2, size=(S, DIM)) * (rng.random((S, DIM)) < 1.0 / 512)
+        quiet = cen + step.astype(np.float32)
+    else:
+        hk = _normal(rng, (S, DIM))
+        cen = np.repeat(np.float32(0.1) * _normal(rng, (nb, DIM)), 64, axis=0)[:S]
+        quiet = cen + np.float32(0.01) * _normal(rng, (S, DIM))
+    kv = _quantize(np.where(hot[:, None], hk, quiet), dtype)
+    del hk, cen, quiet
+    if exact:
+        wv = np.array([0.25, 0.5, 1.0], dtype=np.float32)
+        w = wv[rng.integers(0, 3, size=(T, HEADS))]
+        sv = np.array([0.5, 1.0, 2.0], dtype=np.float32)
+        sc = sv[rng.integers(0, 3, size=S)]
+    else:
+        w = np.abs(_normal(rng, (T, HEADS))).astype(np.float32)
+        sc = rng.uniform(0.5, 1.0, size=S).astype(np.float32)
+    ks, ke = _windows(T, S, windows, docs)
+    kind = "int" if exact else "gauss"
+    return dict(q=q, kv=kv, dtype=dtype, kv_scales=sc, weights=w, ks=ks, ke=ke, topk=int(topk),
+                name=name or f"blocky_{kind}_{dtype}_{T}x{S}_k{topk}")
+
+
 def _windows(T, S, windows, docs):
     if windows == "causal":
         return causal_windows(T, S)
@@ -161,7 +214,7 @@ PACKED_DOCS = (8192, 16384, 24576, 16384)
 
 
 def config(n: int, *, integer_twin: bool = False):
-    """Named workloads 1..5 (integer twins for 3..5 with integer_twin=True)."""
+    """Named workloads 1..6 (integer twins for 3..5 with integer_twin=True)."""
     if integer_twin:
         if n == 3:
             return integer(4096, 131072, 4096, "fp8", 13, name="untrained_int_fp8_4096x131072_k4096")
@@ -183,6 +236,10 @@ def config(n: int, *, integer_twin: bool = False):
     if n == 5:
         return gaussian(65536, 65536, 512, "bf16", 5, weight_scale=32 ** -0.5, scales="ones",
                         windows="packed", docs=PACKED_DOCS, name="packed_bf16_65536_k512")
+    if n == 6:
+        # not one of the pages' workloads: keys with block locality, where
+        # score-bound pruning has something to skip
+        return blocky(4096, 131072, 2048, "fp8", 6, name="blocky_fp8_4096x131072_k2048")
     raise ValueError(n)
 
 
