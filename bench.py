@@ -51,7 +51,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("ftk_common.hpp", "ftk_qbar.hpp", "ftk_score.hpp")
+KERNEL_SOURCES = ("ftk_common.hpp", "ftk_frag.hpp", "ftk_bound.hpp", "ftk_qbar.hpp", "ftk_score.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_score_filter_fp8_trained_4096x131072_k2048.md")
 
 

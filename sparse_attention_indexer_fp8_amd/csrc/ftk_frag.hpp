@@ -32,6 +32,37 @@ __device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, i
     for (int m = 0; m < 4; ++m) f.a[m] = src[m];
 }
 
+// Raw buffer access: a resource (base, size in bytes) held in scalar
+// registers, a per-lane 32-bit offset and a wave-uniform offset.  Word 3 of
+// the resource selects 32-bit data for the gfx9-family buffer unit; reads at
+// or past the size return zeros instead of touching memory.
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kBufWord3);
+}
+
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// Key fragment through a buffer resource: voff is the lane's byte offset of
+// its slice within the key row block, soff the wave's.
+__device__ __forceinline__ void load_kfrag_buf(KFrag<kFP8> &f, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const v4i lo = buf_load16(r, voff, soff), hi = buf_load16(r, voff + 16, soff);
+    f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ void load_kfrag_buf(KFrag<kBF16> &f, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff)
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m) f.a[m] = buf_load16(r, voff + 16 * m, soff);
+}
+
 template <int DT> struct BFrag;
 template <> struct BFrag<kFP8> { v8i a; };
 template <> struct BFrag<kBF16> { v4i a[4]; };

@@ -182,8 +182,7 @@ __device__ __forceinline__ void stage_q_tile(uint8_t *s_q, const ScoreArgs &a, c
 // which would need far more than 256 registers.
 
 struct StepOut {
-    float acc[kSub][4];   // FP8: sum_h w |x|;  BF16: sum_h w ReLU(x)
-    v4f lin[kSub];        // FP8: sum_p part_p . k (unscaled qbar . k)
+    float acc[kSub][4];   // FP8: qbar . k + sum_h w |x|;  BF16: sum_h w ReLU(x)
 };
 
 // First head of a step: acc = w |x| (no zeroing pass).
@@ -225,20 +224,32 @@ __device__ __forceinline__ void mfma_fp8_head(v4f (&x)[kSub], const KFrag<kFP8> 
 
 template <typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[kSub], const uint8_t *s_q,
-                                           const float *s_w, int lane, AfterMfma after_mfma)
+                                           const float *s_w, int lane, float qsc, AfterMfma after_mfma)
 {
     constexpr int HB = 2048;  // LDS bytes per head of the q tile
     const v4f z[kSub] = {};
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
+    // The linear half first: the qbar parts (heads 32..34) accumulate in the
+    // MFMA, and lin * qscale is folded into acc after the third head, so the
+    // 16 lin registers are dead for the rest of the step.
+    const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
+    v4f lin[kSub];
+    mfma_fp8_head(lin, kf, pp, z);
     // Two result sets alternate: the epilogue of head h-1 runs while the
     // MFMAs of head h execute.  The first epilogue initialises acc.
     v4f xa[kSub], xb[kSub];
     mfma_fp8_head(xa, kf, qp, z);
+    mfma_fp8_head(lin, kf, pp + HB, lin);
     mfma_fp8_head(xb, kf, qp + HB, z);
     epi_abs_first(o.acc, xa, wp[0]);
+    mfma_fp8_head(lin, kf, pp + 2 * HB, lin);
     mfma_fp8_head(xa, kf, qp + 2 * HB, z);
     epi_abs(o.acc, xb, wp[kTileQ]);
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.acc[kt][i] = __builtin_fmaf(lin[kt][i], qsc, o.acc[kt][i]);
     qp += 2 * HB;
     wp += 2 * kTileQ;
 #pragma unroll 1
@@ -252,14 +263,9 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
         wp += 2 * kTileQ;
     }
     mfma_fp8_head(xb, kf, qp + HB, z);
-    // The linear half: qbar parts are heads 32..34, accumulated in the MFMA.
-    const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
-    mfma_fp8_head(o.lin, kf, pp, z);
-    epi_abs(o.acc, xa, wp[0]);
-    mfma_fp8_head(o.lin, kf, pp + HB, o.lin);
-    epi_abs(o.acc, xb, wp[kTileQ]);
-    mfma_fp8_head(o.lin, kf, pp + 2 * HB, o.lin);
     after_mfma();  // the key fragments are free from here on
+    epi_abs(o.acc, xa, wp[0]);
+    epi_abs(o.acc, xb, wp[kTileQ]);
 }
 
 __device__ __forceinline__ v4f mfma_bf16_d128(const KFrag<kBF16> &k, const v4i (&qf)[4])
@@ -284,7 +290,7 @@ __device__ __forceinline__ void mfma_bf16_head(v4f (&x)[kSub], const KFrag<kBF16
 
 template <typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[kSub], const uint8_t *s_q,
-                                           const float *s_w, int lane, AfterMfma after_mfma)
+                                           const float *s_w, int lane, float /*qsc*/, AfterMfma after_mfma)
 {
     // One head is 16 MFMAs here, so a one-head lag already covers the MFMA
     // latency and two result sets suffice (the key fragments take 128
@@ -315,12 +321,11 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[
 }
 
 // The score of output element (kt, i) from the step accumulators; sh is the
-// key's scale factor as stored in sigh (sigma / 2 on the FP8 path).
-// FP8: sigma/2 * (qbar . k + sum_h w |x|) with qbar . k = lin * qscale.
+// key's scale factor as stored in sigh (sigma / 2 on the FP8 path, whose acc
+// is qbar . k + sum_h w |x|).
 template <int DT>
-__device__ __forceinline__ float score_of(const StepOut &o, int kt, int i, float qsc, float sh)
+__device__ __forceinline__ float score_of(const StepOut &o, int kt, int i, float sh)
 {
-    if (DT == kFP8) return __builtin_fmaf(o.lin[kt][i], qsc, o.acc[kt][i]) * sh;
     return o.acc[kt][i] * sh;
 }
 
@@ -438,6 +443,12 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             dmin = min(dmin, s_d[n]);
         }
     }
+    // Workgroup-uniform: keep them (and what derives from them) in scalar registers.
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    ilo = __builtin_amdgcn_readfirstlane(ilo);
+    ihi = __builtin_amdgcn_readfirstlane(ihi);
+    dmin = __builtin_amdgcn_readfirstlane(dmin);
     if (hi <= lo) return;
 
     // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode the
@@ -576,11 +587,11 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             total += s_wcnt[v];
         }
         if (keep) s_steps[base + __popcll(bal & ((1ull << ln) - 1ull))] = (uint16_t)i;
-        nstep = total;
+        nstep = __builtin_amdgcn_readfirstlane(total);
         __syncthreads();
     }
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int t = s_row[n];
     const int rks = s_ks[n], rke = s_ke[n];
@@ -596,13 +607,27 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     uint32_t ring_cnt = 0;
 
     // Key fragments of step j: this lane loads key row 16 kt + n of the step.
+    // Filter mode addresses keys and scale factors by 32-bit offsets from the
+    // work item's first key (a workgroup-uniform base held in scalar
+    // registers), which keeps the hot loop's vector registers free.
+    // Keys past num_kv read as zeros (their scores are masked by the windows).
+    const int kbase = jlo * kStepKeys;
+    const int kspan = min(S - kbase, a.chunk + kStepKeys);
+    const __amdgpu_buffer_rsrc_t kvr = make_rsrc(a.kv + (int64_t)kbase * RB, (uint32_t)kspan * RB);
+    const __amdgpu_buffer_rsrc_t shr = make_rsrc(a.sigh + kbase, (uint32_t)(kspan + kStepKeys) * 4u);
+    const uint32_t klane = (uint32_t)(n * RB + (RB / 4) * g);  // lane's slice in a 16-key subtile
     auto load_step = [&](KFrag<DT>(&f)[kSub], int j) {
 #pragma unroll
         for (int kt = 0; kt < kSub; ++kt) {
             const int e = j * kStepKeys + 16 * kt + n;
-            int p = (MODE == kModeSample) ? first_b + e * dmin : e;
-            p = min(p, S - 1);
-            load_kfrag(f[kt], a.kv, p, g);
+            if (MODE == kModeFilter) {
+                const uint32_t soff = (uint32_t)(j * kStepKeys - kbase) * RB;
+                load_kfrag_buf(f[kt], kvr, klane + (uint32_t)(16 * kt * RB), soff);
+            } else {
+                int p = (MODE == kModeSample) ? first_b + e * dmin : e;
+                p = min(p, S - 1);
+                load_kfrag(f[kt], a.kv, p, g);
+            }
         }
     };
 
@@ -612,21 +637,30 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     auto process = [&](KFrag<DT>(&kf)[kSub], int j, auto next) {
         const int sb = j * kStepKeys + 4 * g;  // key of element (kt, i) is sb + 16 kt + i
         // Scale factors of the step's outputs (4 consecutive keys per
-        // subtile), loaded before the MFMA work so their latency hides.
-        // With the prefetching (2-wave) shape they load before the MFMA work
-        // so their latency hides; with 4 waves per SIMD other waves hide it
-        // and the registers are kept free.
+        // subtile).  With the prefetching (2-wave) shape they load before the
+        // MFMA work so their latency hides; with 4 waves per SIMD other waves
+        // hide it and the registers stay free during the head loop.
         v4f shv[kSub];
         auto load_sh = [&]() {
-            if (MODE != kModeSample) {
+            if (MODE == kModeFilter) {
+                const uint32_t soff = (uint32_t)(j * kStepKeys - kbase) * 4u;
+#pragma unroll
+                for (int kt = 0; kt < kSub; ++kt)
+                    shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(16 * g + 64 * kt), soff));
+            } else if (MODE != kModeSample) {
 #pragma unroll
                 for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
             }
         };
         if (Cfg::prefetch) load_sh();
         StepOut o;
-        score_step(o, kf, s_q, s_w, lane, next);
-        if (!Cfg::prefetch) load_sh();
+        // Without prefetching, the scale factors are requested right after
+        // the last MFMA and before the next step's key loads: loads complete
+        // in order, so waiting for them does not wait for the keys.
+        score_step(o, kf, s_q, s_w, lane, qsc, [&]() {
+            if (!Cfg::prefetch) load_sh();
+            next();
+        });
         if (MODE == kModeFilter) {
             // Keep (row, key) when the key is in the row's window and its
             // score reaches the row's threshold (take-all rows: -inf).
@@ -635,7 +669,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[kt * 4 + i] = score_of<DT>(o, kt, i, qsc, shv[kt][i]);
+                for (int i = 0; i < 4; ++i) sc[kt * 4 + i] = score_of<DT>(o, kt, i, shv[kt][i]);
             const bool inside = j * kStepKeys >= ilo && (j + 1) * kStepKeys <= ihi;  // wave-uniform
             if (!inside) {
 #pragma unroll
@@ -697,7 +731,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                     if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
                     const int idx = (p - first_n) >> dsh;
                     a.samp[(int64_t)t * a.sample_target + idx] =
-                        ord_of(score_of<DT>(o, kt, i, qsc, sigh_of<DT>(a.sigma, p)));
+                        ord_of(score_of<DT>(o, kt, i, sigh_of<DT>(a.sigma, p)));
                 }
         } else {
             const int slot = tile * kTileQ + n;
@@ -708,14 +742,14 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                     const int s = sb + 16 * kt + i;
                     if (t < 0 || s < rks || s >= rke) continue;
                     a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] =
-                        raw_cand(score_of<DT>(o, kt, i, qsc, shv[kt][i]), s);
+                        raw_cand(score_of<DT>(o, kt, i, shv[kt][i]), s);
                 }
         }
     };
 
     // Steps of this wave: the wave-th, (wave + kWaves)-th, ... step of the
     // work item (all of [jlo, jhi), or the ones not skipped).
-    auto step_of = [&](int i) { return use_skip ? jlo + (int)s_steps[i] : jlo + i; };
+    auto step_of = [&](int i) { return use_skip ? jlo + __builtin_amdgcn_readfirstlane((int)s_steps[i]) : jlo + i; };
     auto nop = []() {};
     if (Cfg::prefetch) {
         // Two fragment sets alternate so the next step's keys load while this
@@ -733,14 +767,15 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     } else {
         // One fragment set: the next step's keys load into it as soon as this
         // step's last MFMA is issued, so the sink hides their latency.
+        // The load is unconditional (the last step re-reads its own keys) so
+        // the code after it has one path and the wait for the scale factors
+        // never covers these loads.
         KFrag<DT> kf[kSub];
         int i = wave;
         if (i < nstep) load_step(kf, step_of(i));
         for (; i < nstep; i += kWaves) {
-            const int in = i + kWaves;
-            process(kf, step_of(i), [&]() {
-                if (in < nstep) load_step(kf, step_of(in));
-            });
+            const int in = min(i + kWaves, nstep - 1);
+            process(kf, step_of(i), [&]() { load_step(kf, step_of(in)); });
         }
     }
     if (MODE == kModeFilter) {
