@@ -54,9 +54,11 @@ constexpr int kSampleSplit = 1;
 template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? kHeads + kQbarParts : kHeads; };
 
 // Per-dtype launch shape.
-//   FP8: 16 waves per workgroup (4 per SIMD, at most 128 VGPRs each) so that
-//   while one wave waits on LDS or memory three others keep the matrix cores
-//   and vector ALUs busy; each wave loads its step's keys when it starts it.
+//   FP8: 12 waves per workgroup (3 per SIMD, up to 168 VGPRs each, enough to
+//   double-buffer the q fragments without spilling) so that while one wave
+//   waits on LDS or memory the others keep the matrix cores and vector ALUs
+//   busy; each wave loads its next step's keys as soon as its last MFMA of
+//   a step has issued.
 //   BF16: the q tile takes 128 KiB of LDS and each wave's key fragments 64
 //   VGPRs, so 8 waves (2 per SIMD) with the next step's keys prefetched.
 // Candidate ring per (wave, query) in filter mode: survivors are staged in LDS
@@ -67,7 +69,7 @@ template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? k
 //   use the 8-wave prefetching shape for both dtypes.
 template <int DT, int MODE> struct ScoreCfg {
     static constexpr bool wide = DT == kFP8 && MODE == 0;  // 0: filter mode
-    static constexpr int waves = wide ? 16 : 8;
+    static constexpr int waves = wide ? 12 : 8;
     static constexpr int ring = DT == kFP8 ? 40 : 24;
     static constexpr bool prefetch = !wide;
 };
@@ -210,13 +212,18 @@ __device__ __forceinline__ void epi_relu(float (&acc)[kSub][4], const v4f (&x)[k
         for (int i = 0; i < 4; ++i) acc[kt][i] = __builtin_fmaf(w, relu_bits(x[kt][i]), acc[kt][i]);
 }
 
-// qp points at the lane's slot of head 0 (s_q + lane * 16); head h adds h * 2 KiB.
-__device__ __forceinline__ void mfma_fp8_head(v4f (&x)[kSub], const KFrag<kFP8> (&kf)[kSub], const uint8_t *qp,
-                                              const v4f (&c)[kSub])
+// q fragment of one head: qp points at the lane's slot of head 0 (s_q + lane
+// * 16); head h adds h * 2 KiB.
+__device__ __forceinline__ v8i load_qfrag_fp8(const uint8_t *qp)
 {
     const v4i lo = *reinterpret_cast<const v4i *>(qp);
     const v4i hi = *reinterpret_cast<const v4i *>(qp + 1024);
-    const v8i qf = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ void mfma_fp8_head(v4f (&x)[kSub], const KFrag<kFP8> (&kf)[kSub], const v8i &qf,
+                                              const v4f (&c)[kSub])
+{
 #pragma unroll
     for (int kt = 0; kt < kSub; ++kt)
         x[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt].a, qf, c[kt], 0, 0, 0, 0, 0, 0);
@@ -230,21 +237,29 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     const v4f z[kSub] = {};
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
+    // q fragments are double-buffered: the next head's fragment is read from
+    // LDS while the MFMAs of the current one issue.
     // The linear half first: the qbar parts (heads 32..34) accumulate in the
     // MFMA, and lin * qscale is folded into acc after the third head, so the
     // 16 lin registers are dead for the rest of the step.
     const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
     v4f lin[kSub];
-    mfma_fp8_head(lin, kf, pp, z);
+    v8i qa = load_qfrag_fp8(pp), qb = load_qfrag_fp8(qp);
+    mfma_fp8_head(lin, kf, qa, z);
+    qa = load_qfrag_fp8(pp + HB);
     // Two result sets alternate: the epilogue of head h-1 runs while the
     // MFMAs of head h execute.  The first epilogue initialises acc.
     v4f xa[kSub], xb[kSub];
-    mfma_fp8_head(xa, kf, qp, z);
-    mfma_fp8_head(lin, kf, pp + HB, lin);
-    mfma_fp8_head(xb, kf, qp + HB, z);
+    mfma_fp8_head(xa, kf, qb, z);  // head 0
+    qb = load_qfrag_fp8(qp + HB);
+    mfma_fp8_head(lin, kf, qa, lin);
+    qa = load_qfrag_fp8(pp + 2 * HB);
+    mfma_fp8_head(xb, kf, qb, z);  // head 1
+    qb = load_qfrag_fp8(qp + 2 * HB);
     epi_abs_first(o.acc, xa, wp[0]);
-    mfma_fp8_head(lin, kf, pp + 2 * HB, lin);
-    mfma_fp8_head(xa, kf, qp + 2 * HB, z);
+    mfma_fp8_head(lin, kf, qa, lin);
+    qa = load_qfrag_fp8(qp + 3 * HB);
+    mfma_fp8_head(xa, kf, qb, z);  // head 2
     epi_abs(o.acc, xb, wp[kTileQ]);
 #pragma unroll
     for (int kt = 0; kt < kSub; ++kt)
@@ -252,17 +267,20 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
         for (int i = 0; i < 4; ++i) o.acc[kt][i] = __builtin_fmaf(lin[kt][i], qsc, o.acc[kt][i]);
     qp += 2 * HB;
     wp += 2 * kTileQ;
+    // Loop invariant: qa holds head h's fragment, xa head h-1's results.
 #pragma unroll 1
     for (int h = 3; h < kHeads - 1; h += 2) {
         const float w0 = wp[0], w1 = wp[kTileQ];
-        mfma_fp8_head(xb, kf, qp + HB, z);
-        epi_abs(o.acc, xa, w0);
-        mfma_fp8_head(xa, kf, qp + 2 * HB, z);
-        epi_abs(o.acc, xb, w1);
+        qb = load_qfrag_fp8(qp + 2 * HB);  // head h + 1
+        mfma_fp8_head(xb, kf, qa, z);      // head h
+        epi_abs(o.acc, xa, w0);            // head h - 1
+        qa = load_qfrag_fp8(qp + 3 * HB);  // head h + 2 (at most head 31)
+        mfma_fp8_head(xa, kf, qb, z);      // head h + 1
+        epi_abs(o.acc, xb, w1);            // head h
         qp += 2 * HB;
         wp += 2 * kTileQ;
     }
-    mfma_fp8_head(xb, kf, qp + HB, z);
+    mfma_fp8_head(xb, kf, qa, z);  // head 31
     after_mfma();  // the key fragments are free from here on
     epi_abs(o.acc, xa, wp[0]);
     epi_abs(o.acc, xb, wp[kTileQ]);
@@ -671,7 +689,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[kt * 4 + i] = score_of<DT>(o, kt, i, shv[kt][i]);
             const bool inside = j * kStepKeys >= ilo && (j + 1) * kStepKeys <= ihi;  // wave-uniform
-            if (!inside) {
+            if (__builtin_expect(!inside, 0)) {
 #pragma unroll
                 for (int b = 0; b < kSub * 4; ++b) {
                     const int s = sb + 16 * (b >> 2) + (b & 3);
@@ -686,12 +704,12 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                            c3 = __shfl(m, n + 48);
             uint32_t tot = c0 + c1 + c2 + c3;
             const uint32_t pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
-            if (__any(ring_cnt + tot > (uint32_t)RING)) {
+            if (__builtin_expect(__any(ring_cnt + tot > (uint32_t)RING), 0)) {
                 ring_flush<RS>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
                 ring_cnt = 0;
             }
             bool direct = false;
-            if (__any(tot > (uint32_t)RING)) {
+            if (__builtin_expect(__any(tot > (uint32_t)RING), 0)) {
                 // More than a ring holds: reserve slots in the row's list directly.
                 uint32_t base = 0;
                 direct = tot > (uint32_t)RING;
@@ -709,7 +727,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                     }
                 }
             }
-            if (!direct && __any(m != 0)) {
+            if (__builtin_expect(!direct && __any(m != 0), 1)) {
                 uint64_t *rp = ring + n * RS + ring_cnt + pre;
 #pragma unroll
                 for (int b = 0; b < kSub * 4; ++b) {
