@@ -86,8 +86,9 @@ typedef struct flashtopk_options {
     float sample_rank_scale;  /* multiplies the rank of the sampled threshold;
                                  0 = 1.  Below 1 raises the threshold (fewer
                                  candidates), above 1 lowers it */
-    int sample_target;        /* keys sampled per row for the threshold;
-                                 0 = 2048 */
+    int sample_target;        /* most keys sampled per row for the
+                                 threshold; 0 = 2048 (the lattice stride is
+                                 also at least topk / 32) */
     int64_t recover_budget_bytes; /* scratch for dense rescoring; 0 = 1 GiB */
     int profile;              /* nonzero: time each kernel phase with HIP
                                  events on the call's stream (ms_* of

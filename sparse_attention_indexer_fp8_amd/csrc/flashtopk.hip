@@ -1,10 +1,11 @@
 // C ABI of the fused indexer top-k library (declared in include/flashtopk.h).
 //
 // Launch sequence of one call, all on the caller's stream:
-//   0. k_qbar           (FP8) head-weighted query sums, split into FP8 parts
+//   0. k_keyprep        per-key scale factors (+ block extremes for the bound)
+//      k_qbar           (FP8) head-weighted query sums, split into FP8 parts
 //   1. k_score<sample>  strided-sample scores of every long row     (MFMA)
 //   2. k_tau            per-row threshold = r-th largest sample score
-//   3. k_score<filter>  fused score + threshold filter -> candidates (MFMA, hot)
+//   3. k_score<filter>  fused score (+ bound) + threshold filter -> candidates (MFMA, hot)
 //   4. k_triage         flag rows whose candidates under/overflowed
 //   5. k_select         exact top-k of every unflagged row
 //   6. (flagged rows)   k_score<dense> + k_select<dense> in batches
@@ -43,8 +44,8 @@ struct DevBuf {
 struct Workspace {
     int device = -1;
     hipStream_t stream = nullptr;
-    DevBuf tau, cnt, rowflag, rowlist, nflagged, stats, cand, samp, scratch, qbar, qscale, sigh;
-    DevBuf kb, kmeta, vplan, plan, q1;         // score-bound pruning
+    DevBuf tau, cnt, rowlist, stats, cand, samp, scratch, qbar, qscale, sigh;
+    DevBuf kb, kmeta, vplan, q1;               // score-bound pruning
     unsigned long long *host_stats = nullptr;  // pinned
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
@@ -111,7 +112,7 @@ Workspace *get_ws(hipStream_t stream, int *status)
 
 struct Plan {
     int64_t T, S;
-    int dtype, topk, cap, sample_target, path;
+    int dtype, topk, cap, sample_target, sample_min_stride, path;
     float rank_scale;
     int64_t recover_budget;
     int profile;
@@ -124,6 +125,11 @@ int resolve(Plan &p, const flashtopk_options *opt)
     int cap = (opt && opt->cand_capacity > 0) ? opt->cand_capacity : std::min(kMaxCap, 4 * p.topk);
     p.cap = std::min(kMaxCap, std::max(cap, p.topk));
     p.sample_target = (opt && opt->sample_target > 0) ? opt->sample_target : kDefaultSampleTarget;
+    // The threshold is the r-th largest sample score with r about 2 topk / d
+    // for stride d; r >= 64 (relative spread of the admitted count about
+    // 1/8) is enough, so the stride need not go below topk / 32.
+    p.sample_min_stride = 1;
+    while (p.sample_min_stride * 2 <= p.topk / 32) p.sample_min_stride *= 2;
     p.rank_scale = (opt && opt->sample_rank_scale > 0.0f) ? opt->sample_rank_scale : 1.0f;
     p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
     p.profile = (opt && opt->profile) ? 1 : 0;
@@ -155,6 +161,12 @@ void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
     if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
     else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
     else k_score<DT, kModeDense><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
+}
+
+template <typename SH>
+void launch_select(int64_t blocks, hipStream_t st, const SelectArgs &a)
+{
+    k_select<SH><<<dim3((unsigned)blocks), SH::nt, 0, st>>>(a);
 }
 
 void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
@@ -190,9 +202,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     const int64_t T = p.T, S = p.S;
     if ((st = ensure(*w, w->tau, sizeof(float) * T))) return st;
     if ((st = ensure(*w, w->cnt, sizeof(uint32_t) * T))) return st;
-    if ((st = ensure(*w, w->rowflag, sizeof(int32_t) * T))) return st;
     if ((st = ensure(*w, w->rowlist, sizeof(int32_t) * T))) return st;
-    if ((st = ensure(*w, w->nflagged, sizeof(int32_t)))) return st;
     if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
     const bool recover_all = p.path == FLASHTOPK_PATH_RECOVER;
     const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
@@ -215,7 +225,6 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
         if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)nblocks))) return st;
         if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
-        if ((st = ensure(*w, w->plan, sizeof(unsigned long long) * kPlanCount))) return st;
         if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
     }
     const int chunk = chunk_keys(ntiles, S);
@@ -241,6 +250,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.cand = (uint64_t *)w->cand.ptr;
     sa.samp = (uint32_t *)w->samp.ptr;
     sa.sample_target = p.sample_target;
+    sa.sample_min_stride = p.sample_min_stride;
     if (bounds) {
         sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
         sa.kb = (const uint8_t *)w->kb.ptr;
@@ -248,7 +258,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         sa.q1 = (const float *)w->q1.ptr;
         sa.nblocks = nblocks;
         sa.vplan = (float *)w->vplan.ptr;
-        sa.plan = (unsigned long long *)w->plan.ptr;
+        sa.plan = (unsigned long long *)w->stats.ptr + kStPruned;
     }
 
     mark(*w, p, 0, stream);
@@ -257,13 +267,15 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         const unsigned nwg = (unsigned)((S + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
         uint8_t *kbp = bounds ? (uint8_t *)w->kb.ptr : nullptr;
         float2 *kmp = bounds ? (float2 *)w->kmeta.ptr : nullptr;
-        unsigned long long *plp = bounds ? (unsigned long long *)w->plan.ptr : nullptr;
+        unsigned long long *stp = (unsigned long long *)w->stats.ptr;
         if (fp8)
             k_keyprep<kFP8><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)S, nblocks,
-                                                     (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, plp);
+                                                     (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
+                                                     kStCount);
         else
             k_keyprep<kBF16><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)S, nblocks,
-                                                      (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, plp);
+                                                      (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
+                                                      kStCount);
     }
     const dim3 rgrid((unsigned)((T + 3) / 4));
     if (fp8)
@@ -281,6 +293,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     ta.cap = p.cap;
     ta.samp = (const uint32_t *)w->samp.ptr;
     ta.sample_target = p.sample_target;
+    ta.sample_min_stride = p.sample_min_stride;
     ta.rank_scale = p.rank_scale;
     ta.recover_all = recover_all ? 1 : 0;
     ta.tau = (float *)w->tau.ptr;
@@ -299,12 +312,9 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     tr.cap = p.cap;
     tr.cnt = (const uint32_t *)w->cnt.ptr;
     tr.recover_all = recover_all ? 1 : 0;
-    tr.rowflag = (int32_t *)w->rowflag.ptr;
     tr.rowlist = (int32_t *)w->rowlist.ptr;
-    tr.nflagged = (int32_t *)w->nflagged.ptr;
     tr.stats = (unsigned long long *)w->stats.ptr;
-    tr.plan = bounds ? (const unsigned long long *)w->plan.ptr : nullptr;
-    k_triage<<<1, 1024, 0, stream>>>(tr);
+    k_triage<<<dim3((unsigned)((T + kTriageThreads - 1) / kTriageThreads)), kTriageThreads, 0, stream>>>(tr);
     // The triage counts go to pinned host memory right away; the host waits
     // for them (not for the stream) while the select kernel runs, so the GPU
     // never idles on the host between calls.
@@ -321,16 +331,17 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     se.ke = ke;
     se.topk = p.topk;
     se.cap = p.cap;
+    se.recover_all = recover_all ? 1 : 0;
     se.cnt = (const uint32_t *)w->cnt.ptr;
-    se.rowflag = (const int32_t *)w->rowflag.ptr;
     se.cand = (const uint64_t *)w->cand.ptr;
     se.rowlist = (const int32_t *)w->rowlist.ptr;
-    se.nrows = (const int32_t *)w->nflagged.ptr;
+    se.stats = (const unsigned long long *)w->stats.ptr;
     se.out_idx = out_idx;
     se.out_val = out_val;
-    if (p.cap <= 8 * kSelThreads) k_select<8><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
-    else if (p.cap <= 16 * kSelThreads) k_select<16><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
-    else k_select<32><<<dim3((unsigned)T), kSelThreads, 0, stream>>>(se);
+    if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
+    else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
+    else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
+    else launch_select<SelHuge>(T, stream, se);
     mark(*w, p, 5, stream);
 
     e = hipGetLastError();
@@ -347,7 +358,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         rcap = (rcap + kTileQ - 1) / kTileQ * kTileQ;
         if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)rcap * stride))) return st;
         sa.rowlist = (const int32_t *)w->rowlist.ptr;
-        sa.nrows = (const int32_t *)w->nflagged.ptr;
+        sa.nrows = (const unsigned long long *)w->stats.ptr + kStFlagged;
         sa.row_limit = (int)rcap;
         sa.scratch = (uint64_t *)w->scratch.ptr;
         sa.scratch_stride = stride;
@@ -361,7 +372,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             sa.row_base = (int)rb;
             se.row_base = (int)rb;
             launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
-            k_select<0><<<dim3((unsigned)rcap), kSelThreads, 0, stream>>>(se);
+            launch_select<SelDense>(rcap, stream, se);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return hip_status(e);
@@ -385,7 +396,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     info.status = FLASHTOPK_OK;
     info.path = recover_all ? FLASHTOPK_PATH_RECOVER
                             : (hs[kStPruneOn] ? FLASHTOPK_PATH_PRUNE : FLASHTOPK_PATH_SCAN);
-    info.rows = (int64_t)hs[kStRows];
+    info.rows = T;
     info.rows_empty = (int64_t)hs[kStEmpty];
     info.rows_take_all = (int64_t)hs[kStTakeAll];
     info.rows_sampled = (int64_t)hs[kStSampled];
@@ -455,17 +466,23 @@ int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, vo
     const int cap = std::min(kMaxCap, std::max(4 * max_topk, max_topk));
     if ((st = ensure(*w, w->tau, sizeof(float) * T))) return st;
     if ((st = ensure(*w, w->cnt, sizeof(uint32_t) * T))) return st;
-    if ((st = ensure(*w, w->rowflag, sizeof(int32_t) * T))) return st;
     if ((st = ensure(*w, w->rowlist, sizeof(int32_t) * T))) return st;
-    if ((st = ensure(*w, w->nflagged, sizeof(int32_t)))) return st;
     if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
     if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * cap))) return st;
     if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * kDefaultSampleTarget))) return st;
+    if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(max_kv + 64)))) return st;
+    if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
     if (dtype == FLASHTOPK_FP8_E4M3) {
         if ((st = ensure(*w, w->qbar, (size_t)T * kQbarParts * kDim))) return st;
         if ((st = ensure(*w, w->qscale, sizeof(float) * T))) return st;
     }
-    (void)max_kv;
+    if (max_kv > 0) {
+        const int64_t nblocks = (max_kv + kBlockKeys - 1) / kBlockKeys;
+        const int64_t ntiles = (T + kTileQ - 1) / kTileQ;
+        if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (dtype == FLASHTOPK_FP8_E4M3 ? 128 : 256)))) return st;
+        if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)nblocks))) return st;
+        if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
+    }
     return FLASHTOPK_OK;
 }
 
@@ -494,9 +511,9 @@ void flashtopk_release(void)
         (void)hipGetDevice(&prev);
         (void)hipSetDevice(w->device);
         (void)hipStreamSynchronize(w->stream);
-        DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowflag, &w->rowlist, &w->nflagged, &w->stats,
+        DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowlist, &w->stats,
                           &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh,
-                          &w->kb, &w->kmeta, &w->vplan, &w->plan, &w->q1};
+                          &w->kb, &w->kmeta, &w->vplan, &w->q1};
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);

@@ -60,7 +60,7 @@ constexpr int kPlanGroups = 2;          // 16-block groups of each tile in the p
 // kb[b][0][:] = per-dimension max, kb[b][1][:] = min (codes of the operand
 // dtype), meta[b] = (sigmax, kabs) with sigmax NaN when the block holds a
 // negative or non-finite scale.  One wave per 64 keys.  Block 0 also clears
-// the plan counters.
+// the call's statistics (nstats counters), which later kernels accumulate.
 //
 // Codes are compared as sign-magnitude integers: for finite E4M3 and BF16
 // codes the magnitude bits order like the values, and +0 / -0 both map to 0.
@@ -82,14 +82,14 @@ __device__ __forceinline__ uint32_t ord_code(int v)
 template <int DT>
 __global__ __launch_bounds__(256) void k_keyprep(const uint8_t *kv, const float *sigma, int num_kv, int nblocks,
                                                  float *sigh, int bounds, uint8_t *kb, float2 *meta,
-                                                 unsigned long long *plan)
+                                                 unsigned long long *stats, int nstats)
 {
     constexpr int RB = RowBytes<DT>::value;
     constexpr int EPL = DT == kFP8 ? 16 : 8;     // elements per 16-byte load
     constexpr int LPR = kDim / EPL;               // lanes per key row
     constexpr int KPL = 64 / LPR;                 // key rows per load instruction
     constexpr int NLD = kBlockKeys / KPL;         // loads per lane
-    if (bounds && blockIdx.x == 0 && threadIdx.x < kPlanCount) plan[threadIdx.x] = 0ull;
+    if (blockIdx.x == 0 && (int)threadIdx.x < nstats) stats[threadIdx.x] = 0ull;
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int p0 = b * kBlockKeys;

@@ -89,11 +89,12 @@ __device__ __forceinline__ float relu_bits(float x)
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// Smallest power of two d with len <= target * d: the stride of the row's
-// strided sample, so the sample holds at most `target` keys.
-__device__ __host__ __forceinline__ int sample_stride(int64_t len, int target)
+// Stride of the row's strided sample: the smallest power of two d >=
+// min_stride with len <= target * d, so the sample holds at most `target`
+// keys.  (min_stride keeps the sample no denser than the threshold needs.)
+__device__ __host__ __forceinline__ int sample_stride(int64_t len, int target, int min_stride)
 {
-    int d = 1;
+    int d = min_stride;
     while (len > (int64_t)target * d) d <<= 1;
     return d;
 }
@@ -107,9 +108,9 @@ __device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi
     return (hi - 1 - first) / d + 1;
 }
 
-// Counters of the score-bound pruning (zeroed by the per-key pass, written
-// by the scan, read by triage): (row, key) pairs skipped, and work items
-// that evaluated the bound.
+// Counters of the score-bound pruning, kept in the call's statistics (zeroed
+// by the per-key pass, added to by the scan): (row, key) pairs skipped, and
+// work items that evaluated the bound.
 enum PlanCounter { kPlanPruned = 0, kPlanItems, kPlanCount };
 
 }  // namespace ftk

@@ -98,9 +98,10 @@ struct ScoreArgs {
     // sample mode
     uint32_t *samp;            // [num_q, sample_target] sample score codes
     int sample_target;
+    int sample_min_stride;     // power of two, see sample_stride
     // dense mode
     const int32_t *rowlist;    // flagged rows
-    const int32_t *nrows;      // device count of flagged rows
+    const unsigned long long *nrows;  // device count of flagged rows
     int row_base;              // first flagged entry of this batch
     int row_limit;             // entries per batch
     uint64_t *scratch;         // [row_limit, scratch_stride] keys
@@ -112,7 +113,7 @@ struct ScoreArgs {
     const float *q1;           // [num_q] sum_h |w| ||q_h||_1
     int nblocks;
     float *vplan;              // [ntiles, kPlanGroups, 16 blocks, 16 rows] planner sample
-    unsigned long long *plan;  // PlanCounter
+    unsigned long long *plan;  // PlanCounter slots
 };
 
 // LDS layout of the q tile: for head h, the 64 lanes' fragments are stored as
@@ -419,7 +420,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         int t = -1;
         if (MODE == kModeDense) {
             const int e = tile * kTileQ + n;
-            if (e < a.row_limit && a.row_base + e < *a.nrows) t = a.rowlist[a.row_base + e];
+            if (e < a.row_limit && (unsigned long long)(a.row_base + e) < *a.nrows) t = a.rowlist[a.row_base + e];
         } else {
             const int64_t tt = (int64_t)tile * kTileQ + n;
             if (tt < a.num_q) t = (int)tt;
@@ -432,7 +433,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         }
         if (MODE == kModeSample) {
             if (t >= 0 && hi - lo > a.cap) {
-                d = sample_stride(hi - lo, a.sample_target);
+                d = sample_stride(hi - lo, a.sample_target, a.sample_min_stride);
             } else {
                 t = -1;
                 lo = hi = 0;

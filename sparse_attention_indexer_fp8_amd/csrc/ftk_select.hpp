@@ -25,25 +25,25 @@
 
 namespace ftk {
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelThreads = 512;   // threads of the selection workgroups for large rows
 constexpr int kMaxTopk = 4096;
 
 // ---------------------------------------------------------------------------
-// Block-wide radix select.  `each(f)` calls f(key) for every element this
-// thread owns.  Returns the smallest key T such that exactly k elements are
-// >= T (the k-th largest key, or a lower bound with the same count).  All
-// threads of the block must call it; k must satisfy 1 <= k <= n.
+// Block-wide radix select over NW waves.  `each(f)` calls f(key) for every
+// element this thread owns.  Returns the smallest key T such that exactly k
+// elements are >= T (the k-th largest key, or a lower bound with the same
+// count).  All threads of the block must call it; k must satisfy 1 <= k <= n.
 
+template <int NW>
 struct RadixLds {
-    uint32_t hist[kSelWaves][256];
+    uint32_t hist[NW][256];
     uint32_t tot[256];
     uint32_t suf[257];
     uint32_t digit;
 };
 
-template <typename KeyT, int NDIGITS, typename Each>
-__device__ KeyT radix_select_kth(RadixLds &L, Each each, uint32_t k)
+template <typename KeyT, int NDIGITS, int NW, typename Each>
+__device__ KeyT radix_select_kth(RadixLds<NW> &L, Each each, uint32_t k)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int BITS = 8 * sizeof(KeyT);
@@ -51,7 +51,7 @@ __device__ KeyT radix_select_kth(RadixLds &L, Each each, uint32_t k)
     uint32_t remaining = k;
     for (int p = 0; p < NDIGITS; ++p) {
         const int shift = BITS - 8 * (p + 1);
-        for (int i = tid; i < kSelWaves * 256; i += blockDim.x) (&L.hist[0][0])[i] = 0;
+        for (int i = tid; i < NW * 256; i += 64 * NW) (&L.hist[0][0])[i] = 0;
         __syncthreads();
         each([&](KeyT e, bool valid) {
             const bool match = valid && ((p == 0) || (((e ^ prefix) >> (shift + 8)) == 0));
@@ -70,11 +70,11 @@ __device__ KeyT radix_select_kth(RadixLds &L, Each each, uint32_t k)
             }
         });
         __syncthreads();
-        if (tid < 256) {
+        for (int b = tid; b < 256; b += 64 * NW) {
             uint32_t s = 0;
 #pragma unroll
-            for (int w = 0; w < kSelWaves; ++w) s += L.hist[w][tid];
-            L.tot[tid] = s;
+            for (int w = 0; w < NW; ++w) s += L.hist[w][b];
+            L.tot[b] = s;
         }
         __syncthreads();
         if (wave == 0) {
@@ -96,7 +96,8 @@ __device__ KeyT radix_select_kth(RadixLds &L, Each each, uint32_t k)
             if (lane == 0) L.suf[256] = 0;
         }
         __syncthreads();
-        if (tid < 256 && L.suf[tid] >= remaining && L.suf[tid + 1] < remaining) L.digit = tid;
+        for (int b = tid; b < 256; b += 64 * NW)
+            if (L.suf[b] >= remaining && L.suf[b + 1] < remaining) L.digit = b;
         __syncthreads();
         const uint32_t d = L.digit;
         const uint32_t above = L.suf[d + 1];
@@ -163,6 +164,7 @@ struct TauArgs {
     int cap;
     const uint32_t *samp;
     int sample_target;
+    int sample_min_stride;
     float rank_scale;
     int recover_all;
     float *tau;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kTauThreads) void k_tau(TauArgs a)
         if (tid == 0) a.tau[t] = a.recover_all ? __builtin_inff() : -__builtin_inff();
         return;
     }
-    const int d = sample_stride(len, a.sample_target);
+    const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
     const int ns = (int)lattice_count(lo, hi, d);
     const double want = ceil(2.0 * (double)a.topk * (double)ns / (double)len * (double)a.rank_scale);
     const uint32_t r = (uint32_t)min(max(want, 1.0), (double)ns);
@@ -275,13 +277,27 @@ __global__ __launch_bounds__(kTauThreads) void k_tau(TauArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Triage: one block classifies every row, lists the flagged rows in row
-// order and gathers the statistics.
+// Call statistics, accumulated on the device (zeroed by the per-key pass at
+// the start of every call) and copied to the host once selection is done.
+// kStPruned / kStPruneOn are the scan's PlanCounter slots; kStFlagged is also
+// the length of the flagged-row list.
 
 enum Stat {
-    kStRows = 0, kStEmpty, kStTakeAll, kStSampled, kStUnder, kStOver, kStFlagged, kStMaxCand,
-    kStWindow, kStPruned, kStPruneOn, kStCount
+    kStEmpty = 0, kStTakeAll, kStSampled, kStUnder, kStOver, kStFlagged, kStMaxCand, kStWindow,
+    kStPruned, kStPruneOn, kStCount
 };
+static_assert(kStPruneOn == kStPruned + kPlanItems, "the scan's counters live in the statistics");
+
+// Triage of one row (the pages' "recovery triage"): a row with a non-empty
+// window is rescored densely when its candidate count is below
+// min(topk, L) (its threshold was too high) or above the capacity (too low:
+// the list lost candidates), and every row on the recover-all path is.
+__device__ __forceinline__ bool row_flagged(int64_t len, uint32_t c, int topk, int cap, int recover_all)
+{
+    if (len <= 0) return false;
+    if (recover_all) return true;
+    return (int64_t)c < min((int64_t)topk, len) || (int64_t)c > cap;
+}
 
 struct TriageArgs {
     const int32_t *ks;
@@ -291,69 +307,46 @@ struct TriageArgs {
     int cap;
     const uint32_t *cnt;
     int recover_all;
-    int32_t *rowflag;
     int32_t *rowlist;
-    int32_t *nflagged;
-    unsigned long long *stats;
-    const unsigned long long *plan;  // pruning counters, or null (pruning off)
+    unsigned long long *stats;  // Stat
 };
 
-__global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
+// One thread per row; statistics and the flagged-row list are gathered with
+// one atomic per wave and statistic.  The list is in no particular order
+// (each flagged row's result depends on that row alone).
+constexpr int kTriageThreads = 256;
+
+__global__ __launch_bounds__(kTriageThreads) void k_triage(TriageArgs a)
 {
-    __shared__ unsigned long long s_st[kStCount];
-    __shared__ uint32_t s_wave[16];
-    __shared__ uint32_t s_base;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < kStCount) s_st[tid] = 0;
-    if (tid == 0) s_base = 0;
-    __syncthreads();
-    // Per-thread tallies, reduced per wave at the end (no per-row atomics).
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kTriageThreads + threadIdx.x;
     uint32_t n_empty = 0, n_take = 0, n_samp = 0, n_under = 0, n_over = 0, maxc = 0;
     unsigned long long win = 0;
-    for (int64_t b0 = 0; b0 < a.num_q; b0 += 1024) {
-        const int64_t t = b0 + tid;
-        bool flag = false;
-        if (t < a.num_q) {
-            const int64_t lo = a.ks[t], hi = a.ke[t];
-            const int64_t len = hi > lo ? hi - lo : 0;
-            const uint32_t c = a.cnt[t];
-            if (len == 0) {
-                ++n_empty;
-            } else if (a.recover_all) {
-                flag = true;
+    bool flag = false;
+    if (t < a.num_q) {
+        const int64_t lo = a.ks[t], hi = a.ke[t];
+        const int64_t len = hi > lo ? hi - lo : 0;
+        const uint32_t c = a.cnt[t];
+        flag = row_flagged(len, c, a.topk, a.cap, a.recover_all);
+        if (len == 0) {
+            n_empty = 1;
+        } else if (!a.recover_all) {
+            n_under = (int64_t)c < min((int64_t)a.topk, len);
+            n_over = (int64_t)c > a.cap;
+            if (len <= a.cap) {
+                n_take = 1;
             } else {
-                const int64_t need = min((int64_t)a.topk, len);
-                const bool under = (int64_t)c < need;
-                const bool over = (int64_t)c > a.cap;
-                flag = under || over;
-                if (len <= a.cap) {
-                    ++n_take;
-                } else {
-                    ++n_samp;
-                    maxc = max(maxc, c);
-                }
-                n_under += under;
-                n_over += over;
+                n_samp = 1;
+                maxc = c;
             }
-            win += (unsigned long long)len;
-            a.rowflag[t] = flag ? 1 : 0;
         }
-        // Order-preserving compaction of the flagged rows.
-        const uint64_t bal = __ballot(flag);
-        const uint32_t below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) s_wave[wave] = __builtin_popcountll(bal);
-        __syncthreads();
-        uint32_t off = s_base;
-        for (int w = 0; w < wave; ++w) off += s_wave[w];
-        if (flag) a.rowlist[off + below] = (int32_t)t;
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t sum = 0;
-            for (int w = 0; w < 16; ++w) sum += s_wave[w];
-            s_base += sum;
-        }
-        __syncthreads();
+        win = (unsigned long long)len;
     }
+    const uint64_t bal = __ballot(flag);
+    unsigned long long base = 0;
+    if (lane == 0 && bal) base = atomicAdd(a.stats + kStFlagged, (unsigned long long)__builtin_popcountll(bal));
+    base = __shfl(base, 0);
+    if (flag) a.rowlist[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (int32_t)t;
     for (int off = 32; off > 0; off >>= 1) {
         n_empty += __shfl_xor(n_empty, off);
         n_take += __shfl_xor(n_take, off);
@@ -364,24 +357,14 @@ __global__ __launch_bounds__(1024) void k_triage(TriageArgs a)
         win += __shfl_xor(win, off);
     }
     if (lane == 0) {
-        atomicAdd(&s_st[kStEmpty], (unsigned long long)n_empty);
-        atomicAdd(&s_st[kStTakeAll], (unsigned long long)n_take);
-        atomicAdd(&s_st[kStSampled], (unsigned long long)n_samp);
-        atomicAdd(&s_st[kStUnder], (unsigned long long)n_under);
-        atomicAdd(&s_st[kStOver], (unsigned long long)n_over);
-        atomicMax(&s_st[kStMaxCand], (unsigned long long)maxc);
-        atomicAdd(&s_st[kStWindow], win);
+        if (n_empty) atomicAdd(a.stats + kStEmpty, (unsigned long long)n_empty);
+        if (n_take) atomicAdd(a.stats + kStTakeAll, (unsigned long long)n_take);
+        if (n_samp) atomicAdd(a.stats + kStSampled, (unsigned long long)n_samp);
+        if (n_under) atomicAdd(a.stats + kStUnder, (unsigned long long)n_under);
+        if (n_over) atomicAdd(a.stats + kStOver, (unsigned long long)n_over);
+        if (maxc) atomicMax(a.stats + kStMaxCand, (unsigned long long)maxc);
+        if (win) atomicAdd(a.stats + kStWindow, win);
     }
-    __syncthreads();
-    if (tid == 0) {
-        *a.nflagged = (int32_t)s_base;
-        s_st[kStRows] = (unsigned long long)a.num_q;
-        s_st[kStFlagged] = s_base;
-        s_st[kStPruneOn] = (a.plan && a.plan[kPlanItems] > 0) ? 1ull : 0ull;
-        s_st[kStPruned] = a.plan ? a.plan[kPlanPruned] : 0ull;
-    }
-    __syncthreads();
-    if (tid < kStCount) a.stats[tid] = s_st[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -392,13 +375,14 @@ struct SelectArgs {
     const int32_t *ke;
     int topk;
     int cap;
+    int recover_all;
     // candidate rows
     const uint32_t *cnt;
-    const int32_t *rowflag;
     const uint64_t *cand;
-    // dense (recovered) rows
+    // flagged rows (listed by triage, read by dense recovery)
     const int32_t *rowlist;
-    const int32_t *nrows;
+    const unsigned long long *stats;  // Stat; stats[kStFlagged] = list length
+    // dense (recovered) rows
     int row_base;
     int row_limit;
     const uint64_t *scratch;
@@ -407,54 +391,71 @@ struct SelectArgs {
     float *out_val;
 };
 
-// Bucketed selection.  The row's candidates are spread over kBuckets
-// buckets linear in score between their minimum and maximum, highest scores
-// in bucket 0.  The bucket function is monotone (a larger score never lands
-// in a later bucket, equal scores share a bucket), so after one histogram and
+// Bucketed selection.  The row's candidates are spread over NBKT buckets
+// linear in score between their minimum and maximum, highest scores in
+// bucket 0.  The bucket function is monotone (a larger score never lands in
+// a later bucket, equal scores share a bucket), so after one histogram and
 // one prefix sum the bucket holding the k-th key is known, every key of an
 // earlier bucket is selected, and a counting-sort scatter followed by a sort
 // of each (small) bucket by full key yields the top k in order.  Rows whose
 // buckets are too crowded (massive ties) use the radix select + bitonic sort.
-constexpr int kBuckets = 4096;
 constexpr int kSegMax = 48;
-constexpr int kBinsPerThread = kBuckets / kSelThreads;
 
+template <int NT, int NBKT, int MAXK>
 struct SelectLds {
+    static constexpr int NW = NT / 64;
     union {
-        RadixLds radix;
-        uint32_t bucket[kBuckets];
+        RadixLds<NW> radix;
+        uint32_t bucket[NBKT];
     };
-    uint64_t sel[kMaxTopk + kSegMax];
-    float redf[2 * kSelWaves];
-    uint32_t redu[kSelWaves];
+    uint64_t sel[MAXK + kSegMax];
+    float redf[2 * NW];
+    uint32_t redu[NW];
     uint32_t misc[4];
 };
 
 __device__ __forceinline__ float raw_score(uint64_t r) { return __uint_as_float((uint32_t)r); }
 
-// NREG == 0: dense (recovered) rows streamed from scratch; otherwise the
-// row's candidates (count <= NREG * kSelThreads) are held in registers.
-template <int NREG>
-__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
+// Launch shapes of the selection kernel: NREG candidates per thread in
+// registers (0: dense rows streamed from scratch), NT threads, NBKT buckets,
+// rows of at most MAXK outputs.  Small candidate lists get small workgroups
+// with small LDS, so more rows are in flight per compute unit.
+template <int NREG, int NT, int NBKT, int MAXK> struct SelShape {
+    static constexpr int nreg = NREG, nt = NT, nbkt = NBKT, maxk = MAXK;
+};
+using SelSmall = SelShape<8, 256, 2048, 2048>;     // cap <= 2048
+using SelMid = SelShape<8, 512, 4096, kMaxTopk>;   // cap <= 4096
+using SelLarge = SelShape<16, 512, 4096, kMaxTopk>;  // cap <= 8192
+using SelHuge = SelShape<32, 512, 4096, kMaxTopk>;   // cap <= 16384
+using SelDense = SelShape<0, 512, 4096, kMaxTopk>;   // recovered rows
+
+// Candidate mode: rows that triage flags (same predicate) are left to dense
+// recovery; every other row's candidates hold its whole top k.
+template <typename SH>
+__global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
 {
+    constexpr int NREG = SH::nreg, NT = SH::nt, NBKT = SH::nbkt, MAXK = SH::maxk;
+    constexpr int NW = NT / 64, BPT = NBKT / NT;
     constexpr bool DENSE = NREG == 0;
-    __shared__ SelectLds S;
+    __shared__ SelectLds<NT, NBKT, MAXK> S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int t;
     const uint64_t *src;
     int64_t n;
     if (DENSE) {
         const int e = blockIdx.x;
-        if (e >= a.row_limit || a.row_base + e >= *a.nrows) return;
+        if (e >= a.row_limit || (unsigned long long)(a.row_base + e) >= a.stats[kStFlagged]) return;
         t = a.rowlist[a.row_base + e];
         src = a.scratch + (int64_t)e * a.scratch_stride;
         const int64_t lo = a.ks[t], hi = a.ke[t];
         n = hi > lo ? hi - lo : 0;
     } else {
         t = blockIdx.x;
-        if (a.rowflag[t]) return;
+        const int64_t lo = a.ks[t], hi = a.ke[t];
+        const uint32_t c = a.cnt[t];
+        if (row_flagged(hi > lo ? hi - lo : 0, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
         src = a.cand + (int64_t)t * a.cap;
-        n = min((int64_t)a.cnt[t], (int64_t)a.cap);  // a.cap <= NREG * kSelThreads
+        n = min((int64_t)c, (int64_t)a.cap);  // a.cap <= NREG * NT
     }
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
     int32_t *oi = a.out_idx + (int64_t)t * a.topk;
@@ -481,35 +482,35 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
         }
         if (lane == 0) {
             S.redf[wave] = lo;
-            S.redf[kSelWaves + wave] = hi;
+            S.redf[NW + wave] = hi;
         }
-        for (int i = tid; i < kBuckets; i += blockDim.x) S.bucket[i] = 0;
+        for (int i = tid; i < NBKT; i += NT) S.bucket[i] = 0;
         __syncthreads();
         lo = S.redf[0];
-        hi = S.redf[kSelWaves];
-        for (int w = 1; w < kSelWaves; ++w) {
+        hi = S.redf[NW];
+        for (int w = 1; w < NW; ++w) {
             lo = fminf(lo, S.redf[w]);
-            hi = fmaxf(hi, S.redf[kSelWaves + w]);
+            hi = fmaxf(hi, S.redf[NW + w]);
         }
         mx = hi;
-        scale = (float)kBuckets / (hi - lo);
+        scale = (float)NBKT / (hi - lo);
         fast = hi > lo && __builtin_isfinite(scale) && __builtin_isfinite(hi - lo);
     }
     auto bucket_of = [&](float f) -> uint32_t {
         const float x = (mx - f) * scale;
-        return x < (float)(kBuckets - 1) ? (uint32_t)x : (uint32_t)(kBuckets - 1);
+        return x < (float)(NBKT - 1) ? (uint32_t)x : (uint32_t)(NBKT - 1);
     };
     if (fast) {
         el.each([&](uint64_t r, bool v) {
             if (v) atomicAdd(&S.bucket[bucket_of(raw_score(r))], 1u);
         });
         __syncthreads();
-        // Exclusive prefix over buckets; each thread owns kBinsPerThread
-        // consecutive buckets and keeps their counts.
-        uint32_t cntv[kBinsPerThread], run = 0;
+        // Exclusive prefix over buckets; each thread owns BPT consecutive
+        // buckets and keeps their counts.
+        uint32_t cntv[BPT], run = 0;
 #pragma unroll
-        for (int q = 0; q < kBinsPerThread; ++q) {
-            cntv[q] = S.bucket[tid * kBinsPerThread + q];
+        for (int q = 0; q < BPT; ++q) {
+            cntv[q] = S.bucket[tid * BPT + q];
             run += cntv[q];
         }
         uint32_t x = run;
@@ -523,8 +524,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
         uint32_t base = x - run;
         for (int w = 0; w < wave; ++w) base += S.redu[w];
 #pragma unroll
-        for (int q = 0; q < kBinsPerThread; ++q) {
-            const uint32_t b = tid * kBinsPerThread + q;
+        for (int q = 0; q < BPT; ++q) {
+            const uint32_t b = tid * BPT + q;
             S.bucket[b] = base;
             if (base <= k - 1 && k - 1 < base + cntv[q]) S.misc[0] = b;  // bucket of the k-th key
             base += cntv[q];
@@ -533,12 +534,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
         kb = S.misc[0];
         uint32_t seg = 0;
 #pragma unroll
-        for (int q = 0; q < kBinsPerThread; ++q)
-            if ((uint32_t)(tid * kBinsPerThread + q) <= kb) seg = max(seg, cntv[q]);
+        for (int q = 0; q < BPT; ++q)
+            if ((uint32_t)(tid * BPT + q) <= kb) seg = max(seg, cntv[q]);
         for (int off = 32; off > 0; off >>= 1) seg = max(seg, (uint32_t)__shfl_xor(seg, off));
         if (lane == 0) S.redu[wave] = seg;
         __syncthreads();
-        for (int w = 0; w < kSelWaves; ++w) seg = max(seg, S.redu[w]);
+        for (int w = 0; w < NW; ++w) seg = max(seg, S.redu[w]);
         fast = seg <= (uint32_t)kSegMax;
         if (fast) {
             el.each([&](uint64_t r, bool v) {
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
             });
             __syncthreads();
             // Bucket b now spans [bucket[b-1], bucket[b]); sort it descending.
-            for (uint32_t b = tid; b <= kb; b += blockDim.x) {
+            for (uint32_t b = tid; b <= kb; b += NT) {
                 const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
                 for (uint32_t i = s0 + 1; i < s1; ++i) {
                     const uint64_t v = S.sel[i];
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
     if (k > 0 && !fast) {
         uint64_t thr = 0;
         if ((int64_t)k < n)
-            thr = radix_select_kth<uint64_t, 8>(
+            thr = radix_select_kth<uint64_t, 8, NW>(
                 S.radix, [&](auto f) { el.each([&](uint64_t r, bool v) { f(key_of_raw(r), v); }); }, k);
         if (tid == 0) S.misc[1] = 0;
         __syncthreads();
@@ -577,17 +578,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
             const uint64_t e = key_of_raw(r);
             if (v && e >= thr) {
                 const uint32_t pos = atomicAdd(&S.misc[1], 1u);
-                if (pos < (uint32_t)kMaxTopk) S.sel[pos] = e;
+                if (pos < (uint32_t)MAXK) S.sel[pos] = e;
             }
         });
         uint32_t P = 1;
         while (P < k) P <<= 1;
         __syncthreads();
-        for (uint32_t i = k + tid; i < P; i += blockDim.x) S.sel[i] = 0;  // below every real key
+        for (uint32_t i = k + tid; i < P; i += NT) S.sel[i] = 0;  // below every real key
         __syncthreads();
         for (uint32_t size = 2; size <= P; size <<= 1) {
             for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-                for (uint32_t i = tid; i < P / 2; i += blockDim.x) {
+                for (uint32_t i = tid; i < P / 2; i += NT) {
                     const uint32_t l0 = 2 * i - (i & (stride - 1));
                     const uint32_t l1 = l0 + stride;
                     const bool desc = (l0 & size) == 0;
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a)
             }
         }
     }
-    for (int j = tid; j < a.topk; j += blockDim.x) {
+    for (int j = tid; j < a.topk; j += NT) {
         int32_t idx = -1;
         float v = -__builtin_inff();
         if ((uint32_t)j < k) {
