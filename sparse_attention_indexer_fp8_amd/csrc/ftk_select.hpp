@@ -133,6 +133,17 @@ struct RowElems {
             }
         }
     }
+    // f(q, raw, valid) for the register slots q (REG only; q is a
+    // compile-time index after unrolling), every lane of the wave together.
+    template <typename F>
+    __device__ __forceinline__ void each_slot(F f) const
+    {
+#pragma unroll
+        for (int q = 0; q < kRegPer; ++q) {
+            const int64_t i = threadIdx.x + (int64_t)q * blockDim.x;
+            if (__any(i < n)) f(q, r[q], i < n);
+        }
+    }
     // f(raw, valid): visits this thread's elements; REG visits every slot so
     // wave-wide operations inside f see all lanes.
     template <typename F>
@@ -396,10 +407,13 @@ struct SelectArgs {
 // bucket 0.  The bucket function is monotone (a larger score never lands in
 // a later bucket, equal scores share a bucket), so after one histogram and
 // one prefix sum the bucket holding the k-th key is known, every key of an
-// earlier bucket is selected, and a counting-sort scatter followed by a sort
-// of each (small) bucket by full key yields the top k in order.  Rows whose
-// buckets are too crowded (massive ties) use the radix select + bitonic sort.
-constexpr int kSegMax = 48;
+// earlier bucket is selected, and a counting-sort scatter puts each bucket's
+// keys in its slot range.  Each key then finds its place inside its bucket
+// by counting the larger keys there (independent LDS reads, one key per
+// thread, no serial insertion) and moves to it.  Rows with a bucket of more
+// than kSegMax keys up to the k-th (massive ties) use the radix select +
+// bitonic sort.
+constexpr int kSegMax = 256;
 
 template <int NT, int NBKT, int MAXK>
 struct SelectLds {
@@ -425,8 +439,8 @@ template <int NREG, int NT, int NBKT, int MAXK> struct SelShape {
 };
 using SelSmall = SelShape<8, 256, 2048, 2048>;     // cap <= 2048
 using SelMid = SelShape<8, 512, 4096, kMaxTopk>;   // cap <= 4096
-using SelLarge = SelShape<16, 512, 4096, kMaxTopk>;  // cap <= 8192
-using SelHuge = SelShape<32, 512, 4096, kMaxTopk>;   // cap <= 16384
+using SelLarge = SelShape<8, 1024, 4096, kMaxTopk>;  // cap <= 8192
+using SelHuge = SelShape<16, 1024, 4096, kMaxTopk>;  // cap <= 16384
 using SelDense = SelShape<0, 512, 4096, kMaxTopk>;   // recovered rows
 
 // Candidate mode: rows that triage flags (same predicate) are left to dense
@@ -540,7 +554,7 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
         if (lane == 0) S.redu[wave] = seg;
         __syncthreads();
         for (int w = 0; w < NW; ++w) seg = max(seg, S.redu[w]);
-        fast = seg <= (uint32_t)kSegMax;
+        fast = seg <= (DENSE ? 48u : (uint32_t)kSegMax);  // streamed rows sort buckets serially
         if (fast) {
             el.each([&](uint64_t r, bool v) {
                 if (v) {
@@ -549,17 +563,43 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
                 }
             });
             __syncthreads();
-            // Bucket b now spans [bucket[b-1], bucket[b]); sort it descending.
-            for (uint32_t b = tid; b <= kb; b += NT) {
-                const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
-                for (uint32_t i = s0 + 1; i < s1; ++i) {
-                    const uint64_t v = S.sel[i];
-                    uint32_t j = i;
-                    while (j > s0 && S.sel[j - 1] < v) {
-                        S.sel[j] = S.sel[j - 1];
-                        --j;
+            // Bucket b now spans [bucket[b-1], bucket[b]).
+            if (!DENSE) {
+                // Place of each key: the bucket start plus the number of
+                // larger keys in the bucket (keys are distinct), computed
+                // for all keys before any key moves.
+                uint32_t place[NREG > 0 ? NREG : 1];
+                el.each_slot([&](int q, uint64_t r, bool v) {
+                    uint32_t pl = 0xFFFFFFFFu;
+                    if (v) {
+                        const uint32_t b = bucket_of(raw_score(r));
+                        if (b <= kb) {
+                            const uint64_t e = key_of_raw(r);
+                            const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
+                            uint32_t rank = 0;
+                            for (uint32_t j = s0; j < s1; ++j) rank += S.sel[j] > e ? 1u : 0u;
+                            pl = s0 + rank;
+                        }
                     }
-                    S.sel[j] = v;
+                    place[q] = pl;
+                });
+                __syncthreads();
+                el.each_slot([&](int q, uint64_t r, bool v) {
+                    if (v && place[q] != 0xFFFFFFFFu) S.sel[place[q]] = key_of_raw(r);
+                });
+            } else {
+                // Streamed rows (recovery): insertion sort of each bucket.
+                for (uint32_t b = tid; b <= kb; b += NT) {
+                    const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
+                    for (uint32_t i = s0 + 1; i < s1; ++i) {
+                        const uint64_t v = S.sel[i];
+                        uint32_t j = i;
+                        while (j > s0 && S.sel[j - 1] < v) {
+                            S.sel[j] = S.sel[j - 1];
+                            --j;
+                        }
+                        S.sel[j] = v;
+                    }
                 }
             }
             __syncthreads();
