@@ -666,18 +666,29 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 #pragma unroll
                 for (int kt = 0; kt < kSub; ++kt)
                     shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(16 * g + 64 * kt), soff));
-            } else if (MODE != kModeSample) {
+            } else if (MODE == kModeSample) {
+                // Lattice keys first_b + e * dmin: a strided gather from the
+                // padded factors (entries past the end are never used).
+#pragma unroll
+                for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        shv[kt][i] = a.sigh[min(first_b + (sb + 16 * kt + i) * dmin, S + kStepKeys - 1)];
+            } else {
 #pragma unroll
                 for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
             }
         };
-        if (Cfg::prefetch) load_sh();
+        // The factors load before the MFMA work where registers allow (their
+        // latency hides behind it); otherwise right after the last MFMA and
+        // before the next step's key loads (loads complete in order, so
+        // waiting for them does not wait for the keys).  BF16 sampling keeps
+        // its registers for the key fragments.
+        constexpr bool early = Cfg::prefetch && !(DT == kBF16 && MODE == kModeSample);
+        if (early) load_sh();
         StepOut o;
-        // Without prefetching, the scale factors are requested right after
-        // the last MFMA and before the next step's key loads: loads complete
-        // in order, so waiting for them does not wait for the keys.
         score_step(o, kf, s_q, s_w, lane, qsc, [&]() {
-            if (!Cfg::prefetch) load_sh();
+            if (!early) load_sh();
             next();
         });
         if (MODE == kModeFilter) {
@@ -740,18 +751,31 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             }
             ring_cnt += direct ? 0u : tot;
         } else if (MODE == kModeSample) {
+            // The lane's 4 outputs of a subtile are consecutive lattice keys;
+            // when the row samples on the tile's lattice they are consecutive
+            // sample slots and go out as one 16-byte store.
+            uint32_t *srow = a.samp + (int64_t)(t < 0 ? 0 : t) * a.sample_target;
 #pragma unroll
-            for (int kt = 0; kt < kSub; ++kt)
+            for (int kt = 0; kt < kSub; ++kt) {
+                const int e0 = sb + 16 * kt;
+                const int p0 = first_b + e0 * dmin, p3 = p0 + 3 * dmin;
+                const int idx0 = (p0 - first_n) >> dsh;
+                if (t >= 0 && dn == dmin && e0 + 3 < nlat && p0 >= rks && p3 < rke && (idx0 & 3) == 0) {
+                    v4i v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = sb + 16 * kt + i;
-                    if (t < 0 || e >= nlat) continue;
-                    const int p = first_b + e * dmin;
-                    if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
-                    const int idx = (p - first_n) >> dsh;
-                    a.samp[(int64_t)t * a.sample_target + idx] =
-                        ord_of(score_of<DT>(o, kt, i, sigh_of<DT>(a.sigma, p)));
+                    for (int i = 0; i < 4; ++i) v[i] = (int)ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
+                    *reinterpret_cast<v4i *>(srow + idx0) = v;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = e0 + i;
+                        if (t < 0 || e >= nlat) continue;
+                        const int p = first_b + e * dmin;
+                        if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
+                        srow[(p - first_n) >> dsh] = ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
+                    }
                 }
+            }
         } else {
             const int slot = tile * kTileQ + n;
 #pragma unroll
