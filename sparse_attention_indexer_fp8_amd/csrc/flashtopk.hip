@@ -4,7 +4,7 @@
 //   0. k_keyprep        per-key scale factors (+ block extremes for the bound)
 //      k_qbar           (FP8) head-weighted query sums, split into FP8 parts
 //   1. k_score<sample>  strided-sample scores of every long row     (MFMA)
-//   2. k_tau            per-row threshold = r-th largest sample score
+//   2. k_tau            per-row threshold from the row's sample
 //   3. k_score<filter>  fused score (+ bound) + threshold filter -> candidates (MFMA, hot)
 //   4. k_triage         flag rows whose candidates under/overflowed
 //   5. k_select         exact top-k of every unflagged row
@@ -26,6 +26,7 @@
 #include "ftk_bound.hpp"
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
+#include "ftk_tau.hpp"
 
 using namespace ftk;
 
@@ -255,7 +256,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
         sa.kb = (const uint8_t *)w->kb.ptr;
         sa.meta = (const float2 *)w->kmeta.ptr;
-        sa.q1 = (const float *)w->q1.ptr;
+        sa.q1 = (float *)w->q1.ptr;
         sa.nblocks = nblocks;
         sa.vplan = (float *)w->vplan.ptr;
         sa.plan = (unsigned long long *)w->stats.ptr + kStPruned;
@@ -277,28 +278,28 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
                                                       (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
                                                       kStCount);
     }
-    const dim3 rgrid((unsigned)((T + 3) / 4));
     if (fp8)
-        k_qbar<<<rgrid, 256, 0, stream>>>((const uint8_t *)q, weights, T, (uint8_t *)w->qbar.ptr,
-                                          (float *)w->qscale.ptr, bounds ? (float *)w->q1.ptr : nullptr);
-    else if (bounds)
-        k_qnorm_bf16<<<rgrid, 256, 0, stream>>>((const uint8_t *)q, weights, T, (float *)w->q1.ptr);
-    if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * kSampleSplit)), stream, sa);
+        k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T,
+                                                                 (uint8_t *)w->qbar.ptr, (float *)w->qscale.ptr);
+    if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3((unsigned)ntiles), stream, sa);
     mark(*w, p, 1, stream);
 
-    TauArgs ta{};
-    ta.ks = ks;
-    ta.ke = ke;
-    ta.topk = p.topk;
-    ta.cap = p.cap;
-    ta.samp = (const uint32_t *)w->samp.ptr;
-    ta.sample_target = p.sample_target;
-    ta.sample_min_stride = p.sample_min_stride;
-    ta.rank_scale = p.rank_scale;
-    ta.recover_all = recover_all ? 1 : 0;
-    ta.tau = (float *)w->tau.ptr;
-    ta.cnt = (uint32_t *)w->cnt.ptr;
-    k_tau<<<dim3((unsigned)T), kTauThreads, 0, stream>>>(ta);
+    if (!recover_all) {
+        TauArgs ta{};
+        ta.ks = ks;
+        ta.ke = ke;
+        ta.num_q = T;
+        ta.topk = p.topk;
+        ta.cap = p.cap;
+        ta.samp = (const uint32_t *)w->samp.ptr;
+        ta.sample_target = p.sample_target;
+        ta.sample_min_stride = p.sample_min_stride;
+        ta.rank_scale = p.rank_scale;
+        ta.tau = (float *)w->tau.ptr;
+        ta.cnt = (uint32_t *)w->cnt.ptr;
+        k_tau<<<dim3((unsigned)((T + kTauWaves - 1) / kTauWaves)), 64 * kTauWaves, 0, stream>>>(ta);
+    }
+
     mark(*w, p, 2, stream);
 
     if (!recover_all) launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);

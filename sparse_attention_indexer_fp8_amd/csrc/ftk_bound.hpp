@@ -167,30 +167,6 @@ __global__ __launch_bounds__(256) void k_keyprep(const uint8_t *kv, const float 
     }
 }
 
-// Per-row norm of the rounding margin, Q1[t] = sum_h |w[t,h]| ||q[t,h,:]||_1
-// (BF16; the FP8 path gets it from k_qbar).  One wave per row.
-__global__ __launch_bounds__(256) void k_qnorm_bf16(const uint8_t *q, const float *w, int64_t num_q, float *q1)
-{
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= num_q) return;
-    const uint8_t *qr = q + t * kHeads * 256 + 4 * lane;
-    uint32_t c[kHeads];
-    float wv[kHeads];
-#pragma unroll
-    for (int h = 0; h < kHeads; ++h) {
-        c[h] = *reinterpret_cast<const uint32_t *>(qr + h * 256);
-        wv[h] = w[t * kHeads + h];
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kHeads; ++h)
-        s = __builtin_fmaf(fabsf(wv[h]), __uint_as_float((c[h] << 16) & 0x7FFF0000u) + __uint_as_float(c[h] & 0x7FFF0000u),
-                           s);
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) q1[t] = s;
-}
-
 // ---------------------------------------------------------------------------
 // Bound of one 16-block group for a tile: lane (n, g) gets, for the blocks
 // 16 c + 4 g + i (i < 4) and query n, u[i] = sum_h max(w[n,h], 0) ReLU(ub).

@@ -43,10 +43,9 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_trunc(float v)
 }
 
 // One wave per query row; lane l owns dimensions 2l and 2l+1.  Writes
-// parts[t][p][d] (E4M3 codes) and qscale[t] = 2^-e, and when q1 is not null
-// q1[t] = sum_h |w[t,h]| ||q[t,h,:]||_1 (the score-bound rounding margin).
+// parts[t][p][d] (E4M3 codes) and qscale[t] = 2^-e.
 __global__ __launch_bounds__(256) void k_qbar(const uint8_t *q, const float *w, int64_t num_q, uint8_t *parts,
-                                              float *qscale, float *q1)
+                                              float *qscale)
 {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -59,17 +58,11 @@ __global__ __launch_bounds__(256) void k_qbar(const uint8_t *q, const float *w, 
         c[h] = *reinterpret_cast<const uint16_t *>(qr + h * kDim);
         wv[h] = w[t * kHeads + h];
     }
-    float v0 = 0.0f, v1 = 0.0f, l1 = 0.0f;
+    float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) {
-        const float e0 = e4m3_to_f32(c[h] & 0xFFu), e1 = e4m3_to_f32(c[h] >> 8);
-        v0 = __builtin_fmaf(wv[h], e0, v0);
-        v1 = __builtin_fmaf(wv[h], e1, v1);
-        if (q1) l1 = __builtin_fmaf(fabsf(wv[h]), fabsf(e0) + fabsf(e1), l1);
-    }
-    if (q1) {
-        for (int off = 32; off > 0; off >>= 1) l1 += __shfl_xor(l1, off);
-        if (lane == 0) q1[t] = l1;
+        v0 = __builtin_fmaf(wv[h], e4m3_to_f32(c[h] & 0xFFu), v0);
+        v1 = __builtin_fmaf(wv[h], e4m3_to_f32(c[h] >> 8), v1);
     }
     float m = fmaxf(fabsf(v0), fabsf(v1));
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));

@@ -47,8 +47,6 @@ constexpr int kModeFilter = 0;
 constexpr int kModeSample = 1;
 constexpr int kModeDense = 2;
 
-// Workgroups per tile in sample mode (each scores a part of the lattice).
-constexpr int kSampleSplit = 1;
 
 // q-tile "heads" in LDS: the 32 heads, plus the qbar parts on the FP8 path.
 template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? kHeads + kQbarParts : kHeads; };
@@ -110,7 +108,7 @@ struct ScoreArgs {
     int prune;                 // 0: off; 1: per tile, from its planner sample; 2: always
     const uint8_t *kb;         // [nblocks, 2, 128] block extremes
     const float2 *meta;        // [nblocks] (sigmax, kabs)
-    const float *q1;           // [num_q] sum_h |w| ||q_h||_1
+    float *q1;                 // [num_q] sum_h |w| ||q_h||_1 (written by sample mode)
     int nblocks;
     float *vplan;              // [ntiles, kPlanGroups, 16 blocks, 16 rows] planner sample
     unsigned long long *plan;  // PlanCounter slots
@@ -405,6 +403,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     __shared__ uint16_t s_skip[MODE == kModeFilter ? kMaxSteps / 16 + 1 : 1];  // per 16-block group
     __shared__ int s_wcnt[kWaves];
     __shared__ float s_tau[kTileQ], s_q1[kTileQ];
+    __shared__ float s_l1[MODE == kModeSample ? kTileQ * kHeads : 1];
     __shared__ unsigned long long s_pp[2];  // planner sample: pairs, prunable pairs
     float *s_w = reinterpret_cast<float *>(smem);
     uint8_t *s_q = smem + WB;
@@ -444,7 +443,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         s_ke[n] = hi;
         s_d[n] = d;
         if (MODE == kModeFilter) s_tau[n] = t >= 0 ? a.tau[t] : __builtin_inff();
-        if (MODE != kModeDense && a.prune) s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
+        if (MODE == kModeFilter && a.prune) s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
         if (n < 2) s_pp[n] = 0ull;
     }
     __syncthreads();
@@ -477,10 +476,8 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         const int msh = __builtin_ctz((unsigned)dmin);  // power of two
         first_b = ((lo + dmin - 1) >> msh) << msh;
         nlat = (int)lattice_count(lo, hi, dmin);
-        const int nsteps = (nlat + kStepKeys - 1) / kStepKeys;
-        const int per = (nsteps + kSampleSplit - 1) / kSampleSplit;
-        jlo = chunk * per;
-        jhi = min(nsteps, jlo + per);
+        jlo = 0;
+        jhi = (nlat + kStepKeys - 1) / kStepKeys;
         if (jhi <= jlo) return;
     } else {
         const int64_t c0 = (int64_t)chunk * a.chunk;
@@ -500,6 +497,40 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 
     int nstep = jhi - jlo;
     bool use_skip = false;  // workgroup-uniform
+    if (MODE == kModeSample && a.prune) {
+        // Q1[t] = sum_h |w[t,h]| ||q[t,h,:]||_1 of the sampled rows (the
+        // bound's rounding margin), from the q tile in LDS: one (row, head)
+        // per thread, then one thread per row.
+        static_assert(MODE != kModeSample || 64 * kWaves == kTileQ * kHeads, "one (row, head) pair per thread");
+        constexpr int SUB = RB / 64;
+        const int rn = threadIdx.x & (kTileQ - 1), h = threadIdx.x >> 4;
+        float l1 = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                const v4i v = *reinterpret_cast<const v4i *>(s_q + ((h * SUB + sub) * 64 + rn + 16 * gg) * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t u = (uint32_t)v[e];
+                    if (DT == kFP8) {
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) l1 += e4m3_to_f32((u >> (8 * y)) & 0x7Fu);
+                    } else {
+                        l1 += __uint_as_float((u << 16) & 0x7FFF0000u) + __uint_as_float(u & 0x7FFF0000u);
+                    }
+                }
+            }
+        s_l1[rn * kHeads + h] = fabsf(s_w[h * kTileQ + rn]) * l1;
+        __syncthreads();
+        if (threadIdx.x < kTileQ) {
+            float q1 = 0.0f;
+            for (int hh = 0; hh < kHeads; ++hh) q1 += s_l1[threadIdx.x * kHeads + hh];
+            s_q1[threadIdx.x] = q1;
+            if (s_row[threadIdx.x] >= 0) a.q1[s_row[threadIdx.x]] = q1;
+        }
+        __syncthreads();
+    }
     if (MODE == kModeSample && a.prune == 1 && threadIdx.x < 64 * kPlanGroups) {
         // Planner sample: the skip test's left side for kPlanGroups groups
         // spread over the union of ALL the tile's windows (take-all rows

@@ -1,24 +1,18 @@
-// Per-row threshold, triage and exact selection kernels.
+// Triage and exact selection kernels.
 //
-// Threshold ("gate"): FlashTopK README, "Highlights": each row's threshold
-// comes from a strided sample of its own window.  The sample is the lattice of
-// multiples of a power-of-two stride d inside [ks, ke) (at most
-// `sample_target` keys); the threshold is the r-th largest sample score with
-// r = ceil(alpha * topk * n_sample / L), alpha = 2, so about alpha * topk keys
-// of the window are expected to reach it.
-//
-// Exactness ("What you can do": exact; rows the sampled threshold misses are
-// rescored on the GPU): a row whose candidate count is below min(topk, L)
-// (the threshold was too high) or above the candidate capacity (too low) is
-// flagged by triage and rescored densely; every other row's candidates
-// contain its whole top-k, because every key outside them scores below the
-// threshold.
+// Exactness (FlashTopK README, "What you can do": exact; rows the sampled
+// threshold misses are rescored on the GPU): a row whose candidate count is
+// below min(topk, L) (the threshold was too high) or above the candidate
+// capacity (too low) is flagged by triage and rescored densely; every other
+// row's candidates contain its whole top-k, because every key outside them
+// scores below the threshold.
 //
 // Selection: the k-th largest 64-bit key (score code, complemented index) is
-// found by an MSB-first radix select with 8-bit digits; keys at or above it --
-// exactly k, since keys are distinct -- are gathered into LDS and sorted
-// descending by a bitonic network.  Descending key order is score descending
-// with the smaller index first on ties ("What you can do": deterministic).
+// located by bucketing the candidates by score (or, for massive ties, by an
+// MSB-first radix select with 8-bit digits); keys at or above it -- exactly
+// k, since keys are distinct -- are put in descending order.  Descending key
+// order is score descending with the smaller index first on ties ("What you
+// can do": deterministic).
 #pragma once
 
 #include "ftk_common.hpp"
@@ -164,128 +158,6 @@ struct RowElems {
         }
     }
 };
-
-// ---------------------------------------------------------------------------
-// Per-row threshold from the row's strided sample.
-
-struct TauArgs {
-    const int32_t *ks;
-    const int32_t *ke;
-    int topk;
-    int cap;
-    const uint32_t *samp;
-    int sample_target;
-    int sample_min_stride;
-    float rank_scale;
-    int recover_all;
-    float *tau;
-    uint32_t *cnt;
-};
-
-// The threshold needs no exact rank -- only the candidate count it admits
-// matters, and triage catches any row it misjudges -- so the sample is
-// bucketed linearly in score (kTauBuckets buckets between the sample's
-// minimum and maximum, highest first) and the threshold is the lower edge of
-// the bucket that holds the r-th largest sample.  At least r samples reach it.
-constexpr int kTauThreads = 256;
-constexpr int kTauBuckets = 2048;
-
-__global__ __launch_bounds__(kTauThreads) void k_tau(TauArgs a)
-{
-    __shared__ uint32_t s_b[kTauBuckets];
-    __shared__ float s_red[2 * (kTauThreads / 64)];
-    __shared__ uint32_t s_tot[kTauThreads / 64];
-    __shared__ float s_tau;
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int NW = kTauThreads / 64, PER = kTauBuckets / kTauThreads;
-    const int64_t lo = a.ks[t], hi = a.ke[t];
-    const int64_t len = hi > lo ? hi - lo : 0;
-    if (tid == 0) a.cnt[t] = 0;
-    if (a.recover_all || len <= a.cap) {
-        if (tid == 0) a.tau[t] = a.recover_all ? __builtin_inff() : -__builtin_inff();
-        return;
-    }
-    const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
-    const int ns = (int)lattice_count(lo, hi, d);
-    const double want = ceil(2.0 * (double)a.topk * (double)ns / (double)len * (double)a.rank_scale);
-    const uint32_t r = (uint32_t)min(max(want, 1.0), (double)ns);
-    const uint32_t *row = a.samp + (int64_t)t * a.sample_target;
-    // Visits this thread's samples in register chunks of 8 (loads in flight
-    // together); one chunk covers the default sample size.
-    constexpr int CH = 8;
-    auto each = [&](auto f) {
-        for (int base = 0; base < ns; base += CH * kTauThreads) {
-            float v[CH];
-#pragma unroll
-            for (int q = 0; q < CH; ++q) {
-                const int i = base + tid + q * kTauThreads;
-                v[q] = i < ns ? float_of_ord(row[i]) : __builtin_nanf("");
-            }
-#pragma unroll
-            for (int q = 0; q < CH; ++q)
-                if (base + tid + q * kTauThreads < ns) f(v[q]);
-        }
-    };
-    float vmin = __builtin_inff(), vmax = -__builtin_inff();
-    each([&](float f) {
-        vmin = fminf(vmin, f);
-        vmax = fmaxf(vmax, f);
-    });
-    for (int off = 32; off > 0; off >>= 1) {
-        vmin = fminf(vmin, __shfl_xor(vmin, off));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-    }
-    if (lane == 0) {
-        s_red[wave] = vmin;
-        s_red[NW + wave] = vmax;
-    }
-    for (int i = tid; i < kTauBuckets; i += kTauThreads) s_b[i] = 0;
-    __syncthreads();
-    vmin = s_red[0];
-    vmax = s_red[NW];
-    for (int w = 1; w < NW; ++w) {
-        vmin = fminf(vmin, s_red[w]);
-        vmax = fmaxf(vmax, s_red[NW + w]);
-    }
-    const float scale = (float)kTauBuckets / (vmax - vmin);
-    if (!(vmax > vmin) || !__builtin_isfinite(scale)) {
-        if (tid == 0) a.tau[t] = vmin;  // all samples equal: admit them all
-        return;
-    }
-    each([&](float f) {
-        const float x = (vmax - f) * scale;
-        atomicAdd(&s_b[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
-    });
-    __syncthreads();
-    uint32_t c[PER], run = 0;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        c[q] = s_b[tid * PER + q];
-        run += c[q];
-    }
-    uint32_t x = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_tot[wave] = x;
-    __syncthreads();
-    uint32_t base = x - run;
-    for (int w = 0; w < wave; ++w) base += s_tot[w];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        if (base < r && r <= base + c[q]) {
-            // One bucket below the lower edge of bucket b, so rounding cannot
-            // leave a sample of buckets 0..b under the threshold.
-            const int b = tid * PER + q;
-            s_tau = vmax - (float)(b + 2) / scale;
-        }
-        base += c[q];
-    }
-    __syncthreads();
-    if (tid == 0) a.tau[t] = s_tau;
-}
 
 // ---------------------------------------------------------------------------
 // Call statistics, accumulated on the device (zeroed by the per-key pass at
@@ -466,10 +338,11 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
     } else {
         t = blockIdx.x;
         const int64_t lo = a.ks[t], hi = a.ke[t];
+        const int64_t len = hi > lo ? hi - lo : 0;
         const uint32_t c = a.cnt[t];
-        if (row_flagged(hi > lo ? hi - lo : 0, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
+        if (row_flagged(len, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
         src = a.cand + (int64_t)t * a.cap;
-        n = min((int64_t)c, (int64_t)a.cap);  // a.cap <= NREG * NT
+        n = len > 0 ? min((int64_t)c, (int64_t)a.cap) : 0;  // a.cap <= NREG * NT
     }
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
     int32_t *oi = a.out_idx + (int64_t)t * a.topk;

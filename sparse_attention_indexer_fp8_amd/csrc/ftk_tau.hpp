@@ -1,0 +1,138 @@
+// Per-row threshold from the row's strided sample (FlashTopK README,
+// "Highlights": the threshold comes from a strided sample of the row's own
+// window).
+//
+// The threshold needs no exact rank -- only the candidate count it admits
+// matters, and triage catches any row it misjudges -- so the sample is
+// bucketed linearly in score (kTauBuckets buckets between the sample's
+// minimum and maximum, highest first) and the threshold is one bucket below
+// the lower edge of the bucket that holds the r-th largest sample: at least r
+// samples reach it, whatever the rounding of the bucket arithmetic.  With
+// r = ceil(2 * topk * n / L) for n samples of an L-key window, about 2 topk
+// keys of the window are expected to reach it.
+#pragma once
+
+#include "ftk_common.hpp"
+
+namespace ftk {
+
+constexpr int kTauBuckets = 2048;
+
+// Rank of the threshold in a sample of n keys of an L-key window.
+__device__ __forceinline__ uint32_t tau_rank(int topk, int64_t n, int64_t len, float rank_scale)
+{
+    const double want = ceil(2.0 * (double)topk * (double)n / (double)len * (double)rank_scale);
+    return (uint32_t)min(max(want, 1.0), (double)n);
+}
+
+// One wave computes the threshold of one row from its n >= 1 sample codes
+// (ord_of of the scores); hist is kTauBuckets words of LDS private to the
+// wave.  Every lane returns the threshold.  Samples are read 2048 at a time
+// (32 per lane, all loads in flight together); a row of at most 2048 samples
+// is read once and kept in registers for both passes.
+__device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t r, uint32_t *hist, int lane)
+{
+    constexpr int PER = kTauBuckets / 64;
+    constexpr int PERL = 32;             // samples per lane per chunk
+    constexpr int CHUNK = 64 * PERL;
+    float v[PERL];
+    auto load_chunk = [&](int base) {
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) {
+            const int i = base + lane + 64 * q;
+            v[q] = i < n ? float_of_ord(samp[i]) : __builtin_nanf("");
+        }
+    };
+    float vmin = __builtin_inff(), vmax = -__builtin_inff();
+    for (int base = 0; base < n; base += CHUNK) {
+        load_chunk(base);
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) {  // fminf / fmaxf ignore the NaN fill
+            vmin = fminf(vmin, v[q]);
+            vmax = fmaxf(vmax, v[q]);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, off));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    }
+    const float scale = (float)kTauBuckets / (vmax - vmin);
+    if (!(vmax > vmin) || !__builtin_isfinite(scale)) return vmin;  // all samples equal: admit them all
+#pragma unroll
+    for (int q = 0; q < PER; ++q) hist[lane + 64 * q] = 0u;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land before any lane adds
+    __builtin_amdgcn_wave_barrier();
+    for (int base = 0; base < n; base += CHUNK) {
+        if (n > CHUNK) load_chunk(base);  // a single chunk is still in registers
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) {
+            if (base + lane + 64 * q < n) {
+                const float x = (vmax - v[q]) * scale;
+                atomicAdd(&hist[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // Lane l owns buckets [PER l, PER l + PER); exclusive prefix over lanes.
+    uint32_t c[PER], run = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        c[q] = hist[lane * PER + q];
+        run += c[q];
+    }
+    uint32_t x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    uint32_t base = x - run;
+    int b = -1;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (base < r && r <= base + c[q]) b = lane * PER + q;
+        base += c[q];
+    }
+    const uint64_t hit = __ballot(b >= 0);
+    b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
+    return vmax - (float)(b + 2) / scale;
+}
+
+struct TauArgs {
+    const int32_t *ks;
+    const int32_t *ke;
+    int64_t num_q;
+    int topk;
+    int cap;
+    const uint32_t *samp;      // [num_q, sample_target] sample score codes
+    int sample_target;
+    int sample_min_stride;
+    float rank_scale;          // multiplies the rank of the threshold
+    float *tau;                // [num_q]
+    uint32_t *cnt;             // [num_q] candidate counters, reset here
+};
+
+// One wave per row: resets the row's candidate counter and sets its
+// threshold (-inf for rows that take their whole window).
+constexpr int kTauWaves = 4;
+
+__global__ __launch_bounds__(64 * kTauWaves) void k_tau(TauArgs a)
+{
+    __shared__ uint32_t s_hist[kTauWaves][kTauBuckets];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kTauWaves + wave;
+    if (t >= a.num_q) return;
+    const int64_t lo = a.ks[t], hi = a.ke[t];
+    const int64_t len = hi > lo ? hi - lo : 0;
+    if (lane == 0) a.cnt[t] = 0;
+    float tv = -__builtin_inff();
+    if (len > a.cap) {
+        const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
+        const int ns = (int)lattice_count(lo, hi, d);
+        tv = wave_tau(a.samp + t * a.sample_target, ns, tau_rank(a.topk, ns, len, a.rank_scale), s_hist[wave], lane);
+    }
+    if (lane == 0) a.tau[t] = tv;
+}
+
+}  // namespace ftk
