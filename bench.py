@@ -38,7 +38,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4,
                     help="named workload 1..6 (4 is the headline; 6 has block-local keys for pruning)")
     ap.add_argument("--integer-twin", action="store_true")
