@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4,
-                    help="named workload 1..6 (4 is the headline; 6 has block-local keys for pruning)")
+                    help="named workload 1..8 (4 is the headline; 6 has block-local keys for pruning; "
+                         "7 and 8 are decode shapes with 1 and 64 query rows)")
     ap.add_argument("--integer-twin", action="store_true")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scan, 2 prune, 3 recover all")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")

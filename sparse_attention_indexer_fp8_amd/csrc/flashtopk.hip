@@ -140,7 +140,7 @@ int resolve(Plan &p, const flashtopk_options *opt)
 // Keys per work item: large chunks amortise a work item's fixed costs
 // (staging the q tile, flushing candidates), but there must be enough items
 // (about four per compute unit) to fill the GPU.
-int chunk_keys(int ntiles, int64_t S)
+int num_cu()
 {
     static int n_cu = 0;
     if (n_cu == 0) {
@@ -151,9 +151,24 @@ int chunk_keys(int ntiles, int64_t S)
         else
             n_cu = 256;
     }
+    return n_cu;
+}
+
+int chunk_keys(int ntiles, int64_t S)
+{
+    const int64_t n_cu = num_cu();
     int chunk = kMaxChunk;
-    while (chunk > kMinChunk && (int64_t)ntiles * ((S + chunk - 1) / chunk) < 4 * (int64_t)n_cu) chunk >>= 1;
+    while (chunk > kMinChunk && (int64_t)ntiles * ((S + chunk - 1) / chunk) < 4 * n_cu) chunk >>= 1;
     return chunk;
+}
+
+// Workgroups per tile for the sample scores: with few tiles (decode-sized
+// calls) each tile's lattice is split so the pass still spreads over the GPU.
+int sample_split(int ntiles)
+{
+    int split = 1;
+    while (split < 16 && (int64_t)ntiles * split * 2 <= num_cu()) split <<= 1;
+    return split;
 }
 
 template <int DT>
@@ -252,6 +267,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.samp = (uint32_t *)w->samp.ptr;
     sa.sample_target = p.sample_target;
     sa.sample_min_stride = p.sample_min_stride;
+    sa.sample_split = sample_split(ntiles);
     if (bounds) {
         sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
         sa.kb = (const uint8_t *)w->kb.ptr;
@@ -281,7 +297,8 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     if (fp8)
         k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T,
                                                                  (uint8_t *)w->qbar.ptr, (float *)w->qscale.ptr);
-    if (!recover_all) launch_score_dt(p.dtype, kModeSample, dim3((unsigned)ntiles), stream, sa);
+    if (!recover_all)
+        launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * sa.sample_split)), stream, sa);
     mark(*w, p, 1, stream);
 
     if (!recover_all) {

@@ -97,6 +97,7 @@ struct ScoreArgs {
     uint32_t *samp;            // [num_q, sample_target] sample score codes
     int sample_target;
     int sample_min_stride;     // power of two, see sample_stride
+    int sample_split;          // workgroups per tile in sample mode
     // dense mode
     const int32_t *rowlist;    // flagged rows
     const unsigned long long *nrows;  // device count of flagged rows
@@ -410,7 +411,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + WB + QB);
 
     // Work item: tile (fast index) x chunk; in sample mode the "chunk" is the
-    // part of the tile's sample lattice (kSampleSplit parts).
+    // part of the tile's sample lattice (sample_split parts).
     const int chunk = blockIdx.x / a.ntiles;
     const int tile = blockIdx.x - chunk * a.ntiles;
 
@@ -476,8 +477,12 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         const int msh = __builtin_ctz((unsigned)dmin);  // power of two
         first_b = ((lo + dmin - 1) >> msh) << msh;
         nlat = (int)lattice_count(lo, hi, dmin);
-        jlo = 0;
-        jhi = (nlat + kStepKeys - 1) / kStepKeys;
+        // With few tiles the lattice is split over a.sample_split workgroups
+        // (the chunk index is the part).
+        const int nsteps = (nlat + kStepKeys - 1) / kStepKeys;
+        const int per = (nsteps + a.sample_split - 1) / a.sample_split;
+        jlo = chunk * per;
+        jhi = min(nsteps, jlo + per);
         if (jhi <= jlo) return;
     } else {
         const int64_t c0 = (int64_t)chunk * a.chunk;

@@ -214,7 +214,7 @@ PACKED_DOCS = (8192, 16384, 24576, 16384)
 
 
 def config(n: int, *, integer_twin: bool = False):
-    """Named workloads 1..6 (integer twins for 3..5 with integer_twin=True)."""
+    """Named workloads 1..8 (integer twins for 3..5 with integer_twin=True)."""
     if integer_twin:
         if n == 3:
             return integer(4096, 131072, 4096, "fp8", 13, name="untrained_int_fp8_4096x131072_k4096")
@@ -240,6 +240,12 @@ def config(n: int, *, integer_twin: bool = False):
         # not one of the pages' workloads: keys with block locality, where
         # score-bound pruning has something to skip
         return blocky(4096, 131072, 2048, "fp8", 6, name="blocky_fp8_4096x131072_k2048")
+    if n == 7:
+        # decode: one query row over the whole 128K-key context
+        return trained_shaped(1, 131072, 2048, "fp8", 7, name="decode_fp8_1x131072_k2048")
+    if n == 8:
+        # decode with a small batch / speculative tokens: 64 query rows
+        return trained_shaped(64, 131072, 2048, "fp8", 8, name="decode_fp8_64x131072_k2048")
     raise ValueError(n)
 
 
