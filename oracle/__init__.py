@@ -62,6 +62,8 @@ def _load():
     lib.oracle_select.restype = i32
     lib.oracle_select.argtypes = [vp, vp, i32, fp, fp, vp, vp, i64, i64, i32, vp, i64,
                                   vp, vp, vp, vp, i32]
+    lib.oracle_topk_rows.restype = i32
+    lib.oracle_topk_rows.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, i32]
     lib.oracle_max_threads.restype = i32
     lib.oracle_max_threads.argtypes = []
     _lib = lib
@@ -146,6 +148,32 @@ def select(q, kv, dtype, kv_scales, weights, ks, ke, topk: int, rows=None,
     if st != 0:
         raise ValueError(f"oracle_select failed with status {st}")
     return idx, val, sc64, allsc
+
+
+def topk_rows(x, topk: int, ends=None, nthreads: int = 0):
+    """Exact top-k of every row of a materialized score matrix.
+
+    ``x``: float32 [rows, cols] or BF16 codes (uint16) [rows, cols]; ``ends``:
+    per-row number of valid leading entries (None: all).  Returns (idx int32
+    [rows, topk], val float32 [rows, topk]) ordered by value desc, index asc,
+    padded with -1 / -inf."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        code = 0
+    elif x.dtype == np.uint16:
+        code = 1
+    else:
+        raise TypeError(f"x must be float32 or uint16 (BF16 codes), got {x.dtype}")
+    rows, cols = x.shape
+    e = None if ends is None else np.ascontiguousarray(ends, dtype=np.int32)
+    idx = np.empty((rows, topk), dtype=np.int32)
+    val = np.empty((rows, topk), dtype=np.float32)
+    st = lib.oracle_topk_rows(_ptr(x), code, rows, cols, cols, _ptr(e), int(topk), _ptr(idx), _ptr(val),
+                              int(nthreads))
+    if st != 0:
+        raise ValueError(f"oracle_topk_rows failed with status {st}")
+    return idx, val
 
 
 def max_threads() -> int:

@@ -259,6 +259,71 @@ int oracle_select(const void *q, const void *kv, int dtype, const float *kv_scal
     return status;
 }
 
+/* Exact top-k over materialized score rows (DeepSelect README, "Usage" and
+ * "Variable-length rows": each row keeps its topk largest values among its
+ * first end[r] entries; rows shorter than topk are padded with fill values,
+ * here index -1 / value -inf).  Order: value desc, index asc, with +0 and -0
+ * equal -- the same order as the indexer selection above.
+ *   x        [rows, stride] float32 (dtype 0) or BF16 codes (dtype 1)
+ *   ends     [rows] int32 or NULL (every row has cols entries); each end is
+ *            clamped to [0, cols]
+ *   out_idx / out_val  [rows, topk]: positions in the row and their values
+ * Returns 0, -1 on a NaN entry, -2 on allocation failure, -3 bad argument. */
+int oracle_topk_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t stride,
+                     const int32_t *ends, int topk, int32_t *out_idx, float *out_val, int nthreads)
+{
+    if (topk < 1 || rows < 0 || cols < 0 || stride < cols) return -3;
+    if (dtype != 0 && dtype != 1) return -3;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : status)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t n = cols;
+        if (ends) {
+            n = ends[r];
+            if (n < 0) n = 0;
+            if (n > cols) n = cols;
+        }
+        scored_key *keys = (scored_key *)malloc(sizeof(scored_key) * (size_t)(n > 0 ? n : 1));
+        if (!keys) {
+            status = -2;
+            continue;
+        }
+        int st = 0;
+        for (int64_t j = 0; j < n; ++j) {
+            double v;
+            if (dtype == 0)
+                v = (double)((const float *)x)[r * stride + j];
+            else
+                v = oracle_decode_bf16(((const uint16_t *)x)[r * stride + j]);
+            if (isnan(v)) st = -1;
+            keys[j].score = v;
+            keys[j].index = j;
+        }
+        qsort(keys, (size_t)n, sizeof(scored_key), by_score_then_index);
+        for (int j = 0; j < topk; ++j) {
+            if (j < n) {
+                float v = (float)keys[j].score; /* exact: the entries are float32 or BF16 */
+                if (v == 0.0f) v = 0.0f;
+                out_idx[r * topk + j] = (int32_t)keys[j].index;
+                out_val[r * topk + j] = v;
+            } else {
+                out_idx[r * topk + j] = -1;
+                out_val[r * topk + j] = -INFINITY;
+            }
+        }
+        free(keys);
+        if (st < status) status = st;
+    }
+    return status;
+}
+
 /* Number of threads an OpenMP parallel region of this library would use. */
 int oracle_max_threads(void)
 {
