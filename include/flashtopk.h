@@ -137,6 +137,37 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales,
                         int32_t *out_idx, float *out_val, void *stream,
                         const flashtopk_options *opt);
 
+/* Score-row dtypes of flashtopk_topk_rows (DeepSelect README, "Supported
+ * Cases": BF16 rows for the indexer scenario, float32 for sampling). */
+#define FLASHTOPK_SCORES_F32 0
+#define FLASHTOPK_SCORES_BF16 1
+
+/* Exact top-k of every row of an already materialized score matrix
+ * (DeepSelect README, "Usage" and "Variable-length rows").
+ *
+ *   x         [rows, row_stride] float32 or BF16 (score_dtype), device memory;
+ *             the first `cols` entries of each row are its scores.  x must be
+ *             16-byte aligned; when rows > 1, row_stride >= cols and
+ *             row_stride * element size is a multiple of 16 bytes (the
+ *             README's stride requirement; pad rows otherwise).
+ *   ends      [rows] int32, or NULL: row r keeps only its first ends[r]
+ *             entries (exclusive bound, clamped to [0, cols]); NULL = cols.
+ *   out_idx   [rows, topk] int32, out_val [rows, topk] float32 or NULL.
+ *   nan_flag  one int32 in device memory, or NULL: the call sets it to 1 when
+ *             an entry inside some row's bound is NaN (the caller clears it;
+ *             the README's kernel aborts instead).  Rows holding NaN get an
+ *             unspecified selection, but every write stays in bounds.
+ *
+ * Row r lists min(topk, its length) column indices by value descending,
+ * smaller index first among equal values, padded with -1 / -inf; +0 and -0
+ * compare equal and values come back as float32 (BF16 widened exactly), +0
+ * for a zero.  0 <= rows, cols < 2^31, 1 <= topk <= 4096.  rows == 0 is a
+ * no-op.  Enqueued on `stream` without blocking the host and with no
+ * workspace.  Ownership, synchronisation and errors as for flashtopk_select. */
+int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                        const int32_t *ends, int topk, int32_t *out_idx, float *out_val, int32_t *nan_flag,
+                        void *stream);
+
 /* Pre-allocate the workspace of (current device, stream) for calls up to the
  * given sizes, so later calls allocate nothing (README, "Usage": the
  * Selector's plan() owns the workspace and prepares up front). */

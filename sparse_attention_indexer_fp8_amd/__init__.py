@@ -22,6 +22,8 @@ FLASHTOPK_BF16 = 1
 HEADS = 32
 DIM = 128
 MAX_TOPK = 4096
+FLASHTOPK_SCORES_F32 = 0
+FLASHTOPK_SCORES_BF16 = 1
 
 PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER = 0, 1, 2, 3
 
@@ -75,7 +77,7 @@ class Info(ctypes.Structure):
 
 
 # Every symbol include/flashtopk.h declares.
-EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_reserve", "flashtopk_get_last_info",
+EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_topk_rows", "flashtopk_reserve", "flashtopk_get_last_info",
            "flashtopk_release", "flashtopk_status_string", "flashtopk_version")
 
 _lib = None
@@ -95,6 +97,8 @@ def load_library():
     lib.flashtopk_select.restype = I
     lib.flashtopk_select_ex.argtypes = sel + [ctypes.POINTER(Options)]
     lib.flashtopk_select_ex.restype = I
+    lib.flashtopk_topk_rows.argtypes = [P, I, I64, I64, I64, P, I, P, P, P, P]
+    lib.flashtopk_topk_rows.restype = I
     lib.flashtopk_reserve.argtypes = [I64, I64, I, I, P]
     lib.flashtopk_reserve.restype = I
     lib.flashtopk_get_last_info.argtypes = [P, ctypes.POINTER(Info)]
@@ -179,6 +183,47 @@ def flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_va
 
 def flashtopk_select(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=None, stream=None) -> None:
     flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val, stream, None)
+
+
+def flashtopk_topk_rows(x, topk, out_idx, out_val=None, ends=None, nan_flag=None, stream=None) -> None:
+    """Exact top-k of each row of x [rows, cols] (float32 or bfloat16; last
+    dimension contiguous, row stride a multiple of 16 bytes).  Fills out_idx
+    [rows, topk] int32 and out_val [rows, topk] float32 if given; ends [rows]
+    int32 bounds each row; nan_flag (one int32) is set to 1 on a NaN."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    if x.dtype == torch.float32:
+        code = FLASHTOPK_SCORES_F32
+    elif x.dtype == torch.bfloat16:
+        code = FLASHTOPK_SCORES_BF16
+    else:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    rows, cols = x.shape
+    if cols > 1 and x.stride(1) != 1:
+        raise ValueError("x's last dimension must be contiguous")
+    _check_dev("ends", ends, (torch.int32,), (rows,))
+    _check_dev("out_idx", out_idx, (torch.int32,), (rows, topk))
+    _check_dev("out_val", out_val, (torch.float32,), (rows, topk))
+    _check_dev("nan_flag", nan_flag, (torch.int32,), (1,))
+    st = lib.flashtopk_topk_rows(_ptr(x), code, rows, cols, x.stride(0), _ptr(ends), int(topk), _ptr(out_idx),
+                                 _ptr(out_val), _ptr(nan_flag), ctypes.c_void_p(_stream_handle(stream)))
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_topk_rows")
+
+
+def topk_rows(x, topk, ends=None, return_values=True, stream=None):
+    """indices [rows, topk] int32 (and values [rows, topk] float32) of the
+    exact top-k of each row of x; see flashtopk_topk_rows."""
+    torch = _torch()
+    rows = x.shape[0]
+    idx = torch.empty((rows, topk), dtype=torch.int32, device=x.device)
+    val = torch.empty((rows, topk), dtype=torch.float32, device=x.device) if return_values else None
+    flashtopk_topk_rows(x, topk, idx, val, ends, None, stream)
+    return (idx, val) if return_values else idx
 
 
 def flashtopk_reserve(max_q, max_kv, max_topk, dtype=FLASHTOPK_FP8_E4M3, stream=None) -> None:

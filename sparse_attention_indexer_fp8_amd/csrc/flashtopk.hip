@@ -24,6 +24,7 @@
 
 #include "flashtopk.h"
 #include "ftk_bound.hpp"
+#include "ftk_rows.hpp"
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
 #include "ftk_tau.hpp"
@@ -470,6 +471,34 @@ int flashtopk_select(const void *q, const void *kv, const float *kv_scales, cons
 {
     return flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, num_q, num_kv, dtype, topk, out_idx, out_val,
                                stream, nullptr);
+}
+
+int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                        const int32_t *ends, int topk, int32_t *out_idx, float *out_val, int32_t *nan_flag,
+                        void *stream)
+{
+    if (score_dtype != FLASHTOPK_SCORES_F32 && score_dtype != FLASHTOPK_SCORES_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
+    if (rows < 0 || rows >= (int64_t(1) << 31) || cols < 0 || cols >= (int64_t(1) << 31))
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (topk < 1 || topk > FLASHTOPK_MAX_TOPK) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return FLASHTOPK_OK;
+    const int64_t esize = score_dtype == FLASHTOPK_SCORES_F32 ? 4 : 2;
+    if (!out_idx || (!x && cols > 0)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (rows > 1 && row_stride < cols) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (x && !aligned16(x)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (rows > 1 && (row_stride * esize) % 16 != 0) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    RowsArgs a{x, rows, cols, row_stride, ends, topk, out_idx, out_val, nan_flag};
+    const hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)rows);
+    const bool small = topk <= RowsSmall::maxk;
+    if (score_dtype == FLASHTOPK_SCORES_F32) {
+        if (small) hipLaunchKernelGGL((k_topk_rows<float, RowsSmall>), grid, dim3(RowsSmall::nt), 0, s, a);
+        else hipLaunchKernelGGL((k_topk_rows<float, RowsLarge>), grid, dim3(RowsLarge::nt), 0, s, a);
+    } else {
+        if (small) hipLaunchKernelGGL((k_topk_rows<uint16_t, RowsSmall>), grid, dim3(RowsSmall::nt), 0, s, a);
+        else hipLaunchKernelGGL((k_topk_rows<uint16_t, RowsLarge>), grid, dim3(RowsLarge::nt), 0, s, a);
+    }
+    return hip_status(hipGetLastError());
 }
 
 int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream)

@@ -1,0 +1,429 @@
+// Exact top-k over materialized score rows (DeepSelect README, "Usage" and
+// "Variable-length rows": each row keeps its topk largest values among its
+// first end[r] entries; shorter rows are padded).  Same order and padding as
+// the indexer selection: value descending, smaller position first on ties
+// (+0 and -0 equal), then index -1 / value -inf.
+//
+// One workgroup per row, one pass over the row in the common case:
+//   1. a sample of the row (64 runs of 128 contiguous bytes spread over it)
+//      sets a threshold tau that about `target` entries of the row reach
+//      (the same sampled-threshold idea as the indexer's filter);
+//   2. one streaming pass gathers every entry >= tau into LDS and counts
+//      them exactly;
+//   3. when topk <= count <= capacity, the gathered set holds the whole top
+//      k -- every entry tied with the k-th value included -- and the
+//      candidate selection finishes the row exactly.
+// Otherwise (a sample that misjudged the row, values crowding at the top)
+// the row is redone by a two-pass digit histogram: pass 1 counts the top 12
+// bits of each value's order code (4096 digits, an eighth of a binade each),
+// pass 2 gathers every entry of the k-th value's digit or above, and the
+// selection runs on that set, or, if even that does not fit, on the
+// streamed row (radix select).
+#pragma once
+
+#include "ftk_common.hpp"
+#include "ftk_frag.hpp"
+#include "ftk_select.hpp"
+
+namespace ftk {
+
+// Launch shapes: NT threads, REGS gathered entries per thread (the LDS
+// capacity is NT * REGS), and the selection's buckets and largest topk.
+// Small rows outputs fit four workgroups per compute unit, so one
+// workgroup's latency-bound phases (sample, selection) overlap the others'
+// streaming.
+template <int NT_, int REGS_, int NBKT_, int MAXK_> struct RowsShape {
+    static constexpr int nt = NT_, regs = REGS_, cap = NT_ * REGS_, nbkt = NBKT_, maxk = MAXK_;
+};
+using RowsSmall = RowsShape<512, 8, 2048, 1024>;        // topk <= 1024, capacity 4096
+using RowsLarge = RowsShape<1024, 8, 4096, kMaxTopk>;   // topk <= 4096, capacity 8192
+constexpr int kRowsDigitShift = 20;                       // 12-bit digits
+constexpr int kRowsBuckets = 1 << (32 - kRowsDigitShift);  // 4096
+constexpr int kRowsTauBuckets = 2048;
+constexpr int kRowsSampleRuns = 64;                       // 128-byte runs sampled per row
+// 16-byte loads per thread and group; with the next group in flight while
+// one is scanned, 64 bytes per thread are outstanding.
+constexpr int kRowsUnroll = 2;
+
+struct RowsArgs {
+    const void *x;          // [rows, stride] float32 or BF16
+    int64_t rows, cols, stride;
+    const int32_t *ends;    // [rows] or null
+    int topk;
+    int32_t *out_idx;       // [rows, topk]
+    float *out_val;         // [rows, topk] or null
+    int32_t *nan_flag;      // set to 1 when a row holds a NaN; or null
+};
+
+template <typename T> __device__ __forceinline__ float entry_value(T v);
+template <> __device__ __forceinline__ float entry_value<float>(float v) { return v; }
+template <> __device__ __forceinline__ float entry_value<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+template <typename SH>
+struct RowsLds {
+    // The histograms, the gathered entries and the selection's state are
+    // live one after another.
+    union {
+        uint32_t hist[kRowsBuckets];
+        uint64_t cand[SH::cap];
+        SelectLds<SH::nt, SH::nbkt, SH::maxk> sel;
+    };
+    float redf[2 * (SH::nt / 64)];
+    uint32_t redu[SH::nt / 64];
+    uint32_t misc[4];
+};
+
+// Block-wide exclusive prefix over BPT counts per thread, taken in thread
+// order; returns this thread's start.  Ends with the block synchronised.
+template <int NT, int BPT>
+__device__ __forceinline__ uint32_t block_prefix(const uint32_t (&c)[BPT], uint32_t *redu)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t run = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) run += c[q];
+    uint32_t x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) redu[wave] = x;
+    __syncthreads();
+    uint32_t base = x - run;
+    for (int w = 0; w < wave; ++w) base += redu[w];
+    __syncthreads();
+    return base;
+}
+
+// Buffer resource over `entries` entries from p, rounded up to whole 16-byte
+// chunks (the aligned chunk holding a valid entry is always readable) and
+// clamped to the 32-bit size field; nothing if entries <= 0.  Loads past it
+// read zeros, so every load is unconditional and no branch makes the
+// compiler wait for it early.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const T *p, int64_t entries)
+{
+    const uint64_t bytes = entries > 0 ? ((uint64_t)entries * sizeof(T) + 15) & ~(uint64_t)15 : 0;
+    return make_rsrc(p, (bytes >> 32) ? 0xFFFFFFF0u : (uint32_t)bytes);
+}
+
+// One group of U 16-byte chunks per thread: chunk u of thread t covers
+// entries g0 + (u NT + t) V ... + V - 1.  Chunks past the row read as zeros.
+template <typename T, int NT, int U>
+__device__ __forceinline__ void load_group(v4i (&raw)[U], const T *row, int64_t n, int64_t g0)
+{
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row + g0, n - g0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = buf_load16(rs, (uint32_t)((u * NT + threadIdx.x) * 16), 0u);
+}
+
+// Threshold from the row's sample: linear buckets between the finite
+// sample extremes, largest first; tau is one bucket below the lower edge of
+// the bucket holding the r-th largest sample, so at least r samples reach
+// it whatever the rounding.  r = ceil(target * samples / n).
+template <typename T, typename SH>
+__device__ float rows_sample_tau(RowsLds<SH> &L, const T *row, int64_t n, uint32_t target)
+{
+    constexpr int NT = SH::nt, V = 16 / sizeof(T), NW = NT / 64, CPR = 128 / 16;  // chunks per run
+    constexpr int BPT = kRowsTauBuckets / NT;
+    static_assert(kRowsSampleRuns * CPR <= NT, "one sampled chunk per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t nlines = (n * (int64_t)sizeof(T) + 127) / 128;
+    float v[V];
+    bool ok[V];
+    {
+        const int run = tid / CPR, sub = tid % CPR;
+        const int64_t base = ((int64_t)run * nlines / kRowsSampleRuns * CPR + sub) * V;
+        const bool mine = run < kRowsSampleRuns && base < n;
+        // (a row past 4 GiB wraps the offset to another in-row chunk: the
+        // sample only steers speed)
+        const v4i raw = buf_load16(row_rsrc(row, n), mine ? (uint32_t)(base * (int64_t)sizeof(T)) : 0xFFFFFFF0u, 0u);
+        const T *e = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            v[j] = entry_value<T>(e[j]);
+            ok[j] = mine && base + j < n;
+        }
+    }
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    uint32_t ns = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        ns += ok[j] ? 1u : 0u;
+        if (ok[j] && __builtin_isfinite(v[j])) {
+            lo = fminf(lo, v[j]);
+            hi = fmaxf(hi, v[j]);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off));
+        hi = fmaxf(hi, __shfl_xor(hi, off));
+        ns += __shfl_xor(ns, off);
+    }
+    if (lane == 0) {
+        L.redf[wave] = lo;
+        L.redf[NW + wave] = hi;
+        L.redu[wave] = ns;
+    }
+    for (int i = tid; i < kRowsTauBuckets; i += NT) L.hist[i] = 0u;
+    __syncthreads();
+    lo = L.redf[0];
+    hi = L.redf[NW];
+    ns = L.redu[0];
+    for (int w = 1; w < NW; ++w) {
+        lo = fminf(lo, L.redf[w]);
+        hi = fmaxf(hi, L.redf[NW + w]);
+        ns += L.redu[w];
+    }
+    const float scale = (float)kRowsTauBuckets / (hi - lo);
+    const bool spread = hi > lo && __builtin_isfinite(scale) && scale > 0.0f;
+    __syncthreads();  // the reductions are read before the prefix reuses redu
+    if (!spread) return hi > lo ? -__builtin_inff() : lo;  // degenerate sample: let the count decide
+    const uint32_t r = (uint32_t)min(max(ceil((double)target * (double)ns / (double)n), 1.0), (double)ns);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        if (ok[j]) {
+            const float x = (hi - v[j]) * scale;  // +inf -> -inf, -inf and NaN -> last bucket
+            const uint32_t b = v[j] == __builtin_inff() ? 0u
+                               : (x < (float)(kRowsTauBuckets - 1) ? (uint32_t)fmaxf(x, 0.0f) : (uint32_t)(kRowsTauBuckets - 1));
+            atomicAdd(&L.hist[b], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t c[BPT];
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) c[q] = L.hist[tid * BPT + q];
+    uint32_t base = block_prefix<NT, BPT>(c, L.redu);
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        if (base < r && r <= base + c[q]) L.misc[0] = tid * BPT + q;
+        base += c[q];
+    }
+    __syncthreads();
+    const uint32_t b = L.misc[0];
+    __syncthreads();
+    return hi - (float)(b + 2) / scale;
+}
+
+// Appends the entries >= tau of one loaded group (row positions g0 ...) to
+// L.cand, the first SH::cap of the row.  Each thread marks its keepers in a
+// bit mask (entry e of the group at bit U V - 1 - e), reserves their slots
+// with one LDS atomic and stores them in order; keepers are rare, so the
+// store loop walks the mask's set bits and picks each keeper's word out of
+// the group with a select chain.  TAIL: the group may pass the row's end.
+template <typename T, typename SH, int U, bool TAIL>
+__device__ __forceinline__ void scan_group(RowsLds<SH> &L, const v4i (&raw)[U], int64_t g0, int64_t n, float tau,
+                                           bool &nan)
+{
+    constexpr int NT = SH::nt, V = 16 / sizeof(T), PER = sizeof(uint32_t) / sizeof(T);  // entries per word
+    constexpr int E = U * V;
+    static_assert(E <= 32, "one mask bit per entry");
+    const int tid = threadIdx.x;
+    const uint32_t rem = TAIL ? (uint32_t)min(n - g0, (int64_t)NT * E) : 0u;
+    uint32_t mask = 0;
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const T *e = reinterpret_cast<const T *>(&raw[u]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const float f = entry_value<T>(e[j]);
+            const bool valid = !TAIL || (uint32_t)((u * NT + tid) * V + j) < rem;
+            bad |= valid && f != f;
+            mask = (mask << 1) | ((valid && f >= tau) ? 1u : 0u);
+        }
+    }
+    nan |= bad;
+    if (mask == 0) return;
+    uint32_t pos = atomicAdd(&L.misc[3], (uint32_t)__builtin_popcount(mask));
+    do {
+        const int b = E - 1 - (31 - __builtin_clz(mask));  // the lowest-numbered keeper left
+        mask &= ~(1u << (E - 1 - b));
+        const int q = b / PER;  // word of the group
+        uint32_t w = (uint32_t)raw[0][0];
+#pragma unroll
+        for (int x = 1; x < U * 4; ++x)
+            if (q == x) w = (uint32_t)raw[x / 4][x % 4];
+        float f;
+        if (PER == 2) f = __uint_as_float((b & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        else f = __uint_as_float(w);
+        const uint32_t li = (uint32_t)(((b / V) * NT + tid) * V + (b % V));
+        if (pos < (uint32_t)SH::cap) L.cand[pos] = raw_cand(f, (int32_t)(g0 + li));
+        ++pos;
+    } while (mask);
+}
+
+template <typename T, typename SH, int U>
+__device__ __forceinline__ void scan_any(RowsLds<SH> &L, const v4i (&raw)[U], int64_t g0, int64_t n, float tau,
+                                         bool &nan)
+{
+    if (n - g0 >= (int64_t)SH::nt * U * (16 / sizeof(T))) scan_group<T, SH, U, false>(L, raw, g0, n, tau, nan);
+    else scan_group<T, SH, U, true>(L, raw, g0, n, tau, nan);
+}
+
+// Gathers every valid entry >= tau (as raw candidates) into L.cand, the
+// first SH::cap of them, and returns how many there are.  `a` holds the
+// row's first group, already loaded.  Two register sets alternate, so one
+// group is in flight while the other is scanned.
+template <typename T, typename SH, int U>
+__device__ uint32_t rows_gather(RowsLds<SH> &L, v4i (&a)[U], const T *row, int64_t n, float tau, bool &nan)
+{
+    constexpr int64_t G = (int64_t)SH::nt * U * (16 / sizeof(T));
+    if (threadIdx.x == 0) L.misc[3] = 0u;
+    __syncthreads();
+    v4i b[U];
+    for (int64_t g0 = 0; g0 < n; g0 += 2 * G) {
+        load_group<T, SH::nt, U>(b, row, n, g0 + G);
+        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the scan
+        scan_any<T, SH, U>(L, a, g0, n, tau, nan);
+        if (g0 + G >= n) break;  // block-uniform
+        load_group<T, SH::nt, U>(a, row, n, g0 + 2 * G);
+        __builtin_amdgcn_sched_barrier(0);
+        scan_any<T, SH, U>(L, b, g0 + G, n, tau, nan);
+    }
+    __syncthreads();
+    const uint32_t cnt = L.misc[3];
+    __syncthreads();
+    return cnt;
+}
+
+// Visits a row's first n entries as (value, position, valid), every thread
+// of the block the same number of times: 16-byte loads of V entries.  The
+// row starts 16-byte aligned and its stride is a multiple of 16 bytes, so a
+// load never leaves the aligned 16 bytes holding a valid entry.
+template <typename T, int NT, typename F>
+__device__ __forceinline__ void visit_row(const T *row, int64_t n, F f)
+{
+    constexpr int V = 16 / sizeof(T);
+    for (int64_t b0 = 0; b0 < n; b0 += (int64_t)NT * V) {
+        const int64_t base = b0 + (int64_t)threadIdx.x * V;
+        v4i raw = {0, 0, 0, 0};
+        if (base < n) raw = *reinterpret_cast<const v4i *>(row + base);
+        const T *e = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+        for (int j = 0; j < V; ++j) f(entry_value<T>(e[j]), base + j, base + j < n);
+    }
+}
+
+// A row of materialized scores as an element visitor of the candidate
+// selection (streamed: every visit reads the row again).
+template <typename T>
+struct RowStream {
+    static constexpr bool REG = false;
+    static constexpr int kRegPer = 1;
+    const T *row;
+    int64_t n;
+    template <typename F>
+    __device__ __forceinline__ void each(F f) const
+    {
+        const int64_t rounds = (n + blockDim.x - 1) / blockDim.x;
+        for (int64_t q = 0; q < rounds; ++q) {
+            const int64_t i = threadIdx.x + q * blockDim.x;
+            f(i < n ? raw_cand(entry_value<T>(row[i]), (int32_t)i) : 0ull, i < n);
+        }
+    }
+};
+
+// Fallback: boundary digit of the k-th value by a full histogram, then the
+// entries of that digit or above.  Returns how many were gathered into
+// L.cand, or a count above SH::cap when they do not fit.
+template <typename T, typename SH>
+__device__ uint32_t rows_digit_gather(RowsLds<SH> &L, const T *row, int64_t n, uint32_t k, bool &nan)
+{
+    constexpr int NT = SH::nt, BPT = kRowsBuckets / NT;
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < kRowsBuckets; i += NT) L.hist[i] = 0u;
+    __syncthreads();
+    visit_row<T, NT>(row, n, [&](float v, int64_t, bool valid) {
+        nan |= valid && v != v;
+        const uint32_t d = ord_of(v) >> kRowsDigitShift;
+        // Lanes sharing the first active lane's digit add once (rows crowd
+        // into few digits).
+        const uint64_t act = __ballot(valid);
+        if (act) {
+            const int leader = __builtin_ctzll(act);
+            const uint32_t ld = __shfl(d, leader);
+            const bool same = valid && d == ld;
+            const uint64_t sm = __ballot(same);
+            if (lane == leader) atomicAdd(&L.hist[ld], (uint32_t)__builtin_popcountll(sm));
+            if (valid && !same) atomicAdd(&L.hist[d], 1u);
+        }
+    });
+    __syncthreads();
+    // Thread t owns digits 4095 - BPT t ... 4096 - BPT (t + 1), highest first.
+    uint32_t c[BPT];
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) c[q] = L.hist[kRowsBuckets - 1 - (BPT * tid + q)];
+    uint32_t above = block_prefix<NT, BPT>(c, L.redu);
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        if (above < k && k <= above + c[q]) {
+            L.misc[0] = (uint32_t)(kRowsBuckets - 1 - (BPT * tid + q));
+            L.misc[1] = above + c[q];
+        }
+        above += c[q];
+    }
+    if (tid == 0) L.misc[3] = 0u;
+    __syncthreads();
+    const uint32_t bd = L.misc[0];
+    const uint32_t m = L.misc[1];
+    if (m > (uint32_t)SH::cap) return m;
+    visit_row<T, NT>(row, n, [&](float v, int64_t i, bool valid) {
+        const bool keep = valid && (ord_of(v) >> kRowsDigitShift) >= bd;
+        const uint64_t bal = __ballot(keep);
+        if (bal) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&L.misc[3], (uint32_t)__builtin_popcountll(bal));
+            base = __shfl(base, 0);
+            if (keep) L.cand[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = raw_cand(v, (int32_t)i);
+        }
+    });
+    __syncthreads();
+    return m;
+}
+
+// Eight waves per SIMD: both shapes keep 32 waves on a compute unit, so
+// registers are capped at 64 per lane.
+template <typename T, typename SH>
+__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows(RowsArgs a)
+{
+    constexpr int NT = SH::nt, U = kRowsUnroll;
+    __shared__ RowsLds<SH> L;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
+    int64_t n = a.cols;
+    if (a.ends) n = min(max((int64_t)a.ends[r], (int64_t)0), a.cols);
+    const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
+    int32_t *oi = a.out_idx + r * a.topk;
+    float *ov = a.out_val ? a.out_val + r * a.topk : nullptr;
+    if (k == 0) {
+        for (int j = tid; j < a.topk; j += NT) {
+            oi[j] = -1;
+            if (ov) ov[j] = -__builtin_inff();
+        }
+        return;
+    }
+    bool nan = false;
+    v4i first[U];
+    load_group<T, NT, U>(first, row, n, 0);  // in flight while the sample is read
+    // About twice topk entries should reach the threshold, but no more than
+    // halfway from topk to the LDS capacity.
+    const uint32_t target = min(2u * k, k + ((uint32_t)SH::cap - k) / 2u);
+    const float tau = n > SH::cap ? rows_sample_tau<T, SH>(L, row, n, target) : -__builtin_inff();
+    uint32_t m = rows_gather<T, SH, U>(L, first, row, n, tau, nan);
+    if (m < k || m > (uint32_t)SH::cap) m = rows_digit_gather<T, SH>(L, row, n, k, nan);
+    if (a.nan_flag && __any(nan) && (tid & 63) == 0) atomicOr(a.nan_flag, 1);
+    if (m <= (uint32_t)SH::cap) {
+        RowElems<SH::regs> el;
+        el.load(L.cand, m);
+        __syncthreads();  // the gathered entries are in registers; the LDS becomes the selection's
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m, k, a.topk, oi, ov);
+    } else {
+        RowStream<T> el{row, n};
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov);
+    }
+}
+
+}  // namespace ftk

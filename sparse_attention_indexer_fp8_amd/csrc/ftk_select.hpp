@@ -315,16 +315,18 @@ using SelLarge = SelShape<8, 1024, 4096, kMaxTopk>;  // cap <= 8192
 using SelHuge = SelShape<16, 1024, 4096, kMaxTopk>;  // cap <= 16384
 using SelDense = SelShape<0, 512, 4096, kMaxTopk>;   // recovered rows
 
+template <int NT, int NBKT, int MAXK, typename E>
+__device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
+                            int32_t *oi, float *ov);
+
 // Candidate mode: rows that triage flags (same predicate) are left to dense
 // recovery; every other row's candidates hold its whole top k.
 template <typename SH>
 __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
 {
     constexpr int NREG = SH::nreg, NT = SH::nt, NBKT = SH::nbkt, MAXK = SH::maxk;
-    constexpr int NW = NT / 64, BPT = NBKT / NT;
     constexpr bool DENSE = NREG == 0;
     __shared__ SelectLds<NT, NBKT, MAXK> S;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int t;
     const uint64_t *src;
     int64_t n;
@@ -349,7 +351,23 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
     float *ov = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
     RowElems<NREG> el;
     el.load(src, n);
+    select_core<NT, NBKT, MAXK>(S, el, n, k, a.topk, oi, ov);
+}
 
+// Exact top k of one row's elements (raw candidates, see raw_cand) held by
+// the visitor `el`, written to oi / ov (ov may be null) in key order and
+// padded to topk.  All threads of the block call it; S is the block's LDS.
+// Element visitors with registers (E::REG) rank keys inside their buckets in
+// parallel; streamed visitors sort each bucket serially and so only take the
+// bucketed path for buckets of at most 48 keys.
+template <int NT, int NBKT, int MAXK, typename E>
+__device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
+                            int32_t *oi, float *ov)
+{
+    constexpr int NW = NT / 64, BPT = NBKT / NT;
+    constexpr bool DENSE = !E::REG;
+    constexpr int NREG = E::kRegPer;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     bool fast = false;
     float mx = 0.0f, scale = 0.0f;
     uint32_t kb = 0;
@@ -437,7 +455,7 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
             });
             __syncthreads();
             // Bucket b now spans [bucket[b-1], bucket[b]).
-            if (!DENSE) {
+            if constexpr (!DENSE) {
                 // Place of each key: the bucket start plus the number of
                 // larger keys in the bucket (keys are distinct), computed
                 // for all keys before any key moves.
@@ -515,7 +533,7 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
             }
         }
     }
-    for (int j = tid; j < a.topk; j += NT) {
+    for (int j = tid; j < topk; j += NT) {
         int32_t idx = -1;
         float v = -__builtin_inff();
         if ((uint32_t)j < k) {

@@ -52,6 +52,8 @@ def test_header_constants_match_binding():
     assert int(consts["FLASHTOPK_BF16"]) == ftk.FLASHTOPK_BF16
     assert int(consts["FLASHTOPK_MAX_TOPK"]) == ftk.MAX_TOPK
     assert int(consts["FLASHTOPK_PATH_RECOVER"]) == ftk.PATH_RECOVER
+    assert int(consts["FLASHTOPK_SCORES_F32"]) == ftk.FLASHTOPK_SCORES_F32
+    assert int(consts["FLASHTOPK_SCORES_BF16"]) == ftk.FLASHTOPK_SCORES_BF16
 
 
 def test_options_and_info_layout_match_header():
@@ -89,3 +91,30 @@ def test_misaligned_operands_rejected(lib):
     p = ctypes.c_void_p(odd)
     ok = ctypes.c_void_p(base + (-base) % 16)
     assert _call(lib, q=p, kv=ok, weights=ok, ks=ok, ke=ok, out_idx=ok, num_q=1, num_kv=1) == 1
+
+
+def _rows(lib, **kw):
+    args = dict(x=None, dtype=1, rows=0, cols=0, stride=0, ends=None, topk=1, out_idx=None, out_val=None,
+                nan_flag=None, stream=None)
+    args.update(kw)
+    return lib.flashtopk_topk_rows(*[args[k] for k in ("x", "dtype", "rows", "cols", "stride", "ends", "topk",
+                                                       "out_idx", "out_val", "nan_flag", "stream")])
+
+
+def test_topk_rows_argument_errors_without_device(lib):
+    buf = (ctypes.c_uint8 * 64)()
+    base = ctypes.addressof(buf)
+    ok = ctypes.c_void_p(base + (-base) % 16)
+    odd = ctypes.c_void_p(base + (-base) % 16 + 2)
+    assert _rows(lib, dtype=2) == 2
+    assert _rows(lib, topk=0) == 1
+    assert _rows(lib, topk=4097) == 1
+    assert _rows(lib, rows=-1) == 1
+    assert _rows(lib, cols=1 << 31) == 1
+    assert _rows(lib, rows=0, topk=5) == 0                                   # no-op
+    assert _rows(lib, rows=2, cols=8, stride=8, x=ok) == 1                  # null out_idx
+    assert _rows(lib, rows=2, cols=8, stride=8, out_idx=ok) == 1            # null x
+    assert _rows(lib, rows=2, cols=8, stride=8, x=odd, out_idx=ok) == 1     # misaligned x
+    assert _rows(lib, rows=2, cols=8, stride=4, x=ok, out_idx=ok) == 1      # stride < cols
+    assert _rows(lib, rows=2, cols=9, stride=9, x=ok, out_idx=ok) == 1      # 18-byte BF16 stride
+    assert _rows(lib, rows=2, cols=6, stride=6, x=ok, out_idx=ok, dtype=0) == 1  # 24-byte f32 stride

@@ -263,3 +263,84 @@ def digest(wl) -> str:
 
 def window_sum(wl) -> int:
     return int(np.maximum(wl["ke"].astype(np.int64) - wl["ks"].astype(np.int64), 0).sum())
+
+
+# ---------------------------------------------------------------------------
+# Materialized score rows for the standalone row top-k (DeepSelect README,
+# "Supported Cases": BF16 rows of any batch size and vocabulary for the
+# indexer scenario, float32 rows of about 128K entries for sampling, topk up
+# to 4096 and mostly 512; "Variable-length rows": a per-row end).
+
+ROW_KINDS = ("normal", "ties", "skewed", "special")
+
+
+def _row_values(rng, rows, cols, kind):
+    if kind == "normal":
+        return rng.standard_normal((rows, cols), dtype=np.float32)
+    if kind == "ties":
+        # few distinct values: whole binades of equal entries
+        return rng.integers(-4, 5, size=(rows, cols)).astype(np.float32)
+    if kind == "skewed":
+        # the shape of indexer scores: weighted sums of rectified products,
+        # with many exact zeros and a long right tail
+        z = rng.standard_normal((4, rows, cols), dtype=np.float32)
+        w = np.array([1.0, 0.5, 0.25, -0.125], np.float32)[:, None, None]
+        return (w * np.maximum(z, 0.0)).sum(axis=0).astype(np.float32)
+    if kind == "special":
+        x = rng.standard_normal((rows, cols), dtype=np.float32)
+        u = rng.random((rows, cols))
+        x[u < 0.01] = 0.0
+        x[(u >= 0.01) & (u < 0.02)] = -0.0
+        x[(u >= 0.02) & (u < 0.0202)] = np.inf
+        x[(u >= 0.0202) & (u < 0.0204)] = -np.inf
+        return x
+    raise ValueError(kind)
+
+
+def score_rows(rows, cols, dtype, seed, *, kind="normal", topk=512, ends=None, stride=None, name=None):
+    """Score rows on the host.  dtype "f32" | "bf16"; ends None, an int32
+    array, or "ragged" (uniform in [0, cols + 16], clamped by the callee) or
+    "causal" (row r of the last `rows` positions of a sequence of `cols`
+    tokens keeps cols - rows + r + 1 entries).  stride >= cols pads each row
+    (padding filled with a large value that must never be selected).
+    Returns dict(x, dtype, ends, topk, cols, name); x is float32 or BF16
+    codes (uint16) [rows, stride]."""
+    rng = np.random.default_rng(seed)
+    v = _row_values(rng, rows, cols, kind)
+    if isinstance(ends, str):
+        if ends == "ragged":
+            ends = rng.integers(0, cols + 17, size=rows).astype(np.int32)
+        elif ends == "causal":
+            ends = (cols - rows + 1 + np.arange(rows)).clip(0, cols).astype(np.int32)
+        else:
+            raise ValueError(ends)
+    stride = cols if stride is None else stride
+    if stride > cols:
+        v = np.concatenate([v, np.full((rows, stride - cols), 1e30, np.float32)], axis=1)
+    x = v if dtype == "f32" else _quantize(v, "bf16")
+    return dict(x=x, dtype=dtype, ends=ends, topk=topk, cols=cols,
+                name=name or f"rows_{kind}_{dtype}_{rows}x{cols}_k{topk}")
+
+
+def score_rows_device(rows, cols, dtype, seed, *, kind="normal", dev="cuda:0"):
+    """Large score rows drawn on the device with torch's seeded generator
+    (the host generator is too slow at gigabyte sizes): "normal" or "skewed"
+    values, returned as a float32 / bfloat16 device tensor [rows, cols]."""
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = torch.empty((rows, cols), dtype=tdt, device=dev)
+    step = max(1, (1 << 26) // max(cols, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        if kind == "normal":
+            out[r0:r1] = torch.randn((r1 - r0, cols), generator=g, device=dev).to(tdt)
+        elif kind == "skewed":
+            z = torch.randn((4, r1 - r0, cols), generator=g, device=dev)
+            w = torch.tensor([1.0, 0.5, 0.25, -0.125], device=dev)[:, None, None]
+            out[r0:r1] = (w * z.clamp_min(0.0)).sum(0).to(tdt)
+        else:
+            raise ValueError(kind)
+    return out
