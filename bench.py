@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--rows", default="", metavar="NAME",
+                    help="time the standalone row top-k on a named score-row workload instead "
+                         "(indexer_bf16_4096x131072_k512, indexer_bf16_64x131072_k512, "
+                         "sampling_f32_1024x129280_k512, chunk_bf16_causal_4096x131072_k2048)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device (3 times), the reference for HBM counters")
     return ap.parse_args()
@@ -135,6 +139,108 @@ def cpu_baseline(wl, target_s):
                       f"{dt:.1f} s wall, scaled by pairs; {cpu}"}
 
 
+def cpu_baseline_rows(h, ends, topk, target_s):
+    """Times the oracle's row top-k on evenly spaced rows; returns ms per call
+    scaled by entries."""
+    import oracle
+
+    rows, cols = h.shape
+    lens = np.full(rows, cols, np.int64) if ends is None else np.clip(ends.astype(np.int64), 0, cols)
+    threads = oracle.max_threads()
+    probe = np.linspace(0, rows - 1, num=min(rows, max(2, threads)), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.topk_rows(np.ascontiguousarray(h[probe]), topk, None if ends is None else ends[probe])
+    per_entry = (time.perf_counter() - t0) / max(1.0, float(lens[probe].sum()))
+    n = int(min(rows, max(len(probe), target_s / max(per_entry, 1e-12) / max(1.0, lens.mean()))))
+    sel = np.linspace(0, rows - 1, num=n, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.topk_rows(np.ascontiguousarray(h[sel]), topk, None if ends is None else ends[sel])
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 * float(lens.sum()) / max(1.0, float(lens[sel].sum()))
+    return {"value": ms, "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {rows} rows (evenly spaced), {dt:.1f} s wall, scaled by entries"}
+
+
+def main_rows(args):
+    """Standalone row top-k: one step = one flashtopk_topk_rows call over the
+    whole score matrix (DeepSelect README, "Performance": effective memory
+    bandwidth, since top-k does no floating-point math)."""
+    import torch
+
+    import workloads
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    rows, cols, dt, topk, kind, ends_kind = workloads.ROW_CONFIGS[args.rows]
+    dev = torch.device("cuda:0")
+    x = workloads.score_rows_device(rows, cols, dt, 17, kind=kind)
+    ends = None
+    if ends_kind == "causal":
+        ends = (cols - rows + 1 + np.arange(rows)).clip(0, cols).astype(np.int32)
+    ends_d = None if ends is None else torch.from_numpy(ends).to(dev)
+    esize = 4 if dt == "f32" else 2
+    lens = np.full(rows, cols, np.int64) if ends is None else ends.astype(np.int64)
+    in_bytes = float(lens.sum()) * esize
+    out_bytes = float(rows) * topk * 8
+    idx = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    val = torch.empty((rows, topk), dtype=torch.float32, device=dev)
+    print(f"bench: rows {args.rows}", file=sys.stderr, flush=True)
+
+    def step():
+        ftk.flashtopk_topk_rows(x, topk, idx, val, ends_d)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = start.elapsed_time(end) / args.steps
+    gbs = in_bytes / (ms * 1e-3) / 1e9
+    ach = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
+    # torch.topk on the same rows for context (the pages' comparison point)
+    ref_ms = None
+    if ends is None:
+        torch.topk(x, topk, dim=1)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(max(1, args.steps // 4)):
+            torch.topk(x, topk, dim=1)
+        end.record()
+        torch.cuda.synchronize()
+        ref_ms = start.elapsed_time(end) / max(1, args.steps // 4)
+    out = {
+        "metric": "effective memory bandwidth of the standalone row top-k (GB/s of score rows read)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if dt == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.rows, "rows": rows, "cols": cols, "topk": topk, "values": kind,
+                   "ends": ends_kind or "none"},
+        "wall_ms_per_step": round(wall_ms, 4),
+        "torch_topk_ms": None if ref_ms is None else round(ref_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_rows_tau + k_topk_rows (one call)", "achieved": round(ach, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": None,
+                     "bytes_per_launch": in_bytes + out_bytes},
+    }
+    if not args.no_cpu:
+        print("bench: cpu oracle leg", file=sys.stderr, flush=True)
+        h = x.float().cpu().numpy() if dt == "f32" else x.view(torch.int16).cpu().numpy().view(np.uint16)
+        out["cpu_baseline"] = cpu_baseline_rows(h, ends, topk, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -144,6 +250,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.rows:
+        main_rows(args)
         return
 
     import torch

@@ -439,6 +439,30 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Row top-k launch.  When the rows take more than one wave of resident
+// workgroups, the thresholds are computed up front by k_rows_tau, so that no
+// row workgroup waits on its sample.
+template <typename T, typename SH>
+void launch_rows(const RowsArgs &a, hipStream_t s)
+{
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_topk_rows<T, SH, true>, SH::nt, 0) != hipSuccess ||
+            b < 1)
+            b = 1;
+        per_cu = b;
+    }
+    const dim3 grid((unsigned)a.rows);
+    if (a.rows > (int64_t)per_cu * num_cu()) {
+        const dim3 tgrid((unsigned)((a.rows + kRowsTauWaves - 1) / kRowsTauWaves));
+        hipLaunchKernelGGL((k_rows_tau<T, SH>), tgrid, dim3(64 * kRowsTauWaves), 0, s, a);
+        hipLaunchKernelGGL((k_topk_rows<T, SH, true>), grid, dim3(SH::nt), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_topk_rows<T, SH, false>), grid, dim3(SH::nt), 0, s, a);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,14 +513,13 @@ int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t co
     if (rows > 1 && (row_stride * esize) % 16 != 0) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     RowsArgs a{x, rows, cols, row_stride, ends, topk, out_idx, out_val, nan_flag};
     const hipStream_t s = (hipStream_t)stream;
-    const dim3 grid((unsigned)rows);
     const bool small = topk <= RowsSmall::maxk;
     if (score_dtype == FLASHTOPK_SCORES_F32) {
-        if (small) hipLaunchKernelGGL((k_topk_rows<float, RowsSmall>), grid, dim3(RowsSmall::nt), 0, s, a);
-        else hipLaunchKernelGGL((k_topk_rows<float, RowsLarge>), grid, dim3(RowsLarge::nt), 0, s, a);
+        if (small) launch_rows<float, RowsSmall>(a, s);
+        else launch_rows<float, RowsLarge>(a, s);
     } else {
-        if (small) hipLaunchKernelGGL((k_topk_rows<uint16_t, RowsSmall>), grid, dim3(RowsSmall::nt), 0, s, a);
-        else hipLaunchKernelGGL((k_topk_rows<uint16_t, RowsLarge>), grid, dim3(RowsLarge::nt), 0, s, a);
+        if (small) launch_rows<uint16_t, RowsSmall>(a, s);
+        else launch_rows<uint16_t, RowsLarge>(a, s);
     }
     return hip_status(hipGetLastError());
 }

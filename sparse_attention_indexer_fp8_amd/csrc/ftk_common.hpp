@@ -108,6 +108,48 @@ __device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi
     return (hi - 1 - first) / d + 1;
 }
 
+// ---------------------------------------------------------------------------
+// Wave-wide scans and reductions over the 64 lanes through DPP lane moves
+// (every lane must be active).  Rows of 16 lanes scan with row shifts of 1,
+// 2, 4, 8 (lanes shifted in from outside the row read 0); row 15's and row
+// 31's last lanes are then broadcast into the rows above them.
+
+template <int CTRL, int ROW_MASK = 0xf, bool ZERO_FILL = true>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, ZERO_FILL);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x, Op op)
+{
+    x = op(x, dpp_move<0x111>(x));        // row_shr:1
+    x = op(x, dpp_move<0x112>(x));        // row_shr:2
+    x = op(x, dpp_move<0x114>(x));        // row_shr:4
+    x = op(x, dpp_move<0x118>(x));        // row_shr:8
+    x = op(x, dpp_move<0x142, 0xa>(x));   // row_bcast:15 into rows 1 and 3
+    x = op(x, dpp_move<0x143, 0xc>(x));   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Inclusive prefix sum: lane l gets x_0 + ... + x_l.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x)
+{
+    return wave_scan_dpp(x, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Sum and maximum over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_add(x), 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane(
+        (int)wave_scan_dpp(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; }), 63);
+}
+
 // Counters of the score-bound pruning, kept in the call's statistics (zeroed
 // by the per-key pass, added to by the scan): (row, key) pairs skipped, and
 // work items that evaluated the bound.

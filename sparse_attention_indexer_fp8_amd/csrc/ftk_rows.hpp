@@ -6,8 +6,8 @@
 //
 // One workgroup per row, one pass over the row in the common case:
 //   1. a sample of the row (64 runs of 128 contiguous bytes spread over it)
-//      sets a threshold tau that about `target` entries of the row reach
-//      (the same sampled-threshold idea as the indexer's filter);
+//      sets a threshold tau that about three times topk entries of the row
+//      reach (the same sampled-threshold idea as the indexer's filter);
 //   2. one streaming pass gathers every entry >= tau into LDS and counts
 //      them exactly;
 //   3. when topk <= count <= capacity, the gathered set holds the whole top
@@ -68,7 +68,7 @@ struct RowsLds {
         uint64_t cand[SH::cap];
         SelectLds<SH::nt, SH::nbkt, SH::maxk> sel;
     };
-    float redf[2 * (SH::nt / 64)];
+    uint32_t redu2[2 * (SH::nt / 64)];
     uint32_t redu[SH::nt / 64];
     uint32_t misc[4];
 };
@@ -82,12 +82,7 @@ __device__ __forceinline__ uint32_t block_prefix(const uint32_t (&c)[BPT], uint3
     uint32_t run = 0;
 #pragma unroll
     for (int q = 0; q < BPT; ++q) run += c[q];
-    uint32_t x = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_add(run);
     if (lane == 63) redu[wave] = x;
     __syncthreads();
     uint32_t base = x - run;
@@ -114,72 +109,98 @@ template <typename T, int NT, int U>
 __device__ __forceinline__ void load_group(v4i (&raw)[U], const T *row, int64_t n, int64_t g0)
 {
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(row + g0, n - g0);
+    const uint32_t voff = threadIdx.x * 16u;  // one lane offset; the chunk's goes in the scalar offset
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = buf_load16(rs, (uint32_t)((u * NT + threadIdx.x) * 16), 0u);
+    for (int u = 0; u < U; ++u) raw[u] = buf_load16(rs, voff, (uint32_t)(u * NT * 16));
 }
 
 // Threshold from the row's sample: linear buckets between the finite
 // sample extremes, largest first; tau is one bucket below the lower edge of
 // the bucket holding the r-th largest sample, so at least r samples reach
 // it whatever the rounding.  r = ceil(target * samples / n).
-template <typename T, typename SH>
-__device__ float rows_sample_tau(RowsLds<SH> &L, const T *row, int64_t n, uint32_t target)
+// About three times topk entries should reach the threshold, but no more
+// than halfway from topk to the LDS capacity: a sample rank of a few dozen
+// then misses both bounds (fewer than topk, more than the capacity) only in
+// rows far from independent values, and those take the slower exact path.
+__device__ __forceinline__ uint32_t rows_target(uint32_t k, uint32_t cap)
 {
-    constexpr int NT = SH::nt, V = 16 / sizeof(T), NW = NT / 64, CPR = 128 / 16;  // chunks per run
-    constexpr int BPT = kRowsTauBuckets / NT;
-    static_assert(kRowsSampleRuns * CPR <= NT, "one sampled chunk per thread");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    return min(3u * k, k + (cap - k) / 2u);
+}
+
+// The sample: 64 runs of 128 bytes, run j starting at line floor(j lines / 64)
+// of the row; chunk t (0 ... 511) is 16-byte chunk t % 8 of run t / 8.
+// Returns the chunk's first entry, or -1 past the row.
+template <typename T>
+__device__ __forceinline__ int64_t sample_base(int64_t n, int t)
+{
+    constexpr int V = 16 / sizeof(T), CPR = 128 / 16;  // chunks per run
+    const int run = t / CPR, sub = t % CPR;
     const int64_t nlines = (n * (int64_t)sizeof(T) + 127) / 128;
+    const int64_t base = ((int64_t)run * nlines / kRowsSampleRuns * CPR + sub) * V;
+    return run < kRowsSampleRuns && base < n ? base : -1;
+}
+
+template <typename T>
+__device__ __forceinline__ v4i sample_load(const T *row, int64_t n, int t)
+{
+    const int64_t base = sample_base<T>(n, t);
+    // (a row past 4 GiB wraps the offset to another in-row chunk: the sample
+    // only steers speed)
+    return buf_load16(row_rsrc(row, n), base >= 0 ? (uint32_t)(base * (int64_t)sizeof(T)) : 0xFFFFFFF0u, 0u);
+}
+
+template <typename T, typename SH>
+__device__ float rows_sample_tau(RowsLds<SH> &L, const v4i &raw, int64_t n, uint32_t target)
+{
+    constexpr int NT = SH::nt, V = 16 / sizeof(T), NW = NT / 64;
+    constexpr int BPT = kRowsTauBuckets / NT;
+    static_assert(kRowsSampleRuns * 8 <= NT, "one sampled chunk per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float v[V];
     bool ok[V];
     {
-        const int run = tid / CPR, sub = tid % CPR;
-        const int64_t base = ((int64_t)run * nlines / kRowsSampleRuns * CPR + sub) * V;
-        const bool mine = run < kRowsSampleRuns && base < n;
-        // (a row past 4 GiB wraps the offset to another in-row chunk: the
-        // sample only steers speed)
-        const v4i raw = buf_load16(row_rsrc(row, n), mine ? (uint32_t)(base * (int64_t)sizeof(T)) : 0xFFFFFFF0u, 0u);
+        const int64_t base = sample_base<T>(n, tid);
         const T *e = reinterpret_cast<const T *>(&raw);
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             v[j] = entry_value<T>(e[j]);
-            ok[j] = mine && base + j < n;
+            ok[j] = base >= 0 && base + j < n;
         }
     }
-    float lo = __builtin_inff(), hi = -__builtin_inff();
-    uint32_t ns = 0;
+    // finite sample extremes as order codes (maxima of the code and of its
+    // complement), and the sample count
+    uint32_t hic = 0, nloc = 0, ns = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         ns += ok[j] ? 1u : 0u;
         if (ok[j] && __builtin_isfinite(v[j])) {
-            lo = fminf(lo, v[j]);
-            hi = fmaxf(hi, v[j]);
+            const uint32_t c = ord_of(v[j]);
+            hic = max(hic, c);
+            nloc = max(nloc, ~c);
         }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, off));
-        hi = fmaxf(hi, __shfl_xor(hi, off));
-        ns += __shfl_xor(ns, off);
-    }
+    hic = wave_max(hic);
+    nloc = wave_max(nloc);
+    ns = wave_sum(ns);
     if (lane == 0) {
-        L.redf[wave] = lo;
-        L.redf[NW + wave] = hi;
+        L.redu2[wave] = hic;
+        L.redu2[NW + wave] = nloc;
         L.redu[wave] = ns;
     }
     for (int i = tid; i < kRowsTauBuckets; i += NT) L.hist[i] = 0u;
     __syncthreads();
-    lo = L.redf[0];
-    hi = L.redf[NW];
-    ns = L.redu[0];
-    for (int w = 1; w < NW; ++w) {
-        lo = fminf(lo, L.redf[w]);
-        hi = fmaxf(hi, L.redf[NW + w]);
+    ns = 0;
+    for (int w = 0; w < NW; ++w) {
+        hic = max(hic, L.redu2[w]);
+        nloc = max(nloc, L.redu2[NW + w]);
         ns += L.redu[w];
     }
+    const bool any = hic != 0u;  // a finite sample has a nonzero code
+    const float lo = float_of_ord(~nloc), hi = float_of_ord(hic);
     const float scale = (float)kRowsTauBuckets / (hi - lo);
-    const bool spread = hi > lo && __builtin_isfinite(scale) && scale > 0.0f;
+    const bool spread = any && hi > lo && __builtin_isfinite(scale) && scale > 0.0f;
     __syncthreads();  // the reductions are read before the prefix reuses redu
-    if (!spread) return hi > lo ? -__builtin_inff() : lo;  // degenerate sample: let the count decide
+    if (!spread) return any && !(hi > lo) ? lo : -__builtin_inff();  // degenerate sample: let the count decide
     const uint32_t r = (uint32_t)min(max(ceil((double)target * (double)ns / (double)n), 1.0), (double)ns);
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -289,20 +310,32 @@ __device__ uint32_t rows_gather(RowsLds<SH> &L, v4i (&a)[U], const T *row, int64
 }
 
 // Visits a row's first n entries as (value, position, valid), every thread
-// of the block the same number of times: 16-byte loads of V entries.  The
-// row starts 16-byte aligned and its stride is a multiple of 16 bytes, so a
-// load never leaves the aligned 16 bytes holding a valid entry.
+// of the block the same number of times, with the loads of the next group in
+// flight while a group is visited (as in rows_gather).
 template <typename T, int NT, typename F>
 __device__ __forceinline__ void visit_row(const T *row, int64_t n, F f)
 {
-    constexpr int V = 16 / sizeof(T);
-    for (int64_t b0 = 0; b0 < n; b0 += (int64_t)NT * V) {
-        const int64_t base = b0 + (int64_t)threadIdx.x * V;
-        v4i raw = {0, 0, 0, 0};
-        if (base < n) raw = *reinterpret_cast<const v4i *>(row + base);
-        const T *e = reinterpret_cast<const T *>(&raw);
+    constexpr int V = 16 / sizeof(T), U = kRowsUnroll;
+    constexpr int64_t G = (int64_t)NT * U * V;
+    auto visit = [&](const v4i (&raw)[U], int64_t g0) {
 #pragma unroll
-        for (int j = 0; j < V; ++j) f(entry_value<T>(e[j]), base + j, base + j < n);
+        for (int u = 0; u < U; ++u) {
+            const int64_t base = g0 + ((int64_t)u * NT + threadIdx.x) * V;
+            const T *e = reinterpret_cast<const T *>(&raw[u]);
+#pragma unroll
+            for (int j = 0; j < V; ++j) f(entry_value<T>(e[j]), base + j, base + j < n);
+        }
+    };
+    v4i a[U], b[U];
+    load_group<T, NT, U>(a, row, n, 0);
+    for (int64_t g0 = 0; g0 < n; g0 += 2 * G) {
+        load_group<T, NT, U>(b, row, n, g0 + G);
+        __builtin_amdgcn_sched_barrier(0);
+        visit(a, g0);
+        if (g0 + G >= n) break;  // block-uniform
+        load_group<T, NT, U>(a, row, n, g0 + 2 * G);
+        __builtin_amdgcn_sched_barrier(0);
+        visit(b, g0 + G);
     }
 }
 
@@ -383,9 +416,106 @@ __device__ uint32_t rows_digit_gather(RowsLds<SH> &L, const T *row, int64_t n, u
     return m;
 }
 
-// Eight waves per SIMD: both shapes keep 32 waves on a compute unit, so
-// registers are capped at 64 per lane.
+// Thresholds of many rows ahead of the row kernel, one wave per row: the
+// same sample and bucket rule as rows_sample_tau, computed by a wave with the
+// whole sample in registers (8 chunks per lane) and a private LDS histogram.
+// The threshold's bits go to the row's first output index slot.  Rows of at
+// most SH::cap entries take every entry and need none.
+constexpr int kRowsTauWaves = 4;
+
 template <typename T, typename SH>
+__global__ __launch_bounds__(64 * kRowsTauWaves) void k_rows_tau(RowsArgs a)
+{
+    constexpr int V = 16 / sizeof(T), C = kRowsSampleRuns * 8 / 64, PER = kRowsTauBuckets / 64;
+    __shared__ uint32_t s_hist[kRowsTauWaves][kRowsTauBuckets];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * kRowsTauWaves + wave;
+    if (r >= a.rows) return;  // wave-uniform; no block barrier follows
+    const int64_t n = a.ends ? min(max((int64_t)a.ends[r], (int64_t)0), a.cols) : a.cols;
+    const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
+    if (n <= SH::cap || k == 0) return;
+    const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
+    uint32_t *hist = s_hist[wave];
+    v4i raw[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) raw[c] = sample_load(row, n, lane + 64 * c);
+    uint32_t hic = 0, nloc = 0, ns = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int64_t base = sample_base<T>(n, lane + 64 * c);
+        const T *e = reinterpret_cast<const T *>(&raw[c]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const float v = entry_value<T>(e[j]);
+            const bool ok = base >= 0 && base + j < n;
+            ns += ok ? 1u : 0u;
+            if (ok && __builtin_isfinite(v)) {
+                const uint32_t cd = ord_of(v);
+                hic = max(hic, cd);
+                nloc = max(nloc, ~cd);
+            }
+        }
+    }
+    hic = wave_max(hic);
+    nloc = wave_max(nloc);
+    ns = wave_sum(ns);
+    const bool any = hic != 0u;
+    const float lo = float_of_ord(~nloc), hi = float_of_ord(hic);
+    const float scale = (float)kRowsTauBuckets / (hi - lo);
+    float tau;
+    if (!(any && hi > lo && __builtin_isfinite(scale) && scale > 0.0f)) {
+        tau = any && !(hi > lo) ? lo : -__builtin_inff();
+    } else {
+        const uint32_t rk = (uint32_t)min(max(ceil((double)rows_target(k, SH::cap) * (double)ns / (double)n), 1.0),
+                                          (double)ns);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) hist[lane + 64 * q] = 0u;
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land before any lane adds
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t base = sample_base<T>(n, lane + 64 * c);
+            const T *e = reinterpret_cast<const T *>(&raw[c]);
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                const float v = entry_value<T>(e[j]);
+                if (base >= 0 && base + j < n) {
+                    const float x = (hi - v) * scale;
+                    const uint32_t b = v == __builtin_inff() ? 0u
+                                       : (x < (float)(kRowsTauBuckets - 1) ? (uint32_t)fmaxf(x, 0.0f)
+                                                                           : (uint32_t)(kRowsTauBuckets - 1));
+                    atomicAdd(&hist[b], 1u);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        // Lane l owns buckets [PER l, PER l + PER), largest scores first.
+        uint32_t cnt[PER], run = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            cnt[q] = hist[lane * PER + q];
+            run += cnt[q];
+        }
+        uint32_t basec = wave_incl_add(run) - run;
+        int b = -1;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (basec < rk && rk <= basec + cnt[q]) b = lane * PER + q;
+            basec += cnt[q];
+        }
+        const uint64_t hit = __ballot(b >= 0);
+        b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
+        tau = hi - (float)(b + 2) / scale;
+    }
+    if (lane == 0) a.out_idx[r * a.topk] = __float_as_int(tau);
+}
+
+// One workgroup per row.  With PRE_TAU the row's threshold was computed by
+// k_rows_tau and parked in the row's first output index slot (the outputs
+// are written last); otherwise the workgroup reads the sample itself, with
+// its first group of the row already in flight.
+template <typename T, typename SH, bool PRE_TAU>
 __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows(RowsArgs a)
 {
     constexpr int NT = SH::nt, U = kRowsUnroll;
@@ -393,8 +523,7 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
     const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
-    int64_t n = a.cols;
-    if (a.ends) n = min(max((int64_t)a.ends[r], (int64_t)0), a.cols);
+    const int64_t n = a.ends ? min(max((int64_t)a.ends[r], (int64_t)0), a.cols) : a.cols;
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
     int32_t *oi = a.out_idx + r * a.topk;
     float *ov = a.out_val ? a.out_val + r * a.topk : nullptr;
@@ -406,12 +535,14 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
         return;
     }
     bool nan = false;
+    float tau = -__builtin_inff();
+    if (PRE_TAU && n > SH::cap) tau = __int_as_float(__builtin_amdgcn_readfirstlane(oi[0]));
     v4i first[U];
     load_group<T, NT, U>(first, row, n, 0);  // in flight while the sample is read
-    // About twice topk entries should reach the threshold, but no more than
-    // halfway from topk to the LDS capacity.
-    const uint32_t target = min(2u * k, k + ((uint32_t)SH::cap - k) / 2u);
-    const float tau = n > SH::cap ? rows_sample_tau<T, SH>(L, row, n, target) : -__builtin_inff();
+    if (!PRE_TAU && n > SH::cap) {
+        const v4i smp = sample_load(row, n, tid);
+        tau = rows_sample_tau<T, SH>(L, smp, n, rows_target(k, SH::cap));
+    }
     uint32_t m = rows_gather<T, SH, U>(L, first, row, n, tau, nan);
     if (m < k || m > (uint32_t)SH::cap) m = rows_digit_gather<T, SH>(L, row, n, k, nan);
     if (a.nan_flag && __any(nan) && (tid & 63) == 0) atomicOr(a.nan_flag, 1);

@@ -295,7 +295,7 @@ struct SelectLds {
         uint32_t bucket[NBKT];
     };
     uint64_t sel[MAXK + kSegMax];
-    float redf[2 * NW];
+    uint32_t redu2[2 * NW];
     uint32_t redu[NW];
     uint32_t misc[4];
 };
@@ -372,31 +372,29 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
     float mx = 0.0f, scale = 0.0f;
     uint32_t kb = 0;
     if (k > 0) {
-        // Score range of the candidates.
-        float lo = __builtin_inff(), hi = -__builtin_inff();
+        // Score range of the candidates, as order codes (maxima of the code
+        // and of its complement).
+        uint32_t hic = 0, nloc = 0;
         el.each([&](uint64_t r, bool v) {
             if (v) {
-                const float f = raw_score(r);
-                lo = fminf(lo, f);
-                hi = fmaxf(hi, f);
+                const uint32_t c = ord_of(raw_score(r));
+                hic = max(hic, c);
+                nloc = max(nloc, ~c);
             }
         });
-        for (int off = 32; off > 0; off >>= 1) {
-            lo = fminf(lo, __shfl_xor(lo, off));
-            hi = fmaxf(hi, __shfl_xor(hi, off));
-        }
+        hic = wave_max(hic);
+        nloc = wave_max(nloc);
         if (lane == 0) {
-            S.redf[wave] = lo;
-            S.redf[NW + wave] = hi;
+            S.redu2[wave] = hic;
+            S.redu2[NW + wave] = nloc;
         }
         for (int i = tid; i < NBKT; i += NT) S.bucket[i] = 0;
         __syncthreads();
-        lo = S.redf[0];
-        hi = S.redf[NW];
-        for (int w = 1; w < NW; ++w) {
-            lo = fminf(lo, S.redf[w]);
-            hi = fmaxf(hi, S.redf[NW + w]);
+        for (int w = 0; w < NW; ++w) {
+            hic = max(hic, S.redu2[w]);
+            nloc = max(nloc, S.redu2[NW + w]);
         }
+        const float lo = float_of_ord(~nloc), hi = float_of_ord(hic);
         mx = hi;
         scale = (float)NBKT / (hi - lo);
         fast = hi > lo && __builtin_isfinite(scale) && __builtin_isfinite(hi - lo);
@@ -418,12 +416,7 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
             cntv[q] = S.bucket[tid * BPT + q];
             run += cntv[q];
         }
-        uint32_t x = run;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
+        const uint32_t x = wave_incl_add(run);
         if (lane == 63) S.redu[wave] = x;
         __syncthreads();
         uint32_t base = x - run;
@@ -441,7 +434,7 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
 #pragma unroll
         for (int q = 0; q < BPT; ++q)
             if ((uint32_t)(tid * BPT + q) <= kb) seg = max(seg, cntv[q]);
-        for (int off = 32; off > 0; off >>= 1) seg = max(seg, (uint32_t)__shfl_xor(seg, off));
+        seg = wave_max(seg);
         if (lane == 0) S.redu[wave] = seg;
         __syncthreads();
         for (int w = 0; w < NW; ++w) seg = max(seg, S.redu[w]);
@@ -467,8 +460,14 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
                         if (b <= kb) {
                             const uint64_t e = key_of_raw(r);
                             const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
-                            uint32_t rank = 0;
-                            for (uint32_t j = s0; j < s1; ++j) rank += S.sel[j] > e ? 1u : 0u;
+                            // four independent LDS reads per step: buckets of
+                            // tied scores (BF16 inputs) hold dozens of keys
+                            uint32_t rank = 0, j = s0;
+                            for (; j + 4 <= s1; j += 4) {
+                                const uint64_t k0 = S.sel[j], k1 = S.sel[j + 1], k2 = S.sel[j + 2], k3 = S.sel[j + 3];
+                                rank += (k0 > e ? 1u : 0u) + (k1 > e ? 1u : 0u) + (k2 > e ? 1u : 0u) + (k3 > e ? 1u : 0u);
+                            }
+                            for (; j < s1; ++j) rank += S.sel[j] > e ? 1u : 0u;
                             pl = s0 + rank;
                         }
                     }

@@ -344,3 +344,17 @@ def score_rows_device(rows, cols, dtype, seed, *, kind="normal", dev="cuda:0"):
         else:
             raise ValueError(kind)
     return out
+
+
+# Named score-row workloads of the standalone row top-k: (rows, cols, dtype,
+# topk, value kind, ends).  The first three follow the DeepSelect README's
+# "Supported Cases" / "Performance" shapes (BF16 indexer rows with topk 512 at
+# a large and a small batch; float32 sampling rows of vocab 129280, topk 512);
+# the last is the headline indexer chunk's score matrix (4096 causal rows of
+# a 128K context, topk 2048) for comparison with the fused path.
+ROW_CONFIGS = {
+    "indexer_bf16_4096x131072_k512": (4096, 131072, "bf16", 512, "normal", None),
+    "indexer_bf16_64x131072_k512": (64, 131072, "bf16", 512, "normal", None),
+    "sampling_f32_1024x129280_k512": (1024, 129280, "f32", 512, "normal", None),
+    "chunk_bf16_causal_4096x131072_k2048": (4096, 131072, "bf16", 2048, "skewed", "causal"),
+}
