@@ -5,7 +5,9 @@ checked against the oracle on sampled rows (MI355X only).
   topk 2048 (heavy-tailed rows);
 * 64K x 64K BF16 packed sequence of four documents, topk 512, rows shorter
   than topk padded;
-* the integer-valued twins of all three, checked bit-exact.
+* decode shapes: one and 64 query rows over the whole 128K context, topk 2048
+  (the launch configuration splits each tile's sample over many workgroups);
+* the integer-valued twins of all five, checked bit-exact.
 Sampled rows: the first and last rows, random rows, and (packed) rows at
 every document start and in the short-window region.
 """
@@ -21,6 +23,8 @@ pytestmark = pytest.mark.gpu
 
 def _rows(wl, extra=()):
     T = wl["q"].shape[0]
+    if T <= 64:
+        return np.arange(0, T, 4 if T > 16 else 1, dtype=np.int64)
     rows = sample_rows(T, n_mid=20, edge=6, seed=T)
     return np.unique(np.concatenate([rows, np.asarray(extra, np.int64)])).astype(np.int64)
 
@@ -40,6 +44,10 @@ CASES = [
     ("untrained_int_fp8_k4096", 3, True, "exact"),
     ("trained_int_fp8_k2048", 4, True, "exact"),
     ("packed_int_bf16_k512", 5, True, "exact"),
+    ("decode_fp8_1x131072", 7, False, "tolerance"),
+    ("decode_fp8_64x131072", 8, False, "tolerance"),
+    ("decode_int_fp8_1x131072", 7, True, "exact"),
+    ("decode_int_fp8_64x131072", 8, True, "exact"),
 ]
 
 

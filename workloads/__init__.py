@@ -214,7 +214,7 @@ PACKED_DOCS = (8192, 16384, 24576, 16384)
 
 
 def config(n: int, *, integer_twin: bool = False):
-    """Named workloads 1..8 (integer twins for 3..5 with integer_twin=True)."""
+    """Named workloads 1..8 (integer twins for 3..5, 7, 8 with integer_twin=True)."""
     if integer_twin:
         if n == 3:
             return integer(4096, 131072, 4096, "fp8", 13, name="untrained_int_fp8_4096x131072_k4096")
@@ -223,6 +223,10 @@ def config(n: int, *, integer_twin: bool = False):
         if n == 5:
             return integer(65536, 65536, 512, "bf16", 15, windows="packed", docs=PACKED_DOCS,
                            name="packed_int_bf16_65536_k512")
+        if n == 7:
+            return integer(1, 131072, 2048, "fp8", 17, name="decode_int_fp8_1x131072_k2048")
+        if n == 8:
+            return integer(64, 131072, 2048, "fp8", 18, name="decode_int_fp8_64x131072_k2048")
         raise ValueError(n)
     if n == 1:
         return gaussian(64, 2048, 64, "bf16", 1, weight_scale=32 ** -0.5, scales="ones",
