@@ -23,7 +23,7 @@
  *   kv_scales  [num_kv] float32  per-key scale sigma >= 0, or NULL for all ones
  *   weights    [num_q, 32] float32 per-head weights (any sign)
  *   ks, ke     [num_q] int32     window bounds, 0 <= ks[t] <= ke[t] <= num_kv
- *   out_idx    [num_q, topk] int32
+ *   out_idx    [num_q, topk] int32, or int64 with FLASHTOPK_OUT_INT64
  *   out_val    [num_q, topk] float32 (the score of out_idx), or NULL to skip
  *
  * Ownership: the caller allocates and owns every operand and output.  The
@@ -65,7 +65,8 @@ extern "C" {
 
 /* Status codes. */
 #define FLASHTOPK_OK 0
-#define FLASHTOPK_ERR_INVALID_ARGUMENT 1 /* null required pointer, bad size, topk outside [1, 4096] */
+#define FLASHTOPK_ERR_INVALID_ARGUMENT 1 /* null required pointer, bad size, topk outside [1, 4096],
+                                            unknown output flag */
 #define FLASHTOPK_ERR_UNSUPPORTED 2      /* dtype other than FP8 E4M3 / BF16 */
 #define FLASHTOPK_ERR_OUT_OF_MEMORY 3    /* workspace allocation failed */
 #define FLASHTOPK_ERR_HIP 4              /* a HIP runtime or launch error */
@@ -76,6 +77,15 @@ extern "C" {
 #define FLASHTOPK_PATH_SCAN 1     /* sampled threshold + full scan, no pruning */
 #define FLASHTOPK_PATH_PRUNE 2    /* sampled threshold + score-bound key pruning */
 #define FLASHTOPK_PATH_RECOVER 3  /* dense rescoring + exact select for every row */
+
+/* Output options (DeepSelect README, "Usage": sorted_index and indices_type;
+ * "Recommendations": index order costs time).  Bit flags.
+ *   FLASHTOPK_OUT_INDEX_ORDER  the same topk keys, listed by ascending index
+ *                              (values follow their indices); padding still
+ *                              at the end
+ *   FLASHTOPK_OUT_INT64        out_idx holds int64 entries (-1 padding) */
+#define FLASHTOPK_OUT_INDEX_ORDER 1
+#define FLASHTOPK_OUT_INT64 2
 
 /* Knobs for flashtopk_select_ex.  Zero-initialise for defaults. */
 typedef struct flashtopk_options {
@@ -93,6 +103,7 @@ typedef struct flashtopk_options {
     int profile;              /* nonzero: time each kernel phase with HIP
                                  events on the call's stream (ms_* of
                                  flashtopk_info); adds a few microseconds */
+    int out_flags;            /* FLASHTOPK_OUT_* bits; 0 = score order, int32 */
 } flashtopk_options;
 
 /* What the last call on a stream did (README, "Usage": last_info). */
@@ -128,13 +139,13 @@ typedef struct flashtopk_info {
 int flashtopk_select(const void *q, const void *kv, const float *kv_scales,
                      const float *weights, const int32_t *ks, const int32_t *ke,
                      int64_t num_q, int64_t num_kv, int dtype, int topk,
-                     int32_t *out_idx, float *out_val, void *stream);
+                     void *out_idx, float *out_val, void *stream);
 
 /* flashtopk_select with options (opt may be NULL = defaults). */
 int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales,
                         const float *weights, const int32_t *ks, const int32_t *ke,
                         int64_t num_q, int64_t num_kv, int dtype, int topk,
-                        int32_t *out_idx, float *out_val, void *stream,
+                        void *out_idx, float *out_val, void *stream,
                         const flashtopk_options *opt);
 
 /* Score-row dtypes of flashtopk_topk_rows (DeepSelect README, "Supported
@@ -152,7 +163,9 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales,
  *             README's stride requirement; pad rows otherwise).
  *   ends      [rows] int32, or NULL: row r keeps only its first ends[r]
  *             entries (exclusive bound, clamped to [0, cols]); NULL = cols.
- *   out_idx   [rows, topk] int32, out_val [rows, topk] float32 or NULL.
+ *   out_idx   [rows, topk] int32 (int64 with FLASHTOPK_OUT_INT64), out_val
+ *             [rows, topk] float32 or NULL.
+ *   out_flags FLASHTOPK_OUT_* bits (0: score order, int32 indices).
  *   nan_flag  one int32 in device memory, or NULL: the call sets it to 1 when
  *             an entry inside some row's bound is NaN (the caller clears it;
  *             the README's kernel aborts instead).  Rows holding NaN get an
@@ -165,8 +178,8 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales,
  * no-op.  Enqueued on `stream` without blocking the host and with no
  * workspace.  Ownership, synchronisation and errors as for flashtopk_select. */
 int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t cols, int64_t row_stride,
-                        const int32_t *ends, int topk, int32_t *out_idx, float *out_val, int32_t *nan_flag,
-                        void *stream);
+                        const int32_t *ends, int topk, void *out_idx, float *out_val, int32_t *nan_flag,
+                        int out_flags, void *stream);
 
 /* Pre-allocate the workspace of (current device, stream) for calls up to the
  * given sizes, so later calls allocate nothing (README, "Usage": the

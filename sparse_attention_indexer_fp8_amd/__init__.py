@@ -24,6 +24,8 @@ DIM = 128
 MAX_TOPK = 4096
 FLASHTOPK_SCORES_F32 = 0
 FLASHTOPK_SCORES_BF16 = 1
+FLASHTOPK_OUT_INDEX_ORDER = 1
+FLASHTOPK_OUT_INT64 = 2
 
 PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER = 0, 1, 2, 3
 
@@ -45,6 +47,7 @@ class Options(ctypes.Structure):
         ("sample_target", ctypes.c_int),
         ("recover_budget_bytes", ctypes.c_int64),
         ("profile", ctypes.c_int),
+        ("out_flags", ctypes.c_int),
     ]
 
 
@@ -97,7 +100,7 @@ def load_library():
     lib.flashtopk_select.restype = I
     lib.flashtopk_select_ex.argtypes = sel + [ctypes.POINTER(Options)]
     lib.flashtopk_select_ex.restype = I
-    lib.flashtopk_topk_rows.argtypes = [P, I, I64, I64, I64, P, I, P, P, P, P]
+    lib.flashtopk_topk_rows.argtypes = [P, I, I64, I64, I64, P, I, P, P, P, I, P]
     lib.flashtopk_topk_rows.restype = I
     lib.flashtopk_reserve.argtypes = [I64, I64, I, I, P]
     lib.flashtopk_reserve.restype = I
@@ -171,8 +174,11 @@ def flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_va
     _check_dev("weights", weights, (torch.float32,), (T, HEADS))
     _check_dev("ks", ks, (torch.int32,), (T,))
     _check_dev("ke", ke, (torch.int32,), (T,))
-    _check_dev("out_idx", out_idx, (torch.int32,), (T, topk))
+    _check_dev("out_idx", out_idx, (torch.int32, torch.int64), (T, topk))
     _check_dev("out_val", out_val, (torch.float32,), (T, topk))
+    flags = options.out_flags if options is not None else 0
+    if (out_idx.dtype == torch.int64) != bool(flags & FLASHTOPK_OUT_INT64):
+        raise TypeError("out_idx dtype and options.out_flags (FLASHTOPK_OUT_INT64) disagree")
     opt = ctypes.byref(options) if options is not None else None
     st = lib.flashtopk_select_ex(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(weights), _ptr(ks), _ptr(ke),
                                  T, S, code, int(topk), _ptr(out_idx), _ptr(out_val),
@@ -185,11 +191,13 @@ def flashtopk_select(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=N
     flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val, stream, None)
 
 
-def flashtopk_topk_rows(x, topk, out_idx, out_val=None, ends=None, nan_flag=None, stream=None) -> None:
+def flashtopk_topk_rows(x, topk, out_idx, out_val=None, ends=None, nan_flag=None, stream=None,
+                        index_order=False) -> None:
     """Exact top-k of each row of x [rows, cols] (float32 or bfloat16; last
     dimension contiguous, row stride a multiple of 16 bytes).  Fills out_idx
-    [rows, topk] int32 and out_val [rows, topk] float32 if given; ends [rows]
-    int32 bounds each row; nan_flag (one int32) is set to 1 on a NaN."""
+    [rows, topk] int32 or int64 and out_val [rows, topk] float32 if given;
+    ends [rows] int32 bounds each row; nan_flag (one int32) is set to 1 on a
+    NaN; index_order lists each row's top k by ascending index."""
     torch = _torch()
     lib = load_library()
     if x.dim() != 2:
@@ -206,23 +214,26 @@ def flashtopk_topk_rows(x, topk, out_idx, out_val=None, ends=None, nan_flag=None
     if cols > 1 and x.stride(1) != 1:
         raise ValueError("x's last dimension must be contiguous")
     _check_dev("ends", ends, (torch.int32,), (rows,))
-    _check_dev("out_idx", out_idx, (torch.int32,), (rows, topk))
+    _check_dev("out_idx", out_idx, (torch.int32, torch.int64), (rows, topk))
     _check_dev("out_val", out_val, (torch.float32,), (rows, topk))
     _check_dev("nan_flag", nan_flag, (torch.int32,), (1,))
+    flags = (FLASHTOPK_OUT_INDEX_ORDER if index_order else 0) | \
+        (FLASHTOPK_OUT_INT64 if out_idx.dtype == torch.int64 else 0)
     st = lib.flashtopk_topk_rows(_ptr(x), code, rows, cols, x.stride(0), _ptr(ends), int(topk), _ptr(out_idx),
-                                 _ptr(out_val), _ptr(nan_flag), ctypes.c_void_p(_stream_handle(stream)))
+                                 _ptr(out_val), _ptr(nan_flag), flags, ctypes.c_void_p(_stream_handle(stream)))
     if st != 0:
         raise FlashTopKError(st, "flashtopk_topk_rows")
 
 
-def topk_rows(x, topk, ends=None, return_values=True, stream=None):
-    """indices [rows, topk] int32 (and values [rows, topk] float32) of the
-    exact top-k of each row of x; see flashtopk_topk_rows."""
+def topk_rows(x, topk, ends=None, return_values=True, sorted_index=False, indices_type=None, stream=None):
+    """indices [rows, topk] (int32, or indices_type torch.int64) and values
+    [rows, topk] float32 of the exact top-k of each row of x, by score or
+    (sorted_index) by index; see flashtopk_topk_rows."""
     torch = _torch()
     rows = x.shape[0]
-    idx = torch.empty((rows, topk), dtype=torch.int32, device=x.device)
+    idx = torch.empty((rows, topk), dtype=indices_type or torch.int32, device=x.device)
     val = torch.empty((rows, topk), dtype=torch.float32, device=x.device) if return_values else None
-    flashtopk_topk_rows(x, topk, idx, val, ends, None, stream)
+    flashtopk_topk_rows(x, topk, idx, val, ends, None, stream, index_order=sorted_index)
     return (idx, val) if return_values else idx
 
 
@@ -253,13 +264,22 @@ def flashtopk_version() -> int:
     return int(load_library().flashtopk_version())
 
 
-def select(q, kv, weights, ks, ke, kv_scales=None, topk=2048, return_scores=False, options=None, stream=None):
-    """indices [T, topk] int32 (and scores [T, topk] float32 with return_scores)."""
+def select(q, kv, weights, ks, ke, kv_scales=None, topk=2048, return_scores=False, options=None, stream=None,
+           sorted_index=False, indices_type=None):
+    """indices [T, topk] (int32, or indices_type torch.int64) and, with
+    return_scores, scores [T, topk] float32; by score, or (sorted_index) by
+    index."""
     torch = _torch()
     T = q.shape[0]
-    idx = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    o = Options() if options is None else Options.from_buffer_copy(options)
+    if sorted_index:
+        o.out_flags |= FLASHTOPK_OUT_INDEX_ORDER
+    if indices_type == torch.int64:
+        o.out_flags |= FLASHTOPK_OUT_INT64
+    idx = torch.empty((T, topk), dtype=torch.int64 if o.out_flags & FLASHTOPK_OUT_INT64 else torch.int32,
+                      device=q.device)
     val = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
-    flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, idx, val, stream, options)
+    flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, idx, val, stream, o)
     return (idx, val) if return_scores else idx
 
 

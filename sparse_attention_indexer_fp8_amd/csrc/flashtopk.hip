@@ -118,6 +118,7 @@ struct Plan {
     float rank_scale;
     int64_t recover_budget;
     int profile;
+    int out_flags;
 };
 
 int resolve(Plan &p, const flashtopk_options *opt)
@@ -133,6 +134,8 @@ int resolve(Plan &p, const flashtopk_options *opt)
     p.sample_min_stride = 1;
     while (p.sample_min_stride * 2 <= p.topk / 32) p.sample_min_stride *= 2;
     p.rank_scale = (opt && opt->sample_rank_scale > 0.0f) ? opt->sample_rank_scale : 1.0f;
+    p.out_flags = opt ? opt->out_flags : 0;
+    if (p.out_flags & ~(FLASHTOPK_OUT_INDEX_ORDER | FLASHTOPK_OUT_INT64)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
     p.profile = (opt && opt->profile) ? 1 : 0;
     return FLASHTOPK_OK;
@@ -211,7 +214,7 @@ float phase_ms(Workspace &w, const Plan &p, int i)
 }
 
 int run(const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
-        const int32_t *ke, int32_t *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+        const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
 {
     int st = FLASHTOPK_OK;
     Workspace *w = get_ws(stream, &st);
@@ -357,6 +360,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     se.stats = (const unsigned long long *)w->stats.ptr;
     se.out_idx = out_idx;
     se.out_val = out_val;
+    se.out_flags = p.out_flags;
     if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
     else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
     else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
@@ -469,7 +473,7 @@ extern "C" {
 
 int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, const float *weights,
                         const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype,
-                        int topk, int32_t *out_idx, float *out_val, void *stream,
+                        int topk, void *out_idx, float *out_val, void *stream,
                         const flashtopk_options *opt)
 {
     if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
@@ -491,15 +495,15 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, c
 
 int flashtopk_select(const void *q, const void *kv, const float *kv_scales, const float *weights,
                      const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype, int topk,
-                     int32_t *out_idx, float *out_val, void *stream)
+                     void *out_idx, float *out_val, void *stream)
 {
     return flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, num_q, num_kv, dtype, topk, out_idx, out_val,
                                stream, nullptr);
 }
 
 int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t cols, int64_t row_stride,
-                        const int32_t *ends, int topk, int32_t *out_idx, float *out_val, int32_t *nan_flag,
-                        void *stream)
+                        const int32_t *ends, int topk, void *out_idx, float *out_val, int32_t *nan_flag,
+                        int out_flags, void *stream)
 {
     if (score_dtype != FLASHTOPK_SCORES_F32 && score_dtype != FLASHTOPK_SCORES_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
     if (rows < 0 || rows >= (int64_t(1) << 31) || cols < 0 || cols >= (int64_t(1) << 31))
@@ -511,7 +515,8 @@ int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t co
     if (rows > 1 && row_stride < cols) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (x && !aligned16(x)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (rows > 1 && (row_stride * esize) % 16 != 0) return FLASHTOPK_ERR_INVALID_ARGUMENT;
-    RowsArgs a{x, rows, cols, row_stride, ends, topk, out_idx, out_val, nan_flag};
+    if (out_flags & ~(FLASHTOPK_OUT_INDEX_ORDER | FLASHTOPK_OUT_INT64)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    RowsArgs a{x, rows, cols, row_stride, ends, topk, out_idx, out_val, nan_flag, out_flags};
     const hipStream_t s = (hipStream_t)stream;
     const bool small = topk <= RowsSmall::maxk;
     if (score_dtype == FLASHTOPK_SCORES_F32) {

@@ -50,9 +50,10 @@ struct RowsArgs {
     int64_t rows, cols, stride;
     const int32_t *ends;    // [rows] or null
     int topk;
-    int32_t *out_idx;       // [rows, topk]
+    void *out_idx;          // [rows, topk] int32, or int64 (kOutInt64)
     float *out_val;         // [rows, topk] or null
     int32_t *nan_flag;      // set to 1 when a row holds a NaN; or null
+    int out_flags;          // OutFlag
 };
 
 template <typename T> __device__ __forceinline__ float entry_value(T v);
@@ -508,12 +509,12 @@ __global__ __launch_bounds__(64 * kRowsTauWaves) void k_rows_tau(RowsArgs a)
         b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
         tau = hi - (float)(b + 2) / scale;
     }
-    if (lane == 0) a.out_idx[r * a.topk] = __float_as_int(tau);
+    if (lane == 0) *(int32_t *)out_row(a.out_idx, r, a.topk, a.out_flags) = __float_as_int(tau);
 }
 
 // One workgroup per row.  With PRE_TAU the row's threshold was computed by
-// k_rows_tau and parked in the row's first output index slot (the outputs
-// are written last); otherwise the workgroup reads the sample itself, with
+// k_rows_tau and parked in the first 4 bytes of the row's output indices
+// (the outputs are written last); otherwise the workgroup reads the sample itself, with
 // its first group of the row already in flight.
 template <typename T, typename SH, bool PRE_TAU>
 __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows(RowsArgs a)
@@ -525,18 +526,19 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
     const int64_t n = a.ends ? min(max((int64_t)a.ends[r], (int64_t)0), a.cols) : a.cols;
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
-    int32_t *oi = a.out_idx + r * a.topk;
+    void *oi = out_row(a.out_idx, r, a.topk, a.out_flags);
     float *ov = a.out_val ? a.out_val + r * a.topk : nullptr;
     if (k == 0) {
         for (int j = tid; j < a.topk; j += NT) {
-            oi[j] = -1;
+            if (a.out_flags & kOutInt64) ((int64_t *)oi)[j] = -1;
+            else ((int32_t *)oi)[j] = -1;
             if (ov) ov[j] = -__builtin_inff();
         }
         return;
     }
     bool nan = false;
     float tau = -__builtin_inff();
-    if (PRE_TAU && n > SH::cap) tau = __int_as_float(__builtin_amdgcn_readfirstlane(oi[0]));
+    if (PRE_TAU && n > SH::cap) tau = __int_as_float(__builtin_amdgcn_readfirstlane(*(const int32_t *)oi));
     v4i first[U];
     load_group<T, NT, U>(first, row, n, 0);  // in flight while the sample is read
     if (!PRE_TAU && n > SH::cap) {
@@ -550,10 +552,10 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
         RowElems<SH::regs> el;
         el.load(L.cand, m);
         __syncthreads();  // the gathered entries are in registers; the LDS becomes the selection's
-        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m, k, a.topk, oi, ov);
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m, k, a.topk, oi, ov, a.out_flags);
     } else {
         RowStream<T> el{row, n};
-        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov);
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags);
     }
 }
 

@@ -253,6 +253,9 @@ __global__ __launch_bounds__(kTriageThreads) void k_triage(TriageArgs a)
 // ---------------------------------------------------------------------------
 // Exact selection of one row per block.
 
+// Output options (DeepSelect README, "Usage": sorted_index, indices_type).
+enum OutFlag { kOutIndexOrder = 1, kOutInt64 = 2 };
+
 struct SelectArgs {
     const int32_t *ks;
     const int32_t *ke;
@@ -270,8 +273,9 @@ struct SelectArgs {
     int row_limit;
     const uint64_t *scratch;
     int64_t scratch_stride;
-    int32_t *out_idx;
+    void *out_idx;       // int32 or int64 (kOutInt64)
     float *out_val;
+    int out_flags;       // OutFlag
 };
 
 // Bucketed selection.  The row's candidates are spread over NBKT buckets
@@ -317,7 +321,13 @@ using SelDense = SelShape<0, 512, 4096, kMaxTopk>;   // recovered rows
 
 template <int NT, int NBKT, int MAXK, typename E>
 __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
-                            int32_t *oi, float *ov);
+                            void *oi, float *ov, int flags);
+
+// Row r's slots of an output index array of int32 or int64 entries.
+__device__ __forceinline__ void *out_row(void *base, int64_t r, int topk, int flags)
+{
+    return (char *)base + r * topk * ((flags & kOutInt64) ? 8 : 4);
+}
 
 // Candidate mode: rows that triage flags (same predicate) are left to dense
 // recovery; every other row's candidates hold its whole top k.
@@ -347,22 +357,23 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
         n = len > 0 ? min((int64_t)c, (int64_t)a.cap) : 0;  // a.cap <= NREG * NT
     }
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
-    int32_t *oi = a.out_idx + (int64_t)t * a.topk;
+    void *oi = out_row(a.out_idx, t, a.topk, a.out_flags);
     float *ov = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
     RowElems<NREG> el;
     el.load(src, n);
-    select_core<NT, NBKT, MAXK>(S, el, n, k, a.topk, oi, ov);
+    select_core<NT, NBKT, MAXK>(S, el, n, k, a.topk, oi, ov, a.out_flags);
 }
 
 // Exact top k of one row's elements (raw candidates, see raw_cand) held by
-// the visitor `el`, written to oi / ov (ov may be null) in key order and
-// padded to topk.  All threads of the block call it; S is the block's LDS.
+// the visitor `el`, written to oi / ov (ov may be null) in key order -- or,
+// with kOutIndexOrder, the same k keys by ascending index -- and padded to
+// topk; indices as int32, or int64 with kOutInt64.  All threads of the block call it; S is the block's LDS.
 // Element visitors with registers (E::REG) rank keys inside their buckets in
 // parallel; streamed visitors sort each bucket serially and so only take the
 // bucketed path for buckets of at most 48 keys.
 template <int NT, int NBKT, int MAXK, typename E>
 __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
-                            int32_t *oi, float *ov)
+                            void *oi, float *ov, int flags)
 {
     constexpr int NW = NT / 64, BPT = NBKT / NT;
     constexpr bool DENSE = !E::REG;
@@ -532,6 +543,32 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
             }
         }
     }
+    if ((flags & kOutIndexOrder) && k > 1) {
+        // S.sel[0, k) holds the selected keys; a bitonic sort on the low
+        // word (the index's complement) descending orders them by index.
+        // Padding with low word 0 sorts last.
+        uint32_t P = 1;
+        while (P < k) P <<= 1;
+        __syncthreads();
+        for (uint32_t i = k + tid; i < P; i += NT) S.sel[i] = 0;
+        __syncthreads();
+        for (uint32_t size = 2; size <= P; size <<= 1) {
+            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                for (uint32_t i = tid; i < P / 2; i += NT) {
+                    const uint32_t l0 = 2 * i - (i & (stride - 1));
+                    const uint32_t l1 = l0 + stride;
+                    const bool desc = (l0 & size) == 0;
+                    const uint64_t x = S.sel[l0], y = S.sel[l1];
+                    const uint32_t xl = (uint32_t)x, yl = (uint32_t)y;
+                    if (desc ? (xl < yl) : (xl > yl)) {
+                        S.sel[l0] = y;
+                        S.sel[l1] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
     for (int j = tid; j < topk; j += NT) {
         int32_t idx = -1;
         float v = -__builtin_inff();
@@ -540,7 +577,8 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
             idx = key_index(e);
             v = key_score(e);
         }
-        oi[j] = idx;
+        if (flags & kOutInt64) ((int64_t *)oi)[j] = idx;
+        else ((int32_t *)oi)[j] = idx;
         if (ov) ov[j] = v;
     }
 }

@@ -54,11 +54,13 @@ def test_header_constants_match_binding():
     assert int(consts["FLASHTOPK_PATH_RECOVER"]) == ftk.PATH_RECOVER
     assert int(consts["FLASHTOPK_SCORES_F32"]) == ftk.FLASHTOPK_SCORES_F32
     assert int(consts["FLASHTOPK_SCORES_BF16"]) == ftk.FLASHTOPK_SCORES_BF16
+    assert int(consts["FLASHTOPK_OUT_INDEX_ORDER"]) == ftk.FLASHTOPK_OUT_INDEX_ORDER
+    assert int(consts["FLASHTOPK_OUT_INT64"]) == ftk.FLASHTOPK_OUT_INT64
 
 
 def test_options_and_info_layout_match_header():
     # sizes of the C structs as laid out by the platform ABI
-    assert ctypes.sizeof(ftk.Options) == 32
+    assert ctypes.sizeof(ftk.Options) == 32  # out_flags fills the old tail padding
     assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4 + 6 * 4
 
 
@@ -95,10 +97,10 @@ def test_misaligned_operands_rejected(lib):
 
 def _rows(lib, **kw):
     args = dict(x=None, dtype=1, rows=0, cols=0, stride=0, ends=None, topk=1, out_idx=None, out_val=None,
-                nan_flag=None, stream=None)
+                nan_flag=None, flags=0, stream=None)
     args.update(kw)
     return lib.flashtopk_topk_rows(*[args[k] for k in ("x", "dtype", "rows", "cols", "stride", "ends", "topk",
-                                                       "out_idx", "out_val", "nan_flag", "stream")])
+                                                       "out_idx", "out_val", "nan_flag", "flags", "stream")])
 
 
 def test_topk_rows_argument_errors_without_device(lib):
@@ -118,3 +120,4 @@ def test_topk_rows_argument_errors_without_device(lib):
     assert _rows(lib, rows=2, cols=8, stride=4, x=ok, out_idx=ok) == 1      # stride < cols
     assert _rows(lib, rows=2, cols=9, stride=9, x=ok, out_idx=ok) == 1      # 18-byte BF16 stride
     assert _rows(lib, rows=2, cols=6, stride=6, x=ok, out_idx=ok, dtype=0) == 1  # 24-byte f32 stride
+    assert _rows(lib, rows=2, cols=8, stride=8, x=ok, out_idx=ok, flags=4) == 1   # unknown output flag
