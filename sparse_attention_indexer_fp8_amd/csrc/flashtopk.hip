@@ -24,6 +24,7 @@
 
 #include "flashtopk.h"
 #include "ftk_bound.hpp"
+#include "ftk_few.hpp"
 #include "ftk_rows.hpp"
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
@@ -195,6 +196,21 @@ void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const Score
     else launch_score<kBF16>(mode, grid, st, a);
 }
 
+// Calls with at most kFewRows rows score with k_score_few in every mode.
+template <int DT>
+void launch_few(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
+{
+    if (mode == kModeSample) k_score_few<DT, kModeSample><<<grid, kFewThreads, 0, st>>>(a);
+    else if (mode == kModeFilter) k_score_few<DT, kModeFilter><<<grid, kFewThreads, 0, st>>>(a);
+    else k_score_few<DT, kModeDense><<<grid, kFewThreads, 0, st>>>(a);
+}
+
+void launch_few_dt(int dtype, int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
+{
+    if (dtype == FLASHTOPK_FP8_E4M3) launch_few<kFP8>(mode, grid, st, a);
+    else launch_few<kBF16>(mode, grid, st, a);
+}
+
 // Phase boundary i of a profiled call (no-op otherwise).
 void mark(Workspace &w, const Plan &p, int i, hipStream_t stream)
 {
@@ -237,9 +253,11 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
 
     const int ntiles = (int)((T + kTileQ - 1) / kTileQ);
+    // A few rows (decode) score with k_score_few, which has no bound pruning.
+    const bool few = T <= kFewRows;
     // Score-bound pruning: on the auto path (each scan work item decides from
     // its tile's planner sample) and the forced prune path.
-    const bool bounds = S > 0 && (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE);
+    const bool bounds = !few && S > 0 && (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE);
     const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
     if (bounds) {
         if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
@@ -284,25 +302,32 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
 
     mark(*w, p, 0, stream);
     {
-        // Per-key scale factors (and block extremes for the bound).
-        const unsigned nwg = (unsigned)((S + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
+        // Per-key scale factors (and block extremes for the bound); with few
+        // rows only the statistics are cleared (k_score_few reads sigma).
+        const int64_t Sp = few ? 0 : S;
+        const unsigned nwg = (unsigned)((Sp + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
         uint8_t *kbp = bounds ? (uint8_t *)w->kb.ptr : nullptr;
         float2 *kmp = bounds ? (float2 *)w->kmeta.ptr : nullptr;
         unsigned long long *stp = (unsigned long long *)w->stats.ptr;
         if (fp8)
-            k_keyprep<kFP8><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)S, nblocks,
+            k_keyprep<kFP8><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)Sp, nblocks,
                                                      (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
                                                      kStCount);
         else
-            k_keyprep<kBF16><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)S, nblocks,
+            k_keyprep<kBF16><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)Sp, nblocks,
                                                       (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
                                                       kStCount);
     }
-    if (fp8)
+    if (fp8 && !few)
         k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T,
                                                                  (uint8_t *)w->qbar.ptr, (float *)w->qscale.ptr);
-    if (!recover_all)
-        launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * sa.sample_split)), stream, sa);
+    if (!recover_all) {
+        if (few)
+            launch_few_dt(p.dtype, kModeSample,
+                          dim3((unsigned)(T * ((p.sample_target + kFewSamplePart - 1) / kFewSamplePart))), stream, sa);
+        else
+            launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * sa.sample_split)), stream, sa);
+    }
     mark(*w, p, 1, stream);
 
     if (!recover_all) {
@@ -323,7 +348,13 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
 
     mark(*w, p, 2, stream);
 
-    if (!recover_all) launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
+    if (!recover_all) {
+        if (few)
+            launch_few_dt(p.dtype, kModeFilter, dim3((unsigned)std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk)),
+                          stream, sa);
+        else
+            launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
+    }
     mark(*w, p, 3, stream);
 
     TriageArgs tr{};
@@ -394,7 +425,12 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         for (int64_t rb = 0; rb < R; rb += rcap) {
             sa.row_base = (int)rb;
             se.row_base = (int)rb;
-            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
+            if (few)
+                launch_few_dt(p.dtype, kModeDense,
+                              dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream,
+                              sa);
+            else
+                launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
             launch_select<SelDense>(rcap, stream, se);
         }
         e = hipGetLastError();
