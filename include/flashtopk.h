@@ -34,10 +34,13 @@
  * Synchronisation: work is enqueued on `stream` (a hipStream_t; NULL is the
  * device's null stream) and is stream-ordered: out_idx / out_val are complete
  * once the stream has reached the end of the call's work (synchronise the
- * stream, or wait on an event recorded after the call).  The call itself
- * blocks the calling thread until the GPU has classified the rows (it reads
- * back how many rows need dense rescoring), but not until the selection is
- * done.
+ * stream, or wait on an event recorded after the call).  A call with more
+ * than 4 query rows blocks the calling thread until the GPU has classified
+ * the rows (it reads back how many rows need dense rescoring), but not until
+ * the selection is done; a call with at most 4 rows does not block at all
+ * (its rescoring is launched for every row up front, when its scratch fits
+ * the recovery budget, and its statistics are read back when
+ * flashtopk_get_last_info asks for them).
  *
  * Errors: every entry point returns 0 (FLASHTOPK_OK) or a positive status;
  * nothing is thrown across the ABI and nothing is printed.  Preconditions
@@ -97,8 +100,8 @@ typedef struct flashtopk_options {
                                  0 = 1.  Below 1 raises the threshold (fewer
                                  candidates), above 1 lowers it */
     int sample_target;        /* most keys sampled per row for the
-                                 threshold; 0 = 2048 (the lattice stride is
-                                 also at least topk / 32) */
+                                 threshold; 0 = 2048, at most 2048 (the
+                                 lattice stride is also at least topk / 32) */
     int64_t recover_budget_bytes; /* scratch for dense rescoring; 0 = 1 GiB */
     int profile;              /* nonzero: time each kernel phase with HIP
                                  events on the call's stream (ms_* of
@@ -186,7 +189,8 @@ int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t co
  * Selector's plan() owns the workspace and prepares up front). */
 int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream);
 
-/* Statistics of the last call issued on `stream` from this process. */
+/* Statistics of the last call issued on `stream` from this process (waits
+ * for that call's statistics to reach the host if they have not yet). */
 int flashtopk_get_last_info(void *stream, flashtopk_info *out);
 
 /* Frees every cached workspace.  No call may be in flight. */

@@ -49,11 +49,14 @@ struct Workspace {
     hipStream_t stream = nullptr;
     DevBuf tau, cnt, rowlist, stats, cand, samp, scratch, qbar, qscale, sigh;
     DevBuf kb, kmeta, vplan, q1;               // score-bound pruning
+    DevBuf ticket;                             // few-row sample finish counters (kept zero between calls)
     unsigned long long *host_stats = nullptr;  // pinned
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
     flashtopk_info last{};
     bool has_last = false;
+    bool last_pending = false;   // counts of `last` not yet read from host_stats
+    bool last_recover_all = false;
 };
 
 std::mutex g_mu;
@@ -87,6 +90,15 @@ int ensure(Workspace &w, DevBuf &b, size_t bytes)
     }
     b.bytes = std::max<size_t>(want, 256);
     return FLASHTOPK_OK;
+}
+
+// ensure() for a buffer that must read zero when (re)allocated.
+int ensure_zeroed(Workspace &w, DevBuf &b, size_t bytes)
+{
+    if (b.bytes >= bytes && b.ptr) return FLASHTOPK_OK;
+    int st = ensure(w, b, bytes);
+    if (st) return st;
+    return hip_status(hipMemset(b.ptr, 0, b.bytes));
 }
 
 Workspace *get_ws(hipStream_t stream, int *status)
@@ -128,7 +140,8 @@ int resolve(Plan &p, const flashtopk_options *opt)
     if (p.path < FLASHTOPK_PATH_AUTO || p.path > FLASHTOPK_PATH_RECOVER) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     int cap = (opt && opt->cand_capacity > 0) ? opt->cand_capacity : std::min(kMaxCap, 4 * p.topk);
     p.cap = std::min(kMaxCap, std::max(cap, p.topk));
-    p.sample_target = (opt && opt->sample_target > 0) ? opt->sample_target : kDefaultSampleTarget;
+    p.sample_target = (opt && opt->sample_target > 0) ? std::min(opt->sample_target, (int)kTauBuckets)
+                                                       : kDefaultSampleTarget;
     // The threshold is the r-th largest sample score with r about 2 topk / d
     // for stride d; r >= 64 (relative spread of the admitted count about
     // 1/8) is enough, so the stride need not go below topk / 32.
@@ -229,6 +242,26 @@ float phase_ms(Workspace &w, const Plan &p, int i)
     return ms;
 }
 
+// Copies the statistics of the workspace's last call (already in pinned host
+// memory) into its record.
+void fill_counts(Workspace &w)
+{
+    flashtopk_info &info = w.last;
+    const unsigned long long *hs = w.host_stats;
+    info.path = w.last_recover_all ? FLASHTOPK_PATH_RECOVER
+                                   : (hs[kStPruneOn] ? FLASHTOPK_PATH_PRUNE : FLASHTOPK_PATH_SCAN);
+    info.rows_empty = (int64_t)hs[kStEmpty];
+    info.rows_take_all = (int64_t)hs[kStTakeAll];
+    info.rows_sampled = (int64_t)hs[kStSampled];
+    info.rows_underflow = (int64_t)hs[kStUnder];
+    info.rows_overflow = (int64_t)hs[kStOver];
+    info.rows_recovered = (int64_t)hs[kStFlagged];
+    info.max_candidates = (int64_t)hs[kStMaxCand];
+    info.window_keys = (int64_t)hs[kStWindow];
+    info.pruned_keys = (int64_t)hs[kStPruned];
+    w.last_pending = false;
+}
+
 int run(const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
         const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
 {
@@ -300,8 +333,21 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         sa.plan = (unsigned long long *)w->stats.ptr + kStPruned;
     }
 
+    // Few rows: the sample kernel clears the statistics and sets every row's
+    // threshold (no per-key pass, no separate threshold kernel).
+    const bool few_sample = few && !recover_all;
+    if (few_sample) {
+        if ((st = ensure_zeroed(*w, w->ticket, sizeof(uint32_t) * (size_t)T))) return st;
+        sa.topk = p.topk;
+        sa.rank_scale = p.rank_scale;
+        sa.tau_w = (float *)w->tau.ptr;
+        sa.ticket = (uint32_t *)w->ticket.ptr;
+        sa.stats = (unsigned long long *)w->stats.ptr;
+        sa.nstats = kStCount;
+    }
+
     mark(*w, p, 0, stream);
-    {
+    if (!few_sample) {
         // Per-key scale factors (and block extremes for the bound); with few
         // rows only the statistics are cleared (k_score_few reads sigma).
         const int64_t Sp = few ? 0 : S;
@@ -330,7 +376,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
     mark(*w, p, 1, stream);
 
-    if (!recover_all) {
+    if (!recover_all && !few_sample) {
         TauArgs ta{};
         ta.ks = ks;
         ta.ke = ke;
@@ -357,28 +403,6 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
     mark(*w, p, 3, stream);
 
-    TriageArgs tr{};
-    tr.ks = ks;
-    tr.ke = ke;
-    tr.num_q = T;
-    tr.topk = p.topk;
-    tr.cap = p.cap;
-    tr.cnt = (const uint32_t *)w->cnt.ptr;
-    tr.recover_all = recover_all ? 1 : 0;
-    tr.rowlist = (int32_t *)w->rowlist.ptr;
-    tr.stats = (unsigned long long *)w->stats.ptr;
-    k_triage<<<dim3((unsigned)((T + kTriageThreads - 1) / kTriageThreads)), kTriageThreads, 0, stream>>>(tr);
-    // The triage counts go to pinned host memory right away; the host waits
-    // for them (not for the stream) while the select kernel runs, so the GPU
-    // never idles on the host between calls.
-    hipError_t e = hipMemcpyAsync(w->host_stats, w->stats.ptr, sizeof(unsigned long long) * kStCount,
-                                  hipMemcpyDeviceToHost, stream);
-    if (e != hipSuccess) return hip_status(e);
-    if (!w->stats_ev && (e = hipEventCreateWithFlags(&w->stats_ev, hipEventDisableTiming)) != hipSuccess)
-        return hip_status(e);
-    if ((e = hipEventRecord(w->stats_ev, stream)) != hipSuccess) return hip_status(e);
-    mark(*w, p, 4, stream);
-
     SelectArgs se{};
     se.ks = ks;
     se.ke = ke;
@@ -392,49 +416,100 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     se.out_idx = out_idx;
     se.out_val = out_val;
     se.out_flags = p.out_flags;
-    if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
-    else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
-    else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
-    else launch_select<SelHuge>(T, stream, se);
-    mark(*w, p, 5, stream);
-
-    e = hipGetLastError();
-    if (e == hipSuccess) e = hipEventSynchronize(w->stats_ev);
-    if (e != hipSuccess) return hip_status(e);
-
-    const int64_t R = (int64_t)w->host_stats[kStFlagged];
-    mark(*w, p, 6, stream);  // recovery timed from here (0 when nothing is flagged)
-    if (R > 0) {
-        // Dense rescoring of flagged rows, in batches that fit the budget.
-        const int64_t stride = std::max<int64_t>(S, 1);
-        int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(uint64_t) * stride));
-        rcap = std::min<int64_t>(rcap, (R + kTileQ - 1) / kTileQ * kTileQ);
-        rcap = (rcap + kTileQ - 1) / kTileQ * kTileQ;
-        if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)rcap * stride))) return st;
+    auto select_rows = [&]() {
+        if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
+        else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
+        else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
+        else launch_select<SelHuge>(T, stream, se);
+    };
+    hipError_t e = hipSuccess;
+    if (!w->stats_ev && (e = hipEventCreateWithFlags(&w->stats_ev, hipEventDisableTiming)) != hipSuccess)
+        return hip_status(e);
+    auto copy_stats = [&]() -> hipError_t {
+        hipError_t ce = hipMemcpyAsync(w->host_stats, w->stats.ptr, sizeof(unsigned long long) * kStCount,
+                                       hipMemcpyDeviceToHost, stream);
+        if (ce == hipSuccess) ce = hipEventRecord(w->stats_ev, stream);
+        return ce;
+    };
+    // Dense rescoring of flagged entries [rb, rb + rcap) of the list.
+    auto recover_batch = [&](int64_t rb, int64_t rcap, int64_t stride) {
         sa.rowlist = (const int32_t *)w->rowlist.ptr;
         sa.nrows = (const unsigned long long *)w->stats.ptr + kStFlagged;
         sa.row_limit = (int)rcap;
         sa.scratch = (uint64_t *)w->scratch.ptr;
         sa.scratch_stride = stride;
-        sa.ntiles = (int)(rcap / kTileQ);
-        sa.chunk = chunk_keys(sa.ntiles, S);
-        const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
+        sa.row_base = (int)rb;
         se.row_limit = (int)rcap;
         se.scratch = (const uint64_t *)w->scratch.ptr;
         se.scratch_stride = stride;
-        for (int64_t rb = 0; rb < R; rb += rcap) {
-            sa.row_base = (int)rb;
-            se.row_base = (int)rb;
-            if (few)
-                launch_few_dt(p.dtype, kModeDense,
-                              dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream,
-                              sa);
-            else
-                launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
-            launch_select<SelDense>(rcap, stream, se);
+        se.row_base = (int)rb;
+        if (few) {
+            launch_few_dt(p.dtype, kModeDense,
+                          dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream, sa);
+        } else {
+            sa.ntiles = (int)(rcap / kTileQ);
+            sa.chunk = chunk_keys(sa.ntiles, S);
+            const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
+            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
         }
+        launch_select<SelDense>(rcap, stream, se);
+    };
+    const int64_t stride = std::max<int64_t>(S, 1);
+
+    // Few rows whose whole windows fit the recovery budget: the selection
+    // does each row's triage, recovery of every row is launched up front
+    // (rows that need none exit at once), and the call returns without
+    // waiting for the GPU; the statistics are read when asked for.
+    const bool speculative = few && !p.profile && (int64_t)sizeof(uint64_t) * T * stride <= p.recover_budget;
+    int64_t R = 0;
+    if (speculative) {
+        if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)T * stride))) return st;
+        se.triage = 1;
+        se.rowlist_w = (int32_t *)w->rowlist.ptr;
+        se.stats_w = (unsigned long long *)w->stats.ptr;
+        select_rows();
+        mark(*w, p, 4, stream);
+        mark(*w, p, 5, stream);
+        mark(*w, p, 6, stream);
+        recover_batch(0, T, stride);
+        if ((e = copy_stats()) != hipSuccess) return hip_status(e);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_status(e);
+    } else {
+        TriageArgs tr{};
+        tr.ks = ks;
+        tr.ke = ke;
+        tr.num_q = T;
+        tr.topk = p.topk;
+        tr.cap = p.cap;
+        tr.cnt = (const uint32_t *)w->cnt.ptr;
+        tr.recover_all = recover_all ? 1 : 0;
+        tr.rowlist = (int32_t *)w->rowlist.ptr;
+        tr.stats = (unsigned long long *)w->stats.ptr;
+        k_triage<<<dim3((unsigned)((T + kTriageThreads - 1) / kTriageThreads)), kTriageThreads, 0, stream>>>(tr);
+        // The triage counts go to pinned host memory right away; the host
+        // waits for them (not for the stream) while the select kernel runs,
+        // so the GPU never idles on the host between calls.
+        if ((e = copy_stats()) != hipSuccess) return hip_status(e);
+        mark(*w, p, 4, stream);
+        select_rows();
+        mark(*w, p, 5, stream);
+
         e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventSynchronize(w->stats_ev);
         if (e != hipSuccess) return hip_status(e);
+
+        R = (int64_t)w->host_stats[kStFlagged];
+        mark(*w, p, 6, stream);  // recovery timed from here (0 when nothing is flagged)
+        if (R > 0) {
+            // Dense rescoring of flagged rows, in batches that fit the budget.
+            int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(uint64_t) * stride));
+            rcap = std::min<int64_t>(rcap, (R + kTileQ - 1) / kTileQ * kTileQ);
+            rcap = (rcap + kTileQ - 1) / kTileQ * kTileQ;
+            if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)rcap * stride))) return st;
+            for (int64_t rb = 0; rb < R; rb += rcap) recover_batch(rb, rcap, stride);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_status(e);
+        }
     }
     float ms_rec = 0.0f;
     if (p.profile) {
@@ -449,22 +524,13 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         (void)hipEventDestroy(end);
     }
 
+    // The call's record; its counts are filled in from the statistics once
+    // they have reached the host (now, or on the first read of a
+    // speculative call's record).
     flashtopk_info &info = w->last;
     std::memset(&info, 0, sizeof(info));
-    const unsigned long long *hs = w->host_stats;
     info.status = FLASHTOPK_OK;
-    info.path = recover_all ? FLASHTOPK_PATH_RECOVER
-                            : (hs[kStPruneOn] ? FLASHTOPK_PATH_PRUNE : FLASHTOPK_PATH_SCAN);
     info.rows = T;
-    info.rows_empty = (int64_t)hs[kStEmpty];
-    info.rows_take_all = (int64_t)hs[kStTakeAll];
-    info.rows_sampled = (int64_t)hs[kStSampled];
-    info.rows_underflow = (int64_t)hs[kStUnder];
-    info.rows_overflow = (int64_t)hs[kStOver];
-    info.rows_recovered = R;
-    info.max_candidates = (int64_t)hs[kStMaxCand];
-    info.window_keys = (int64_t)hs[kStWindow];
-    info.pruned_keys = (int64_t)hs[kStPruned];
     info.cand_capacity = p.cap;
     info.sample_target = p.sample_target;
     info.ms_sample = phase_ms(*w, p, 0);
@@ -473,7 +539,10 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     info.ms_triage = phase_ms(*w, p, 3);
     info.ms_select = phase_ms(*w, p, 4);
     info.ms_recover = R > 0 ? ms_rec : 0.0f;
+    w->last_recover_all = recover_all;
     w->has_last = true;
+    w->last_pending = true;
+    if (!speculative) fill_counts(*w);
     return FLASHTOPK_OK;
 }
 
@@ -583,6 +652,7 @@ int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, vo
     if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * kDefaultSampleTarget))) return st;
     if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(max_kv + 64)))) return st;
     if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
+    if ((st = ensure_zeroed(*w, w->ticket, sizeof(uint32_t) * T))) return st;
     if (dtype == FLASHTOPK_FP8_E4M3) {
         if ((st = ensure(*w, w->qbar, (size_t)T * kQbarParts * kDim))) return st;
         if ((st = ensure(*w, w->qscale, sizeof(float) * T))) return st;
@@ -606,6 +676,11 @@ int flashtopk_get_last_info(void *stream, flashtopk_info *out)
     std::lock_guard<std::mutex> lk(g_mu);
     for (Workspace *w : g_ws) {
         if (w->device == dev && w->stream == (hipStream_t)stream && w->has_last) {
+            if (w->last_pending) {
+                e = hipEventSynchronize(w->stats_ev);
+                if (e != hipSuccess) return hip_status(e);
+                fill_counts(*w);
+            }
             *out = w->last;
             return FLASHTOPK_OK;
         }
@@ -624,7 +699,7 @@ void flashtopk_release(void)
         (void)hipStreamSynchronize(w->stream);
         DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowlist, &w->stats,
                           &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh,
-                          &w->kb, &w->kmeta, &w->vplan, &w->q1};
+                          &w->kb, &w->kmeta, &w->vplan, &w->q1, &w->ticket};
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);

@@ -23,6 +23,7 @@
 #include "ftk_common.hpp"
 #include "ftk_frag.hpp"
 #include "ftk_score.hpp"
+#include "ftk_tau.hpp"
 
 namespace ftk {
 
@@ -104,18 +105,28 @@ __global__ __launch_bounds__(kFewThreads) void k_score_few(ScoreArgs a)
     int64_t klo = 0, khi = 0;   // filter / dense: key range; sample: lattice entries
     int t_dense = -1, e_dense = 0;
     int64_t first = 0, d = 1;   // sample lattice
+    int64_t nlat = 0;
     if (MODE == kModeSample) {
+        // Workgroup 0 clears the call's statistics; a row that takes its
+        // whole window gets threshold -inf; a sampled row's threshold comes
+        // from its last workgroup (below).
+        if (blockIdx.x == 0 && tid < a.nstats) a.stats[tid] = 0ull;
         const int parts = (a.sample_target + kFewSamplePart - 1) / kFewSamplePart;
         const int t = blockIdx.x / parts, part = blockIdx.x - t * parts;
         if (t >= a.num_q) return;
         const int64_t lo = a.ks[t], hi = max((int64_t)a.ke[t], lo);
-        if (hi - lo <= a.cap) return;  // the row takes its whole window
+        if (hi - lo <= a.cap) {
+            if (part == 0 && tid == 0) {
+                a.tau_w[t] = -__builtin_inff();
+                a.cnt[t] = 0u;
+            }
+            return;
+        }
         d = sample_stride(hi - lo, a.sample_target, a.sample_min_stride);
         first = (lo + d - 1) / d * d;
-        const int64_t nlat = lattice_count(lo, hi, (int)d);
+        nlat = lattice_count(lo, hi, (int)d);
         klo = (int64_t)part * kFewSamplePart;
-        khi = min(nlat, klo + kFewSamplePart);
-        if (khi <= klo) return;
+        khi = max(klo, min(nlat, klo + kFewSamplePart));  // may be empty: the workgroup still counts
         r0 = t;
         r1 = t + 1;
     } else if (MODE == kModeDense) {
@@ -223,6 +234,28 @@ __global__ __launch_bounds__(kFewThreads) void k_score_few(ScoreArgs a)
                     }
                 }
             }
+        }
+    }
+    if (MODE == kModeSample) {
+        // The row's last workgroup to finish (a self-resetting counter)
+        // computes its threshold from all of its samples.
+        __shared__ uint32_t s_hist[kTauBuckets];
+        __shared__ uint32_t s_red[3 * kFewWaves + 1];
+        __shared__ int s_last;
+        const int t = r0;
+        const int parts = (a.sample_target + kFewSamplePart - 1) / kFewSamplePart;
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = atomicInc(&a.ticket[t], (unsigned)(parts - 1)) == (unsigned)(parts - 1);
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        const int64_t lo = a.ks[t], hi = max((int64_t)a.ke[t], lo);
+        const float tv = block_tau<kFewThreads>(a.samp + (int64_t)t * a.sample_target, (int)nlat,
+                                                tau_rank(a.topk, nlat, hi - lo, a.rank_scale), s_hist, s_red);
+        if (tid == 0) {
+            a.tau_w[t] = tv;
+            a.cnt[t] = 0u;
         }
     }
     if (MODE == kModeFilter) {

@@ -113,6 +113,14 @@ struct ScoreArgs {
     int nblocks;
     float *vplan;              // [ntiles, kPlanGroups, 16 blocks, 16 rows] planner sample
     unsigned long long *plan;  // PlanCounter slots
+    // few-row sample mode (k_score_few): the threshold of each row is
+    // computed by the row's last workgroup to finish its samples
+    int topk;
+    float rank_scale;
+    float *tau_w;              // [num_q] written threshold
+    uint32_t *ticket;          // [num_q] self-resetting finish counters
+    unsigned long long *stats; // call statistics, cleared by workgroup 0
+    int nstats;
 };
 
 // LDS layout of the q tile: for head h, the 64 lanes' fragments are stored as

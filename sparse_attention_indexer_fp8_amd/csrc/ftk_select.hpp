@@ -194,6 +194,27 @@ struct TriageArgs {
     unsigned long long *stats;  // Stat
 };
 
+// Triage bookkeeping of one row by one thread (one atomic per statistic).
+__device__ __forceinline__ void triage_one(int64_t t, int64_t len, uint32_t c, int topk, int cap, int recover_all,
+                                           int32_t *rowlist, unsigned long long *stats)
+{
+    if (row_flagged(len, c, topk, cap, recover_all))
+        rowlist[atomicAdd(stats + kStFlagged, 1ull)] = (int32_t)t;
+    if (len == 0) {
+        atomicAdd(stats + kStEmpty, 1ull);
+    } else if (!recover_all) {
+        if ((int64_t)c < min((int64_t)topk, len)) atomicAdd(stats + kStUnder, 1ull);
+        if ((int64_t)c > cap) atomicAdd(stats + kStOver, 1ull);
+        if (len <= cap) {
+            atomicAdd(stats + kStTakeAll, 1ull);
+        } else {
+            atomicAdd(stats + kStSampled, 1ull);
+            atomicMax(stats + kStMaxCand, (unsigned long long)c);
+        }
+    }
+    if (len) atomicAdd(stats + kStWindow, (unsigned long long)len);
+}
+
 // One thread per row; statistics and the flagged-row list are gathered with
 // one atomic per wave and statistic.  The list is in no particular order
 // (each flagged row's result depends on that row alone).
@@ -276,6 +297,12 @@ struct SelectArgs {
     void *out_idx;       // int32 or int64 (kOutInt64)
     float *out_val;
     int out_flags;       // OutFlag
+    // candidate mode with triage: each row's workgroup also does the row's
+    // triage bookkeeping (statistics, flagged-row list) -- calls with few
+    // rows skip the separate triage pass
+    int triage;
+    int32_t *rowlist_w;
+    unsigned long long *stats_w;
 };
 
 // Bucketed selection.  The row's candidates are spread over NBKT buckets
@@ -352,6 +379,7 @@ __global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
         const int64_t lo = a.ks[t], hi = a.ke[t];
         const int64_t len = hi > lo ? hi - lo : 0;
         const uint32_t c = a.cnt[t];
+        if (a.triage && threadIdx.x == 0) triage_one(t, len, c, a.topk, a.cap, a.recover_all, a.rowlist_w, a.stats_w);
         if (row_flagged(len, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
         src = a.cand + (int64_t)t * a.cap;
         n = len > 0 ? min((int64_t)c, (int64_t)a.cap) : 0;  // a.cap <= NREG * NT
