@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                    help="hold the keys in a shuffled page pool of PAGE_SIZE keys per page and call "
+                         "flashtopk_select_paged (the gather is inside the timed call)")
     ap.add_argument("--rows", default="", metavar="NAME",
                     help="time the standalone row top-k on a named score-row workload instead "
                          "(indexer_bf16_4096x131072_k512, indexer_bf16_64x131072_k512, "
@@ -286,8 +289,26 @@ def main():
     opt = Options()
     opt.path = args.path
 
-    def step(o=opt):
-        ftk.flashtopk_select_ex(q, kv, sc, w, ks, ke, topk, idx, val, options=o)
+    if args.paged:
+        ps = args.paged
+        nblk = (S + ps - 1) // ps
+        g = torch.Generator(device=dev)
+        g.manual_seed(99)
+        table = torch.randperm(nblk + 8, generator=g, device=dev)[:nblk].to(torch.int32)
+        pool = torch.zeros(((nblk + 8) * ps, kv.shape[1]), dtype=kv.dtype, device=dev)
+        spool = torch.zeros((nblk + 8) * ps, dtype=torch.float32, device=dev)
+        pos = (table.long()[:, None] * ps + torch.arange(ps, device=dev)[None, :]).reshape(-1)[:S]
+        pool.view(torch.uint8 if dt == "fp8" else torch.int16)[pos] = kv.view(torch.uint8 if dt == "fp8" else torch.int16)
+        if sc is not None:
+            spool[pos] = sc
+        pool = pool.view(nblk + 8, ps, kv.shape[1])
+        spool = None if sc is None else spool.view(nblk + 8, ps)
+
+        def step(o=opt):
+            ftk.flashtopk_select_paged(q, pool, spool, table, S, w, ks, ke, topk, idx, val, options=o)
+    else:
+        def step(o=opt):
+            ftk.flashtopk_select_ex(q, kv, sc, w, ks, ke, topk, idx, val, options=o)
 
     for _ in range(args.warmup):
         step()
@@ -340,7 +361,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["name"], "num_q": T, "num_kv": S, "topk": topk, "heads": 32, "dim": 128,
                    "windows": "packed" if args.workload == 5 else "causal", "window_pairs": pairs,
-                   "path": {0: "auto", 1: "scan", 2: "prune", 3: "recover"}[args.path]},
+                   "path": {0: "auto", 1: "scan", 2: "prune", 3: "recover"}[args.path],
+                   "kv": f"paged, {args.paged} keys per page" if args.paged else "contiguous"},
         "rows_per_s": round(T / (ms * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * whole / peak, 2),
         "dense_equiv_tflops": round(whole, 1),

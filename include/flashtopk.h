@@ -184,6 +184,23 @@ int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t co
                         const int32_t *ends, int topk, void *out_idx, float *out_val, int32_t *nan_flag,
                         int out_flags, void *stream);
 
+/* flashtopk_select_ex over keys held in a paged cache (README, "Roadmap":
+ * paged KV cache).  Logical key s (0 <= s < num_kv; windows, outputs and the
+ * tie rule use logical positions) is row s % page_size of page
+ * block_table[s / page_size] of the pool
+ *   kv_pages     [num_pages, page_size, 128] FP8 / BF16 (16-byte aligned)
+ *   scale_pages  [num_pages, page_size] float32, or NULL for all ones
+ *   block_table  [ceil(num_kv / page_size)] int32 page ids in [0, num_pages)
+ * shared by every query row of the call.  The call gathers its keys into the
+ * workspace (one streaming pass over num_kv keys) and then runs as
+ * flashtopk_select_ex; results are bit-identical to a call on the gathered
+ * contiguous keys.  A page id outside [0, num_pages) is a precondition
+ * violation: its keys read as zero with zero scale.  page_size >= 1. */
+int flashtopk_select_paged(const void *q, const void *kv_pages, const float *scale_pages, const int32_t *block_table,
+                           int page_size, int64_t num_pages, const float *weights, const int32_t *ks,
+                           const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype, int topk, void *out_idx,
+                           float *out_val, void *stream, const flashtopk_options *opt);
+
 /* Pre-allocate the workspace of (current device, stream) for calls up to the
  * given sizes, so later calls allocate nothing (README, "Usage": the
  * Selector's plan() owns the workspace and prepares up front). */

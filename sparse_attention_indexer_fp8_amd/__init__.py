@@ -80,7 +80,7 @@ class Info(ctypes.Structure):
 
 
 # Every symbol include/flashtopk.h declares.
-EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_topk_rows", "flashtopk_reserve", "flashtopk_get_last_info",
+EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_select_paged", "flashtopk_topk_rows", "flashtopk_reserve", "flashtopk_get_last_info",
            "flashtopk_release", "flashtopk_status_string", "flashtopk_version")
 
 _lib = None
@@ -100,6 +100,9 @@ def load_library():
     lib.flashtopk_select.restype = I
     lib.flashtopk_select_ex.argtypes = sel + [ctypes.POINTER(Options)]
     lib.flashtopk_select_ex.restype = I
+    lib.flashtopk_select_paged.argtypes = [P, P, P, P, I, I64, P, P, P, I64, I64, I, I, P, P, P,
+                                           ctypes.POINTER(Options)]
+    lib.flashtopk_select_paged.restype = I
     lib.flashtopk_topk_rows.argtypes = [P, I, I64, I64, I64, P, I, P, P, P, I, P]
     lib.flashtopk_topk_rows.restype = I
     lib.flashtopk_reserve.argtypes = [I64, I64, I, I, P]
@@ -185,6 +188,44 @@ def flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_va
                                  ctypes.c_void_p(_stream_handle(stream)), opt)
     if st != 0:
         raise FlashTopKError(st, "flashtopk_select_ex")
+
+
+def flashtopk_select_paged(q, kv_pages, scale_pages, block_table, num_kv, weights, ks, ke, topk, out_idx,
+                           out_val=None, stream=None, options: Options | None = None) -> None:
+    """flashtopk_select_ex over keys in a paged cache: kv_pages [num_pages,
+    page_size, 128], scale_pages [num_pages, page_size] float32 or None,
+    block_table [ceil(num_kv / page_size)] int32; num_kv logical keys."""
+    torch = _torch()
+    lib = load_library()
+    T = q.shape[0]
+    code = _dtype_code(q)
+    if _dtype_code(kv_pages) != code:
+        raise TypeError("q and kv_pages must have the same dtype")
+    if kv_pages.dim() != 3 or kv_pages.shape[2] != DIM or tuple(q.shape[1:]) != (HEADS, DIM):
+        raise ValueError("kv_pages must be [num_pages, page_size, 128] and q [T, 32, 128]")
+    num_pages, page_size = kv_pages.shape[0], kv_pages.shape[1]
+    nblk = (int(num_kv) + page_size - 1) // page_size
+    _check_dev("q", q)
+    _check_dev("kv_pages", kv_pages)
+    _check_dev("scale_pages", scale_pages, (torch.float32,), (num_pages, page_size))
+    _check_dev("block_table", block_table, (torch.int32,))
+    if block_table.numel() < nblk:
+        raise ValueError(f"block_table needs {nblk} entries")
+    _check_dev("weights", weights, (torch.float32,), (T, HEADS))
+    _check_dev("ks", ks, (torch.int32,), (T,))
+    _check_dev("ke", ke, (torch.int32,), (T,))
+    _check_dev("out_idx", out_idx, (torch.int32, torch.int64), (T, topk))
+    _check_dev("out_val", out_val, (torch.float32,), (T, topk))
+    flags = options.out_flags if options is not None else 0
+    if (out_idx.dtype == torch.int64) != bool(flags & FLASHTOPK_OUT_INT64):
+        raise TypeError("out_idx dtype and options.out_flags (FLASHTOPK_OUT_INT64) disagree")
+    opt = ctypes.byref(options) if options is not None else None
+    st = lib.flashtopk_select_paged(_ptr(q), _ptr(kv_pages), _ptr(scale_pages), _ptr(block_table), int(page_size),
+                                    int(num_pages), _ptr(weights), _ptr(ks), _ptr(ke), T, int(num_kv), code,
+                                    int(topk), _ptr(out_idx), _ptr(out_val), ctypes.c_void_p(_stream_handle(stream)),
+                                    opt)
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_select_paged")
 
 
 def flashtopk_select(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=None, stream=None) -> None:

@@ -25,6 +25,7 @@
 #include "flashtopk.h"
 #include "ftk_bound.hpp"
 #include "ftk_few.hpp"
+#include "ftk_paged.hpp"
 #include "ftk_rows.hpp"
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
@@ -50,6 +51,7 @@ struct Workspace {
     DevBuf tau, cnt, rowlist, stats, cand, samp, scratch, qbar, qscale, sigh;
     DevBuf kb, kmeta, vplan, q1;               // score-bound pruning
     DevBuf ticket;                             // few-row sample finish counters (kept zero between calls)
+    DevBuf pkv, psig;                          // keys and scales gathered from a paged cache
     unsigned long long *host_stats = nullptr;  // pinned
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
@@ -132,6 +134,10 @@ struct Plan {
     int64_t recover_budget;
     int profile;
     int out_flags;
+    // keys in a paged cache, read in place (calls with at most kFewRows rows)
+    const int32_t *table = nullptr;
+    int page_size = 0;
+    int64_t num_pages = 0;
 };
 
 int resolve(Plan &p, const flashtopk_options *opt)
@@ -323,6 +329,9 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.sample_target = p.sample_target;
     sa.sample_min_stride = p.sample_min_stride;
     sa.sample_split = sample_split(ntiles);
+    sa.table = p.table;
+    sa.page_size = p.page_size;
+    sa.num_pages = p.num_pages;
     if (bounds) {
         sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
         sa.kb = (const uint8_t *)w->kb.ptr;
@@ -598,6 +607,56 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, c
     return run(q, kv, kv_scales, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
 }
 
+int flashtopk_select_paged(const void *q, const void *kv_pages, const float *scale_pages, const int32_t *block_table,
+                           int page_size, int64_t num_pages, const float *weights, const int32_t *ks,
+                           const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype, int topk, void *out_idx,
+                           float *out_val, void *stream, const flashtopk_options *opt)
+{
+    if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
+    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 31))
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (page_size < 1 || num_pages < 0) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (topk < 1 || topk > FLASHTOPK_MAX_TOPK) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (num_q == 0) return FLASHTOPK_OK;
+    if (!q || !weights || !ks || !ke || !out_idx) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (num_kv > 0 && (!kv_pages || !block_table || num_pages == 0)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || (kv_pages && !aligned16(kv_pages))) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    Plan p{};
+    p.T = num_q;
+    p.S = num_kv;
+    p.dtype = dtype;
+    p.topk = topk;
+    int st = resolve(p, opt);
+    if (st) return st;
+    if (num_kv == 0) return run(q, nullptr, nullptr, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
+    const hipStream_t s = (hipStream_t)stream;
+    if (num_q <= kFewRows) {
+        // few rows read their keys from the pages directly
+        p.table = block_table;
+        p.page_size = page_size;
+        p.num_pages = num_pages;
+        return run(q, kv_pages, scale_pages, weights, ks, ke, out_idx, out_val, s, p);
+    }
+    Workspace *w = get_ws(s, &st);
+    if (!w) return st;
+    const bool fp8 = dtype == FLASHTOPK_FP8_E4M3;
+    const int RB = fp8 ? 128 : 256;
+    if ((st = ensure(*w, w->pkv, (size_t)num_kv * RB))) return st;
+    if (scale_pages && (st = ensure(*w, w->psig, sizeof(float) * (size_t)num_kv))) return st;
+    const int64_t pieces = num_kv * (RB / 16);
+    const dim3 grid((unsigned)((pieces + kGatherThreads * kGatherUnroll - 1) / (kGatherThreads * kGatherUnroll)));
+    float *sig = scale_pages ? (float *)w->psig.ptr : nullptr;
+    if (fp8)
+        k_gather_pages<kFP8><<<grid, kGatherThreads, 0, s>>>((const uint8_t *)kv_pages, scale_pages, block_table,
+                                                             page_size, num_pages, num_kv, (uint8_t *)w->pkv.ptr, sig);
+    else
+        k_gather_pages<kBF16><<<grid, kGatherThreads, 0, s>>>((const uint8_t *)kv_pages, scale_pages, block_table,
+                                                              page_size, num_pages, num_kv, (uint8_t *)w->pkv.ptr, sig);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    return run(q, w->pkv.ptr, sig, weights, ks, ke, out_idx, out_val, s, p);
+}
+
 int flashtopk_select(const void *q, const void *kv, const float *kv_scales, const float *weights,
                      const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype, int topk,
                      void *out_idx, float *out_val, void *stream)
@@ -699,7 +758,7 @@ void flashtopk_release(void)
         (void)hipStreamSynchronize(w->stream);
         DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowlist, &w->stats,
                           &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh,
-                          &w->kb, &w->kmeta, &w->vplan, &w->q1, &w->ticket};
+                          &w->kb, &w->kmeta, &w->vplan, &w->q1, &w->ticket, &w->pkv, &w->psig};
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);

@@ -14,6 +14,10 @@
 // scales the sum.  The work is bound by reading the keys once (128 B per key
 // FP8, 256 B BF16); the matrix cores and vector ALUs have room to spare.
 //
+// Keys may sit in a paged cache (a.table non-null: logical key p is row
+// p % page_size of page table[p / page_size]); each lane then reads its key
+// from its page, so such calls need no gathered copy of the keys.
+//
 // Every mode of a call with at most kFewRows rows uses this arithmetic, so a
 // row's scores have the same bits on every path of such a call (the sums run
 // in another order than k_score's, so a row's last bits may differ between a
@@ -197,11 +201,23 @@ __global__ __launch_bounds__(kFewThreads) void k_score_few(ScoreArgs a)
             const int64_t e = e0 + 16 * gi + n;
             const bool in = e < khi;
             const int64_t p = MODE == kModeSample ? first + (in ? e : 0) * d : e;
-            if (MODE == kModeSample)
-                load_kfrag(kf[gi], a.kv, (int)p, g);
-            else
-                load_kfrag_buf(kf[gi], rs, in ? (uint32_t)((e - klo) * RB + g * (RB / 4)) : 0xFFFFFFF0u, 0u);
-            sig[gi] = (in && a.sigma) ? a.sigma[p] : 1.0f;
+            if (a.table) {
+                // paged keys: the lane reads its key's row from its page
+                // (a page id out of range reads the pool's first row with
+                // scale 0); p is in range here, so the table read is too
+                const int64_t pq = in ? p : (MODE == kModeSample ? first : klo);
+                const int64_t pg = a.table[pq / a.page_size];
+                const bool ok = pg >= 0 && pg < a.num_pages;
+                const int64_t slot = ok ? pg * a.page_size + pq % a.page_size : 0;
+                load_kfrag(kf[gi], a.kv + slot * RB, 0, g);
+                sig[gi] = !ok ? 0.0f : (a.sigma ? a.sigma[slot] : 1.0f);
+            } else {
+                if (MODE == kModeSample)
+                    load_kfrag(kf[gi], a.kv, (int)p, g);
+                else
+                    load_kfrag_buf(kf[gi], rs, in ? (uint32_t)((e - klo) * RB + g * (RB / 4)) : 0xFFFFFFF0u, 0u);
+                sig[gi] = (in && a.sigma) ? a.sigma[p] : 1.0f;
+            }
         }
         for (int rr = 0; rr < nr; ++rr) {
             const int t = r0 + rr;

@@ -121,6 +121,10 @@ struct ScoreArgs {
     uint32_t *ticket;          // [num_q] self-resetting finish counters
     unsigned long long *stats; // call statistics, cleared by workgroup 0
     int nstats;
+    // few-row kernels over a paged key cache: kv and sigma are the page pools
+    const int32_t *table;      // [ceil(num_kv / page_size)] page ids, or null (contiguous keys)
+    int page_size;
+    int64_t num_pages;
 };
 
 // LDS layout of the q tile: for head h, the 64 lanes' fragments are stored as

@@ -121,3 +121,24 @@ def test_topk_rows_argument_errors_without_device(lib):
     assert _rows(lib, rows=2, cols=9, stride=9, x=ok, out_idx=ok) == 1      # 18-byte BF16 stride
     assert _rows(lib, rows=2, cols=6, stride=6, x=ok, out_idx=ok, dtype=0) == 1  # 24-byte f32 stride
     assert _rows(lib, rows=2, cols=8, stride=8, x=ok, out_idx=ok, flags=4) == 1   # unknown output flag
+
+
+def test_select_paged_argument_errors_without_device(lib):
+    buf = (ctypes.c_uint8 * 64)()
+    base = ctypes.addressof(buf)
+    ok = ctypes.c_void_p(base + (-base) % 16)
+
+    def call(**kw):
+        a = dict(q=ok, pages=ok, spages=None, table=ok, page_size=64, num_pages=4, w=ok, ks=ok, ke=ok, num_q=1,
+                 num_kv=100, dtype=0, topk=1, oi=ok, ov=None, stream=None, opt=None)
+        a.update(kw)
+        return lib.flashtopk_select_paged(*a.values())
+
+    assert call(dtype=5) == 2
+    assert call(page_size=0) == 1
+    assert call(num_pages=-1) == 1
+    assert call(topk=0) == 1
+    assert call(num_q=0) == 0                  # no-op
+    assert call(table=None) == 1               # keys without a block table
+    assert call(num_pages=0) == 1              # keys without pages
+    assert call(pages=ctypes.c_void_p(ok.value + 2)) == 1  # misaligned pool
