@@ -62,6 +62,11 @@ def _load():
     lib.oracle_select.restype = i32
     lib.oracle_select.argtypes = [vp, vp, i32, fp, fp, vp, vp, i64, i64, i32, vp, i64,
                                   vp, vp, vp, vp, i32]
+    lib.oracle_scores_h.restype = i32
+    lib.oracle_scores_h.argtypes = [vp, vp, i32, i32, fp, fp, i64, i64, i64, dp]
+    lib.oracle_select_h.restype = i32
+    lib.oracle_select_h.argtypes = [vp, vp, i32, i32, fp, fp, vp, vp, i64, i64, i32, vp, i64,
+                                    vp, vp, vp, vp, i32]
     lib.oracle_topk_rows.restype = i32
     lib.oracle_topk_rows.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, i32]
     lib.oracle_max_threads.restype = i32
@@ -102,6 +107,14 @@ def decode_bf16(codes) -> np.ndarray:
     return np.array([lib.oracle_decode_bf16(int(c)) for c in codes.ravel()]).reshape(codes.shape)
 
 
+def _heads(q, weights) -> int:
+    """Head count from the operand shapes: q [num_q, heads, 128], weights [num_q, heads]."""
+    h = int(q.shape[1])
+    if np.shape(weights)[-1] != h:
+        raise ValueError(f"weights have {np.shape(weights)[-1]} heads, q has {h}")
+    return h
+
+
 def scores(q, kv, dtype, kv_scales, weights, t: int, s_begin: int, s_end: int) -> np.ndarray:
     """Binary64 scores of query row t against keys [s_begin, s_end)."""
     lib = _load()
@@ -110,7 +123,8 @@ def scores(q, kv, dtype, kv_scales, weights, t: int, s_begin: int, s_end: int) -
     w = np.ascontiguousarray(weights, dtype=np.float32)
     sc = None if kv_scales is None else np.ascontiguousarray(kv_scales, dtype=np.float32)
     out = np.empty(max(0, s_end - s_begin), dtype=np.float64)
-    st = lib.oracle_scores(_ptr(q), _ptr(kv), code, _ptr(sc), _ptr(w), t, s_begin, s_end, _ptr(out))
+    st = lib.oracle_scores_h(_ptr(q), _ptr(kv), code, _heads(q, w), _ptr(sc), _ptr(w), t, s_begin, s_end,
+                             _ptr(out))
     if st != 0:
         raise ValueError("NaN operand code")
     return out
@@ -142,9 +156,9 @@ def select(q, kv, dtype, kv_scales, weights, ks, ke, topk: int, rows=None,
     val = np.empty((n, topk), dtype=np.float32)
     sc64 = np.empty((n, topk), dtype=np.float64)
     allsc = np.empty((n, num_kv), dtype=np.float64) if all_scores else None
-    st = lib.oracle_select(_ptr(q), _ptr(kv), code, _ptr(sc), _ptr(w), _ptr(ks), _ptr(ke),
-                           num_q, num_kv, int(topk), _ptr(rows_arr), n, _ptr(idx), _ptr(val),
-                           _ptr(sc64), _ptr(allsc), int(nthreads))
+    st = lib.oracle_select_h(_ptr(q), _ptr(kv), code, _heads(q, w), _ptr(sc), _ptr(w), _ptr(ks), _ptr(ke),
+                             num_q, num_kv, int(topk), _ptr(rows_arr), n, _ptr(idx), _ptr(val),
+                             _ptr(sc64), _ptr(allsc), int(nthreads))
     if st != 0:
         raise ValueError(f"oracle_select failed with status {st}")
     return idx, val, sc64, allsc

@@ -92,19 +92,19 @@ static void decode_key(const void *kv, int dtype, int64_t s, double *out)
         out[d] = decode(kv, dtype, s * ORACLE_DIM + d);
 }
 
-/* Decode the 32 x 128 query components of row t. */
-static void decode_query(const void *q, int dtype, int64_t t, double *out)
+/* Decode the heads x 128 query components of row t. */
+static void decode_query(const void *q, int dtype, int heads, int64_t t, double *out)
 {
-    for (int i = 0; i < ORACLE_HEADS * ORACLE_DIM; ++i)
-        out[i] = decode(q, dtype, t * ORACLE_HEADS * ORACLE_DIM + i);
+    for (int i = 0; i < heads * ORACLE_DIM; ++i)
+        out[i] = decode(q, dtype, t * heads * ORACLE_DIM + i);
 }
 
 /* The score of one (query, key) pair from already-decoded operands. */
 static double score_pair(const double *qrow, const double *key,
-                         const float *wrow, double sigma)
+                         const float *wrow, int heads, double sigma)
 {
     double acc = 0.0;
-    for (int h = 0; h < ORACLE_HEADS; ++h) {
+    for (int h = 0; h < heads; ++h) {
         double x = 0.0;
         for (int d = 0; d < ORACLE_DIM; ++d)
             x += qrow[h * ORACLE_DIM + d] * key[d];
@@ -117,25 +117,34 @@ static double score_pair(const double *qrow, const double *key,
 /* Scores of row t for keys s in [s_begin, s_end), written to out[s - s_begin].
  * Any key range is allowed (the window is not consulted).  Returns 0, or -1 if
  * an operand decodes to NaN. */
-int oracle_scores(const void *q, const void *kv, int dtype, const float *kv_scales,
-                  const float *weights, int64_t t, int64_t s_begin, int64_t s_end,
-                  double *out)
+int oracle_scores_h(const void *q, const void *kv, int dtype, int heads, const float *kv_scales,
+                    const float *weights, int64_t t, int64_t s_begin, int64_t s_end,
+                    double *out)
 {
-    double *qrow = (double *)malloc(sizeof(double) * ORACLE_HEADS * ORACLE_DIM);
+    if (heads < 1) return -3;
+    double *qrow = (double *)malloc(sizeof(double) * heads * ORACLE_DIM);
     double key[ORACLE_DIM];
     int bad = 0;
-    decode_query(q, dtype, t, qrow);
-    for (int i = 0; i < ORACLE_HEADS * ORACLE_DIM; ++i)
+    if (!qrow) return -2;
+    decode_query(q, dtype, heads, t, qrow);
+    for (int i = 0; i < heads * ORACLE_DIM; ++i)
         if (isnan(qrow[i])) bad = 1;
     for (int64_t s = s_begin; s < s_end && !bad; ++s) {
         decode_key(kv, dtype, s, key);
         for (int d = 0; d < ORACLE_DIM; ++d)
             if (isnan(key[d])) bad = 1;
         double sigma = kv_scales ? (double)kv_scales[s] : 1.0;
-        out[s - s_begin] = score_pair(qrow, key, weights + t * ORACLE_HEADS, sigma);
+        out[s - s_begin] = score_pair(qrow, key, weights + t * heads, heads, sigma);
     }
     free(qrow);
     return bad ? -1 : 0;
+}
+
+int oracle_scores(const void *q, const void *kv, int dtype, const float *kv_scales,
+                  const float *weights, int64_t t, int64_t s_begin, int64_t s_end,
+                  double *out)
+{
+    return oracle_scores_h(q, kv, dtype, ORACLE_HEADS, kv_scales, weights, t, s_begin, s_end, out);
 }
 
 typedef struct {
@@ -161,7 +170,7 @@ static int by_score_then_index(const void *pa, const void *pb)
  * all_scores, when given, receives the binary64 score of every key of the
  * window in key order (length ke - ks).  Returns 0, -1 on NaN operands, -2 on
  * allocation failure. */
-static int select_row(const void *q, int dtype, const float *kv_scales,
+static int select_row(const void *q, int dtype, int heads, const float *kv_scales,
                       const float *weights, int64_t t, int32_t ks, int32_t ke, int topk,
                       const double *kv_decoded, int32_t *out_idx, float *out_val,
                       double *out_score, double *all_scores)
@@ -169,17 +178,17 @@ static int select_row(const void *q, int dtype, const float *kv_scales,
     int64_t len = (int64_t)ke - (int64_t)ks;
     if (len < 0) len = 0;
     scored_key *keys = (scored_key *)malloc(sizeof(scored_key) * (size_t)(len > 0 ? len : 1));
-    double *qrow = (double *)malloc(sizeof(double) * ORACLE_HEADS * ORACLE_DIM);
+    double *qrow = (double *)malloc(sizeof(double) * heads * ORACLE_DIM);
     if (!keys || !qrow) { free(keys); free(qrow); return -2; }
     int bad = 0;
-    decode_query(q, dtype, t, qrow);
-    for (int i = 0; i < ORACLE_HEADS * ORACLE_DIM; ++i)
+    decode_query(q, dtype, heads, t, qrow);
+    for (int i = 0; i < heads * ORACLE_DIM; ++i)
         if (isnan(qrow[i])) bad = 1;
     for (int64_t j = 0; j < len; ++j) {
         int64_t s = ks + j;
         const double *key = kv_decoded + s * ORACLE_DIM;
         double sigma = kv_scales ? (double)kv_scales[s] : 1.0;
-        keys[j].score = score_pair(qrow, key, weights + t * ORACLE_HEADS, sigma);
+        keys[j].score = score_pair(qrow, key, weights + t * heads, heads, sigma);
         keys[j].index = s;
         if (isnan(keys[j].score)) bad = 1;
         if (all_scores) all_scores[j] = keys[j].score;
@@ -204,10 +213,12 @@ static int select_row(const void *q, int dtype, const float *kv_scales,
 }
 
 /* Exact top-k for a list of rows.
- *   q        [num_q, 32, 128]  FP8 E4M3FN bytes or BF16 codes
+ *   q        [num_q, heads, 128]  FP8 E4M3FN bytes or BF16 codes (heads = 32 for
+ *            oracle_select; the head count is a parameter of oracle_select_h, for
+ *            indexers with other head counts such as 64: README "Roadmap")
  *   kv       [num_kv, 128]     same dtype
  *   kv_scales[num_kv] fp32 or NULL (all ones)
- *   weights  [num_q, 32] fp32
+ *   weights  [num_q, heads] fp32
  *   ks, ke   [num_q] int32, window [ks, ke)
  *   rows     the nrows query rows to process (NULL: rows 0..nrows-1)
  *   out_idx / out_val  [nrows, topk]; out_score [nrows, topk] binary64 or NULL
@@ -216,13 +227,13 @@ static int select_row(const void *q, int dtype, const float *kv_scales,
  *   nthreads OpenMP threads (<= 0: runtime default)
  * Returns 0, or a negative code (-1 NaN operand, -2 allocation failure,
  * -3 bad argument). */
-int oracle_select(const void *q, const void *kv, int dtype, const float *kv_scales,
-                  const float *weights, const int32_t *ks, const int32_t *ke,
-                  int64_t num_q, int64_t num_kv, int topk, const int64_t *rows,
-                  int64_t nrows, int32_t *out_idx, float *out_val, double *out_score,
-                  double *all_scores, int nthreads)
+int oracle_select_h(const void *q, const void *kv, int dtype, int heads, const float *kv_scales,
+                    const float *weights, const int32_t *ks, const int32_t *ke,
+                    int64_t num_q, int64_t num_kv, int topk, const int64_t *rows,
+                    int64_t nrows, int32_t *out_idx, float *out_val, double *out_score,
+                    double *all_scores, int nthreads)
 {
-    if (topk < 1 || num_q < 0 || num_kv < 0 || nrows < 0) return -3;
+    if (topk < 1 || num_q < 0 || num_kv < 0 || nrows < 0 || heads < 1) return -3;
     if (dtype != ORACLE_FP8_E4M3 && dtype != ORACLE_BF16) return -3;
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t t = rows ? rows[r] : r;
@@ -250,13 +261,23 @@ int oracle_select(const void *q, const void *kv, int dtype, const float *kv_scal
             for (int64_t s = 0; s < num_kv; ++s) row_all[s] = NAN;
             if (ke[t] > ks[t]) row_all += ks[t];
         }
-        int st = select_row(q, dtype, kv_scales, weights, t, ks[t], ke[t], topk,
+        int st = select_row(q, dtype, heads, kv_scales, weights, t, ks[t], ke[t], topk,
                             kv_decoded, out_idx + r * topk, out_val + r * topk,
                             out_score ? out_score + r * topk : NULL, row_all);
         if (st < status) status = st;
     }
     free(kv_decoded);
     return status;
+}
+
+int oracle_select(const void *q, const void *kv, int dtype, const float *kv_scales,
+                  const float *weights, const int32_t *ks, const int32_t *ke,
+                  int64_t num_q, int64_t num_kv, int topk, const int64_t *rows,
+                  int64_t nrows, int32_t *out_idx, float *out_val, double *out_score,
+                  double *all_scores, int nthreads)
+{
+    return oracle_select_h(q, kv, dtype, ORACLE_HEADS, kv_scales, weights, ks, ke, num_q, num_kv, topk, rows,
+                           nrows, out_idx, out_val, out_score, all_scores, nthreads);
 }
 
 /* Exact top-k over materialized score rows (DeepSelect README, "Usage" and

@@ -77,14 +77,14 @@ def _normal(rng, shape):
 
 
 def gaussian(T, S, topk, dtype, seed, *, weight_scale=1.0, scales="uniform01",
-             windows="causal", docs=None, name=None):
+             windows="causal", docs=None, name=None, heads=HEADS):
     """q, kv ~ N(0,1); weights ~ N(0,1) * weight_scale; kv_scales per ``scales``.
 
     Draw order: q, kv, weights, kv_scales."""
     rng = np.random.default_rng(seed)
-    q = _quantize(_normal(rng, (T, HEADS, DIM)), dtype)
+    q = _quantize(_normal(rng, (T, heads, DIM)), dtype)
     kv = _quantize(_normal(rng, (S, DIM)), dtype)
-    w = (_normal(rng, (T, HEADS)) * np.float32(weight_scale)).astype(np.float32)
+    w = (_normal(rng, (T, heads)) * np.float32(weight_scale)).astype(np.float32)
     if scales == "ones":
         sc = None
     elif scales == "uniform01":
@@ -96,17 +96,17 @@ def gaussian(T, S, topk, dtype, seed, *, weight_scale=1.0, scales="uniform01",
                 name=name or f"gaussian_{dtype}_{T}x{S}_k{topk}")
 
 
-def integer(T, S, topk, dtype, seed, *, windows="causal", docs=None, name=None):
+def integer(T, S, topk, dtype, seed, *, windows="causal", docs=None, name=None, heads=HEADS):
     """Tie-heavy exact data: q, kv integers uniform in [-4, 4]; weights uniform in
     {+-1/4, +-1/2, +-1}; kv_scales uniform in {1/2, 1, 2}.  Every partial sum of
     the score is a multiple of 1/8 below 2^18, so binary32 arithmetic is exact.
 
     Draw order: q, kv, weights, kv_scales."""
     rng = np.random.default_rng(seed)
-    q = _quantize(rng.integers(-4, 5, size=(T, HEADS, DIM)).astype(np.float32), dtype)
+    q = _quantize(rng.integers(-4, 5, size=(T, heads, DIM)).astype(np.float32), dtype)
     kv = _quantize(rng.integers(-4, 5, size=(S, DIM)).astype(np.float32), dtype)
     wv = np.array([-1.0, -0.5, -0.25, 0.25, 0.5, 1.0], dtype=np.float32)
-    w = wv[rng.integers(0, 6, size=(T, HEADS))]
+    w = wv[rng.integers(0, 6, size=(T, heads))]
     sv = np.array([0.5, 1.0, 2.0], dtype=np.float32)
     sc = sv[rng.integers(0, 3, size=S)]
     ks, ke = _windows(T, S, windows, docs)
@@ -115,7 +115,7 @@ def integer(T, S, topk, dtype, seed, *, windows="causal", docs=None, name=None):
 
 
 def trained_shaped(T, S, topk, dtype, seed, *, heavy_frac=0.03, windows="causal", docs=None,
-                   name=None):
+                   name=None, heads=HEADS):
     """Heavy-tailed rows, shaped like a trained indexer.
 
     u = normalize(N(0, I_128)); per head c_h ~ U(0.5, 1.5) (shared by all
@@ -127,16 +127,16 @@ def trained_shaped(T, S, topk, dtype, seed, *, heavy_frac=0.03, windows="causal"
     rng = np.random.default_rng(seed)
     u = rng.standard_normal(DIM)
     u = (u / np.linalg.norm(u)).astype(np.float32)
-    c = rng.uniform(0.5, 1.5, size=HEADS).astype(np.float32)
+    c = rng.uniform(0.5, 1.5, size=heads).astype(np.float32)
     heavy = rng.random(S) < heavy_frac
     g = np.where(heavy, rng.normal(4.0, 1.0, size=S), rng.normal(0.0, 1.0, size=S)).astype(np.float32)
-    qf = c[None, :, None] * u[None, None, :] + np.float32(0.5) * _normal(rng, (T, HEADS, DIM))
+    qf = c[None, :, None] * u[None, None, :] + np.float32(0.5) * _normal(rng, (T, heads, DIM))
     q = _quantize(qf, dtype)
     del qf
     kf = g[:, None] * u[None, :] + np.float32(0.5) * _normal(rng, (S, DIM))
     kv = _quantize(kf, dtype)
     del kf
-    w = np.abs(_normal(rng, (T, HEADS))).astype(np.float32)
+    w = np.abs(_normal(rng, (T, heads))).astype(np.float32)
     sc = rng.uniform(0.5, 1.0, size=S).astype(np.float32)
     ks, ke = _windows(T, S, windows, docs)
     return dict(q=q, kv=kv, dtype=dtype, kv_scales=sc, weights=w, ks=ks, ke=ke, topk=int(topk),
