@@ -341,7 +341,7 @@ def main():
     kern = {k[3:]: float(np.mean(v)) for k, v in phases.items()}
     traffic = recorded_traffic() if (args.workload == 4 and not args.integer_twin and dt == "fp8") else None
     filt_ms = kern["filter"]
-    flops = float(FLOP_PER_PAIR) * pairs
+    flops = float(FLOP_PER_PAIR) * (wl["q"].shape[1] // 32) * pairs
     peak = PEAK_TFLOPS[dt]
     achieved = flops / (filt_ms * 1e-3) / 1e12 if filt_ms > 0 else 0.0
     whole = flops / (ms * 1e-3) / 1e12
@@ -359,7 +359,8 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": wl["name"], "num_q": T, "num_kv": S, "topk": topk, "heads": 32, "dim": 128,
+        "config": {"workload": wl["name"], "num_q": T, "num_kv": S, "topk": topk, "heads": int(wl["q"].shape[1]),
+                   "dim": 128,
                    "windows": "packed" if args.workload == 5 else "causal", "window_pairs": pairs,
                    "path": {0: "auto", 1: "scan", 2: "prune", 3: "recover"}[args.path],
                    "kv": f"paged, {args.paged} keys per page" if args.paged else "contiguous"},

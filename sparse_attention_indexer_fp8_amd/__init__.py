@@ -48,6 +48,7 @@ class Options(ctypes.Structure):
         ("recover_budget_bytes", ctypes.c_int64),
         ("profile", ctypes.c_int),
         ("out_flags", ctypes.c_int),
+        ("heads", ctypes.c_int),
     ]
 
 
@@ -169,12 +170,18 @@ def flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_va
     code = _dtype_code(q)
     if _dtype_code(kv) != code:
         raise TypeError("q and kv must have the same dtype")
-    if tuple(q.shape[1:]) != (HEADS, DIM) or tuple(kv.shape[1:]) != (DIM,):
-        raise ValueError("q must be [T, 32, 128] and kv [S, 128]")
+    heads = q.shape[1] if q.dim() == 3 else 0
+    if heads not in (32, 64) or q.shape[2] != DIM or tuple(kv.shape[1:]) != (DIM,):
+        raise ValueError("q must be [T, 32 or 64, 128] and kv [S, 128]")
     _check_dev("q", q)
     _check_dev("kv", kv)
     _check_dev("kv_scales", kv_scales, (torch.float32,), (S,))
-    _check_dev("weights", weights, (torch.float32,), (T, HEADS))
+    _check_dev("weights", weights, (torch.float32,), (T, heads))
+    if heads != HEADS or (options is not None and options.heads not in (0, heads)):
+        if options is not None and options.heads not in (0, heads):
+            raise ValueError(f"options.heads {options.heads} does not match q's {heads} heads")
+        options = Options() if options is None else Options.from_buffer_copy(options)
+        options.heads = heads
     _check_dev("ks", ks, (torch.int32,), (T,))
     _check_dev("ke", ke, (torch.int32,), (T,))
     _check_dev("out_idx", out_idx, (torch.int32, torch.int64), (T, topk))

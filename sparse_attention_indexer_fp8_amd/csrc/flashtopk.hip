@@ -134,6 +134,7 @@ struct Plan {
     int64_t recover_budget;
     int profile;
     int out_flags;
+    int heads;  // 32, or 64 (each row's halves are a pair of tile columns)
     // keys in a paged cache, read in place (calls with at most kFewRows rows)
     const int32_t *table = nullptr;
     int page_size = 0;
@@ -155,6 +156,8 @@ int resolve(Plan &p, const flashtopk_options *opt)
     while (p.sample_min_stride * 2 <= p.topk / 32) p.sample_min_stride *= 2;
     p.rank_scale = (opt && opt->sample_rank_scale > 0.0f) ? opt->sample_rank_scale : 1.0f;
     p.out_flags = opt ? opt->out_flags : 0;
+    p.heads = (opt && opt->heads) ? opt->heads : FLASHTOPK_HEADS;
+    if (p.heads != 32 && p.heads != 64) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (p.out_flags & ~(FLASHTOPK_OUT_INDEX_ORDER | FLASHTOPK_OUT_INT64)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
     p.profile = (opt && opt->profile) ? 1 : 0;
@@ -198,9 +201,15 @@ int sample_split(int ntiles)
 template <int DT>
 void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
 {
-    if (mode == kModeFilter) k_score<DT, kModeFilter><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
-    else if (mode == kModeSample) k_score<DT, kModeSample><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
-    else k_score<DT, kModeDense><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
+    if (a.pair) {
+        if (mode == kModeFilter) k_score<DT, kModeFilter, true><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
+        else if (mode == kModeSample) k_score<DT, kModeSample, true><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
+        else k_score<DT, kModeDense, true><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
+    } else {
+        if (mode == kModeFilter) k_score<DT, kModeFilter, false><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
+        else if (mode == kModeSample) k_score<DT, kModeSample, false><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
+        else k_score<DT, kModeDense, false><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
+    }
 }
 
 template <typename SH>
@@ -281,9 +290,12 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
     const bool recover_all = p.path == FLASHTOPK_PATH_RECOVER;
     const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
+    // 64 heads: row t's two 32-head halves are tile columns 2t and 2t + 1.
+    const int ps = p.heads == 64 ? 1 : 0;
+    const int64_t TC = T << ps;  // tile columns
     if (fp8) {
-        if ((st = ensure(*w, w->qbar, (size_t)T * kQbarParts * kDim))) return st;
-        if ((st = ensure(*w, w->qscale, sizeof(float) * T))) return st;
+        if ((st = ensure(*w, w->qbar, (size_t)TC * kQbarParts * kDim))) return st;
+        if ((st = ensure(*w, w->qscale, sizeof(float) * TC))) return st;
     }
     if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(S + 64)))) return st;
     if (!recover_all) {
@@ -291,12 +303,12 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * p.sample_target))) return st;
     }
 
-    const int ntiles = (int)((T + kTileQ - 1) / kTileQ);
+    const int ntiles = (int)((TC + kTileQ - 1) / kTileQ);
     // A few rows (decode) score with k_score_few, which has no bound pruning.
-    const bool few = T <= kFewRows;
+    const bool few = !ps && T <= kFewRows;
     // Score-bound pruning: on the auto path (each scan work item decides from
-    // its tile's planner sample) and the forced prune path.
-    const bool bounds = !few && S > 0 && (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE);
+    // its tile's planner sample) and the forced prune path; not for 64 heads.
+    const bool bounds = !few && !ps && S > 0 && (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE);
     const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
     if (bounds) {
         if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
@@ -315,8 +327,9 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     sa.w = weights;
     sa.ks = ks;
     sa.ke = ke;
-    sa.num_q = (int)T;
+    sa.num_q = (int)TC;
     sa.num_kv = (int)S;
+    sa.pair = ps;
     sa.qbar = (const uint8_t *)w->qbar.ptr;
     sa.qscale = (const float *)w->qscale.ptr;
     sa.ntiles = ntiles;
@@ -374,8 +387,8 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
                                                       kStCount);
     }
     if (fp8 && !few)
-        k_qbar<<<dim3((unsigned)((T + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, T,
-                                                                 (uint8_t *)w->qbar.ptr, (float *)w->qscale.ptr);
+        k_qbar<<<dim3((unsigned)((TC + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, TC,
+                                                                  (uint8_t *)w->qbar.ptr, (float *)w->qscale.ptr);
     if (!recover_all) {
         if (few)
             launch_few_dt(p.dtype, kModeSample,
@@ -456,7 +469,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             launch_few_dt(p.dtype, kModeDense,
                           dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream, sa);
         } else {
-            sa.ntiles = (int)(rcap / kTileQ);
+            sa.ntiles = (int)((rcap << ps) / kTileQ);
             sa.chunk = chunk_keys(sa.ntiles, S);
             const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
             launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
@@ -630,7 +643,7 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
     if (st) return st;
     if (num_kv == 0) return run(q, nullptr, nullptr, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
     const hipStream_t s = (hipStream_t)stream;
-    if (num_q <= kFewRows) {
+    if (num_q <= kFewRows && p.heads == 32) {
         // few rows read their keys from the pages directly
         p.table = block_table;
         p.page_size = page_size;

@@ -121,6 +121,12 @@ struct ScoreArgs {
     uint32_t *ticket;          // [num_q] self-resetting finish counters
     unsigned long long *stats; // call statistics, cleared by workgroup 0
     int nstats;
+    // 64-head indexers: row t's heads 0-31 and 32-63 are the tile columns 2t
+    // and 2t + 1 (q [num_q / 2, 64, 128] read as [num_q, 32, 128], weights
+    // likewise, num_q counting columns); the two columns' head sums are
+    // added before the threshold, and only even columns emit results, for
+    // row column / 2.
+    int pair;
     // few-row kernels over a paged key cache: kv and sigma are the page pools
     const int32_t *table;      // [ceil(num_kv / page_size)] page ids, or null (contiguous keys)
     int page_size;
@@ -391,7 +397,8 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
 
 // ---------------------------------------------------------------------------
 
-template <int DT, int MODE>
+// PAIR: 64-head rows, two tile columns each (see ScoreArgs::pair).
+template <int DT, int MODE, bool PAIR>
 __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(ScoreArgs a)
 {
     using Cfg = ScoreCfg<DT, MODE>;
@@ -408,6 +415,9 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     constexpr int RGB = (MODE == kModeFilter) ? kWaves * kTileQ * RS * 8 : 0;
     __shared__ __attribute__((aligned(16))) uint8_t smem[WB + QB + RGB];
     __shared__ int s_row[kTileQ], s_ks[kTileQ], s_ke[kTileQ], s_d[kTileQ];
+    // output row of each column (-1: none; with pair, odd columns), and its
+    // scratch slot in dense mode
+    __shared__ int s_out[PAIR ? kTileQ : 1], s_slot[PAIR ? kTileQ : 1];
     // Filter mode with pruning: offsets (from jlo) of the steps whose block
     // is not skipped, in order.
     constexpr int kMaxSteps = kMaxChunk / kStepKeys;
@@ -429,18 +439,22 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 
     if (threadIdx.x < kTileQ) {
         const int n = threadIdx.x;
-        int t = -1;
+        const int ps = PAIR ? 1 : 0;  // two columns per row
+        int t = -1, slot = -1;  // t: the column's q row (row, or 2 row + half)
         if (MODE == kModeDense) {
-            const int e = tile * kTileQ + n;
-            if (e < a.row_limit && (unsigned long long)(a.row_base + e) < *a.nrows) t = a.rowlist[a.row_base + e];
+            const int e = (tile * kTileQ + n) >> ps;
+            if (e < a.row_limit && (unsigned long long)(a.row_base + e) < *a.nrows) {
+                t = (a.rowlist[a.row_base + e] << ps) + (n & ps);
+                slot = e;
+            }
         } else {
             const int64_t tt = (int64_t)tile * kTileQ + n;
             if (tt < a.num_q) t = (int)tt;
         }
         int lo = 0, hi = 0, d = 1;
         if (t >= 0) {
-            lo = a.ks[t];
-            hi = a.ke[t];
+            lo = a.ks[t >> ps];
+            hi = a.ke[t >> ps];
             if (hi < lo) hi = lo;
         }
         if (MODE == kModeSample) {
@@ -455,7 +469,11 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         s_ks[n] = lo;
         s_ke[n] = hi;
         s_d[n] = d;
-        if (MODE == kModeFilter) s_tau[n] = t >= 0 ? a.tau[t] : __builtin_inff();
+        if (PAIR) {
+            s_out[n] = (t >= 0 && (n & 1) == 0) ? (t >> 1) : -1;
+            s_slot[n] = (n & 1) == 0 ? slot : -1;
+        }
+        if (MODE == kModeFilter) s_tau[n] = t >= 0 ? a.tau[t >> ps] : __builtin_inff();
         if (MODE == kModeFilter && a.prune) s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
         if (n < 2) s_pp[n] = 0ull;
     }
@@ -661,12 +679,13 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int t = s_row[n];
+    const int to = PAIR ? s_out[n] : t;  // the row this lane's results belong to, or -1
     const int rks = s_ks[n], rke = s_ke[n];
     const int S = a.num_kv;
     const float qsc = (DT == kFP8 && t >= 0) ? a.qscale[t] : 1.0f;
 
     float tau = __builtin_inff();
-    if (MODE == kModeFilter && t >= 0) tau = a.tau[t];
+    if (MODE == kModeFilter && to >= 0) tau = a.tau[to];
     const int dn = s_d[n];                       // power of two
     const int dsh = __builtin_ctz((unsigned)dn);
     const int first_n = ((rks + dn - 1) >> dsh) << dsh;
@@ -739,6 +758,15 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             if (!early) load_sh();
             next();
         });
+        if (PAIR) {
+            // a row's two columns are neighbouring lanes: add their head sums
+#pragma unroll
+            for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o.acc[kt][i] += __int_as_float(__builtin_amdgcn_update_dpp(
+                        0, __float_as_int(o.acc[kt][i]), 0xB1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false));
+        }
         if (MODE == kModeFilter) {
             // Keep (row, key) when the key is in the row's window and its
             // score reaches the row's threshold (take-all rows: -inf).
@@ -765,7 +793,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             uint32_t tot = c0 + c1 + c2 + c3;
             const uint32_t pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
             if (__builtin_expect(__any(ring_cnt + tot > (uint32_t)RING), 0)) {
-                ring_flush<RS>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
+                ring_flush<RS>(ring, ring_cnt, n, g, to, a.cnt, a.cand, a.cap);
                 ring_cnt = 0;
             }
             bool direct = false;
@@ -773,15 +801,15 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                 // More than a ring holds: reserve slots in the row's list directly.
                 uint32_t base = 0;
                 direct = tot > (uint32_t)RING;
-                if (direct && g == 0 && t >= 0) base = atomicAdd(a.cnt + t, tot);
+                if (direct && g == 0 && to >= 0) base = atomicAdd(a.cnt + to, tot);
                 base = __shfl(base, n);
                 uint32_t pos = base + pre;
-                if (direct && t >= 0) {
+                if (direct && to >= 0) {
 #pragma unroll
                     for (int b = 0; b < kSub * 4; ++b) {
                         if (sc[b] >= tau) {
                             if (pos < (uint32_t)a.cap)
-                                a.cand[(int64_t)t * a.cap + pos] = raw_cand(sc[b], sb + 16 * (b >> 2) + (b & 3));
+                                a.cand[(int64_t)to * a.cap + pos] = raw_cand(sc[b], sb + 16 * (b >> 2) + (b & 3));
                             ++pos;
                         }
                     }
@@ -802,13 +830,13 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             // The lane's 4 outputs of a subtile are consecutive lattice keys;
             // when the row samples on the tile's lattice they are consecutive
             // sample slots and go out as one 16-byte store.
-            uint32_t *srow = a.samp + (int64_t)(t < 0 ? 0 : t) * a.sample_target;
+            uint32_t *srow = a.samp + (int64_t)(to < 0 ? 0 : to) * a.sample_target;
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt) {
                 const int e0 = sb + 16 * kt;
                 const int p0 = first_b + e0 * dmin, p3 = p0 + 3 * dmin;
                 const int idx0 = (p0 - first_n) >> dsh;
-                if (t >= 0 && dn == dmin && e0 + 3 < nlat && p0 >= rks && p3 < rke && (idx0 & 3) == 0) {
+                if (to >= 0 && dn == dmin && e0 + 3 < nlat && p0 >= rks && p3 < rke && (idx0 & 3) == 0) {
                     v4i v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = (int)ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
@@ -817,7 +845,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int e = e0 + i;
-                        if (t < 0 || e >= nlat) continue;
+                        if (to < 0 || e >= nlat) continue;
                         const int p = first_b + e * dmin;
                         if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
                         srow[(p - first_n) >> dsh] = ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
@@ -825,13 +853,13 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                 }
             }
         } else {
-            const int slot = tile * kTileQ + n;
+            const int slot = PAIR ? s_slot[n] : (t >= 0 ? tile * kTileQ + n : -1);
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s = sb + 16 * kt + i;
-                    if (t < 0 || s < rks || s >= rke) continue;
+                    if (slot < 0 || s < rks || s >= rke) continue;
                     a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] =
                         raw_cand(score_of<DT>(o, kt, i, shv[kt][i]), s);
                 }
@@ -870,7 +898,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         }
     }
     if (MODE == kModeFilter) {
-        if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, t, a.cnt, a.cand, a.cap);
+        if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, to, a.cnt, a.cand, a.cap);
     }
 }
 

@@ -60,7 +60,7 @@ def test_header_constants_match_binding():
 
 def test_options_and_info_layout_match_header():
     # sizes of the C structs as laid out by the platform ABI
-    assert ctypes.sizeof(ftk.Options) == 32  # out_flags fills the old tail padding
+    assert ctypes.sizeof(ftk.Options) == 40
     assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4 + 6 * 4
 
 

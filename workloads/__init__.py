@@ -214,7 +214,7 @@ PACKED_DOCS = (8192, 16384, 24576, 16384)
 
 
 def config(n: int, *, integer_twin: bool = False):
-    """Named workloads 1..8 (integer twins for 3..5, 7, 8 with integer_twin=True)."""
+    """Named workloads 1..9 (integer twins for 3..5, 7, 8 with integer_twin=True)."""
     if integer_twin:
         if n == 3:
             return integer(4096, 131072, 4096, "fp8", 13, name="untrained_int_fp8_4096x131072_k4096")
@@ -250,6 +250,9 @@ def config(n: int, *, integer_twin: bool = False):
     if n == 8:
         # decode with a small batch / speculative tokens: 64 query rows
         return trained_shaped(64, 131072, 2048, "fp8", 8, name="decode_fp8_64x131072_k2048")
+    if n == 9:
+        # the headline chunk for a 64-head indexer (DeepSeek-V3.2's head count)
+        return trained_shaped(4096, 131072, 2048, "fp8", 9, heads=64, name="trained_h64_fp8_4096x131072_k2048")
     raise ValueError(n)
 
 
