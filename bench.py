@@ -339,6 +339,28 @@ def main():
         for k in phases:
             phases[k].append(pi[k])
     kern = {k[3:]: float(np.mean(v)) for k, v in phases.items()}
+
+    # Per-call device times (events around each call; the steps above run
+    # back to back, these one at a time), and one cold call after a 1 GiB
+    # scrub of the caches.
+    per = []
+    for _ in range(max(20, min(args.steps, 50))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scrub.fill_(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    step()
+    e1.record()
+    torch.cuda.synchronize()
+    cold_ms = e0.elapsed_time(e1)
+    del scrub
     traffic = recorded_traffic() if (args.workload == 4 and not args.integer_twin and dt == "fp8") else None
     filt_ms = kern["filter"]
     flops = float(FLOP_PER_PAIR) * (wl["q"].shape[1] // 32) * pairs
@@ -368,6 +390,9 @@ def main():
         "pct_mfma_peak": round(100.0 * whole / peak, 2),
         "dense_equiv_tflops": round(whole, 1),
         "wall_ms_per_step": round(wall_ms, 4),
+        "ms_per_call_median": round(float(np.median(per)), 4),
+        "ms_per_call_min": round(float(np.min(per)), 4),
+        "ms_cold_call": round(cold_ms, 4),
         "pruned_key_fraction": info["pruned_keys"] / max(1, info["window_keys"]),
         "path_taken": {1: "scan", 2: "prune", 3: "recover"}.get(info["path"], "?"),
         "rows_recovered": info["rows_recovered"],
