@@ -3,8 +3,10 @@
 // Launch sequence of one call, all on the caller's stream:
 //   0. k_keyprep        per-key scale factors (+ block extremes for the bound)
 //      k_qbar           (FP8) head-weighted query sums, split into FP8 parts
-//   1. k_score<sample>  strided-sample scores of every long row     (MFMA)
-//   2. k_tau            per-row threshold from the row's sample
+//   1. k_score<sample>  strided-sample scores of every long row     (MFMA);
+//                       with one workgroup per tile it also sets the
+//                       tile's per-row thresholds from those samples
+//   2. k_tau            (several workgroups per tile) the thresholds
 //   3. k_score<filter>  fused score (+ bound) + threshold filter -> candidates (MFMA, hot)
 //   4. k_triage         flag rows whose candidates under/overflowed
 //   5. k_select         exact top-k of every unflagged row
@@ -355,14 +357,17 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         sa.plan = (unsigned long long *)w->stats.ptr + kStPruned;
     }
 
-    // Few rows: the sample kernel clears the statistics and sets every row's
-    // threshold (no per-key pass, no separate threshold kernel).
+    // The sample kernel sets the thresholds itself when each row's samples
+    // come from one workgroup per tile, or (few rows) from the row's last
+    // workgroup to finish, which also clears the statistics (no per-key
+    // pass); otherwise k_tau follows it.
     const bool few_sample = few && !recover_all;
+    const bool fused_tau = !few && !recover_all && sa.sample_split == 1;
+    sa.topk = p.topk;
+    sa.rank_scale = p.rank_scale;
+    sa.tau_w = (float *)w->tau.ptr;
     if (few_sample) {
         if ((st = ensure_zeroed(*w, w->ticket, sizeof(uint32_t) * (size_t)T))) return st;
-        sa.topk = p.topk;
-        sa.rank_scale = p.rank_scale;
-        sa.tau_w = (float *)w->tau.ptr;
         sa.ticket = (uint32_t *)w->ticket.ptr;
         sa.stats = (unsigned long long *)w->stats.ptr;
         sa.nstats = kStCount;
@@ -398,7 +403,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
     mark(*w, p, 1, stream);
 
-    if (!recover_all && !few_sample) {
+    if (!recover_all && !few_sample && !fused_tau) {
         TauArgs ta{};
         ta.ks = ks;
         ta.ke = ke;
@@ -413,7 +418,6 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         ta.cnt = (uint32_t *)w->cnt.ptr;
         k_tau<<<dim3((unsigned)((T + kTauWaves - 1) / kTauWaves)), 64 * kTauWaves, 0, stream>>>(ta);
     }
-
     mark(*w, p, 2, stream);
 
     if (!recover_all) {

@@ -40,6 +40,7 @@
 #include "ftk_common.hpp"
 #include "ftk_frag.hpp"
 #include "ftk_qbar.hpp"
+#include "ftk_tau.hpp"
 
 namespace ftk {
 
@@ -113,12 +114,13 @@ struct ScoreArgs {
     int nblocks;
     float *vplan;              // [ntiles, kPlanGroups, 16 blocks, 16 rows] planner sample
     unsigned long long *plan;  // PlanCounter slots
-    // few-row sample mode (k_score_few): the threshold of each row is
-    // computed by the row's last workgroup to finish its samples
+    // sample mode: the threshold of each row is computed by the last
+    // workgroup to finish the samples of its row (k_score_few), or by the
+    // tile's workgroup when it is the only one (k_score, sample_split 1)
     int topk;
     float rank_scale;
-    float *tau_w;              // [num_q] written threshold
-    uint32_t *ticket;          // [num_q] self-resetting finish counters
+    float *tau_w;              // [rows] written threshold
+    uint32_t *ticket;          // [rows] self-resetting finish counters (k_score_few)
     unsigned long long *stats; // call statistics, cleared by workgroup 0
     int nstats;
     // 64-head indexers: row t's heads 0-31 and 32-63 are the tile columns 2t
@@ -260,6 +262,10 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     // The linear half first: the qbar parts (heads 32..34) accumulate in the
     // MFMA, and lin * qscale is folded into acc after the third head, so the
     // 16 lin registers are dead for the rest of the step.
+    // While its MFMAs issue the wave runs at raised priority: the matrix
+    // cores are the bound, so waves that feed them go before waves in their
+    // survivor sink (which has no MFMA), and the sink fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
     const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
     v4f lin[kSub];
     v8i qa = load_qfrag_fp8(pp), qb = load_qfrag_fp8(qp);
@@ -299,6 +305,7 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
         wp += 2 * kTileQ;
     }
     mfma_fp8_head(xb, kf, qa, z);  // head 31
+    __builtin_amdgcn_s_setprio(0);
     after_mfma();  // the key fragments are free from here on
     epi_abs(o.acc, xa, wp[0]);
     epi_abs(o.acc, xb, wp[kTileQ]);
@@ -397,6 +404,42 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
 
 // ---------------------------------------------------------------------------
 
+// Sample mode with one workgroup per tile (sample_split == 1), after the
+// workgroup's samples are written: it sets the threshold of each of the
+// tile's rows from the row's samples, one wave per row (wave_tau), and
+// resets the row's candidate counter.  The samples were written by this
+// workgroup's own waves, so workgroup-scope ordering is all it needs (an
+// agent-scope fence would write back and invalidate the L2 and cost more
+// than the thresholds).  hist: NW * kTauBuckets words of LDS that nothing
+// else uses any more.  Called by every thread of the workgroup.
+template <int NW, bool PAIR>
+__device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t *hist)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int R = PAIR ? kTileQ / 2 : kTileQ;  // rows per tile
+    const int64_t nrows = PAIR ? (int64_t)a.num_q >> 1 : (int64_t)a.num_q;
+    for (int rr = wave; rr < R; rr += NW) {
+        const int64_t t = (int64_t)tile * R + rr;
+        if (t >= nrows) break;
+        const int64_t lo = a.ks[t], hi = a.ke[t];
+        const int64_t len = hi > lo ? hi - lo : 0;
+        float tv = -__builtin_inff();
+        if (len > a.cap) {
+            const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
+            const int ns = (int)lattice_count(lo, hi, d);
+            tv = wave_tau(a.samp + t * a.sample_target, ns, tau_rank(a.topk, ns, len, a.rank_scale),
+                          hist + wave * kTauBuckets, lane);
+        }
+        if (lane == 0) {
+            a.tau_w[t] = tv;
+            a.cnt[t] = 0u;
+        }
+    }
+}
+
 // PAIR: 64-head rows, two tile columns each (see ScoreArgs::pair).
 template <int DT, int MODE, bool PAIR>
 __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(ScoreArgs a)
@@ -436,6 +479,14 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     // part of the tile's sample lattice (sample_split parts).
     const int chunk = blockIdx.x / a.ntiles;
     const int tile = blockIdx.x - chunk * a.ntiles;
+    // Sample mode: every workgroup, with or without work, ends here; with
+    // one workgroup per tile it sets the tile's thresholds (the q tile's LDS
+    // is free by then and holds the histograms).
+    static_assert(MODE != kModeSample || QB >= kWaves * kTauBuckets * 4, "histograms fit the q tile");
+    auto finish = [&]() {
+        if constexpr (MODE == kModeSample)
+            if (a.sample_split == 1) tile_tau<kWaves, PAIR>(a, tile, reinterpret_cast<uint32_t *>(s_q));
+    };
 
     if (threadIdx.x < kTileQ) {
         const int n = threadIdx.x;
@@ -498,7 +549,10 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     ilo = __builtin_amdgcn_readfirstlane(ilo);
     ihi = __builtin_amdgcn_readfirstlane(ihi);
     dmin = __builtin_amdgcn_readfirstlane(dmin);
-    if (hi <= lo) return;
+    if (hi <= lo) {
+        finish();
+        return;
+    }
 
     // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode the
     // steps index the lattice first_b + e * dmin, e < nlat.
@@ -513,7 +567,10 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         const int per = (nsteps + a.sample_split - 1) / a.sample_split;
         jlo = chunk * per;
         jhi = min(nsteps, jlo + per);
-        if (jhi <= jlo) return;
+        if (jhi <= jlo) {
+            finish();
+            return;
+        }
     } else {
         const int64_t c0 = (int64_t)chunk * a.chunk;
         const int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + a.chunk);
@@ -900,6 +957,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     if (MODE == kModeFilter) {
         if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, to, a.cnt, a.cand, a.cap);
     }
+    finish();
 }
 
 }  // namespace ftk

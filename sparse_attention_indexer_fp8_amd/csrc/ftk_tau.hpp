@@ -36,12 +36,14 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
     constexpr int PERL = 32;             // samples per lane per chunk
     constexpr int CHUNK = 64 * PERL;
     float v[PERL];
+    // Loads are unconditional (index clamped, n >= 1) so all of a chunk's
+    // loads are in flight before the first wait.
     auto load_chunk = [&](int base) {
+        uint32_t u[PERL];
 #pragma unroll
-        for (int q = 0; q < PERL; ++q) {
-            const int i = base + lane + 64 * q;
-            v[q] = i < n ? float_of_ord(samp[i]) : __builtin_nanf("");
-        }
+        for (int q = 0; q < PERL; ++q) u[q] = samp[min(base + lane + 64 * q, n - 1)];
+#pragma unroll
+        for (int q = 0; q < PERL; ++q) v[q] = base + lane + 64 * q < n ? float_of_ord(u[q]) : __builtin_nanf("");
     };
     float vmin = __builtin_inff(), vmax = -__builtin_inff();
     for (int base = 0; base < n; base += CHUNK) {
@@ -111,9 +113,11 @@ __device__ float block_tau(const uint32_t *samp, int n, uint32_t r, uint32_t *hi
     uint32_t c[PER];
     uint32_t hic = 0, nloc = 0;
 #pragma unroll
+    for (int j = 0; j < PER; ++j) c[j] = samp[min(tid + NT * j, max(n, 1) - 1)];  // all loads in flight
+#pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int i = tid + NT * j;
-        c[j] = i < n ? samp[i] : 0u;
+        if (i >= n) c[j] = 0u;
         if (i < n) {
             hic = max(hic, c[j]);
             nloc = max(nloc, ~c[j]);
@@ -180,7 +184,9 @@ struct TauArgs {
 };
 
 // One wave per row: resets the row's candidate counter and sets its
-// threshold (-inf for rows that take their whole window).
+// threshold (-inf for rows that take their whole window).  Used when the
+// sample scores of a tile come from several workgroups (with one, the
+// sample kernel sets the thresholds itself).
 constexpr int kTauWaves = 4;
 
 __global__ __launch_bounds__(64 * kTauWaves) void k_tau(TauArgs a)
