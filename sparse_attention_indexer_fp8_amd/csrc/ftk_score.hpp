@@ -53,11 +53,12 @@ constexpr int kModeDense = 2;
 template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? kHeads + kQbarParts : kHeads; };
 
 // Per-dtype launch shape.
-//   FP8: 12 waves per workgroup (3 per SIMD, up to 168 VGPRs each, enough to
-//   double-buffer the q fragments without spilling) so that while one wave
-//   waits on LDS or memory the others keep the matrix cores and vector ALUs
-//   busy; each wave loads its next step's keys as soon as its last MFMA of
-//   a step has issued.
+//   FP8: 16 waves per workgroup (4 per SIMD, up to 128 VGPRs each: the
+//   linear half accumulates with the row scale applied inside the MFMA, so
+//   its fold needs no extra registers) so that while one wave waits on LDS
+//   or memory the others keep the matrix cores and vector ALUs busy; each
+//   wave loads its next step's keys as soon as its last MFMA of a step has
+//   issued.  The candidate rings then fill the rest of the 160 KiB of LDS.
 //   BF16: the q tile takes 128 KiB of LDS and each wave's key fragments 64
 //   VGPRs, so 8 waves (2 per SIMD) with the next step's keys prefetched.
 // Candidate ring per (wave, query) in filter mode: survivors are staged in LDS
@@ -68,7 +69,7 @@ template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? k
 //   use the 8-wave prefetching shape for both dtypes.
 template <int DT, int MODE> struct ScoreCfg {
     static constexpr bool wide = DT == kFP8 && MODE == 0;  // 0: filter mode
-    static constexpr int waves = wide ? 12 : 8;
+    static constexpr int waves = wide ? 16 : 8;
     static constexpr int ring = DT == kFP8 ? 40 : 24;
     static constexpr bool prefetch = !wide;
 };
@@ -207,15 +208,6 @@ struct StepOut {
     float acc[kSub][4];   // FP8: qbar . k + sum_h w |x|;  BF16: sum_h w ReLU(x)
 };
 
-// First head of a step: acc = w |x| (no zeroing pass).
-__device__ __forceinline__ void epi_abs_first(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
-{
-#pragma unroll
-    for (int kt = 0; kt < kSub; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[kt][i] = w * __builtin_fabsf(x[kt][i]);
-}
-
 __device__ __forceinline__ void epi_abs(float (&acc)[kSub][4], const v4f (&x)[kSub], float w)
 {
 #pragma unroll
@@ -249,6 +241,24 @@ __device__ __forceinline__ void mfma_fp8_head(v4f (&x)[kSub], const KFrag<kFP8> 
         x[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt].a, qf, c[kt], 0, 0, 0, 0, 0, 0);
 }
 
+// The linear half: the qbar parts times the keys, scaled by the row's power
+// of two through the B operand's E8M0 scale (A unscaled: code 127).
+__device__ __forceinline__ void mfma_lin(v4f (&x)[kSub], const KFrag<kFP8> (&kf)[kSub], const v8i &qf,
+                                         const v4f (&c)[kSub], int sb)
+{
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+        x[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt].a, qf, c[kt], 0, 0, 0, 127, 0, sb);
+}
+
+__device__ __forceinline__ void epi_abs_lin(float (&acc)[kSub][4], const v4f (&x)[kSub], float w, const v4f (&lin)[kSub])
+{
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[kt][i] = __builtin_fmaf(w, __builtin_fabsf(x[kt][i]), lin[kt][i]);
+}
+
 template <typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[kSub], const uint8_t *s_q,
                                            const float *s_w, int lane, float qsc, AfterMfma after_mfma)
@@ -260,35 +270,32 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     // q fragments are double-buffered: the next head's fragment is read from
     // LDS while the MFMAs of the current one issue.
     // The linear half first: the qbar parts (heads 32..34) accumulate in the
-    // MFMA, and lin * qscale is folded into acc after the third head, so the
-    // 16 lin registers are dead for the rest of the step.
+    // MFMA with the row's power-of-two scale as the B operand's E8M0 block
+    // scale (A unscaled: code 127), so lin = qscale * (qbar . k) exactly, and
+    // it seeds acc in the first epilogue; the 16 lin registers are dead
+    // after the second head.
     // While its MFMAs issue the wave runs at raised priority: the matrix
     // cores are the bound, so waves that feed them go before waves in their
     // survivor sink (which has no MFMA), and the sink fills the gaps.
     __builtin_amdgcn_s_setprio(1);
     const uint8_t *pp = s_q + lane * 16 + kHeads * HB;
+    const int sb = (int)((__float_as_uint(qsc) >> 23) & 0xFFu);  // E8M0 code of qscale (a power of two)
     v4f lin[kSub];
-    v8i qa = load_qfrag_fp8(pp), qb = load_qfrag_fp8(qp);
-    mfma_fp8_head(lin, kf, qa, z);
-    qa = load_qfrag_fp8(pp + HB);
-    // Two result sets alternate: the epilogue of head h-1 runs while the
-    // MFMAs of head h execute.  The first epilogue initialises acc.
+    v8i qa = load_qfrag_fp8(pp), qb = load_qfrag_fp8(pp + HB);
+    mfma_lin(lin, kf, qa, z, sb);           // part 0
+    qa = load_qfrag_fp8(qp);
+    mfma_lin(lin, kf, qb, lin, sb);         // part 1
+    qb = load_qfrag_fp8(pp + 2 * HB);
     v4f xa[kSub], xb[kSub];
-    mfma_fp8_head(xa, kf, qb, z);  // head 0
-    qb = load_qfrag_fp8(qp + HB);
-    mfma_fp8_head(lin, kf, qa, lin);
-    qa = load_qfrag_fp8(pp + 2 * HB);
-    mfma_fp8_head(xb, kf, qb, z);  // head 1
+    mfma_fp8_head(xa, kf, qa, z);  // head 0
+    qa = load_qfrag_fp8(qp + HB);
+    mfma_lin(lin, kf, qb, lin, sb);         // part 2
     qb = load_qfrag_fp8(qp + 2 * HB);
-    epi_abs_first(o.acc, xa, wp[0]);
-    mfma_fp8_head(lin, kf, qa, lin);
+    mfma_fp8_head(xb, kf, qa, z);  // head 1
+    epi_abs_lin(o.acc, xa, wp[0], lin);
     qa = load_qfrag_fp8(qp + 3 * HB);
     mfma_fp8_head(xa, kf, qb, z);  // head 2
     epi_abs(o.acc, xb, wp[kTileQ]);
-#pragma unroll
-    for (int kt = 0; kt < kSub; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.acc[kt][i] = __builtin_fmaf(lin[kt][i], qsc, o.acc[kt][i]);
     qp += 2 * HB;
     wp += 2 * kTileQ;
     // Loop invariant: qa holds head h's fragment, xa head h-1's results.
@@ -303,6 +310,21 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
         epi_abs(o.acc, xb, w1);            // head h
         qp += 2 * HB;
         wp += 2 * kTileQ;
+        // Issue order: one MFMA, then four epilogue FMAs, so each wave keeps
+        // the matrix core fed while its vector work fills the gaps; the LDS
+        // reads of the next fragments go out early.
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
     }
     mfma_fp8_head(xb, kf, qa, z);  // head 31
     __builtin_amdgcn_s_setprio(0);
