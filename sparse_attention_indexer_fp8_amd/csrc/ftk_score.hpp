@@ -368,6 +368,7 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[
     const uint8_t *qp = s_q + lane * 16;
     const float *wp = s_w + (lane & 15);
     v4f xa[kSub], xb[kSub];
+    __builtin_amdgcn_s_setprio(1);  // as on the FP8 path
     mfma_bf16_head(xa, kf, qp);
 #pragma unroll 1
     for (int h = 1; h < kHeads - 1; h += 2) {
@@ -378,8 +379,20 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[
         epi_relu(o.acc, xb, w1);
         qp += 2 * HB;
         wp += 2 * kTileQ;
+        // Issue order: one MFMA, then two epilogue instructions (max, fma);
+        // each head's four LDS reads go out first.
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+        }
     }
     mfma_bf16_head(xb, kf, qp + HB);
+    __builtin_amdgcn_s_setprio(0);
     after_mfma();
     epi_relu(o.acc, xa, wp[0]);
     epi_relu(o.acc, xb, wp[kTileQ]);
