@@ -1,8 +1,9 @@
 // C ABI of the fused indexer top-k library (declared in include/flashtopk.h).
 //
 // Launch sequence of one call, all on the caller's stream:
-//   0. k_keyprep        per-key scale factors (+ block extremes for the bound)
-//      k_qbar           (FP8) head-weighted query sums, split into FP8 parts
+//   0. k_prep           per-key scale factors (+ block extremes for the bound)
+//                       and (FP8) head-weighted query sums split into FP8
+//                       parts, in one launch
 //   1. k_score<sample>  strided-sample scores of every long row     (MFMA);
 //                       with one workgroup per tile it also sets the
 //                       tile's per-row thresholds from those samples
@@ -374,26 +375,39 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     }
 
     mark(*w, p, 0, stream);
-    if (!few_sample) {
+    {
         // Per-key scale factors (and block extremes for the bound); with few
-        // rows only the statistics are cleared (k_score_few reads sigma).
+        // rows only the statistics are cleared (k_score_few reads sigma), and
+        // those calls' sample kernel does even that.  FP8 calls of more rows
+        // also get their query sums from the same launch.
+        PrepArgs pa{};
         const int64_t Sp = few ? 0 : S;
-        const unsigned nwg = (unsigned)((Sp + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
-        uint8_t *kbp = bounds ? (uint8_t *)w->kb.ptr : nullptr;
-        float2 *kmp = bounds ? (float2 *)w->kmeta.ptr : nullptr;
-        unsigned long long *stp = (unsigned long long *)w->stats.ptr;
-        if (fp8)
-            k_keyprep<kFP8><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)Sp, nblocks,
-                                                     (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
-                                                     kStCount);
-        else
-            k_keyprep<kBF16><<<nwg, 256, 0, stream>>>((const uint8_t *)kv, kv_scales, (int)Sp, nblocks,
-                                                      (float *)w->sigh.ptr, bounds ? 1 : 0, kbp, kmp, stp,
-                                                      kStCount);
+        pa.key_blocks = few_sample ? 0 : (int)((Sp + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
+        pa.kv = (const uint8_t *)kv;
+        pa.sigma = kv_scales;
+        pa.num_kv = (int)Sp;
+        pa.nblocks = nblocks;
+        pa.sigh = (float *)w->sigh.ptr;
+        pa.bounds = bounds ? 1 : 0;
+        pa.kb = bounds ? (uint8_t *)w->kb.ptr : nullptr;
+        pa.meta = bounds ? (float2 *)w->kmeta.ptr : nullptr;
+        pa.stats = (unsigned long long *)w->stats.ptr;
+        pa.nstats = kStCount;
+        int64_t qblocks = 0;
+        if (fp8 && !few) {
+            pa.q = (const uint8_t *)q;
+            pa.w = weights;
+            pa.num_q = TC;
+            pa.parts = (uint8_t *)w->qbar.ptr;
+            pa.qscale = (float *)w->qscale.ptr;
+            qblocks = (TC + 3) / 4;
+        }
+        const unsigned nwg = (unsigned)(pa.key_blocks + qblocks);
+        if (nwg > 0) {
+            if (fp8) k_prep<kFP8><<<nwg, 256, 0, stream>>>(pa);
+            else k_prep<kBF16><<<nwg, 256, 0, stream>>>(pa);
+        }
     }
-    if (fp8 && !few)
-        k_qbar<<<dim3((unsigned)((TC + 3) / 4)), 256, 0, stream>>>((const uint8_t *)q, weights, TC,
-                                                                  (uint8_t *)w->qbar.ptr, (float *)w->qscale.ptr);
     if (!recover_all) {
         if (few)
             launch_few_dt(p.dtype, kModeSample,

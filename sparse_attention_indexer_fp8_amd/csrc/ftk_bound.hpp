@@ -80,18 +80,18 @@ __device__ __forceinline__ uint32_t ord_code(int v)
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_keyprep(const uint8_t *kv, const float *sigma, int num_kv, int nblocks,
-                                                 float *sigh, int bounds, uint8_t *kb, float2 *meta,
-                                                 unsigned long long *stats, int nstats)
+__device__ __forceinline__ void keyprep_blocks(const uint8_t *kv, const float *sigma, int num_kv, int nblocks,
+                                               float *sigh, int bounds, uint8_t *kb, float2 *meta,
+                                               unsigned long long *stats, int nstats, int blk)
 {
     constexpr int RB = RowBytes<DT>::value;
     constexpr int EPL = DT == kFP8 ? 16 : 8;     // elements per 16-byte load
     constexpr int LPR = kDim / EPL;               // lanes per key row
     constexpr int KPL = 64 / LPR;                 // key rows per load instruction
     constexpr int NLD = kBlockKeys / KPL;         // loads per lane
-    if (blockIdx.x == 0 && (int)threadIdx.x < nstats) stats[threadIdx.x] = 0ull;
+    if (blk == 0 && (int)threadIdx.x < nstats) stats[threadIdx.x] = 0ull;
     const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int b = blk * 4 + (threadIdx.x >> 6);
     const int p0 = b * kBlockKeys;
     if (p0 >= num_kv + 64) return;
     const int p = p0 + lane;
@@ -165,6 +165,40 @@ __global__ __launch_bounds__(256) void k_keyprep(const uint8_t *kv, const float 
         const float ka = DT == kFP8 ? e4m3_to_f32((uint32_t)am) : __uint_as_float((uint32_t)am << 16);
         meta[b] = make_float2(bad ? __builtin_nanf("") : smax, ka);
     }
+}
+
+// The call's two independent prologue passes in one launch: workgroups
+// [0, key_blocks) run the per-key pass (4 blocks of 64 keys each), the rest
+// the FP8 query sums (4 rows each, qbar_rows).  Both are short and
+// latency-bound, so sharing a launch overlaps them and saves a kernel
+// boundary.
+struct PrepArgs {
+    const uint8_t *kv;
+    const float *sigma;
+    int num_kv;
+    int nblocks;
+    float *sigh;
+    int bounds;
+    uint8_t *kb;
+    float2 *meta;
+    unsigned long long *stats;
+    int nstats;
+    int key_blocks;            // workgroups of the per-key pass
+    const uint8_t *q;          // FP8 query sums (q null: none)
+    const float *w;
+    int64_t num_q;
+    uint8_t *parts;
+    float *qscale;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a)
+{
+    if ((int)blockIdx.x < a.key_blocks)
+        keyprep_blocks<DT>(a.kv, a.sigma, a.num_kv, a.nblocks, a.sigh, a.bounds, a.kb, a.meta, a.stats, a.nstats,
+                           (int)blockIdx.x);
+    else if (DT == kFP8)
+        qbar_rows(a.q, a.w, a.num_q, a.parts, a.qscale, (int64_t)blockIdx.x - a.key_blocks);
 }
 
 // ---------------------------------------------------------------------------

@@ -42,13 +42,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_trunc(float v)
     return s | ((uint32_t)(E + 7) << 3) | ((b >> 20) & 7u);  // normal: top 3 mantissa bits
 }
 
-// One wave per query row; lane l owns dimensions 2l and 2l+1.  Writes
-// parts[t][p][d] (E4M3 codes) and qscale[t] = 2^-e.
-__global__ __launch_bounds__(256) void k_qbar(const uint8_t *q, const float *w, int64_t num_q, uint8_t *parts,
-                                              float *qscale)
+// Rows 4 blk .. 4 blk + 3, one wave per query row (a 256-thread
+// workgroup); lane l owns dimensions 2l and 2l+1.  Writes parts[t][p][d]
+// (E4M3 codes) and qscale[t] = 2^-e.  Run by k_prep.
+__device__ __forceinline__ void qbar_rows(const uint8_t *q, const float *w, int64_t num_q, uint8_t *parts,
+                                          float *qscale, int64_t blk)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = blk * 4 + (threadIdx.x >> 6);
     if (t >= num_q) return;
     const uint8_t *qr = q + t * kHeads * kDim + 2 * lane;
     uint32_t c[kHeads];
