@@ -400,6 +400,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             pa.num_q = TC;
             pa.parts = (uint8_t *)w->qbar.ptr;
             pa.qscale = (float *)w->qscale.ptr;
+            pa.q1 = bounds ? (float *)w->q1.ptr : nullptr;
             qblocks = (TC + 3) / 4;
         }
         const unsigned nwg = (unsigned)(pa.key_blocks + qblocks);

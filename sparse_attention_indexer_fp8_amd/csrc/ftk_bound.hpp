@@ -189,6 +189,7 @@ struct PrepArgs {
     int64_t num_q;
     uint8_t *parts;
     float *qscale;
+    float *q1;                 // Q1 per row (score-bound paths) or null
 };
 
 template <int DT>
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a)
         keyprep_blocks<DT>(a.kv, a.sigma, a.num_kv, a.nblocks, a.sigh, a.bounds, a.kb, a.meta, a.stats, a.nstats,
                            (int)blockIdx.x);
     else if (DT == kFP8)
-        qbar_rows(a.q, a.w, a.num_q, a.parts, a.qscale, (int64_t)blockIdx.x - a.key_blocks);
+        qbar_rows(a.q, a.w, a.num_q, a.parts, a.qscale, a.q1, (int64_t)blockIdx.x - a.key_blocks);
 }
 
 // ---------------------------------------------------------------------------
@@ -256,7 +257,9 @@ __device__ __forceinline__ v4f mfma_ub(const KFrag<kBF16> &kx, const KFrag<kBF16
     return x;
 }
 
-template <int DT>
+// UNR heads are unrolled (their LDS reads and MFMA chains overlap): many
+// where registers are plentiful (the sample kernel), few in the scan.
+template <int DT, int UNR = 2>
 __device__ __forceinline__ v4f bound_group(const uint8_t *kb, int nblocks, int c, const uint8_t *qp, int HB,
                                            const float *s_w, int lane)
 {
@@ -266,7 +269,7 @@ __device__ __forceinline__ v4f bound_group(const uint8_t *kb, int nblocks, int c
     load_kfrag(kx, kb, 2 * bb, g);
     load_kfrag(kn, kb, 2 * bb + 1, g);
     v4f u = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
+#pragma unroll UNR
     for (int h = 0; h < kHeads; ++h) {
         BFrag<DT> qf, qpos, qneg;
         load_bfrag(qf, qp + h * HB);

@@ -44,9 +44,11 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_trunc(float v)
 
 // Rows 4 blk .. 4 blk + 3, one wave per query row (a 256-thread
 // workgroup); lane l owns dimensions 2l and 2l+1.  Writes parts[t][p][d]
-// (E4M3 codes) and qscale[t] = 2^-e.  Run by k_prep.
+// (E4M3 codes) and qscale[t] = 2^-e, and with q1 non-null
+// q1[t] = sum_h |w[t,h]| ||q[t,h,:]||_1 (the score bound's rounding margin).
+// Run by k_prep.
 __device__ __forceinline__ void qbar_rows(const uint8_t *q, const float *w, int64_t num_q, uint8_t *parts,
-                                          float *qscale, int64_t blk)
+                                          float *qscale, float *q1, int64_t blk)
 {
     const int lane = threadIdx.x & 63;
     const int64_t t = blk * 4 + (threadIdx.x >> 6);
@@ -59,11 +61,17 @@ __device__ __forceinline__ void qbar_rows(const uint8_t *q, const float *w, int6
         c[h] = *reinterpret_cast<const uint16_t *>(qr + h * kDim);
         wv[h] = w[t * kHeads + h];
     }
-    float v0 = 0.0f, v1 = 0.0f;
+    float v0 = 0.0f, v1 = 0.0f, l1 = 0.0f;
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) {
-        v0 = __builtin_fmaf(wv[h], e4m3_to_f32(c[h] & 0xFFu), v0);
-        v1 = __builtin_fmaf(wv[h], e4m3_to_f32(c[h] >> 8), v1);
+        const float d0 = e4m3_to_f32(c[h] & 0xFFu), d1 = e4m3_to_f32(c[h] >> 8);
+        v0 = __builtin_fmaf(wv[h], d0, v0);
+        v1 = __builtin_fmaf(wv[h], d1, v1);
+        l1 = __builtin_fmaf(fabsf(wv[h]), fabsf(d0) + fabsf(d1), l1);
+    }
+    if (q1) {
+        for (int off = 32; off > 0; off >>= 1) l1 += __shfl_xor(l1, off);
+        if (lane == 0) q1[t] = l1;
     }
     float m = fmaxf(fabsf(v0), fabsf(v1));
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));

@@ -455,24 +455,36 @@ __device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int R = PAIR ? kTileQ / 2 : kTileQ;  // rows per tile
+    constexpr int K = (R + NW - 1) / NW;           // rows per wave, computed together
     const int64_t nrows = PAIR ? (int64_t)a.num_q >> 1 : (int64_t)a.num_q;
-    for (int rr = wave; rr < R; rr += NW) {
-        const int64_t t = (int64_t)tile * R + rr;
-        if (t >= nrows) break;
-        const int64_t lo = a.ks[t], hi = a.ke[t];
-        const int64_t len = hi > lo ? hi - lo : 0;
-        float tv = -__builtin_inff();
-        if (len > a.cap) {
-            const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
-            const int ns = (int)lattice_count(lo, hi, d);
-            tv = wave_tau(a.samp + t * a.sample_target, ns, tau_rank(a.topk, ns, len, a.rank_scale),
-                          hist + wave * kTauBuckets, lane);
+    const uint32_t *sp[K];
+    int ns[K];
+    uint32_t rk[K];
+    int64_t tt[K];
+    bool sampled[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t t = (int64_t)tile * R + wave + k * NW;
+        tt[k] = t < nrows && wave + k * NW < R ? t : -1;
+        int64_t lo = 0, hi = 0;
+        if (tt[k] >= 0) {
+            lo = a.ks[t];
+            hi = max((int64_t)a.ke[t], lo);
         }
-        if (lane == 0) {
-            a.tau_w[t] = tv;
-            a.cnt[t] = 0u;
-        }
+        sampled[k] = hi - lo > a.cap;  // else: take the whole window
+        const int d = sampled[k] ? sample_stride(hi - lo, a.sample_target, a.sample_min_stride) : 1;
+        ns[k] = sampled[k] ? (int)lattice_count(lo, hi, d) : 1;
+        rk[k] = sampled[k] ? tau_rank(a.topk, ns[k], hi - lo, a.rank_scale) : 1u;
+        sp[k] = a.samp + (sampled[k] ? tt[k] : 0) * a.sample_target;
     }
+    float tv[K];
+    wave_tau_rows<K>(sp, ns, rk, hist + wave * kTauBuckets, lane, tv);
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if (lane == 0 && tt[k] >= 0) {
+            a.tau_w[tt[k]] = sampled[k] ? tv[k] : -__builtin_inff();
+            a.cnt[tt[k]] = 0u;
+        }
 }
 
 // PAIR: 64-head rows, two tile columns each (see ScoreArgs::pair).
@@ -560,7 +572,10 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             s_slot[n] = (n & 1) == 0 ? slot : -1;
         }
         if (MODE == kModeFilter) s_tau[n] = t >= 0 ? a.tau[t >> ps] : __builtin_inff();
-        if (MODE == kModeFilter && a.prune) s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
+        // Q1 of the FP8 rows comes from the query-sum pass; BF16 sampling
+        // computes it below.
+        if ((MODE == kModeFilter || (MODE == kModeSample && DT == kFP8)) && a.prune)
+            s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
         if (n < 2) s_pp[n] = 0ull;
     }
     __syncthreads();
@@ -624,7 +639,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 
     int nstep = jhi - jlo;
     bool use_skip = false;  // workgroup-uniform
-    if (MODE == kModeSample && a.prune) {
+    if (MODE == kModeSample && DT == kBF16 && a.prune) {
         // Q1[t] = sum_h |w[t,h]| ||q[t,h,:]||_1 of the sampled rows (the
         // bound's rounding margin), from the q tile in LDS: one (row, head)
         // per thread, then one thread per row.
@@ -677,7 +692,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         }
         const int g0 = ulo / (16 * kBlockKeys), g1 = (uhi + 16 * kBlockKeys - 1) / (16 * kBlockKeys);
         const int gs = g0 + ((2 * wv + 1) * (g1 - g0)) / (2 * kPlanGroups);
-        const v4f u = bound_group<DT>(a.kb, a.nblocks, gs, s_q + ln * 16, 16 * RB, s_w, ln);
+        const v4f u = bound_group<DT, 8>(a.kb, a.nblocks, gs, s_q + ln * 16, 16 * RB, s_w, ln);
         const bool sampled = s_row[n] >= 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

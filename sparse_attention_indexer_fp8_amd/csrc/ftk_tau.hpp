@@ -101,6 +101,86 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
     return vmax - (float)(b + 2) / scale;
 }
 
+// wave_tau for K rows, each of n[k] <= 2048 samples: the same buckets and
+// rule, with the K rows' sample loads and range reductions interleaved so
+// their latencies overlap; the histogram passes then take the rows in turn.
+// hist: kTauBuckets words of LDS private to the wave.  Every lane gets the
+// K thresholds.
+template <int K>
+__device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], const int (&n)[K],
+                                              const uint32_t (&r)[K], uint32_t *hist, int lane, float (&tv)[K])
+{
+    constexpr int PER = kTauBuckets / 64;  // buckets per lane, and samples per lane
+    float v[K][PER];
+    {
+        uint32_t u[K][PER];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int q = 0; q < PER; ++q) u[k][q] = samp[k][min(lane + 64 * q, n[k] - 1)];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int q = 0; q < PER; ++q) v[k][q] = lane + 64 * q < n[k] ? float_of_ord(u[k][q]) : __builtin_nanf("");
+    }
+    float vmin[K], vmax[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        vmin[k] = __builtin_inff();
+        vmax[k] = -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {  // fminf / fmaxf ignore the NaN fill
+            vmin[k] = fminf(vmin[k], v[k][q]);
+            vmax[k] = fmaxf(vmax[k], v[k][q]);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            vmin[k] = fminf(vmin[k], __shfl_xor(vmin[k], off));
+            vmax[k] = fmaxf(vmax[k], __shfl_xor(vmax[k], off));
+        }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float scale = (float)kTauBuckets / (vmax[k] - vmin[k]);
+        if (!(vmax[k] > vmin[k]) || !__builtin_isfinite(scale)) {  // all samples equal: admit them all
+            tv[k] = vmin[k];
+            continue;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) hist[lane + 64 * q] = 0u;
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land before any lane adds
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (lane + 64 * q < n[k]) {
+                const float x = (vmax[k] - v[k][q]) * scale;
+                atomicAdd(&hist[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        // Lane l owns buckets [PER l, PER l + PER); exclusive prefix over lanes.
+        uint32_t c[PER], run = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            c[q] = hist[lane * PER + q];
+            run += c[q];
+        }
+        uint32_t base = wave_incl_add(run) - run;
+        int b = -1;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (base < r[k] && r[k] <= base + c[q]) b = lane * PER + q;
+            base += c[q];
+        }
+        const uint64_t hit = __ballot(b >= 0);
+        b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
+        tv[k] = vmax[k] - (float)(b + 2) / scale;
+        __builtin_amdgcn_wave_barrier();  // every lane has read the counts before the next row clears them
+    }
+}
+
 // The same threshold computed by a whole workgroup of NT threads from n <=
 // kTauBuckets sample codes (at most kTauBuckets / NT per thread): the same
 // buckets and rule as wave_tau.  hist is kTauBuckets words of LDS, red 3 *
