@@ -359,7 +359,7 @@ __device__ __forceinline__ void *out_row(void *base, int64_t r, int topk, int fl
 // Candidate mode: rows that triage flags (same predicate) are left to dense
 // recovery; every other row's candidates hold its whole top k.
 template <typename SH>
-__global__ __launch_bounds__(SH::nt) void k_select(SelectArgs a)
+__global__ __launch_bounds__(SH::nt, SH::nt == 1024 ? 8 : 1) void k_select(SelectArgs a)
 {
     constexpr int NREG = SH::nreg, NT = SH::nt, NBKT = SH::nbkt, MAXK = SH::maxk;
     constexpr bool DENSE = NREG == 0;
@@ -488,34 +488,40 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
             __syncthreads();
             // Bucket b now spans [bucket[b-1], bucket[b]).
             if constexpr (!DENSE) {
-                // Place of each key: the bucket start plus the number of
-                // larger keys in the bucket (keys are distinct), computed
-                // for all keys before any key moves.
-                uint32_t place[NREG > 0 ? NREG : 1];
-                el.each_slot([&](int q, uint64_t r, bool v) {
-                    uint32_t pl = 0xFFFFFFFFu;
-                    if (v) {
-                        const uint32_t b = bucket_of(raw_score(r));
-                        if (b <= kb) {
-                            const uint64_t e = key_of_raw(r);
-                            const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
-                            // four independent LDS reads per step: buckets of
-                            // tied scores (BF16 inputs) hold dozens of keys
-                            uint32_t rank = 0, j = s0;
-                            for (; j + 4 <= s1; j += 4) {
-                                const uint64_t k0 = S.sel[j], k1 = S.sel[j + 1], k2 = S.sel[j + 2], k3 = S.sel[j + 3];
-                                rank += (k0 > e ? 1u : 0u) + (k1 > e ? 1u : 0u) + (k2 > e ? 1u : 0u) + (k3 > e ? 1u : 0u);
-                            }
-                            for (; j < s1; ++j) rank += S.sel[j] > e ? 1u : 0u;
-                            pl = s0 + rank;
+                // Place of each gathered key: the bucket start plus the
+                // number of larger keys in the bucket (keys are distinct),
+                // computed for all keys before any key moves.  The keys are
+                // visited by their position in S.sel (bucket kb ends at
+                // S.bucket[kb]), so the candidate registers are dead here.
+                constexpr int PE = (MAXK + kSegMax + NT - 1) / NT;  // gathered keys per thread
+                const uint32_t tot = S.bucket[kb];
+                uint32_t place[PE];
+                uint64_t key[PE];
+#pragma unroll
+                for (int m = 0; m < PE; ++m) {
+                    const uint32_t jj = tid + m * NT;
+                    place[m] = 0xFFFFFFFFu;
+                    key[m] = 0;
+                    if (jj < tot) {
+                        const uint64_t e = S.sel[jj];
+                        const uint32_t b = bucket_of(key_score(e));
+                        const uint32_t s0 = b ? S.bucket[b - 1] : 0u, s1 = S.bucket[b];
+                        // four independent LDS reads per step: buckets of
+                        // tied scores (BF16 inputs) hold dozens of keys
+                        uint32_t rank = 0, j = s0;
+                        for (; j + 4 <= s1; j += 4) {
+                            const uint64_t k0 = S.sel[j], k1 = S.sel[j + 1], k2 = S.sel[j + 2], k3 = S.sel[j + 3];
+                            rank += (k0 > e ? 1u : 0u) + (k1 > e ? 1u : 0u) + (k2 > e ? 1u : 0u) + (k3 > e ? 1u : 0u);
                         }
+                        for (; j < s1; ++j) rank += S.sel[j] > e ? 1u : 0u;
+                        place[m] = s0 + rank;
+                        key[m] = e;
                     }
-                    place[q] = pl;
-                });
+                }
                 __syncthreads();
-                el.each_slot([&](int q, uint64_t r, bool v) {
-                    if (v && place[q] != 0xFFFFFFFFu) S.sel[place[q]] = key_of_raw(r);
-                });
+#pragma unroll
+                for (int m = 0; m < PE; ++m)
+                    if (place[m] != 0xFFFFFFFFu) S.sel[place[m]] = key[m];
             } else {
                 // Streamed rows (recovery): insertion sort of each bucket.
                 for (uint32_t b = tid; b <= kb; b += NT) {
