@@ -280,7 +280,7 @@ template <typename T, typename SH, int U>
 __device__ __forceinline__ void scan_any(RowsLds<SH> &L, const v4i (&raw)[U], int64_t g0, int64_t n, float tau,
                                          bool &nan)
 {
-    if (n - g0 >= (int64_t)SH::nt * U * (16 / sizeof(T))) scan_group<T, SH, U, false>(L, raw, g0, n, tau, nan);
+    if (n - g0 >= (int64_t)(SH::nt * U * (16 / sizeof(T)))) scan_group<T, SH, U, false>(L, raw, g0, n, tau, nan);
     else scan_group<T, SH, U, true>(L, raw, g0, n, tau, nan);
 }
 

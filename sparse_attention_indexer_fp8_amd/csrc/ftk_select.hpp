@@ -405,7 +405,6 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
 {
     constexpr int NW = NT / 64, BPT = NBKT / NT;
     constexpr bool DENSE = !E::REG;
-    constexpr int NREG = E::kRegPer;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     bool fast = false;
     float mx = 0.0f, scale = 0.0f;
