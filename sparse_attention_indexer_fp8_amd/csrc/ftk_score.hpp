@@ -448,7 +448,8 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
 // than the thresholds).  hist: NW * kTauBuckets words of LDS that nothing
 // else uses any more.  Called by every thread of the workgroup.
 template <int NW, bool PAIR>
-__device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t *hist)
+__device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t *hist, const int *s_row, const int *s_ks,
+                                         const int *s_ke, const int *s_nl)
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
@@ -464,17 +465,14 @@ __device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t 
     bool sampled[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int64_t t = (int64_t)tile * R + wave + k * NW;
-        tt[k] = t < nrows && wave + k * NW < R ? t : -1;
-        int64_t lo = 0, hi = 0;
-        if (tt[k] >= 0) {
-            lo = a.ks[t];
-            hi = max((int64_t)a.ke[t], lo);
-        }
-        sampled[k] = hi - lo > a.cap;  // else: take the whole window
-        const int d = sampled[k] ? sample_stride(hi - lo, a.sample_target, a.sample_min_stride) : 1;
-        ns[k] = sampled[k] ? (int)lattice_count(lo, hi, d) : 1;
-        rk[k] = sampled[k] ? tau_rank(a.topk, ns[k], hi - lo, a.rank_scale) : 1u;
+        // the row's window and lattice as the workgroup set them up (its
+        // first column); unsampled rows take their whole window
+        const int rr = wave + k * NW, col = PAIR ? 2 * rr : rr;
+        const int64_t t = (int64_t)tile * R + rr;
+        tt[k] = rr < R && t < nrows ? t : -1;
+        sampled[k] = tt[k] >= 0 && s_row[col] >= 0;
+        ns[k] = sampled[k] ? s_nl[col] : 1;
+        rk[k] = sampled[k] ? tau_rank(a.topk, ns[k], (int64_t)s_ke[col] - s_ks[col], a.rank_scale) : 1u;
         sp[k] = a.samp + (sampled[k] ? tt[k] : 0) * a.sample_target;
     }
     float tv[K];
@@ -505,6 +503,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     constexpr int RGB = (MODE == kModeFilter) ? kWaves * kTileQ * RS * 8 : 0;
     __shared__ __attribute__((aligned(16))) uint8_t smem[WB + QB + RGB];
     __shared__ int s_row[kTileQ], s_ks[kTileQ], s_ke[kTileQ], s_d[kTileQ];
+    __shared__ int s_nl[MODE == kModeSample ? kTileQ : 1];  // sample mode: lattice size of each column
     // output row of each column (-1: none; with pair, odd columns), and its
     // scratch slot in dense mode
     __shared__ int s_out[PAIR ? kTileQ : 1], s_slot[PAIR ? kTileQ : 1];
@@ -532,7 +531,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     static_assert(MODE != kModeSample || QB >= kWaves * kTauBuckets * 4, "histograms fit the q tile");
     auto finish = [&]() {
         if constexpr (MODE == kModeSample)
-            if (a.sample_split == 1) tile_tau<kWaves, PAIR>(a, tile, reinterpret_cast<uint32_t *>(s_q));
+            if (a.sample_split == 1) tile_tau<kWaves, PAIR>(a, tile, reinterpret_cast<uint32_t *>(s_q), s_row, s_ks, s_ke, s_nl);
     };
 
     if (threadIdx.x < kTileQ) {
@@ -558,6 +557,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         if (MODE == kModeSample) {
             if (t >= 0 && hi - lo > a.cap) {
                 d = sample_stride(hi - lo, a.sample_target, a.sample_min_stride);
+                s_nl[n] = (int)lattice_count(lo, hi, d);
             } else {
                 t = -1;
                 lo = hi = 0;

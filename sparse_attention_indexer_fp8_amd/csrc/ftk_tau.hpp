@@ -134,12 +134,11 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
             vmax[k] = fmaxf(vmax[k], v[k][q]);
         }
     }
-    for (int off = 32; off > 0; off >>= 1)
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            vmin[k] = fminf(vmin[k], __shfl_xor(vmin[k], off));
-            vmax[k] = fmaxf(vmax[k], __shfl_xor(vmax[k], off));
-        }
+    for (int k = 0; k < K; ++k) {  // wave extremes through DPP on the order codes (lanes with no sample hold +-inf)
+        vmax[k] = float_of_ord(wave_max(ord_of(vmax[k])));
+        vmin[k] = float_of_ord(~wave_max(~ord_of(vmin[k])));
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const float scale = (float)kTauBuckets / (vmax[k] - vmin[k]);
