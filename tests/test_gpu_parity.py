@@ -188,6 +188,22 @@ def test_scale_doubling_metamorphic():
     assert np.array_equal(b[1][fin], a[1][fin] * np.float32(2))
 
 
+@pytest.mark.parametrize("dt,T,S", [("fp8", 40, 6000), ("bf16", 40, 6000), ("fp8", 300, 9000)])
+def test_head_permutation_metamorphic(dt, T, S):
+    # Jointly permuting the heads of q and weights is a symmetry of the
+    # score; on integer data every partial sum is exact, so the output bits
+    # must not change (the tile path sums the heads in a fixed order).
+    wl = workloads.integer(T, S, 96, dt, 407 + T)
+    perm = np.random.default_rng(408).permutation(32)
+    wl2 = dict(wl, q=np.ascontiguousarray(wl["q"][:, perm, :]), weights=np.ascontiguousarray(wl["weights"][:, perm]))
+    a = run_gpu(wl)
+    b = run_gpu(wl2)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    rep = parity(wl, a[0], a[1], "exact")
+    assert rep["ok"], rep
+
+
 def test_without_values_output():
     import torch
 
