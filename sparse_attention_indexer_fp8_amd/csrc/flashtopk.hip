@@ -167,9 +167,7 @@ int resolve(Plan &p, const flashtopk_options *opt)
     return FLASHTOPK_OK;
 }
 
-// Keys per work item: large chunks amortise a work item's fixed costs
-// (staging the q tile, flushing candidates), but there must be enough items
-// (about four per compute unit) to fill the GPU.
+// Compute units of the current device (queried once).
 int num_cu()
 {
     static int n_cu = 0;
@@ -184,12 +182,29 @@ int num_cu()
     return n_cu;
 }
 
-int chunk_keys(int ntiles, int64_t S)
+// Keys per work item (a power of two in [kMinChunk, kMaxChunk]), from a cost
+// model: a work item takes a whole compute unit (its LDS), so items run in
+// rounds of one per CU, and an item costs a fixed part (setting up and
+// staging the q tile, flushing candidates: about one wave step) plus the wave
+// steps of each of its `waves` waves.  The chunk of least cost wins, the
+// larger one on a tie: large chunks amortise the fixed part, small ones fill
+// the GPU when the call has few tiles.
+int chunk_keys(int ntiles, int64_t S, int waves)
 {
     const int64_t n_cu = num_cu();
-    int chunk = kMaxChunk;
-    while (chunk > kMinChunk && (int64_t)ntiles * ((S + chunk - 1) / chunk) < 4 * n_cu) chunk >>= 1;
-    return chunk;
+    int best = kMaxChunk;
+    int64_t best_cost = INT64_MAX;
+    for (int chunk = kMaxChunk; chunk >= kMinChunk; chunk >>= 1) {
+        const int64_t items = (int64_t)ntiles * ((S + chunk - 1) / chunk);
+        const int64_t rounds = (items + n_cu - 1) / n_cu;
+        const int64_t steps = (chunk / kStepKeys + waves - 1) / waves;
+        const int64_t cost = rounds * (1 + steps);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = chunk;
+        }
+    }
+    return best;
 }
 
 // Workgroups per tile for the sample scores: with few tiles (decode-sized
@@ -319,7 +334,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
         if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
     }
-    const int chunk = chunk_keys(ntiles, S);
+    const int chunk = chunk_keys(ntiles, S, fp8 ? ScoreCfg<kFP8, kModeFilter>::waves : ScoreCfg<kBF16, kModeFilter>::waves);
     const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
 
     ScoreArgs sa{};
@@ -489,7 +504,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
                           dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream, sa);
         } else {
             sa.ntiles = (int)((rcap << ps) / kTileQ);
-            sa.chunk = chunk_keys(sa.ntiles, S);
+            sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves);
             const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
             launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
         }
