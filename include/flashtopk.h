@@ -112,7 +112,28 @@ typedef struct flashtopk_options {
                                  of DeepSeek-V3.2); q is [num_q, heads, 128]
                                  and weights [num_q, heads].  64-head calls
                                  take the scan path (no score-bound pruning) */
+    int validate;             /* nonzero: check the data preconditions on the
+                                 device first and wait for the result (a debug
+                                 aid, it synchronises the stream): windows in
+                                 [0, num_kv] with ks <= ke, no NaN / infinity
+                                 codes in q and (contiguous) kv, finite
+                                 weights, finite non-negative kv_scales, page
+                                 ids inside the pool.  Violations are reported
+                                 in flashtopk_info.invalid (FLASHTOPK_INVALID_*
+                                 bits) and any violation makes the call return
+                                 FLASHTOPK_ERR_INVALID_ARGUMENT before a
+                                 scoring kernel runs: the outputs are not
+                                 written.  Paged calls check q, weights,
+                                 windows and page ids, not the pool's keys */
 } flashtopk_options;
+
+/* Bits of flashtopk_info.invalid (calls made with options.validate). */
+#define FLASHTOPK_INVALID_WINDOW 1   /* a window outside [0, num_kv] or with ks > ke */
+#define FLASHTOPK_INVALID_Q 2        /* a NaN / infinity code in q */
+#define FLASHTOPK_INVALID_KV 4       /* a NaN / infinity code in kv */
+#define FLASHTOPK_INVALID_WEIGHT 8   /* a non-finite weight */
+#define FLASHTOPK_INVALID_SCALE 16   /* a negative or non-finite kv_scale */
+#define FLASHTOPK_INVALID_PAGE 32    /* a block_table entry outside [0, num_pages) */
 
 /* What the last call on a stream did (README, "Usage": last_info). */
 typedef struct flashtopk_info {
@@ -138,6 +159,7 @@ typedef struct flashtopk_info {
      * filter (with the score bound), triage, candidate selection, dense
      * recovery. */
     float ms_sample, ms_tau, ms_filter, ms_triage, ms_select, ms_recover;
+    int32_t invalid;            /* FLASHTOPK_INVALID_* bits found by options.validate, else 0 */
 } flashtopk_info;
 
 /* Exact top-k of the indexer score for every query row (see the file comment

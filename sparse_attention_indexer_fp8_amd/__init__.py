@@ -26,6 +26,12 @@ FLASHTOPK_SCORES_F32 = 0
 FLASHTOPK_SCORES_BF16 = 1
 FLASHTOPK_OUT_INDEX_ORDER = 1
 FLASHTOPK_OUT_INT64 = 2
+FLASHTOPK_INVALID_WINDOW = 1
+FLASHTOPK_INVALID_Q = 2
+FLASHTOPK_INVALID_KV = 4
+FLASHTOPK_INVALID_WEIGHT = 8
+FLASHTOPK_INVALID_SCALE = 16
+FLASHTOPK_INVALID_PAGE = 32
 
 PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER = 0, 1, 2, 3
 
@@ -49,6 +55,7 @@ class Options(ctypes.Structure):
         ("profile", ctypes.c_int),
         ("out_flags", ctypes.c_int),
         ("heads", ctypes.c_int),
+        ("validate", ctypes.c_int),
     ]
 
 
@@ -74,6 +81,7 @@ class Info(ctypes.Structure):
         ("ms_triage", ctypes.c_float),
         ("ms_select", ctypes.c_float),
         ("ms_recover", ctypes.c_float),
+        ("invalid", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -33,6 +33,7 @@
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
 #include "ftk_tau.hpp"
+#include "ftk_validate.hpp"
 
 using namespace ftk;
 
@@ -55,7 +56,8 @@ struct Workspace {
     DevBuf kb, kmeta, vplan, q1;               // score-bound pruning
     DevBuf ticket;                             // few-row sample finish counters (kept zero between calls)
     DevBuf pkv, psig;                          // keys and scales gathered from a paged cache
-    unsigned long long *host_stats = nullptr;  // pinned
+    DevBuf vflag;                              // precondition flags (options.validate)
+    unsigned long long *host_stats = nullptr;  // pinned: kStCount statistics, then the precondition flags
     hipEvent_t ev[7] = {};                     // phase boundaries when profiling
     hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
     flashtopk_info last{};
@@ -120,7 +122,7 @@ Workspace *get_ws(hipStream_t stream, int *status)
     Workspace *w = new Workspace();
     w->device = dev;
     w->stream = stream;
-    e = hipHostMalloc((void **)&w->host_stats, sizeof(unsigned long long) * kStCount, hipHostMallocDefault);
+    e = hipHostMalloc((void **)&w->host_stats, sizeof(unsigned long long) * (kStCount + 1), hipHostMallocDefault);
     if (e != hipSuccess) {
         delete w;
         *status = hip_status(e);
@@ -131,6 +133,8 @@ Workspace *get_ws(hipStream_t stream, int *status)
 }
 
 struct Plan {
+    int validate = 0;     // options.validate
+    unsigned invalid = 0; // the flags it found
     int64_t T, S;
     int dtype, topk, cap, sample_target, sample_min_stride, path;
     float rank_scale;
@@ -164,6 +168,7 @@ int resolve(Plan &p, const flashtopk_options *opt)
     if (p.out_flags & ~(FLASHTOPK_OUT_INDEX_ORDER | FLASHTOPK_OUT_INT64)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     p.recover_budget = (opt && opt->recover_budget_bytes > 0) ? opt->recover_budget_bytes : kDefaultRecoverBudget;
     p.profile = (opt && opt->profile) ? 1 : 0;
+    p.validate = (opt && opt->validate) ? 1 : 0;
     return FLASHTOPK_OK;
 }
 
@@ -595,6 +600,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     info.ms_triage = phase_ms(*w, p, 3);
     info.ms_select = phase_ms(*w, p, 4);
     info.ms_recover = R > 0 ? ms_rec : 0.0f;
+    info.invalid = (int32_t)p.invalid;
     w->last_recover_all = recover_all;
     w->has_last = true;
     w->last_pending = true;
@@ -628,6 +634,39 @@ void launch_rows(const RowsArgs &a, hipStream_t s)
     }
 }
 
+// options.validate: runs k_validate on the call's inputs, waits for its flags
+// (p.invalid) and, when it found any, fails the call before a scoring kernel
+// runs, recording it as the stream's last call.
+int check_inputs(hipStream_t s, Plan &p, ValidateArgs va)
+{
+    int st = FLASHTOPK_OK;
+    Workspace *w = get_ws(s, &st);
+    if (!w) return st;
+    if ((st = ensure(*w, w->vflag, sizeof(unsigned)))) return st;
+    va.flags = (unsigned *)w->vflag.ptr;
+    va.dtype = p.dtype == FLASHTOPK_FP8_E4M3 ? kFP8 : kBF16;
+    const int64_t n = std::max({va.q_pieces, va.kv_pieces, va.nw, va.nscales, va.num_q, va.ntable, (int64_t)1});
+    const unsigned grid = (unsigned)std::min<int64_t>(2048, (n + 255) / 256);
+    k_zero_word<<<1, 64, 0, s>>>(va.flags);
+    k_validate<<<grid, 256, 0, s>>>(va);
+    unsigned *hf = reinterpret_cast<unsigned *>(w->host_stats + kStCount);
+    hipError_t e = hipMemcpyAsync(hf, va.flags, sizeof(unsigned), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e);
+    p.invalid = *hf;
+    if (p.invalid) {
+        flashtopk_info &info = w->last;
+        std::memset(&info, 0, sizeof(info));
+        info.status = FLASHTOPK_ERR_INVALID_ARGUMENT;
+        info.rows = p.T;
+        info.invalid = (int32_t)p.invalid;
+        w->has_last = true;
+        w->last_pending = false;
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    }
+    return FLASHTOPK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -651,6 +690,23 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, c
     p.topk = topk;
     int st = resolve(p, opt);
     if (st) return st;
+    if (p.validate) {
+        const int64_t rb = dtype == FLASHTOPK_FP8_E4M3 ? kDim : 2 * kDim;
+        ValidateArgs va{};
+        va.q = (const uint8_t *)q;
+        va.q_pieces = num_q * p.heads * rb / 16;
+        va.kv = (const uint8_t *)kv;
+        va.kv_pieces = kv ? num_kv * rb / 16 : 0;
+        va.w = weights;
+        va.nw = num_q * p.heads;
+        va.scales = kv_scales;
+        va.nscales = kv_scales ? num_kv : 0;
+        va.ks = ks;
+        va.ke = ke;
+        va.num_q = num_q;
+        va.num_kv = num_kv;
+        if ((st = check_inputs((hipStream_t)stream, p, va))) return st;
+    }
     return run(q, kv, kv_scales, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
 }
 
@@ -675,6 +731,23 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
     p.topk = topk;
     int st = resolve(p, opt);
     if (st) return st;
+    if (p.validate) {
+        // the pool may hold unused pages: q, weights, windows and page ids only
+        const int64_t rb = dtype == FLASHTOPK_FP8_E4M3 ? kDim : 2 * kDim;
+        ValidateArgs va{};
+        va.q = (const uint8_t *)q;
+        va.q_pieces = num_q * p.heads * rb / 16;
+        va.w = weights;
+        va.nw = num_q * p.heads;
+        va.ks = ks;
+        va.ke = ke;
+        va.num_q = num_q;
+        va.num_kv = num_kv;
+        va.table = num_kv > 0 ? block_table : nullptr;
+        va.ntable = num_kv > 0 ? (num_kv + page_size - 1) / page_size : 0;
+        va.num_pages = num_pages;
+        if ((st = check_inputs((hipStream_t)stream, p, va))) return st;
+    }
     if (num_kv == 0) return run(q, nullptr, nullptr, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
     const hipStream_t s = (hipStream_t)stream;
     if (num_q <= kFewRows && p.heads == 32) {
@@ -805,7 +878,7 @@ void flashtopk_release(void)
         (void)hipStreamSynchronize(w->stream);
         DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowlist, &w->stats,
                           &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh,
-                          &w->kb, &w->kmeta, &w->vplan, &w->q1, &w->ticket, &w->pkv, &w->psig};
+                          &w->kb, &w->kmeta, &w->vplan, &w->q1, &w->ticket, &w->pkv, &w->psig, &w->vflag};
         for (DevBuf *b : bufs)
             if (b->ptr) (void)hipFree(b->ptr);
         if (w->host_stats) (void)hipHostFree(w->host_stats);

@@ -56,12 +56,41 @@ def test_header_constants_match_binding():
     assert int(consts["FLASHTOPK_SCORES_BF16"]) == ftk.FLASHTOPK_SCORES_BF16
     assert int(consts["FLASHTOPK_OUT_INDEX_ORDER"]) == ftk.FLASHTOPK_OUT_INDEX_ORDER
     assert int(consts["FLASHTOPK_OUT_INT64"]) == ftk.FLASHTOPK_OUT_INT64
+    for name in ("WINDOW", "Q", "KV", "WEIGHT", "SCALE", "PAGE"):
+        assert int(consts["FLASHTOPK_INVALID_" + name]) == getattr(ftk, "FLASHTOPK_INVALID_" + name)
 
 
 def test_options_and_info_layout_match_header():
     # sizes of the C structs as laid out by the platform ABI
     assert ctypes.sizeof(ftk.Options) == 40
-    assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4 + 6 * 4
+    assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4 + 6 * 4 + 4 + 4  # invalid, padding
+
+
+def test_struct_layout_matches_the_c_compiler(tmp_path):
+    # The binding's ctypes structs against the header as a C compiler lays
+    # it out: sizes and the offset of every field.
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "flashtopk.h"', "int main(void) {"]
+    for cname, py in (("flashtopk_options", ftk.Options), ("flashtopk_info", ftk.Info)):
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in (("flashtopk_options", ftk.Options), ("flashtopk_info", ftk.Info)):
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
 
 
 def _call(lib, **kw):
