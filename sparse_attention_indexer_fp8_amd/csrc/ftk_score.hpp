@@ -517,6 +517,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     __shared__ float s_tau[kTileQ], s_q1[kTileQ];
     __shared__ float s_l1[MODE == kModeSample ? kTileQ * kHeads : 1];
     __shared__ unsigned long long s_pp[2];  // planner sample: pairs, prunable pairs
+    __shared__ int s_next;                  // sample mode: next unclaimed step
     float *s_w = reinterpret_cast<float *>(smem);
     uint8_t *s_q = smem + WB;
     uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + WB + QB);
@@ -577,6 +578,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         if ((MODE == kModeFilter || (MODE == kModeSample && DT == kFP8)) && a.prune)
             s_q1[n] = t >= 0 ? a.q1[t] : 0.0f;
         if (n < 2) s_pp[n] = 0ull;
+        if (n == 0) s_next = 0;
     }
     __syncthreads();
 
@@ -973,11 +975,34 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         }
     };
 
-    // Steps of this wave: the wave-th, (wave + kWaves)-th, ... step of the
-    // work item (all of [jlo, jhi), or the ones not skipped).
+    // Steps of this wave in filter and dense modes: the wave-th,
+    // (wave + kWaves)-th, ... step of the work item (all of [jlo, jhi), or
+    // the ones not skipped).
     auto step_of = [&](int i) { return use_skip ? jlo + __builtin_amdgcn_readfirstlane((int)s_steps[i]) : jlo + i; };
     auto nop = []() {};
-    if (Cfg::prefetch) {
+    if (MODE == kModeSample) {
+        // Sample mode claims steps from a workgroup counter, so the waves that
+        // evaluated the planner sample first take fewer of them.  Each wave
+        // claims a step when it issues its key loads, one step ahead.
+        auto claim = [&]() {
+            int v = 0;
+            if (lane == 0) v = atomicAdd(&s_next, 1);
+            return __builtin_amdgcn_readfirstlane(__shfl(v, 0));
+        };
+        KFrag<DT> ka[kSub], kb[kSub];
+        int i = claim();
+        if (i < nstep) load_step(ka, step_of(i));
+        while (i < nstep) {
+            const int i2 = claim();
+            if (i2 < nstep) load_step(kb, step_of(i2));
+            process(ka, step_of(i), nop);
+            if (i2 >= nstep) break;
+            const int i3 = claim();
+            if (i3 < nstep) load_step(ka, step_of(i3));
+            process(kb, step_of(i2), nop);
+            i = i3;
+        }
+    } else if (Cfg::prefetch) {
         // Two fragment sets alternate so the next step's keys load while this
         // step computes.
         KFrag<DT> ka[kSub], kb[kSub];
