@@ -341,6 +341,7 @@ template <int NREG, int NT, int NBKT, int MAXK> struct SelShape {
     static constexpr int nreg = NREG, nt = NT, nbkt = NBKT, maxk = MAXK;
 };
 using SelSmall = SelShape<8, 256, 2048, 2048>;     // cap <= 2048
+using SelSmallK = SelShape<8, 256, 2048, 512>;     // cap <= 2048, topk <= 512: 8 rows per compute unit
 using SelMid = SelShape<8, 512, 4096, kMaxTopk>;   // cap <= 4096
 using SelLarge = SelShape<8, 1024, 4096, kMaxTopk>;  // cap <= 8192
 using SelHuge = SelShape<16, 1024, 4096, kMaxTopk>;  // cap <= 16384
