@@ -547,7 +547,11 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         tr.recover_all = recover_all ? 1 : 0;
         tr.rowlist = (int32_t *)w->rowlist.ptr;
         tr.stats = (unsigned long long *)w->stats.ptr;
-        k_triage<<<dim3((unsigned)((T + kTriageThreads - 1) / kTriageThreads)), kTriageThreads, 0, stream>>>(tr);
+        if (T <= kTriageFewRows)
+            k_triage<1><<<dim3((unsigned)((T + kTriageThreads - 1) / kTriageThreads)), kTriageThreads, 0, stream>>>(tr);
+        else
+            k_triage<16><<<dim3((unsigned)((T + 16 * kTriageThreads - 1) / (16 * kTriageThreads))), kTriageThreads, 0,
+                           stream>>>(tr);
         // The triage counts go to pinned host memory right away; the host
         // waits for them (not for the stream) while the select kernel runs,
         // so the GPU never idles on the host between calls.

@@ -215,42 +215,69 @@ __device__ __forceinline__ void triage_one(int64_t t, int64_t len, uint32_t c, i
     if (len) atomicAdd(stats + kStWindow, (unsigned long long)len);
 }
 
-// One thread per row; statistics and the flagged-row list are gathered with
-// one atomic per wave and statistic.  The list is in no particular order
-// (each flagged row's result depends on that row alone).
+// RPT rows per thread (strided by the workgroup size, so loads coalesce);
+// statistics are summed per workgroup and added with one atomic per
+// workgroup and statistic (the counters are few and shared by every
+// workgroup, so per-wave atomics on them serialise).  Flagged rows are
+// appended with one atomic per wave and row round that holds any; the list
+// is in no particular order (each flagged row's result depends on that row
+// alone).  Calls of up to kTriageFewRows rows take one row per thread (more
+// workgroups, each short); larger ones 16 (fewer atomics).
 constexpr int kTriageThreads = 256;
+constexpr int kTriageFewRows = 16384;
 
+template <int RPT>
 __global__ __launch_bounds__(kTriageThreads) void k_triage(TriageArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kTriageThreads + threadIdx.x;
+    constexpr int NW = kTriageThreads / 64;
+    constexpr int kTriageRowsPerThread = RPT;
+    __shared__ unsigned long long s_sum[NW][7];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * (kTriageThreads * RPT) + threadIdx.x;
     uint32_t n_empty = 0, n_take = 0, n_samp = 0, n_under = 0, n_over = 0, maxc = 0;
     unsigned long long win = 0;
-    bool flag = false;
-    if (t < a.num_q) {
-        const int64_t lo = a.ks[t], hi = a.ke[t];
-        const int64_t len = hi > lo ? hi - lo : 0;
-        const uint32_t c = a.cnt[t];
-        flag = row_flagged(len, c, a.topk, a.cap, a.recover_all);
-        if (len == 0) {
-            n_empty = 1;
-        } else if (!a.recover_all) {
-            n_under = (int64_t)c < min((int64_t)a.topk, len);
-            n_over = (int64_t)c > a.cap;
-            if (len <= a.cap) {
-                n_take = 1;
-            } else {
-                n_samp = 1;
-                maxc = c;
-            }
-        }
-        win = (unsigned long long)len;
+    // Every row's loads are issued before the first is used (indices past
+    // the last row re-read it; their results are not counted).
+    int32_t rlo[kTriageRowsPerThread], rhi[kTriageRowsPerThread];
+    uint32_t rc[kTriageRowsPerThread];
+#pragma unroll
+    for (int r = 0; r < kTriageRowsPerThread; ++r) {
+        const int64_t t = min(t0 + (int64_t)r * kTriageThreads, a.num_q - 1);
+        rlo[r] = a.ks[t];
+        rhi[r] = a.ke[t];
+        rc[r] = a.cnt[t];
     }
-    const uint64_t bal = __ballot(flag);
-    unsigned long long base = 0;
-    if (lane == 0 && bal) base = atomicAdd(a.stats + kStFlagged, (unsigned long long)__builtin_popcountll(bal));
-    base = __shfl(base, 0);
-    if (flag) a.rowlist[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (int32_t)t;
+#pragma unroll
+    for (int r = 0; r < kTriageRowsPerThread; ++r) {
+        const int64_t t = t0 + (int64_t)r * kTriageThreads;
+        bool flag = false;
+        if (t < a.num_q) {
+            const int64_t lo = rlo[r], hi = rhi[r];
+            const int64_t len = hi > lo ? hi - lo : 0;
+            const uint32_t c = rc[r];
+            flag = row_flagged(len, c, a.topk, a.cap, a.recover_all);
+            if (len == 0) {
+                ++n_empty;
+            } else if (!a.recover_all) {
+                n_under += (int64_t)c < min((int64_t)a.topk, len) ? 1u : 0u;
+                n_over += (int64_t)c > a.cap ? 1u : 0u;
+                if (len <= a.cap) {
+                    ++n_take;
+                } else {
+                    ++n_samp;
+                    maxc = max(maxc, c);
+                }
+            }
+            win += (unsigned long long)len;
+        }
+        const uint64_t bal = __ballot(flag);
+        if (bal) {  // wave-uniform
+            unsigned long long base = 0;
+            if (lane == 0) base = atomicAdd(a.stats + kStFlagged, (unsigned long long)__builtin_popcountll(bal));
+            base = __shfl(base, 0);
+            if (flag) a.rowlist[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (int32_t)t;
+        }
+    }
     for (int off = 32; off > 0; off >>= 1) {
         n_empty += __shfl_xor(n_empty, off);
         n_take += __shfl_xor(n_take, off);
@@ -261,13 +288,26 @@ __global__ __launch_bounds__(kTriageThreads) void k_triage(TriageArgs a)
         win += __shfl_xor(win, off);
     }
     if (lane == 0) {
-        if (n_empty) atomicAdd(a.stats + kStEmpty, (unsigned long long)n_empty);
-        if (n_take) atomicAdd(a.stats + kStTakeAll, (unsigned long long)n_take);
-        if (n_samp) atomicAdd(a.stats + kStSampled, (unsigned long long)n_samp);
-        if (n_under) atomicAdd(a.stats + kStUnder, (unsigned long long)n_under);
-        if (n_over) atomicAdd(a.stats + kStOver, (unsigned long long)n_over);
-        if (maxc) atomicMax(a.stats + kStMaxCand, (unsigned long long)maxc);
-        if (win) atomicAdd(a.stats + kStWindow, win);
+        s_sum[wave][0] = n_empty;
+        s_sum[wave][1] = n_take;
+        s_sum[wave][2] = n_samp;
+        s_sum[wave][3] = n_under;
+        s_sum[wave][4] = n_over;
+        s_sum[wave][5] = maxc;
+        s_sum[wave][6] = win;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long v[7] = {0, 0, 0, 0, 0, 0, 0};
+        for (int w = 0; w < NW; ++w)
+            for (int i = 0; i < 7; ++i) v[i] = i == 5 ? (s_sum[w][i] > v[i] ? s_sum[w][i] : v[i]) : v[i] + s_sum[w][i];
+        if (v[0]) atomicAdd(a.stats + kStEmpty, v[0]);
+        if (v[1]) atomicAdd(a.stats + kStTakeAll, v[1]);
+        if (v[2]) atomicAdd(a.stats + kStSampled, v[2]);
+        if (v[3]) atomicAdd(a.stats + kStUnder, v[3]);
+        if (v[4]) atomicAdd(a.stats + kStOver, v[4]);
+        if (v[5]) atomicMax(a.stats + kStMaxCand, v[5]);
+        if (v[6]) atomicAdd(a.stats + kStWindow, v[6]);
     }
 }
 

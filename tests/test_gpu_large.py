@@ -37,6 +37,19 @@ def _packed_extra():
     return extra
 
 
+def _check_row_classes(wl, info):
+    """The call's row classes and window total, recomputed on the host."""
+    T = wl["q"].shape[0]
+    lens = np.maximum(wl["ke"].astype(np.int64) - wl["ks"].astype(np.int64), 0)
+    cap = info["cand_capacity"]
+    assert info["rows"] == T
+    assert info["rows_empty"] == int((lens == 0).sum())
+    assert info["rows_take_all"] == int(((lens > 0) & (lens <= cap)).sum())
+    assert info["rows_sampled"] == int((lens > cap).sum())
+    assert info["window_keys"] == int(lens.sum())
+    assert info["rows_recovered"] == info["rows_underflow"] + info["rows_overflow"]
+
+
 CASES = [
     ("untrained_fp8_k4096", 3, False, "tolerance"),
     ("trained_fp8_k2048", 4, False, "tolerance"),
@@ -60,6 +73,8 @@ def test_full_size_sampled_rows(name, n, twin, mode):
     idx, val = run_gpu(wl)
     info = ftk.flashtopk_get_last_info()
     print("info", info, flush=True)
+    if n in (3, 4, 5):
+        _check_row_classes(wl, info)
     rows = _rows(wl, _packed_extra() if n == 5 else ())
     rep = parity(wl, idx, val, mode, rows=rows)
     assert rep["ok"], rep
@@ -73,3 +88,29 @@ def test_full_size_sampled_rows(name, n, twin, mode):
         short = (wl["ke"] - wl["ks"]) < wl["topk"]
         assert short.sum() == 4 * 511
         assert np.all(idx[short][:, -1] == -1)
+
+
+def test_many_rows_mixed_windows():
+    # 20001 rows (more than one triage workgroup's 4096, the last one
+    # partial): empty, take-all and sampled windows mixed; class counts on
+    # every row, parity on sampled rows.
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    wl = workloads.integer(20001, 3000, 64, "fp8", 2301, windows="full")
+    rng = np.random.default_rng(2302)
+    kind = rng.integers(0, 3, size=20001)
+    lo = rng.integers(0, 3000, size=20001)
+    ln = np.where(kind == 0, 0, np.where(kind == 1, rng.integers(1, 257, size=20001), rng.integers(257, 3001, size=20001)))
+    lo = np.minimum(lo, 3000 - ln)
+    wl["ks"] = lo.astype(np.int32)
+    wl["ke"] = (lo + ln).astype(np.int32)
+    print("case many rows", flush=True)
+    idx, val = run_gpu(wl)
+    info = ftk.flashtopk_get_last_info()
+    print("info", info, flush=True)
+    assert info["cand_capacity"] == 256
+    _check_row_classes(wl, info)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(20001 - 8, 20001),
+                                     rng.choice(20001, size=24, replace=False)])).astype(np.int64)
+    rep = parity(wl, idx, val, "exact", rows=rows)
+    assert rep["ok"], rep
