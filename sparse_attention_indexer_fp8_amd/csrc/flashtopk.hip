@@ -481,6 +481,7 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         if (p.cap <= SelSmallK::nreg * SelSmallK::nt && p.topk <= SelSmallK::maxk) launch_select<SelSmallK>(T, stream, se);
         else if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
         else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
+        else if (p.cap <= SelLargeK::nreg * SelLargeK::nt && p.topk <= SelLargeK::maxk) launch_select<SelLargeK>(T, stream, se);
         else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
         else launch_select<SelHuge>(T, stream, se);
     };

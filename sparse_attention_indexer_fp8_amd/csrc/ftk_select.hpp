@@ -377,14 +377,17 @@ __device__ __forceinline__ float raw_score(uint64_t r) { return __uint_as_float(
 // registers (0: dense rows streamed from scratch), NT threads, NBKT buckets,
 // rows of at most MAXK outputs.  Small candidate lists get small workgroups
 // with small LDS, so more rows are in flight per compute unit.
-template <int NREG, int NT, int NBKT, int MAXK> struct SelShape {
-    static constexpr int nreg = NREG, nt = NT, nbkt = NBKT, maxk = MAXK;
+// MINW is the launch bound's minimum waves per SIMD (0: none), which caps
+// the registers so that many rows fit per compute unit.
+template <int NREG, int NT, int NBKT, int MAXK, int MINW = 0> struct SelShape {
+    static constexpr int nreg = NREG, nt = NT, nbkt = NBKT, maxk = MAXK, minw = MINW;
 };
 using SelSmall = SelShape<8, 256, 2048, 2048>;     // cap <= 2048
 using SelSmallK = SelShape<8, 256, 2048, 512>;     // cap <= 2048, topk <= 512: 8 rows per compute unit
 using SelMid = SelShape<8, 512, 4096, kMaxTopk>;   // cap <= 4096
-using SelLarge = SelShape<8, 1024, 4096, kMaxTopk>;  // cap <= 8192
-using SelHuge = SelShape<16, 1024, 4096, kMaxTopk>;  // cap <= 16384
+using SelLarge = SelShape<8, 1024, 4096, kMaxTopk, 8>;  // cap <= 8192
+using SelLargeK = SelShape<16, 512, 4096, 2048, 6>;     // cap <= 8192, topk <= 2048: 3 rows per compute unit, no spills
+using SelHuge = SelShape<16, 1024, 4096, kMaxTopk, 8>;  // cap <= 16384 (2 rows per compute unit beat 1 without spills)
 using SelDense = SelShape<0, 512, 4096, kMaxTopk>;   // recovered rows
 
 template <int NT, int NBKT, int MAXK, typename E>
@@ -400,7 +403,7 @@ __device__ __forceinline__ void *out_row(void *base, int64_t r, int topk, int fl
 // Candidate mode: rows that triage flags (same predicate) are left to dense
 // recovery; every other row's candidates hold its whole top k.
 template <typename SH>
-__global__ __launch_bounds__(SH::nt, SH::nt == 1024 ? 8 : 1) void k_select(SelectArgs a)
+__global__ __launch_bounds__(SH::nt, SH::minw > 0 ? SH::minw : 1) void k_select(SelectArgs a)
 {
     constexpr int NREG = SH::nreg, NT = SH::nt, NBKT = SH::nbkt, MAXK = SH::maxk;
     constexpr bool DENSE = NREG == 0;
