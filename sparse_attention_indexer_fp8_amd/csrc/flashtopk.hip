@@ -300,6 +300,9 @@ void fill_counts(Workspace &w)
     w.last_pending = false;
 }
 
+template <typename T, typename SH>
+void launch_rows(const RowsArgs &a, hipStream_t s);
+
 int run(const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
         const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
 {
@@ -472,8 +475,6 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
     se.recover_all = recover_all ? 1 : 0;
     se.cnt = (const uint32_t *)w->cnt.ptr;
     se.cand = (const uint64_t *)w->cand.ptr;
-    se.rowlist = (const int32_t *)w->rowlist.ptr;
-    se.stats = (const unsigned long long *)w->stats.ptr;
     se.out_idx = out_idx;
     se.out_val = out_val;
     se.out_flags = p.out_flags;
@@ -499,13 +500,9 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         sa.rowlist = (const int32_t *)w->rowlist.ptr;
         sa.nrows = (const unsigned long long *)w->stats.ptr + kStFlagged;
         sa.row_limit = (int)rcap;
-        sa.scratch = (uint64_t *)w->scratch.ptr;
+        sa.scratch = (float *)w->scratch.ptr;
         sa.scratch_stride = stride;
         sa.row_base = (int)rb;
-        se.row_limit = (int)rcap;
-        se.scratch = (const uint64_t *)w->scratch.ptr;
-        se.scratch_stride = stride;
-        se.row_base = (int)rb;
         if (few) {
             launch_few_dt(p.dtype, kModeDense,
                           dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream, sa);
@@ -515,18 +512,37 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
             const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
             launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
         }
-        launch_select<SelDense>(rcap, stream, se);
+        // Exact top k of each batch row's window scores: the row top-k
+        // kernels in mapped-row mode (outputs to the flagged row, indices
+        // offset by its window start; entries past the list exit).
+        RowsArgs ra{};
+        ra.x = w->scratch.ptr;
+        ra.rows = rcap;
+        ra.cols = S;
+        ra.stride = stride;
+        ra.topk = p.topk;
+        ra.out_idx = out_idx;
+        ra.out_val = out_val;
+        ra.out_flags = p.out_flags;
+        ra.rowmap = (const int32_t *)w->rowlist.ptr;
+        ra.nrows = (const unsigned long long *)w->stats.ptr + kStFlagged;
+        ra.row_base = rb;
+        ra.ks = ks;
+        ra.ke = ke;
+        if (p.topk <= RowsSmall::maxk) launch_rows<float, RowsSmall>(ra, stream);
+        else launch_rows<float, RowsLarge>(ra, stream);
     };
-    const int64_t stride = std::max<int64_t>(S, 1);
+    // Scratch rows of float scores, 16-byte aligned (the row kernels' loads).
+    const int64_t stride = (std::max<int64_t>(S, 1) + 3) / 4 * 4;
 
     // Few rows whose whole windows fit the recovery budget: the selection
     // does each row's triage, recovery of every row is launched up front
     // (rows that need none exit at once), and the call returns without
     // waiting for the GPU; the statistics are read when asked for.
-    const bool speculative = few && !p.profile && (int64_t)sizeof(uint64_t) * T * stride <= p.recover_budget;
+    const bool speculative = few && !p.profile && (int64_t)sizeof(float) * T * stride <= p.recover_budget;
     int64_t R = 0;
     if (speculative) {
-        if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)T * stride))) return st;
+        if ((st = ensure(*w, w->scratch, sizeof(float) * (size_t)T * stride))) return st;
         se.triage = 1;
         se.rowlist_w = (int32_t *)w->rowlist.ptr;
         se.stats_w = (unsigned long long *)w->stats.ptr;
@@ -569,10 +585,10 @@ int run(const void *q, const void *kv, const float *kv_scales, const float *weig
         mark(*w, p, 6, stream);  // recovery timed from here (0 when nothing is flagged)
         if (R > 0) {
             // Dense rescoring of flagged rows, in batches that fit the budget.
-            int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(uint64_t) * stride));
+            int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(float) * stride));
             rcap = std::min<int64_t>(rcap, (R + kTileQ - 1) / kTileQ * kTileQ);
             rcap = (rcap + kTileQ - 1) / kTileQ * kTileQ;
-            if ((st = ensure(*w, w->scratch, sizeof(uint64_t) * (size_t)rcap * stride))) return st;
+            if ((st = ensure(*w, w->scratch, sizeof(float) * (size_t)rcap * stride))) return st;
             for (int64_t rb = 0; rb < R; rb += rcap) recover_batch(rb, rcap, stride);
             e = hipGetLastError();
             if (e != hipSuccess) return hip_status(e);

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kFewThreads) void k_score_few(ScoreArgs a)
                     if (g == 0 && e < khi) a.samp[(int64_t)t * a.sample_target + e] = ord_of(sc);
                 } else if (MODE == kModeDense) {
                     if (g == 0 && e < khi)
-                        a.scratch[(int64_t)e_dense * a.scratch_stride + (e - lo)] = raw_cand(sc, (int32_t)e);
+                        a.scratch[(int64_t)e_dense * a.scratch_stride + (e - lo)] = sc;
                 } else {
                     const bool keep = g == 0 && e < khi && e >= lo && e < hi && sc >= tau;
                     const uint64_t bal = __ballot(keep);

@@ -54,7 +54,36 @@ struct RowsArgs {
     float *out_val;         // [rows, topk] or null
     int32_t *nan_flag;      // set to 1 when a row holds a NaN; or null
     int out_flags;          // OutFlag
+    // Mapped rows (dense recovery of the fused call), when rowmap is set:
+    // input row r is entry row_base + r of rowmap, present while that entry
+    // is below *nrows; its outputs go to row rowmap[row_base + r], its length
+    // is that row's window ke - ks (at most cols) and its indices are offset
+    // by the window start ks.
+    const int32_t *rowmap;
+    const unsigned long long *nrows;
+    int64_t row_base;
+    const int32_t *ks;
+    const int32_t *ke;
 };
+
+// Output row, length and index offset of input row r (present = false: a
+// mapped row past the list, nothing to do).
+struct RowPlace {
+    int64_t out, n;
+    int32_t base;
+    bool present;
+};
+
+__device__ __forceinline__ RowPlace row_place(const RowsArgs &a, int64_t r)
+{
+    if (a.rowmap) {
+        if ((unsigned long long)(a.row_base + r) >= *a.nrows) return {0, 0, 0, false};
+        const int64_t t = a.rowmap[a.row_base + r];
+        const int64_t lo = a.ks[t], hi = max((int64_t)a.ke[t], lo);
+        return {t, min(hi - lo, a.cols), (int32_t)lo, true};
+    }
+    return {r, a.ends ? min(max((int64_t)a.ends[r], (int64_t)0), a.cols) : a.cols, 0, true};
+}
 
 template <typename T> __device__ __forceinline__ float entry_value(T v);
 template <> __device__ __forceinline__ float entry_value<float>(float v) { return v; }
@@ -432,7 +461,9 @@ __global__ __launch_bounds__(64 * kRowsTauWaves) void k_rows_tau(RowsArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r = (int64_t)blockIdx.x * kRowsTauWaves + wave;
     if (r >= a.rows) return;  // wave-uniform; no block barrier follows
-    const int64_t n = a.ends ? min(max((int64_t)a.ends[r], (int64_t)0), a.cols) : a.cols;
+    const RowPlace pl = row_place(a, r);
+    if (!pl.present) return;
+    const int64_t n = pl.n;
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
     if (n <= SH::cap || k == 0) return;
     const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
@@ -509,7 +540,7 @@ __global__ __launch_bounds__(64 * kRowsTauWaves) void k_rows_tau(RowsArgs a)
         b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
         tau = hi - (float)(b + 2) / scale;
     }
-    if (lane == 0) *(int32_t *)out_row(a.out_idx, r, a.topk, a.out_flags) = __float_as_int(tau);
+    if (lane == 0) *(int32_t *)out_row(a.out_idx, pl.out, a.topk, a.out_flags) = __float_as_int(tau);
 }
 
 // One workgroup per row.  With PRE_TAU the row's threshold was computed by
@@ -523,11 +554,13 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     __shared__ RowsLds<SH> L;
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
+    const RowPlace pl = row_place(a, r);
+    if (!pl.present) return;  // block-uniform
     const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
-    const int64_t n = a.ends ? min(max((int64_t)a.ends[r], (int64_t)0), a.cols) : a.cols;
+    const int64_t n = pl.n;
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
-    void *oi = out_row(a.out_idx, r, a.topk, a.out_flags);
-    float *ov = a.out_val ? a.out_val + r * a.topk : nullptr;
+    void *oi = out_row(a.out_idx, pl.out, a.topk, a.out_flags);
+    float *ov = a.out_val ? a.out_val + pl.out * a.topk : nullptr;
     if (k == 0) {
         for (int j = tid; j < a.topk; j += NT) {
             if (a.out_flags & kOutInt64) ((int64_t *)oi)[j] = -1;
@@ -552,10 +585,10 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
         RowElems<SH::regs> el;
         el.load(L.cand, m);
         __syncthreads();  // the gathered entries are in registers; the LDS becomes the selection's
-        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m, k, a.topk, oi, ov, a.out_flags);
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m, k, a.topk, oi, ov, a.out_flags, pl.base);
     } else {
         RowStream<T> el{row, n};
-        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags);
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags, pl.base);
     }
 }
 

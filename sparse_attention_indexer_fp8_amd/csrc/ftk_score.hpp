@@ -105,7 +105,7 @@ struct ScoreArgs {
     const unsigned long long *nrows;  // device count of flagged rows
     int row_base;              // first flagged entry of this batch
     int row_limit;             // entries per batch
-    uint64_t *scratch;         // [row_limit, scratch_stride] keys
+    float *scratch;            // [row_limit, scratch_stride] window scores (dense mode)
     int64_t scratch_stride;
     // score-bound pruning (sample and filter modes)
     int prune;                 // 0: off; 1: per tile, from its planner sample; 2: always
@@ -969,8 +969,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                 for (int i = 0; i < 4; ++i) {
                     const int s = sb + 16 * kt + i;
                     if (slot < 0 || s < rks || s >= rke) continue;
-                    a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] =
-                        raw_cand(score_of<DT>(o, kt, i, shv[kt][i]), s);
+                    a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] = score_of<DT>(o, kt, i, shv[kt][i]);
                 }
         }
     };

@@ -326,14 +326,7 @@ struct SelectArgs {
     // candidate rows
     const uint32_t *cnt;
     const uint64_t *cand;
-    // flagged rows (listed by triage, read by dense recovery)
-    const int32_t *rowlist;
-    const unsigned long long *stats;  // Stat; stats[kStFlagged] = list length
-    // dense (recovered) rows
-    int row_base;
-    int row_limit;
-    const uint64_t *scratch;
-    int64_t scratch_stride;
+    // outputs
     void *out_idx;       // int32 or int64 (kOutInt64)
     float *out_val;
     int out_flags;       // OutFlag
@@ -374,7 +367,7 @@ struct SelectLds {
 __device__ __forceinline__ float raw_score(uint64_t r) { return __uint_as_float((uint32_t)r); }
 
 // Launch shapes of the selection kernel: NREG candidates per thread in
-// registers (0: dense rows streamed from scratch), NT threads, NBKT buckets,
+// registers, NT threads, NBKT buckets,
 // rows of at most MAXK outputs.  Small candidate lists get small workgroups
 // with small LDS, so more rows are in flight per compute unit.
 // MINW is the launch bound's minimum waves per SIMD (0: none), which caps
@@ -388,11 +381,10 @@ using SelMid = SelShape<8, 512, 4096, kMaxTopk>;   // cap <= 4096
 using SelLarge = SelShape<8, 1024, 4096, kMaxTopk, 8>;  // cap <= 8192
 using SelLargeK = SelShape<16, 512, 4096, 2048, 6>;     // cap <= 8192, topk <= 2048: 3 rows per compute unit, no spills
 using SelHuge = SelShape<16, 1024, 4096, kMaxTopk, 8>;  // cap <= 16384 (2 rows per compute unit beat 1 without spills)
-using SelDense = SelShape<0, 512, 4096, kMaxTopk>;   // recovered rows
 
 template <int NT, int NBKT, int MAXK, typename E>
 __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
-                            void *oi, float *ov, int flags);
+                            void *oi, float *ov, int flags, int32_t ibase = 0);
 
 // Row r's slots of an output index array of int32 or int64 entries.
 __device__ __forceinline__ void *out_row(void *base, int64_t r, int topk, int flags)
@@ -406,28 +398,15 @@ template <typename SH>
 __global__ __launch_bounds__(SH::nt, SH::minw > 0 ? SH::minw : 1) void k_select(SelectArgs a)
 {
     constexpr int NREG = SH::nreg, NT = SH::nt, NBKT = SH::nbkt, MAXK = SH::maxk;
-    constexpr bool DENSE = NREG == 0;
     __shared__ SelectLds<NT, NBKT, MAXK> S;
-    int t;
-    const uint64_t *src;
-    int64_t n;
-    if (DENSE) {
-        const int e = blockIdx.x;
-        if (e >= a.row_limit || (unsigned long long)(a.row_base + e) >= a.stats[kStFlagged]) return;
-        t = a.rowlist[a.row_base + e];
-        src = a.scratch + (int64_t)e * a.scratch_stride;
-        const int64_t lo = a.ks[t], hi = a.ke[t];
-        n = hi > lo ? hi - lo : 0;
-    } else {
-        t = blockIdx.x;
-        const int64_t lo = a.ks[t], hi = a.ke[t];
-        const int64_t len = hi > lo ? hi - lo : 0;
-        const uint32_t c = a.cnt[t];
-        if (a.triage && threadIdx.x == 0) triage_one(t, len, c, a.topk, a.cap, a.recover_all, a.rowlist_w, a.stats_w);
-        if (row_flagged(len, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
-        src = a.cand + (int64_t)t * a.cap;
-        n = len > 0 ? min((int64_t)c, (int64_t)a.cap) : 0;  // a.cap <= NREG * NT
-    }
+    const int t = blockIdx.x;
+    const int64_t lo = a.ks[t], hi = a.ke[t];
+    const int64_t len = hi > lo ? hi - lo : 0;
+    const uint32_t c = a.cnt[t];
+    if (a.triage && threadIdx.x == 0) triage_one(t, len, c, a.topk, a.cap, a.recover_all, a.rowlist_w, a.stats_w);
+    if (row_flagged(len, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
+    const uint64_t *src = a.cand + (int64_t)t * a.cap;
+    const int64_t n = len > 0 ? min((int64_t)c, (int64_t)a.cap) : 0;  // a.cap <= NREG * NT
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
     void *oi = out_row(a.out_idx, t, a.topk, a.out_flags);
     float *ov = a.out_val ? a.out_val + (int64_t)t * a.topk : nullptr;
@@ -439,13 +418,14 @@ __global__ __launch_bounds__(SH::nt, SH::minw > 0 ? SH::minw : 1) void k_select(
 // Exact top k of one row's elements (raw candidates, see raw_cand) held by
 // the visitor `el`, written to oi / ov (ov may be null) in key order -- or,
 // with kOutIndexOrder, the same k keys by ascending index -- and padded to
-// topk; indices as int32, or int64 with kOutInt64.  All threads of the block call it; S is the block's LDS.
+// topk; indices (the elements' own plus ibase) as int32, or int64 with
+// kOutInt64.  All threads of the block call it; S is the block's LDS.
 // Element visitors with registers (E::REG) rank keys inside their buckets in
 // parallel; streamed visitors sort each bucket serially and so only take the
 // bucketed path for buckets of at most 48 keys.
 template <int NT, int NBKT, int MAXK, typename E>
 __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
-                            void *oi, float *ov, int flags)
+                            void *oi, float *ov, int flags, int32_t ibase)
 {
     constexpr int NW = NT / 64, BPT = NBKT / NT;
     constexpr bool DENSE = !E::REG;
@@ -651,7 +631,7 @@ __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n
         float v = -__builtin_inff();
         if ((uint32_t)j < k) {
             const uint64_t e = S.sel[j];
-            idx = key_index(e);
+            idx = key_index(e) + ibase;
             v = key_score(e);
         }
         if (flags & kOutInt64) ((int64_t *)oi)[j] = idx;
