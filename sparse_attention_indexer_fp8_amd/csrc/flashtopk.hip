@@ -11,7 +11,7 @@
 //   3. k_score<filter>  fused score (+ bound) + threshold filter -> candidates (MFMA, hot)
 //   4. k_triage         flag rows whose candidates under/overflowed
 //   5. k_select         exact top-k of every unflagged row
-//   6. (flagged rows)   k_score<dense> + k_select<dense> in batches
+//   6. (flagged rows)   k_score<dense> + the row top-k kernels in batches
 // The triage counts are copied to pinned host memory behind step 4; the host
 // waits for that copy (an event, while step 5 runs on the GPU) to size step
 // 6, then returns.  Outputs are complete when the stream reaches the end of
