@@ -380,7 +380,7 @@ using SelSmallK = SelShape<8, 256, 2048, 512>;     // cap <= 2048, topk <= 512: 
 using SelMid = SelShape<8, 512, 4096, kMaxTopk>;   // cap <= 4096
 using SelLarge = SelShape<8, 1024, 4096, kMaxTopk, 8>;  // cap <= 8192
 using SelLargeK = SelShape<16, 512, 4096, 2048, 6>;     // cap <= 8192, topk <= 2048: 3 rows per compute unit, no spills
-using SelHuge = SelShape<16, 1024, 4096, kMaxTopk, 8>;  // cap <= 16384 (2 rows per compute unit beat 1 without spills)
+using SelHuge = SelShape<16, 1024, 8192, kMaxTopk, 8>;  // cap <= 16384: 2 rows per compute unit beat 1 without spills; 8192 buckets thin the dense ones
 
 template <int NT, int NBKT, int MAXK, typename E>
 __device__ void select_core(SelectLds<NT, NBKT, MAXK> &S, const E &el, int64_t n, uint32_t k, int topk,
