@@ -51,9 +51,15 @@ def _run(wl, d, flags, path=0):
     return idx.cpu().numpy(), val.cpu().numpy()
 
 
+def _packed_int():
+    # windows starting inside the keys (ks > 0), several shorter than topk
+    return workloads.integer(600, 600, 64, "fp8", 2501, windows="packed", docs=(40, 300, 20, 240))
+
+
+@pytest.mark.parametrize("make", [lambda: workloads.config(2), _packed_int], ids=["tieheavy", "packed"])
 @pytest.mark.parametrize("path", [0, 3], ids=["candidates", "recover_all"])
-def test_fused_index_order_and_int64(path):
-    wl = workloads.config(2)  # tie-heavy integer data, topk 512, rows shorter than topk
+def test_fused_index_order_and_int64(path, make):
+    wl = make()  # tie-heavy integer data; rows shorter than topk
     d = to_device(wl)
     base = _run(wl, d, 0, path)
     rep = parity(wl, base[0], base[1], "exact")
