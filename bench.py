@@ -43,7 +43,10 @@ def parse():
                     help="named workload 1..8 (4 is the headline; 6 has block-local keys for pruning; "
                          "7 and 8 are decode shapes with 1 and 64 query rows)")
     ap.add_argument("--integer-twin", action="store_true")
-    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scan, 2 prune, 3 recover all")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scan, 2 prune, 3 dense (recover all), 4 fused")
+    ap.add_argument("--also", default="3,5", metavar="N,N",
+                    help="other named workloads timed in the same run and reported under 'other_workloads' "
+                         "(empty: none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--profile-steps", type=int, default=5)
@@ -262,11 +265,82 @@ def main():
 
     import workloads
     import sparse_attention_indexer_fp8_amd as ftk
-    from sparse_attention_indexer_fp8_amd import Options
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
     wl = workloads.config(args.workload, integer_twin=args.integer_twin)
+    m = measure(wl, args, full=True)
+    T, S, topk, dt, pairs = m["T"], m["S"], m["topk"], m["dtype"], m["pairs"]
+    traffic = recorded_traffic() if (args.workload == 4 and not args.integer_twin and dt == "fp8") else None
+    peak = PEAK_TFLOPS[dt]
+    out = {
+        "metric": METRIC,
+        "value": round(m["ms"], 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "num_q": T, "num_kv": S, "topk": topk, "heads": int(wl["q"].shape[1]),
+                   "dim": 128,
+                   "windows": "packed" if args.workload == 5 else "causal", "window_pairs": pairs,
+                   "path": PATH_NAMES[args.path],
+                   "kv": f"paged, {args.paged} keys per page" if args.paged else "contiguous"},
+        "rows_per_s": round(T / (m["ms"] * 1e-3), 1),
+        "pct_mfma_peak": m["pct_mfma_peak"],
+        "dense_equiv_tflops": m["dense_equiv_tflops"],
+        "wall_ms_per_step": round(m["wall_ms"], 4),
+        "ms_per_call_median": m["ms_per_call_median"],
+        "ms_per_call_min": m["ms_per_call_min"],
+        "ms_cold_call": m["ms_cold_call"],
+        "pruned_key_fraction": m["pruned_key_fraction"],
+        "path_taken": m["path_taken"],
+        "rows_recovered": m["rows_recovered"],
+        "max_candidates": m["max_candidates"],
+        "kernels_ms": m["kernels_ms"],
+        "roofline": {"bound": "mfma", "kernel": m["roofline_kernel"], "achieved": m["achieved_tflops"],
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(m["achieved_tflops"] / peak, 4),
+                     "traffic": traffic, "flops_per_launch": m["flops"]},
+    }
+    others = {}
+    for n in [int(x) for x in args.also.split(",") if x.strip()]:
+        if n == args.workload:
+            continue
+        owl = workloads.config(n)
+        om = measure(owl, args, full=False)
+        others[owl["name"]] = {k: om[k] for k in ("ms", "pct_mfma_peak", "dense_equiv_tflops", "path_taken",
+                                                  "rows_recovered", "kernels_ms", "achieved_tflops",
+                                                  "roofline_kernel")}
+        others[owl["name"]]["ms"] = round(om["ms"], 4)
+        others[owl["name"]]["roofline_frac"] = round(om["achieved_tflops"] / PEAK_TFLOPS[om["dtype"]], 4)
+        others[owl["name"]]["peak_tflops"] = PEAK_TFLOPS[om["dtype"]]
+        del owl
+    if others:
+        out["other_workloads"] = others
+    if not args.no_cpu:
+        print("bench: cpu oracle leg", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+PATH_NAMES = {0: "auto", 1: "scan", 2: "prune", 3: "dense", 4: "fused"}
+
+
+def measure(wl, args, full):
+    """Times one workload: K back-to-back calls after W warm-up calls (HIP
+    events on the stream), then per-phase device times (options.profile);
+    with full, also calls one at a time and one cold call."""
+    import torch
+
+    import workloads
+    import sparse_attention_indexer_fp8_amd as ftk
+    from sparse_attention_indexer_fp8_amd import Options
+
+    dev = torch.device("cuda:0")
     T, S, topk, dt = wl["q"].shape[0], wl["kv"].shape[0], wl["topk"], wl["dtype"]
     pairs = workloads.window_sum(wl)
     print(f"bench: workload {wl['name']} T={T} S={S} topk={topk} dtype={dt} pairs={pairs}", file=sys.stderr,
@@ -289,7 +363,7 @@ def main():
     opt = Options()
     opt.path = args.path
 
-    if args.paged:
+    if args.paged and full:
         ps = args.paged
         nblk = (S + ps - 1) // ps
         g = torch.Generator(device=dev)
@@ -332,80 +406,60 @@ def main():
     popt = Options()
     popt.path = args.path
     popt.profile = 1
-    phases = {k: [] for k in ("ms_sample", "ms_tau", "ms_filter", "ms_triage", "ms_select", "ms_recover")}
+    phases = {k: [] for k in ("ms_sample", "ms_tau", "ms_filter", "ms_select", "ms_recover")}
     for _ in range(args.profile_steps):
         step(popt)
         pi = ftk.flashtopk_get_last_info()
         for k in phases:
             phases[k].append(pi[k])
     kern = {k[3:]: float(np.mean(v)) for k, v in phases.items()}
+    dense = info["path"] == ftk.PATH_RECOVER
 
-    # Per-call device times (events around each call; the steps above run
-    # back to back, these one at a time), and one cold call after a 1 GiB
-    # scrub of the caches.
-    per = []
-    for _ in range(max(20, min(args.steps, 50))):
+    res = {"T": T, "S": S, "topk": topk, "dtype": dt, "pairs": pairs, "ms": ms, "wall_ms": wall_ms}
+    if full:
+        # Per-call device times (events around each call; the steps above run
+        # back to back, these one at a time), and one cold call after a 1 GiB
+        # scrub of the caches.
+        per = []
+        for _ in range(max(20, min(args.steps, 50))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        scrub.fill_(1)
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         step()
         e1.record()
         torch.cuda.synchronize()
-        per.append(e0.elapsed_time(e1))
-    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    scrub.fill_(1)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    step()
-    e1.record()
-    torch.cuda.synchronize()
-    cold_ms = e0.elapsed_time(e1)
-    del scrub
-    traffic = recorded_traffic() if (args.workload == 4 and not args.integer_twin and dt == "fp8") else None
-    filt_ms = kern["filter"]
+        res["ms_cold_call"] = round(e0.elapsed_time(e1), 4)
+        res["ms_per_call_median"] = round(float(np.median(per)), 4)
+        res["ms_per_call_min"] = round(float(np.min(per)), 4)
+        del scrub
+    # The dominant kernel: the fused filter scan, or (dense path) the whole
+    # dense call (its scoring kernel and the row top-k).
+    filt_ms = kern["recover"] if dense else kern["filter"]
     flops = float(FLOP_PER_PAIR) * (wl["q"].shape[1] // 32) * pairs
     peak = PEAK_TFLOPS[dt]
     achieved = flops / (filt_ms * 1e-3) / 1e12 if filt_ms > 0 else 0.0
     whole = flops / (ms * 1e-3) / 1e12
-
-    out = {
-        "metric": METRIC,
-        "value": round(ms, 4),
-        "unit": "ms",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dt,
-        "data": "synthetic",
-        "config": {"workload": wl["name"], "num_q": T, "num_kv": S, "topk": topk, "heads": int(wl["q"].shape[1]),
-                   "dim": 128,
-                   "windows": "packed" if args.workload == 5 else "causal", "window_pairs": pairs,
-                   "path": {0: "auto", 1: "scan", 2: "prune", 3: "recover"}[args.path],
-                   "kv": f"paged, {args.paged} keys per page" if args.paged else "contiguous"},
-        "rows_per_s": round(T / (ms * 1e-3), 1),
+    res.update({
         "pct_mfma_peak": round(100.0 * whole / peak, 2),
         "dense_equiv_tflops": round(whole, 1),
-        "wall_ms_per_step": round(wall_ms, 4),
-        "ms_per_call_median": round(float(np.median(per)), 4),
-        "ms_per_call_min": round(float(np.min(per)), 4),
-        "ms_cold_call": round(cold_ms, 4),
         "pruned_key_fraction": info["pruned_keys"] / max(1, info["window_keys"]),
-        "path_taken": {1: "scan", 2: "prune", 3: "recover"}.get(info["path"], "?"),
+        "path_taken": {1: "scan", 2: "prune", 3: "dense"}.get(info["path"], "?"),
         "rows_recovered": info["rows_recovered"],
         "max_candidates": info["max_candidates"],
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
-        "roofline": {"bound": "mfma", "kernel": "k_score<filter>", "achieved": round(achieved, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "flops_per_launch": flops},
-    }
-    if not args.no_cpu:
-        print("bench: cpu oracle leg", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+        "achieved_tflops": round(achieved, 1),
+        "flops": flops,
+        "roofline_kernel": "k_score<dense> + row top-k (dense path)" if dense else "k_score<filter>",
+    })
+    return res
 
 
 if __name__ == "__main__":

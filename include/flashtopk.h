@@ -34,13 +34,15 @@
  * Synchronisation: work is enqueued on `stream` (a hipStream_t; NULL is the
  * device's null stream) and is stream-ordered: out_idx / out_val are complete
  * once the stream has reached the end of the call's work (synchronise the
- * stream, or wait on an event recorded after the call).  A call with more
- * than 4 query rows blocks the calling thread until the GPU has classified
- * the rows (it reads back how many rows need dense rescoring), but not until
- * the selection is done; a call with at most 4 rows does not block at all
- * (its rescoring is launched for every row up front, when its scratch fits
- * the recovery budget, and its statistics are read back when
- * flashtopk_get_last_info asks for them).
+ * stream, or wait on an event recorded after the call).  A call does not
+ * block the calling thread: every decision (which rows need dense
+ * rescoring, whether a tile prunes) stays on the device, and the rescoring
+ * is launched up front in batches sized for the worst case, whose work
+ * items exit at once when no row needs them.  Exceptions: a call that grows
+ * the workspace first drains the stream (flashtopk_reserve avoids this), and
+ * options.validate / options.profile wait for the GPU.  Calls on one stream
+ * from several host threads are serialised by a lock on the stream's
+ * workspace; calls on different streams run concurrently.
  *
  * Errors: every entry point returns 0 (FLASHTOPK_OK) or a positive status;
  * nothing is thrown across the ABI and nothing is printed.  Preconditions
@@ -75,11 +77,21 @@ extern "C" {
 #define FLASHTOPK_ERR_HIP 4              /* a HIP runtime or launch error */
 
 /* Execution paths.  Every path returns bit-identical results; they differ only
- * in speed.  Used by tests and benchmarks to force a path. */
-#define FLASHTOPK_PATH_AUTO 0     /* the planner decides per call */
-#define FLASHTOPK_PATH_SCAN 1     /* sampled threshold + full scan, no pruning */
-#define FLASHTOPK_PATH_PRUNE 2    /* sampled threshold + score-bound key pruning */
-#define FLASHTOPK_PATH_RECOVER 3  /* dense rescoring + exact select for every row */
+ * in speed.  Used by tests and benchmarks to force a path.
+ *   AUTO     calls of at most 16M (row, key) pairs (num_q * num_kv) take the
+ *            dense path, larger ones the fused path with the per-tile prune
+ *            decision
+ *   SCAN     fused: sampled threshold + full filtering scan, no pruning
+ *   PRUNE    fused: sampled threshold + score-bound key pruning everywhere
+ *   RECOVER  dense: every row's window scores are materialised in the
+ *            workspace and selected exactly (the rescoring that the fused
+ *            path applies to rows its threshold misjudged)
+ *   FUSED    fused with the per-tile prune decision, whatever the size */
+#define FLASHTOPK_PATH_AUTO 0
+#define FLASHTOPK_PATH_SCAN 1
+#define FLASHTOPK_PATH_PRUNE 2
+#define FLASHTOPK_PATH_RECOVER 3
+#define FLASHTOPK_PATH_FUSED 4
 
 /* Output options (DeepSelect README, "Usage": sorted_index and indices_type;
  * "Recommendations": index order costs time).  Bit flags.
@@ -102,7 +114,12 @@ typedef struct flashtopk_options {
     int sample_target;        /* most keys sampled per row for the
                                  threshold; 0 = 2048, at most 2048 (the
                                  lattice stride is also at least topk / 32) */
-    int64_t recover_budget_bytes; /* scratch for dense rescoring; 0 = 1 GiB */
+    int64_t recover_budget_bytes; /* scratch for dense scores; 0 = 1 GiB.  The
+                                 fused path reserves it for the rescoring it
+                                 launches up front; rows are rescored in
+                                 batches of budget / (4 * num_kv) rows (at
+                                 least 16), so a smaller budget means more
+                                 batches */
     int profile;              /* nonzero: time each kernel phase with HIP
                                  events on the call's stream (ms_* of
                                  flashtopk_info); adds a few microseconds */
@@ -138,16 +155,18 @@ typedef struct flashtopk_options {
 /* What the last call on a stream did (README, "Usage": last_info). */
 typedef struct flashtopk_info {
     int32_t status;             /* status of that call */
-    int32_t path;               /* FLASHTOPK_PATH_SCAN / _PRUNE / _RECOVER */
+    int32_t path;               /* FLASHTOPK_PATH_SCAN / _PRUNE (fused path, pruned
+                                   somewhere or not) or _RECOVER (dense path) */
     int64_t rows;               /* num_q */
     int64_t rows_empty;         /* ks == ke */
-    int64_t rows_take_all;      /* window no longer than the candidate capacity:
-                                   every key is a candidate */
-    int64_t rows_sampled;       /* rows filtered by a sampled threshold */
-    int64_t rows_underflow;     /* sampled rows left with fewer than topk candidates */
-    int64_t rows_overflow;      /* sampled rows with more candidates than capacity */
-    int64_t rows_recovered;     /* rows rescored densely (underflow + overflow,
-                                   or every row on the recover path) */
+    int64_t rows_take_all;      /* fused path: window no longer than the candidate
+                                   capacity, every key is a candidate */
+    int64_t rows_sampled;       /* fused path: rows filtered by a sampled threshold */
+    int64_t rows_underflow;     /* fused path: rows left with fewer than min(topk,
+                                   window) candidates */
+    int64_t rows_overflow;      /* fused path: rows with more candidates than capacity */
+    int64_t rows_recovered;     /* rows rescored densely (fused path: underflow +
+                                   overflow; dense path: every non-empty row) */
     int64_t max_candidates;     /* largest candidate count of a sampled row */
     int64_t window_keys;        /* sum of window lengths */
     int64_t pruned_keys;        /* (row, key) pairs skipped by the score bound */
@@ -156,8 +175,9 @@ typedef struct flashtopk_info {
     /* Device time of each phase in milliseconds when the call ran with
      * options.profile set, else 0: strided-sample scoring (with the per-key
      * and per-row preparation passes), per-row threshold, fused score +
-     * filter (with the score bound), triage, candidate selection, dense
-     * recovery. */
+     * filter (with the score bound), triage (0: done inside the selection),
+     * candidate selection with triage, dense recovery (the dense path: the
+     * whole call). */
     float ms_sample, ms_tau, ms_filter, ms_triage, ms_select, ms_recover;
     int32_t invalid;            /* FLASHTOPK_INVALID_* bits found by options.validate, else 0 */
 } flashtopk_info;
@@ -205,8 +225,11 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales,
  * smaller index first among equal values, padded with -1 / -inf; +0 and -0
  * compare equal and values come back as float32 (BF16 widened exactly), +0
  * for a zero.  0 <= rows, cols < 2^31, 1 <= topk <= 4096.  rows == 0 is a
- * no-op.  Enqueued on `stream` without blocking the host and with no
- * workspace.  Ownership, synchronisation and errors as for flashtopk_select. */
+ * no-op.  Enqueued on `stream` without blocking the host.  Calls of few rows
+ * (fewer than the GPU has compute units) split each row over several
+ * workgroups and keep per-row state in the stream's workspace (a few bytes
+ * per row plus 64 KiB per row of candidates); others use no workspace.
+ * Ownership, synchronisation and errors as for flashtopk_select. */
 int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t cols, int64_t row_stride,
                         const int32_t *ends, int topk, void *out_idx, float *out_val, int32_t *nan_flag,
                         int out_flags, void *stream);
@@ -229,13 +252,31 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
                            float *out_val, void *stream, const flashtopk_options *opt);
 
 /* Pre-allocate the workspace of (current device, stream) for calls up to the
- * given sizes, so later calls allocate nothing (README, "Usage": the
- * Selector's plan() owns the workspace and prepares up front). */
+ * given sizes (README, "Usage": the Selector's plan() owns the workspace and
+ * prepares up front), so that later calls of at most max_q rows, max_kv keys
+ * and max_topk, of this dtype, with 32 or 64 heads, on either path, with the
+ * default candidate capacity, sample size and recovery budget, and row top-k
+ * calls of at most max_q rows of max_kv entries, allocate nothing and never
+ * drain the stream.  Calls whose options raise the capacity, the sample size
+ * or the budget may still grow it.  The workspace holds about
+ * max_q * (8 * min(16384, 4 * max_topk) + 8 KiB) bytes plus the recovery
+ * scratch (up to 1 GiB by default). */
 int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream);
 
-/* Statistics of the last call issued on `stream` from this process (waits
- * for that call's statistics to reach the host if they have not yet). */
+/* Record of the last call issued on `stream` from this process.  Synchronises
+ * the stream, then counts the row classes from the workspace's arrays (so it
+ * must be read before the next call on the stream overwrites them).  Returns
+ * FLASHTOPK_ERR_INVALID_ARGUMENT if the stream has had no call. */
 int flashtopk_get_last_info(void *stream, flashtopk_info *out);
+
+/* Rows that the last call on `stream` scored densely (README, "Highlights":
+ * rows whose sampled threshold misjudged them are rescored; on the dense
+ * path, every row with a non-empty window), as a diagnostic: synchronises
+ * the stream, writes the first min(count, max_rows) row indices, in no
+ * particular order, to the host array `rows`, and their number to *count.
+ * Like flashtopk_get_last_info it must be read before the next call on the
+ * stream.  rows may be NULL when max_rows is 0. */
+int flashtopk_get_last_recovered(void *stream, int32_t *rows, int64_t max_rows, int64_t *count);
 
 /* Frees every cached workspace.  No call may be in flight. */
 void flashtopk_release(void);

@@ -33,7 +33,7 @@ FLASHTOPK_INVALID_WEIGHT = 8
 FLASHTOPK_INVALID_SCALE = 16
 FLASHTOPK_INVALID_PAGE = 32
 
-PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER = 0, 1, 2, 3
+PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER, PATH_FUSED = 0, 1, 2, 3, 4
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "out of device memory",
           4: "HIP runtime error"}
@@ -89,8 +89,9 @@ class Info(ctypes.Structure):
 
 
 # Every symbol include/flashtopk.h declares.
-EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_select_paged", "flashtopk_topk_rows", "flashtopk_reserve", "flashtopk_get_last_info",
-           "flashtopk_release", "flashtopk_status_string", "flashtopk_version")
+EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_select_paged", "flashtopk_topk_rows",
+           "flashtopk_reserve", "flashtopk_get_last_info", "flashtopk_get_last_recovered", "flashtopk_release",
+           "flashtopk_status_string", "flashtopk_version")
 
 _lib = None
 
@@ -118,6 +119,8 @@ def load_library():
     lib.flashtopk_reserve.restype = I
     lib.flashtopk_get_last_info.argtypes = [P, ctypes.POINTER(Info)]
     lib.flashtopk_get_last_info.restype = I
+    lib.flashtopk_get_last_recovered.argtypes = [P, P, I64, ctypes.POINTER(I64)]
+    lib.flashtopk_get_last_recovered.restype = I
     lib.flashtopk_release.argtypes = []
     lib.flashtopk_release.restype = None
     lib.flashtopk_status_string.argtypes = [I]
@@ -306,6 +309,25 @@ def flashtopk_get_last_info(stream=None) -> dict:
     if st != 0:
         raise FlashTopKError(st, "flashtopk_get_last_info")
     return info.as_dict()
+
+
+def flashtopk_get_last_recovered(stream=None):
+    """Row indices (sorted int32 numpy array) that the last call on the stream
+    scored densely."""
+    import numpy as np
+
+    lib = load_library()
+    h = ctypes.c_void_p(_stream_handle(stream))
+    n = ctypes.c_int64(0)
+    st = lib.flashtopk_get_last_recovered(h, None, 0, ctypes.byref(n))
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_get_last_recovered")
+    out = np.zeros(n.value, dtype=np.int32)
+    if n.value:
+        st = lib.flashtopk_get_last_recovered(h, out.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n))
+        if st != 0:
+            raise FlashTopKError(st, "flashtopk_get_last_recovered")
+    return np.sort(out)
 
 
 def flashtopk_release() -> None:

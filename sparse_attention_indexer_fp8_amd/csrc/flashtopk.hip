@@ -1,21 +1,36 @@
 // C ABI of the fused indexer top-k library (declared in include/flashtopk.h).
 //
-// Launch sequence of one call, all on the caller's stream:
+// Two call sequences, both entirely on the caller's stream and neither
+// waiting on the host:
+//
+// Fused path (FlashTopK README, "Highlights": a per-row threshold from a
+// strided sample of the row's own window, candidates, exact selection; rows
+// the threshold misjudges are rescored):
 //   0. k_prep           per-key scale factors (+ block extremes for the bound)
 //                       and (FP8) head-weighted query sums split into FP8
-//                       parts, in one launch
+//                       parts, in one launch; clears the call's counters
 //   1. k_score<sample>  strided-sample scores of every long row     (MFMA);
 //                       with one workgroup per tile it also sets the
 //                       tile's per-row thresholds from those samples
 //   2. k_tau            (several workgroups per tile) the thresholds
 //   3. k_score<filter>  fused score (+ bound) + threshold filter -> candidates (MFMA, hot)
-//   4. k_triage         flag rows whose candidates under/overflowed
-//   5. k_select         exact top-k of every unflagged row
-//   6. (flagged rows)   k_score<dense> + the row top-k kernels in batches
-// The triage counts are copied to pinned host memory behind step 4; the host
-// waits for that copy (an event, while step 5 runs on the GPU) to size step
-// 6, then returns.  Outputs are complete when the stream reaches the end of
-// the call's work.
+//   4. k_select         triage (flagged rows go to a list on the device) and
+//                       the exact top-k of every other row
+//   5. recovery         k_score<dense> + k_topk_rows over the flagged rows, in
+//                       batches whose scratch fits the budget; launched
+//                       without knowing how many rows were flagged (batch
+//                       rows past the list's device-side length exit)
+//
+// Dense path (calls of few rows, and the forced recover-all path): every
+// row's window scores are materialised (k_score<dense>, computing its own
+// query sums and scale factors) and the row top-k kernels select from them;
+// with few rows each row is split over several workgroups.
+//
+// Both paths score a (row, key) pair with the same instruction sequence, so
+// a row's results do not depend on the path or on the other rows of the
+// call.  Outputs are complete when the stream reaches the end of the call's
+// work.  The counts of flashtopk_info are computed on the host, from each
+// row's window length and candidate count, when the record is read.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -27,7 +42,6 @@
 
 #include "flashtopk.h"
 #include "ftk_bound.hpp"
-#include "ftk_few.hpp"
 #include "ftk_paged.hpp"
 #include "ftk_rows.hpp"
 #include "ftk_score.hpp"
@@ -42,6 +56,16 @@ namespace {
 constexpr int kMaxCap = 16384;
 constexpr int kDefaultSampleTarget = 2048;
 constexpr int64_t kDefaultRecoverBudget = int64_t(1) << 30;
+// The auto path scores every row densely when the call's (row, key) pairs
+// are at most this many: materialising the scores then costs less than the
+// fused path's fixed passes (preparation, sample, thresholds, selection).
+constexpr int64_t kDensePairs = int64_t(16) << 20;
+// Smallest key chunk of a dense-mode work item.
+constexpr int kMinDenseChunk = 512;
+// Split-row top-k: at most this many workgroups per row, each streaming at
+// least kMinSplitEntries entries.
+constexpr int kMaxSplit = 64;
+constexpr int64_t kMinSplitEntries = 4096;
 
 // Grow-only device buffer.
 struct DevBuf {
@@ -49,21 +73,24 @@ struct DevBuf {
     size_t bytes = 0;
 };
 
+// Record of the last call on a stream; its counts are computed from the
+// workspace's device arrays when flashtopk_get_last_info reads it.
+enum CallKind { kCallNone = 0, kCallFailed, kCallFused, kCallDense };
+
 struct Workspace {
     int device = -1;
     hipStream_t stream = nullptr;
-    DevBuf tau, cnt, rowlist, stats, cand, samp, scratch, qbar, qscale, sigh;
-    DevBuf kb, kmeta, vplan, q1;               // score-bound pruning
-    DevBuf ticket;                             // few-row sample finish counters (kept zero between calls)
-    DevBuf pkv, psig;                          // keys and scales gathered from a paged cache
-    DevBuf vflag;                              // precondition flags (options.validate)
-    unsigned long long *host_stats = nullptr;  // pinned: kStCount statistics, then the precondition flags
-    hipEvent_t ev[7] = {};                     // phase boundaries when profiling
-    hipEvent_t stats_ev = nullptr;             // triage counts have reached the host
-    flashtopk_info last{};
-    bool has_last = false;
-    bool last_pending = false;   // counts of `last` not yet read from host_stats
-    bool last_recover_all = false;
+    std::mutex mu;  // held while a call is enqueued or its record read
+    DevBuf tau, cnt, rowlist, stats, wlen, cand, samp, scratch, qbar, qscale, sigh;
+    DevBuf kb, kmeta, vplan, q1;                 // score-bound pruning
+    DevBuf scnt, sover, sticket, scand;          // split-row top-k (kept zero between calls)
+    DevBuf pkv, psig;                            // keys and scales gathered from a paged cache
+    DevBuf vflag;                                // precondition flags (options.validate)
+    unsigned *host_flag = nullptr;               // pinned: the precondition flags
+    hipEvent_t ev[7] = {};                       // phase boundaries when profiling
+    int last_kind = kCallNone;
+    flashtopk_info last{};                       // status, sizes, timings of the last call
+    int last_topk = 0;
 };
 
 std::mutex g_mu;
@@ -122,7 +149,7 @@ Workspace *get_ws(hipStream_t stream, int *status)
     Workspace *w = new Workspace();
     w->device = dev;
     w->stream = stream;
-    e = hipHostMalloc((void **)&w->host_stats, sizeof(unsigned long long) * (kStCount + 1), hipHostMallocDefault);
+    e = hipHostMalloc((void **)&w->host_flag, sizeof(unsigned), hipHostMallocDefault);
     if (e != hipSuccess) {
         delete w;
         *status = hip_status(e);
@@ -142,7 +169,7 @@ struct Plan {
     int profile;
     int out_flags;
     int heads;  // 32, or 64 (each row's halves are a pair of tile columns)
-    // keys in a paged cache, read in place (calls with at most kFewRows rows)
+    // keys in a paged cache, read in place (dense path)
     const int32_t *table = nullptr;
     int page_size = 0;
     int64_t num_pages = 0;
@@ -151,7 +178,7 @@ struct Plan {
 int resolve(Plan &p, const flashtopk_options *opt)
 {
     p.path = opt ? opt->path : FLASHTOPK_PATH_AUTO;
-    if (p.path < FLASHTOPK_PATH_AUTO || p.path > FLASHTOPK_PATH_RECOVER) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (p.path < FLASHTOPK_PATH_AUTO || p.path > FLASHTOPK_PATH_FUSED) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     int cap = (opt && opt->cand_capacity > 0) ? opt->cand_capacity : std::min(kMaxCap, 4 * p.topk);
     p.cap = std::min(kMaxCap, std::max(cap, p.topk));
     p.sample_target = (opt && opt->sample_target > 0) ? std::min(opt->sample_target, (int)kTauBuckets)
@@ -187,19 +214,19 @@ int num_cu()
     return n_cu;
 }
 
-// Keys per work item (a power of two in [kMinChunk, kMaxChunk]), from a cost
+// Keys per work item (a power of two in [min_chunk, kMaxChunk]), from a cost
 // model: a work item takes a whole compute unit (its LDS), so items run in
 // rounds of one per CU, and an item costs a fixed part (setting up and
 // staging the q tile, flushing candidates: about one wave step) plus the wave
 // steps of each of its `waves` waves.  The chunk of least cost wins, the
 // larger one on a tie: large chunks amortise the fixed part, small ones fill
 // the GPU when the call has few tiles.
-int chunk_keys(int ntiles, int64_t S, int waves)
+int chunk_keys(int ntiles, int64_t S, int waves, int min_chunk = kMinChunk)
 {
     const int64_t n_cu = num_cu();
     int best = kMaxChunk;
     int64_t best_cost = INT64_MAX;
-    for (int chunk = kMaxChunk; chunk >= kMinChunk; chunk >>= 1) {
+    for (int chunk = kMaxChunk; chunk >= min_chunk; chunk >>= 1) {
         const int64_t items = (int64_t)ntiles * ((S + chunk - 1) / chunk);
         const int64_t rounds = (items + n_cu - 1) / n_cu;
         const int64_t steps = (chunk / kStepKeys + waves - 1) / waves;
@@ -219,6 +246,17 @@ int sample_split(int ntiles)
     int split = 1;
     while (split < 16 && (int64_t)ntiles * split * 2 <= num_cu()) split <<= 1;
     return split;
+}
+
+// Workgroups per row of the row top-k: rows that leave most compute units
+// idle are split so the GPU streams them with about two workgroups per CU.
+int split_parts(int64_t rows, int64_t cols)
+{
+    int parts = 1;
+    while (parts < kMaxSplit && rows * parts * 2 <= 2 * (int64_t)num_cu() &&
+           cols / (parts * 2) >= kMinSplitEntries)
+        parts <<= 1;
+    return parts;
 }
 
 template <int DT>
@@ -247,21 +285,6 @@ void launch_score_dt(int dtype, int mode, dim3 grid, hipStream_t st, const Score
     else launch_score<kBF16>(mode, grid, st, a);
 }
 
-// Calls with at most kFewRows rows score with k_score_few in every mode.
-template <int DT>
-void launch_few(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
-{
-    if (mode == kModeSample) k_score_few<DT, kModeSample><<<grid, kFewThreads, 0, st>>>(a);
-    else if (mode == kModeFilter) k_score_few<DT, kModeFilter><<<grid, kFewThreads, 0, st>>>(a);
-    else k_score_few<DT, kModeDense><<<grid, kFewThreads, 0, st>>>(a);
-}
-
-void launch_few_dt(int dtype, int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
-{
-    if (dtype == FLASHTOPK_FP8_E4M3) launch_few<kFP8>(mode, grid, st, a);
-    else launch_few<kBF16>(mode, grid, st, a);
-}
-
 // Phase boundary i of a profiled call (no-op otherwise).
 void mark(Workspace &w, const Plan &p, int i, hipStream_t stream)
 {
@@ -270,374 +293,28 @@ void mark(Workspace &w, const Plan &p, int i, hipStream_t stream)
     (void)hipEventRecord(w.ev[i], stream);
 }
 
-float phase_ms(Workspace &w, const Plan &p, int i)
+float phase_ms(Workspace &w, const Plan &p, int i, int j)
 {
     float ms = 0.0f;
-    if (p.profile && w.ev[i] && w.ev[i + 1] && hipEventElapsedTime(&ms, w.ev[i], w.ev[i + 1]) != hipSuccess) {
+    if (p.profile && w.ev[i] && w.ev[j] && hipEventElapsedTime(&ms, w.ev[i], w.ev[j]) != hipSuccess) {
         (void)hipGetLastError();
         ms = 0.0f;
     }
     return ms;
 }
 
-// Copies the statistics of the workspace's last call (already in pinned host
-// memory) into its record.
-void fill_counts(Workspace &w)
-{
-    flashtopk_info &info = w.last;
-    const unsigned long long *hs = w.host_stats;
-    info.path = w.last_recover_all ? FLASHTOPK_PATH_RECOVER
-                                   : (hs[kStPruneOn] ? FLASHTOPK_PATH_PRUNE : FLASHTOPK_PATH_SCAN);
-    info.rows_empty = (int64_t)hs[kStEmpty];
-    info.rows_take_all = (int64_t)hs[kStTakeAll];
-    info.rows_sampled = (int64_t)hs[kStSampled];
-    info.rows_underflow = (int64_t)hs[kStUnder];
-    info.rows_overflow = (int64_t)hs[kStOver];
-    info.rows_recovered = (int64_t)hs[kStFlagged];
-    info.max_candidates = (int64_t)hs[kStMaxCand];
-    info.window_keys = (int64_t)hs[kStWindow];
-    info.pruned_keys = (int64_t)hs[kStPruned];
-    w.last_pending = false;
-}
-
-template <typename T, typename SH>
-void launch_rows(const RowsArgs &a, hipStream_t s);
-
-int run(const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
-        const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
-{
-    int st = FLASHTOPK_OK;
-    Workspace *w = get_ws(stream, &st);
-    if (!w) return st;
-    const int64_t T = p.T, S = p.S;
-    if ((st = ensure(*w, w->tau, sizeof(float) * T))) return st;
-    if ((st = ensure(*w, w->cnt, sizeof(uint32_t) * T))) return st;
-    if ((st = ensure(*w, w->rowlist, sizeof(int32_t) * T))) return st;
-    if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
-    const bool recover_all = p.path == FLASHTOPK_PATH_RECOVER;
-    const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
-    // 64 heads: row t's two 32-head halves are tile columns 2t and 2t + 1.
-    const int ps = p.heads == 64 ? 1 : 0;
-    const int64_t TC = T << ps;  // tile columns
-    if (fp8) {
-        if ((st = ensure(*w, w->qbar, (size_t)TC * kQbarParts * kDim))) return st;
-        if ((st = ensure(*w, w->qscale, sizeof(float) * TC))) return st;
-    }
-    if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(S + 64)))) return st;
-    if (!recover_all) {
-        if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * p.cap))) return st;
-        if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * p.sample_target))) return st;
-    }
-
-    const int ntiles = (int)((TC + kTileQ - 1) / kTileQ);
-    // A few rows (decode) score with k_score_few, which has no bound pruning.
-    const bool few = !ps && T <= kFewRows;
-    // Score-bound pruning: on the auto path (each scan work item decides from
-    // its tile's planner sample) and the forced prune path; not for 64 heads.
-    const bool bounds = !few && !ps && S > 0 && (p.path == FLASHTOPK_PATH_AUTO || p.path == FLASHTOPK_PATH_PRUNE);
-    const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
-    if (bounds) {
-        if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
-        if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)nblocks))) return st;
-        if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
-        if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
-    }
-    const int chunk = chunk_keys(ntiles, S, fp8 ? ScoreCfg<kFP8, kModeFilter>::waves : ScoreCfg<kBF16, kModeFilter>::waves);
-    const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
-
-    ScoreArgs sa{};
-    sa.q = (const uint8_t *)q;
-    sa.kv = (const uint8_t *)kv;
-    sa.sigma = kv_scales;
-    sa.sigh = (const float *)w->sigh.ptr;
-    sa.w = weights;
-    sa.ks = ks;
-    sa.ke = ke;
-    sa.num_q = (int)TC;
-    sa.num_kv = (int)S;
-    sa.pair = ps;
-    sa.qbar = (const uint8_t *)w->qbar.ptr;
-    sa.qscale = (const float *)w->qscale.ptr;
-    sa.ntiles = ntiles;
-    sa.chunk = chunk;
-    sa.cap = p.cap;
-    sa.tau = (const float *)w->tau.ptr;
-    sa.cnt = (uint32_t *)w->cnt.ptr;
-    sa.cand = (uint64_t *)w->cand.ptr;
-    sa.samp = (uint32_t *)w->samp.ptr;
-    sa.sample_target = p.sample_target;
-    sa.sample_min_stride = p.sample_min_stride;
-    sa.sample_split = sample_split(ntiles);
-    sa.table = p.table;
-    sa.page_size = p.page_size;
-    sa.num_pages = p.num_pages;
-    if (bounds) {
-        sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
-        sa.kb = (const uint8_t *)w->kb.ptr;
-        sa.meta = (const float2 *)w->kmeta.ptr;
-        sa.q1 = (float *)w->q1.ptr;
-        sa.nblocks = nblocks;
-        sa.vplan = (float *)w->vplan.ptr;
-        sa.plan = (unsigned long long *)w->stats.ptr + kStPruned;
-    }
-
-    // The sample kernel sets the thresholds itself when each row's samples
-    // come from one workgroup per tile, or (few rows) from the row's last
-    // workgroup to finish, which also clears the statistics (no per-key
-    // pass); otherwise k_tau follows it.
-    const bool few_sample = few && !recover_all;
-    const bool fused_tau = !few && !recover_all && sa.sample_split == 1;
-    sa.topk = p.topk;
-    sa.rank_scale = p.rank_scale;
-    sa.tau_w = (float *)w->tau.ptr;
-    if (few_sample) {
-        if ((st = ensure_zeroed(*w, w->ticket, sizeof(uint32_t) * (size_t)T))) return st;
-        sa.ticket = (uint32_t *)w->ticket.ptr;
-        sa.stats = (unsigned long long *)w->stats.ptr;
-        sa.nstats = kStCount;
-    }
-
-    mark(*w, p, 0, stream);
-    {
-        // Per-key scale factors (and block extremes for the bound); with few
-        // rows only the statistics are cleared (k_score_few reads sigma), and
-        // those calls' sample kernel does even that.  FP8 calls of more rows
-        // also get their query sums from the same launch.
-        PrepArgs pa{};
-        const int64_t Sp = few ? 0 : S;
-        pa.key_blocks = few_sample ? 0 : (int)((Sp + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
-        pa.kv = (const uint8_t *)kv;
-        pa.sigma = kv_scales;
-        pa.num_kv = (int)Sp;
-        pa.nblocks = nblocks;
-        pa.sigh = (float *)w->sigh.ptr;
-        pa.bounds = bounds ? 1 : 0;
-        pa.kb = bounds ? (uint8_t *)w->kb.ptr : nullptr;
-        pa.meta = bounds ? (float2 *)w->kmeta.ptr : nullptr;
-        pa.stats = (unsigned long long *)w->stats.ptr;
-        pa.nstats = kStCount;
-        int64_t qblocks = 0;
-        if (fp8 && !few) {
-            pa.q = (const uint8_t *)q;
-            pa.w = weights;
-            pa.num_q = TC;
-            pa.parts = (uint8_t *)w->qbar.ptr;
-            pa.qscale = (float *)w->qscale.ptr;
-            pa.q1 = bounds ? (float *)w->q1.ptr : nullptr;
-            qblocks = (TC + 3) / 4;
-        }
-        const unsigned nwg = (unsigned)(pa.key_blocks + qblocks);
-        if (nwg > 0) {
-            if (fp8) k_prep<kFP8><<<nwg, 256, 0, stream>>>(pa);
-            else k_prep<kBF16><<<nwg, 256, 0, stream>>>(pa);
-        }
-    }
-    if (!recover_all) {
-        if (few)
-            launch_few_dt(p.dtype, kModeSample,
-                          dim3((unsigned)(T * ((p.sample_target + kFewSamplePart - 1) / kFewSamplePart))), stream, sa);
-        else
-            launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * sa.sample_split)), stream, sa);
-    }
-    mark(*w, p, 1, stream);
-
-    if (!recover_all && !few_sample && !fused_tau) {
-        TauArgs ta{};
-        ta.ks = ks;
-        ta.ke = ke;
-        ta.num_q = T;
-        ta.topk = p.topk;
-        ta.cap = p.cap;
-        ta.samp = (const uint32_t *)w->samp.ptr;
-        ta.sample_target = p.sample_target;
-        ta.sample_min_stride = p.sample_min_stride;
-        ta.rank_scale = p.rank_scale;
-        ta.tau = (float *)w->tau.ptr;
-        ta.cnt = (uint32_t *)w->cnt.ptr;
-        k_tau<<<dim3((unsigned)((T + kTauWaves - 1) / kTauWaves)), 64 * kTauWaves, 0, stream>>>(ta);
-    }
-    mark(*w, p, 2, stream);
-
-    if (!recover_all) {
-        if (few)
-            launch_few_dt(p.dtype, kModeFilter, dim3((unsigned)std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk)),
-                          stream, sa);
-        else
-            launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
-    }
-    mark(*w, p, 3, stream);
-
-    SelectArgs se{};
-    se.ks = ks;
-    se.ke = ke;
-    se.topk = p.topk;
-    se.cap = p.cap;
-    se.recover_all = recover_all ? 1 : 0;
-    se.cnt = (const uint32_t *)w->cnt.ptr;
-    se.cand = (const uint64_t *)w->cand.ptr;
-    se.out_idx = out_idx;
-    se.out_val = out_val;
-    se.out_flags = p.out_flags;
-    auto select_rows = [&]() {
-        if (p.cap <= SelSmallK::nreg * SelSmallK::nt && p.topk <= SelSmallK::maxk) launch_select<SelSmallK>(T, stream, se);
-        else if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
-        else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
-        else if (p.cap <= SelLargeK::nreg * SelLargeK::nt && p.topk <= SelLargeK::maxk) launch_select<SelLargeK>(T, stream, se);
-        else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
-        else launch_select<SelHuge>(T, stream, se);
-    };
-    hipError_t e = hipSuccess;
-    if (!w->stats_ev && (e = hipEventCreateWithFlags(&w->stats_ev, hipEventDisableTiming)) != hipSuccess)
-        return hip_status(e);
-    auto copy_stats = [&]() -> hipError_t {
-        hipError_t ce = hipMemcpyAsync(w->host_stats, w->stats.ptr, sizeof(unsigned long long) * kStCount,
-                                       hipMemcpyDeviceToHost, stream);
-        if (ce == hipSuccess) ce = hipEventRecord(w->stats_ev, stream);
-        return ce;
-    };
-    // Dense rescoring of flagged entries [rb, rb + rcap) of the list.
-    auto recover_batch = [&](int64_t rb, int64_t rcap, int64_t stride) {
-        sa.rowlist = (const int32_t *)w->rowlist.ptr;
-        sa.nrows = (const unsigned long long *)w->stats.ptr + kStFlagged;
-        sa.row_limit = (int)rcap;
-        sa.scratch = (float *)w->scratch.ptr;
-        sa.scratch_stride = stride;
-        sa.row_base = (int)rb;
-        if (few) {
-            launch_few_dt(p.dtype, kModeDense,
-                          dim3((unsigned)(rcap * std::max<int64_t>(1, (S + kFewChunk - 1) / kFewChunk))), stream, sa);
-        } else {
-            sa.ntiles = (int)((rcap << ps) / kTileQ);
-            sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves);
-            const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
-            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
-        }
-        // Exact top k of each batch row's window scores: the row top-k
-        // kernels in mapped-row mode (outputs to the flagged row, indices
-        // offset by its window start; entries past the list exit).
-        RowsArgs ra{};
-        ra.x = w->scratch.ptr;
-        ra.rows = rcap;
-        ra.cols = S;
-        ra.stride = stride;
-        ra.topk = p.topk;
-        ra.out_idx = out_idx;
-        ra.out_val = out_val;
-        ra.out_flags = p.out_flags;
-        ra.rowmap = (const int32_t *)w->rowlist.ptr;
-        ra.nrows = (const unsigned long long *)w->stats.ptr + kStFlagged;
-        ra.row_base = rb;
-        ra.ks = ks;
-        ra.ke = ke;
-        if (p.topk <= RowsSmall::maxk) launch_rows<float, RowsSmall>(ra, stream);
-        else launch_rows<float, RowsLarge>(ra, stream);
-    };
-    // Scratch rows of float scores, 16-byte aligned (the row kernels' loads).
-    const int64_t stride = (std::max<int64_t>(S, 1) + 3) / 4 * 4;
-
-    // Few rows whose whole windows fit the recovery budget: the selection
-    // does each row's triage, recovery of every row is launched up front
-    // (rows that need none exit at once), and the call returns without
-    // waiting for the GPU; the statistics are read when asked for.
-    const bool speculative = few && !p.profile && (int64_t)sizeof(float) * T * stride <= p.recover_budget;
-    int64_t R = 0;
-    if (speculative) {
-        if ((st = ensure(*w, w->scratch, sizeof(float) * (size_t)T * stride))) return st;
-        se.triage = 1;
-        se.rowlist_w = (int32_t *)w->rowlist.ptr;
-        se.stats_w = (unsigned long long *)w->stats.ptr;
-        select_rows();
-        mark(*w, p, 4, stream);
-        mark(*w, p, 5, stream);
-        mark(*w, p, 6, stream);
-        recover_batch(0, T, stride);
-        if ((e = copy_stats()) != hipSuccess) return hip_status(e);
-        if ((e = hipGetLastError()) != hipSuccess) return hip_status(e);
-    } else {
-        TriageArgs tr{};
-        tr.ks = ks;
-        tr.ke = ke;
-        tr.num_q = T;
-        tr.topk = p.topk;
-        tr.cap = p.cap;
-        tr.cnt = (const uint32_t *)w->cnt.ptr;
-        tr.recover_all = recover_all ? 1 : 0;
-        tr.rowlist = (int32_t *)w->rowlist.ptr;
-        tr.stats = (unsigned long long *)w->stats.ptr;
-        if (T <= kTriageFewRows)
-            k_triage<1><<<dim3((unsigned)((T + kTriageThreads - 1) / kTriageThreads)), kTriageThreads, 0, stream>>>(tr);
-        else
-            k_triage<16><<<dim3((unsigned)((T + 16 * kTriageThreads - 1) / (16 * kTriageThreads))), kTriageThreads, 0,
-                           stream>>>(tr);
-        // The triage counts go to pinned host memory right away; the host
-        // waits for them (not for the stream) while the select kernel runs,
-        // so the GPU never idles on the host between calls.
-        if ((e = copy_stats()) != hipSuccess) return hip_status(e);
-        mark(*w, p, 4, stream);
-        select_rows();
-        mark(*w, p, 5, stream);
-
-        e = hipGetLastError();
-        if (e == hipSuccess) e = hipEventSynchronize(w->stats_ev);
-        if (e != hipSuccess) return hip_status(e);
-
-        R = (int64_t)w->host_stats[kStFlagged];
-        mark(*w, p, 6, stream);  // recovery timed from here (0 when nothing is flagged)
-        if (R > 0) {
-            // Dense rescoring of flagged rows, in batches that fit the budget.
-            int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(float) * stride));
-            rcap = std::min<int64_t>(rcap, (R + kTileQ - 1) / kTileQ * kTileQ);
-            rcap = (rcap + kTileQ - 1) / kTileQ * kTileQ;
-            if ((st = ensure(*w, w->scratch, sizeof(float) * (size_t)rcap * stride))) return st;
-            for (int64_t rb = 0; rb < R; rb += rcap) recover_batch(rb, rcap, stride);
-            e = hipGetLastError();
-            if (e != hipSuccess) return hip_status(e);
-        }
-    }
-    float ms_rec = 0.0f;
-    if (p.profile) {
-        hipEvent_t end = nullptr;
-        (void)hipEventCreate(&end);
-        (void)hipEventRecord(end, stream);
-        (void)hipEventSynchronize(end);
-        if (hipEventElapsedTime(&ms_rec, w->ev[6], end) != hipSuccess) {
-            (void)hipGetLastError();
-            ms_rec = 0.0f;
-        }
-        (void)hipEventDestroy(end);
-    }
-
-    // The call's record; its counts are filled in from the statistics once
-    // they have reached the host (now, or on the first read of a
-    // speculative call's record).
-    flashtopk_info &info = w->last;
-    std::memset(&info, 0, sizeof(info));
-    info.status = FLASHTOPK_OK;
-    info.rows = T;
-    info.cand_capacity = p.cap;
-    info.sample_target = p.sample_target;
-    info.ms_sample = phase_ms(*w, p, 0);
-    info.ms_tau = phase_ms(*w, p, 1);
-    info.ms_filter = phase_ms(*w, p, 2);
-    info.ms_triage = phase_ms(*w, p, 3);
-    info.ms_select = phase_ms(*w, p, 4);
-    info.ms_recover = R > 0 ? ms_rec : 0.0f;
-    info.invalid = (int32_t)p.invalid;
-    w->last_recover_all = recover_all;
-    w->has_last = true;
-    w->last_pending = true;
-    if (!speculative) fill_counts(*w);
-    return FLASHTOPK_OK;
-}
-
-bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
-// Row top-k launch.  When the rows take more than one wave of resident
-// workgroups, the thresholds are computed up front by k_rows_tau, so that no
+// Row top-k launch.  Few rows are split over several workgroups each (split
+// non-null, split->parts > 1); with more rows than resident workgroups and
+// pre_tau, the thresholds are computed up front by k_rows_tau, so that no
 // row workgroup waits on its sample.
 template <typename T, typename SH>
-void launch_rows(const RowsArgs &a, hipStream_t s)
+void launch_rows(const RowsArgs &a, hipStream_t s, bool pre_tau, const RowsSplit *split)
 {
+    if (split && split->parts > 1) {
+        hipLaunchKernelGGL((k_topk_rows_split<T, SH>), dim3((unsigned)(a.rows * split->parts)), dim3(SH::nt), 0, s, a,
+                           *split);
+        return;
+    }
     static int per_cu = 0;
     if (per_cu == 0) {
         int b = 0;
@@ -647,7 +324,7 @@ void launch_rows(const RowsArgs &a, hipStream_t s)
         per_cu = b;
     }
     const dim3 grid((unsigned)a.rows);
-    if (a.rows > (int64_t)per_cu * num_cu()) {
+    if (pre_tau && a.rows > (int64_t)per_cu * num_cu()) {
         const dim3 tgrid((unsigned)((a.rows + kRowsTauWaves - 1) / kRowsTauWaves));
         hipLaunchKernelGGL((k_rows_tau<T, SH>), tgrid, dim3(64 * kRowsTauWaves), 0, s, a);
         hipLaunchKernelGGL((k_topk_rows<T, SH, true>), grid, dim3(SH::nt), 0, s, a);
@@ -656,37 +333,439 @@ void launch_rows(const RowsArgs &a, hipStream_t s)
     }
 }
 
+template <typename T>
+void launch_rows_k(const RowsArgs &a, hipStream_t s, bool pre_tau, const RowsSplit *split)
+{
+    if (a.topk <= RowsSmall::maxk) launch_rows<T, RowsSmall>(a, s, pre_tau, split);
+    else launch_rows<T, RowsLarge>(a, s, pre_tau, split);
+}
+
+// Split-row state for `rows` rows of `parts` workgroups each (nothing when
+// parts is 1).
+int ensure_split(Workspace &w, int64_t rows, int parts, RowsSplit &sp)
+{
+    sp = RowsSplit{};
+    sp.parts = parts;
+    if (parts <= 1) return FLASHTOPK_OK;
+    int st;
+    if ((st = ensure_zeroed(w, w.scnt, sizeof(uint32_t) * (size_t)rows))) return st;
+    if ((st = ensure_zeroed(w, w.sover, sizeof(uint32_t) * (size_t)rows))) return st;
+    if ((st = ensure_zeroed(w, w.sticket, sizeof(uint32_t) * (size_t)rows))) return st;
+    if ((st = ensure(w, w.scand, sizeof(uint64_t) * (size_t)rows * RowsLarge::cap))) return st;
+    sp.cnt = (uint32_t *)w.scnt.ptr;
+    sp.over = (uint32_t *)w.sover.ptr;
+    sp.ticket = (uint32_t *)w.sticket.ptr;
+    sp.cand = (uint64_t *)w.scand.ptr;
+    return FLASHTOPK_OK;
+}
+
+// Scratch rows of float window scores, 16-byte aligned (the row kernels'
+// loads), and the rows per recovery / dense batch that fit the budget (a
+// multiple of the 16-column tile).
+int64_t scratch_stride(int64_t S) { return (std::max<int64_t>(S, 1) + 3) / 4 * 4; }
+
+int64_t batch_rows(const Plan &p)
+{
+    const int64_t stride = scratch_stride(p.S);
+    int64_t rcap = std::max<int64_t>(kTileQ, p.recover_budget / (int64_t)(sizeof(float) * stride));
+    rcap = std::min<int64_t>(rcap, (p.T + kTileQ - 1) / kTileQ * kTileQ);
+    return (rcap + kTileQ - 1) / kTileQ * kTileQ;
+}
+
+void begin_record(Workspace &w, const Plan &p, int kind)
+{
+    flashtopk_info &info = w.last;
+    std::memset(&info, 0, sizeof(info));
+    info.status = FLASHTOPK_OK;
+    info.rows = p.T;
+    info.invalid = (int32_t)p.invalid;
+    w.last_kind = kind;
+    w.last_topk = p.topk;
+}
+
+// Every row scored densely: window scores in scratch, then the row top-k.
+int run_dense(Workspace &w, const void *q, const void *kv, const float *kv_scales, const float *weights,
+              const int32_t *ks, const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+{
+    int st = FLASHTOPK_OK;
+    const int64_t T = p.T, S = p.S;
+    const int ps = p.heads == 64 ? 1 : 0;
+    const int64_t stride = scratch_stride(S);
+    const int64_t rcap = batch_rows(p);
+    const int64_t brows = std::min(rcap, T);
+    if ((st = ensure(w, w.scratch, sizeof(float) * (size_t)rcap * stride))) return st;
+    if ((st = ensure(w, w.wlen, sizeof(int32_t) * (size_t)T))) return st;
+    RowsSplit sp;
+    if ((st = ensure_split(w, brows, split_parts(brows, S), sp))) return st;
+
+    mark(w, p, 0, stream);
+    for (int64_t rb = 0; rb < T; rb += rcap) {
+        const int64_t nb = std::min(rcap, T - rb);
+        ScoreArgs sa{};
+        sa.q = (const uint8_t *)q;
+        sa.kv = (const uint8_t *)kv;
+        sa.sigma = kv_scales;
+        sa.w = weights;
+        sa.ks = ks;
+        sa.ke = ke;
+        sa.num_q = (int)(T << ps);
+        sa.num_kv = (int)S;
+        sa.pair = ps;
+        sa.table = p.table;
+        sa.page_size = p.page_size;
+        sa.num_pages = p.num_pages;
+        sa.rowlist = nullptr;
+        sa.nrows_direct = (int)T;
+        sa.row_base = (int)rb;
+        sa.row_limit = (int)nb;
+        sa.scratch = (float *)w.scratch.ptr;
+        sa.scratch_stride = stride;
+        sa.wlen = (int32_t *)w.wlen.ptr;
+        sa.own_prep = 1;
+        sa.ntiles = (int)(((nb << ps) + kTileQ - 1) / kTileQ);
+        sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves, kMinDenseChunk);
+        const int nch = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
+        launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * nch)), stream, sa);
+
+        RowsArgs ra{};
+        ra.x = w.scratch.ptr;
+        ra.rows = nb;
+        ra.cols = S;
+        ra.stride = stride;
+        ra.topk = p.topk;
+        ra.out_idx = out_idx;
+        ra.out_val = out_val;
+        ra.out_flags = p.out_flags;
+        ra.ks = ks;
+        ra.ke = ke;
+        ra.row_base = rb;
+        ra.rows_total = T;
+        launch_rows_k<float>(ra, stream, true, &sp);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    mark(w, p, 1, stream);
+
+    begin_record(w, p, kCallDense);
+    w.last.path = FLASHTOPK_PATH_RECOVER;
+    w.last.cand_capacity = 0;
+    w.last.sample_target = 0;
+    if (p.profile) {
+        (void)hipEventSynchronize(w.ev[1]);
+        w.last.ms_recover = phase_ms(w, p, 0, 1);
+    }
+    return FLASHTOPK_OK;
+}
+
+// The fused path: sampled thresholds, the filtering scan, selection, and
+// dense recovery of the rows the threshold misjudged.
+int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scales, const float *weights,
+              const int32_t *ks, const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+{
+    int st = FLASHTOPK_OK;
+    const int64_t T = p.T, S = p.S;
+    if ((st = ensure(w, w.tau, sizeof(float) * T))) return st;
+    if ((st = ensure(w, w.cnt, sizeof(uint32_t) * T))) return st;
+    if ((st = ensure(w, w.rowlist, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(w, w.wlen, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(w, w.stats, sizeof(unsigned long long) * kStCount))) return st;
+    const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
+    // 64 heads: row t's two 32-head halves are tile columns 2t and 2t + 1.
+    const int ps = p.heads == 64 ? 1 : 0;
+    const int64_t TC = T << ps;  // tile columns
+    if (fp8) {
+        if ((st = ensure(w, w.qbar, (size_t)TC * kQbarParts * kDim))) return st;
+        if ((st = ensure(w, w.qscale, sizeof(float) * TC))) return st;
+    }
+    if ((st = ensure(w, w.sigh, sizeof(float) * (size_t)(S + 64)))) return st;
+    if ((st = ensure(w, w.cand, sizeof(uint64_t) * (size_t)T * p.cap))) return st;
+    if ((st = ensure(w, w.samp, sizeof(uint32_t) * (size_t)T * p.sample_target))) return st;
+
+    const int ntiles = (int)((TC + kTileQ - 1) / kTileQ);
+    // Score-bound pruning: on the auto path (each scan work item decides from
+    // its tile's planner sample) and the forced prune path; not for 64 heads.
+    const bool bounds = !ps && S > 0 && p.path != FLASHTOPK_PATH_SCAN;
+    const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
+    if (bounds) {
+        if ((st = ensure(w, w.kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
+        if ((st = ensure(w, w.kmeta, sizeof(float2) * (size_t)nblocks))) return st;
+        if ((st = ensure(w, w.vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
+        if ((st = ensure(w, w.q1, sizeof(float) * (size_t)T))) return st;
+    }
+    // Recovery batches: rows of scratch that fit the budget.
+    const int64_t stride = scratch_stride(S);
+    const int64_t rcap = batch_rows(p);
+    if ((st = ensure(w, w.scratch, sizeof(float) * (size_t)rcap * stride))) return st;
+
+    const int chunk = chunk_keys(ntiles, S, fp8 ? ScoreCfg<kFP8, kModeFilter>::waves : ScoreCfg<kBF16, kModeFilter>::waves);
+    const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
+
+    ScoreArgs sa{};
+    sa.q = (const uint8_t *)q;
+    sa.kv = (const uint8_t *)kv;
+    sa.sigma = kv_scales;
+    sa.sigh = (const float *)w.sigh.ptr;
+    sa.w = weights;
+    sa.ks = ks;
+    sa.ke = ke;
+    sa.num_q = (int)TC;
+    sa.num_kv = (int)S;
+    sa.pair = ps;
+    sa.qbar = (const uint8_t *)w.qbar.ptr;
+    sa.qscale = (const float *)w.qscale.ptr;
+    sa.ntiles = ntiles;
+    sa.chunk = chunk;
+    sa.cap = p.cap;
+    sa.tau = (const float *)w.tau.ptr;
+    sa.cnt = (uint32_t *)w.cnt.ptr;
+    sa.cand = (uint64_t *)w.cand.ptr;
+    sa.samp = (uint32_t *)w.samp.ptr;
+    sa.sample_target = p.sample_target;
+    sa.sample_min_stride = p.sample_min_stride;
+    sa.sample_split = sample_split(ntiles);
+    if (bounds) {
+        sa.prune = p.path == FLASHTOPK_PATH_PRUNE ? 2 : 1;
+        sa.kb = (const uint8_t *)w.kb.ptr;
+        sa.meta = (const float2 *)w.kmeta.ptr;
+        sa.q1 = (float *)w.q1.ptr;
+        sa.nblocks = nblocks;
+        sa.vplan = (float *)w.vplan.ptr;
+        sa.plan = (unsigned long long *)w.stats.ptr + kStPruned;
+    }
+
+    // The sample kernel sets the thresholds itself when each row's samples
+    // come from one workgroup per tile; otherwise k_tau follows it.
+    const bool fused_tau = sa.sample_split == 1;
+    sa.topk = p.topk;
+    sa.rank_scale = p.rank_scale;
+    sa.tau_w = (float *)w.tau.ptr;
+
+    mark(w, p, 0, stream);
+    {
+        // Per-key scale factors (and block extremes for the bound), the
+        // statistics cleared, and (FP8) the query sums, in one launch.
+        PrepArgs pa{};
+        pa.key_blocks = (int)((S + 64 + 4 * kBlockKeys - 1) / (4 * kBlockKeys));
+        pa.kv = (const uint8_t *)kv;
+        pa.sigma = kv_scales;
+        pa.num_kv = (int)S;
+        pa.nblocks = nblocks;
+        pa.sigh = (float *)w.sigh.ptr;
+        pa.bounds = bounds ? 1 : 0;
+        pa.kb = bounds ? (uint8_t *)w.kb.ptr : nullptr;
+        pa.meta = bounds ? (float2 *)w.kmeta.ptr : nullptr;
+        pa.stats = (unsigned long long *)w.stats.ptr;
+        pa.nstats = kStCount;
+        int64_t qblocks = 0;
+        if (fp8) {
+            pa.q = (const uint8_t *)q;
+            pa.w = weights;
+            pa.num_q = TC;
+            pa.parts = (uint8_t *)w.qbar.ptr;
+            pa.qscale = (float *)w.qscale.ptr;
+            pa.q1 = bounds ? (float *)w.q1.ptr : nullptr;
+            qblocks = (TC + 3) / 4;
+        }
+        const unsigned nwg = (unsigned)(pa.key_blocks + qblocks);
+        if (fp8) k_prep<kFP8><<<nwg, 256, 0, stream>>>(pa);
+        else k_prep<kBF16><<<nwg, 256, 0, stream>>>(pa);
+    }
+    launch_score_dt(p.dtype, kModeSample, dim3((unsigned)(ntiles * sa.sample_split)), stream, sa);
+    mark(w, p, 1, stream);
+
+    if (!fused_tau) {
+        TauArgs ta{};
+        ta.ks = ks;
+        ta.ke = ke;
+        ta.num_q = T;
+        ta.topk = p.topk;
+        ta.cap = p.cap;
+        ta.samp = (const uint32_t *)w.samp.ptr;
+        ta.sample_target = p.sample_target;
+        ta.sample_min_stride = p.sample_min_stride;
+        ta.rank_scale = p.rank_scale;
+        ta.tau = (float *)w.tau.ptr;
+        ta.cnt = (uint32_t *)w.cnt.ptr;
+        k_tau<<<dim3((unsigned)((T + kTauWaves - 1) / kTauWaves)), 64 * kTauWaves, 0, stream>>>(ta);
+    }
+    mark(w, p, 2, stream);
+
+    launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
+    mark(w, p, 3, stream);
+
+    SelectArgs se{};
+    se.ks = ks;
+    se.ke = ke;
+    se.topk = p.topk;
+    se.cap = p.cap;
+    se.cnt = (const uint32_t *)w.cnt.ptr;
+    se.cand = (const uint64_t *)w.cand.ptr;
+    se.out_idx = out_idx;
+    se.out_val = out_val;
+    se.out_flags = p.out_flags;
+    se.wlen = (int32_t *)w.wlen.ptr;
+    se.rowlist = (int32_t *)w.rowlist.ptr;
+    se.nflagged = (unsigned long long *)w.stats.ptr + kStFlagged;
+    if (p.cap <= SelSmallK::nreg * SelSmallK::nt && p.topk <= SelSmallK::maxk) launch_select<SelSmallK>(T, stream, se);
+    else if (p.cap <= SelSmall::nreg * SelSmall::nt && p.topk <= SelSmall::maxk) launch_select<SelSmall>(T, stream, se);
+    else if (p.cap <= SelMid::nreg * SelMid::nt) launch_select<SelMid>(T, stream, se);
+    else if (p.cap <= SelLargeK::nreg * SelLargeK::nt && p.topk <= SelLargeK::maxk) launch_select<SelLargeK>(T, stream, se);
+    else if (p.cap <= SelLarge::nreg * SelLarge::nt) launch_select<SelLarge>(T, stream, se);
+    else launch_select<SelHuge>(T, stream, se);
+    mark(w, p, 4, stream);
+
+    // Dense recovery of the flagged rows, batch by batch: batch b covers
+    // entries [b rcap, (b + 1) rcap) of the list; entries past its
+    // device-side length exit at once, so a call that flags nothing pays
+    // two near-empty launches per batch.
+    for (int64_t rb = 0; rb < T; rb += rcap) {
+        sa.rowlist = (const int32_t *)w.rowlist.ptr;
+        sa.nrows = (const unsigned long long *)w.stats.ptr + kStFlagged;
+        sa.row_limit = (int)rcap;
+        sa.row_base = (int)rb;
+        sa.scratch = (float *)w.scratch.ptr;
+        sa.scratch_stride = stride;
+        sa.ntiles = (int)((rcap << ps) / kTileQ);
+        sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves);
+        const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
+        launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
+        // Exact top k of each batch row's window scores: the row top-k
+        // kernels in mapped-row mode (outputs to the flagged row, indices
+        // offset by its window start; entries past the list exit).
+        RowsArgs ra{};
+        ra.x = w.scratch.ptr;
+        ra.rows = rcap;
+        ra.cols = S;
+        ra.stride = stride;
+        ra.topk = p.topk;
+        ra.out_idx = out_idx;
+        ra.out_val = out_val;
+        ra.out_flags = p.out_flags;
+        ra.rowmap = (const int32_t *)w.rowlist.ptr;
+        ra.nrows = (const unsigned long long *)w.stats.ptr + kStFlagged;
+        ra.row_base = rb;
+        ra.ks = ks;
+        ra.ke = ke;
+        launch_rows_k<float>(ra, stream, false, nullptr);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    mark(w, p, 5, stream);
+
+    begin_record(w, p, kCallFused);
+    w.last.cand_capacity = p.cap;
+    w.last.sample_target = p.sample_target;
+    if (p.profile) {
+        (void)hipEventSynchronize(w.ev[5]);
+        w.last.ms_sample = phase_ms(w, p, 0, 1);
+        w.last.ms_tau = phase_ms(w, p, 1, 2);
+        w.last.ms_filter = phase_ms(w, p, 2, 3);
+        w.last.ms_select = phase_ms(w, p, 3, 4);
+        w.last.ms_recover = phase_ms(w, p, 4, 5);
+    }
+    return FLASHTOPK_OK;
+}
+
+// The auto path's choice between the fused and the dense sequence.
+bool dense_path(const Plan &p)
+{
+    if (p.path == FLASHTOPK_PATH_RECOVER) return true;
+    if (p.path != FLASHTOPK_PATH_AUTO) return false;
+    return p.T * std::max<int64_t>(p.S, 1) <= kDensePairs;
+}
+
+int run(Workspace &w, const void *q, const void *kv, const float *kv_scales, const float *weights, const int32_t *ks,
+        const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+{
+    if (dense_path(p)) return run_dense(w, q, kv, kv_scales, weights, ks, ke, out_idx, out_val, stream, p);
+    return run_fused(w, q, kv, kv_scales, weights, ks, ke, out_idx, out_val, stream, p);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 // options.validate: runs k_validate on the call's inputs, waits for its flags
 // (p.invalid) and, when it found any, fails the call before a scoring kernel
 // runs, recording it as the stream's last call.
-int check_inputs(hipStream_t s, Plan &p, ValidateArgs va)
+int check_inputs(Workspace &w, hipStream_t s, Plan &p, ValidateArgs va)
 {
     int st = FLASHTOPK_OK;
-    Workspace *w = get_ws(s, &st);
-    if (!w) return st;
-    if ((st = ensure(*w, w->vflag, sizeof(unsigned)))) return st;
-    va.flags = (unsigned *)w->vflag.ptr;
+    if ((st = ensure(w, w.vflag, sizeof(unsigned)))) return st;
+    va.flags = (unsigned *)w.vflag.ptr;
     va.dtype = p.dtype == FLASHTOPK_FP8_E4M3 ? kFP8 : kBF16;
     const int64_t n = std::max({va.q_pieces, va.kv_pieces, va.nw, va.nscales, va.num_q, va.ntable, (int64_t)1});
     const unsigned grid = (unsigned)std::min<int64_t>(2048, (n + 255) / 256);
     k_zero_word<<<1, 64, 0, s>>>(va.flags);
     k_validate<<<grid, 256, 0, s>>>(va);
-    unsigned *hf = reinterpret_cast<unsigned *>(w->host_stats + kStCount);
-    hipError_t e = hipMemcpyAsync(hf, va.flags, sizeof(unsigned), hipMemcpyDeviceToHost, s);
+    hipError_t e = hipMemcpyAsync(w.host_flag, va.flags, sizeof(unsigned), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_status(e);
-    p.invalid = *hf;
+    p.invalid = *w.host_flag;
     if (p.invalid) {
-        flashtopk_info &info = w->last;
-        std::memset(&info, 0, sizeof(info));
-        info.status = FLASHTOPK_ERR_INVALID_ARGUMENT;
-        info.rows = p.T;
-        info.invalid = (int32_t)p.invalid;
-        w->has_last = true;
-        w->last_pending = false;
+        begin_record(w, p, kCallFailed);
+        w.last.status = FLASHTOPK_ERR_INVALID_ARGUMENT;
         return FLASHTOPK_ERR_INVALID_ARGUMENT;
     }
     return FLASHTOPK_OK;
+}
+
+// Counts of the record from the last call's device arrays (the stream has
+// been synchronised).
+int fill_counts(Workspace &w)
+{
+    flashtopk_info &info = w.last;
+    const int64_t T = info.rows;
+    std::vector<int32_t> len((size_t)T);
+    hipError_t e = hipMemcpy(len.data(), w.wlen.ptr, sizeof(int32_t) * (size_t)T, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    info.rows_empty = info.rows_take_all = info.rows_sampled = info.rows_underflow = info.rows_overflow = 0;
+    info.rows_recovered = info.max_candidates = info.window_keys = info.pruned_keys = 0;
+    if (w.last_kind == kCallDense) {
+        for (int64_t t = 0; t < T; ++t) {
+            info.window_keys += len[t];
+            if (len[t] == 0) ++info.rows_empty;
+            else ++info.rows_recovered;
+        }
+        return FLASHTOPK_OK;
+    }
+    std::vector<uint32_t> cnt((size_t)T);
+    unsigned long long stats[kStCount];
+    e = hipMemcpy(cnt.data(), w.cnt.ptr, sizeof(uint32_t) * (size_t)T, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(stats, w.stats.ptr, sizeof(stats), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    const int64_t cap = info.cand_capacity;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t L = len[t];
+        const uint32_t c = cnt[t];
+        info.window_keys += L;
+        if (L == 0) {
+            ++info.rows_empty;
+            continue;
+        }
+        if ((int64_t)c < std::min<int64_t>(w.last_topk, L)) ++info.rows_underflow;
+        if ((int64_t)c > cap) ++info.rows_overflow;
+        if (row_flagged(L, c, w.last_topk, (int)cap)) ++info.rows_recovered;
+        if (L <= cap) {
+            ++info.rows_take_all;
+        } else {
+            ++info.rows_sampled;
+            info.max_candidates = std::max<int64_t>(info.max_candidates, c);
+        }
+    }
+    info.pruned_keys = (int64_t)stats[kStPruned];
+    info.path = stats[kStPruneOn] ? FLASHTOPK_PATH_PRUNE : FLASHTOPK_PATH_SCAN;
+    // the device's own count of the list (the recovery launches read it)
+    if ((int64_t)stats[kStFlagged] != info.rows_recovered) return FLASHTOPK_ERR_HIP;
+    return FLASHTOPK_OK;
+}
+
+Workspace *find_ws(hipStream_t stream)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (Workspace *w : g_ws)
+        if (w->device == dev && w->stream == stream) return w;
+    return nullptr;
 }
 
 }  // namespace
@@ -699,7 +778,7 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, c
                         const flashtopk_options *opt)
 {
     if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
-    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 31))
+    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 30))
         return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (topk < 1 || topk > FLASHTOPK_MAX_TOPK) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (num_q == 0) return FLASHTOPK_OK;
@@ -712,6 +791,10 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, c
     p.topk = topk;
     int st = resolve(p, opt);
     if (st) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    Workspace *w = get_ws(s, &st);
+    if (!w) return st;
+    std::lock_guard<std::mutex> lk(w->mu);
     if (p.validate) {
         const int64_t rb = dtype == FLASHTOPK_FP8_E4M3 ? kDim : 2 * kDim;
         ValidateArgs va{};
@@ -727,9 +810,9 @@ int flashtopk_select_ex(const void *q, const void *kv, const float *kv_scales, c
         va.ke = ke;
         va.num_q = num_q;
         va.num_kv = num_kv;
-        if ((st = check_inputs((hipStream_t)stream, p, va))) return st;
+        if ((st = check_inputs(*w, s, p, va))) return st;
     }
-    return run(q, kv, kv_scales, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
+    return run(*w, q, kv, kv_scales, weights, ks, ke, out_idx, out_val, s, p);
 }
 
 int flashtopk_select_paged(const void *q, const void *kv_pages, const float *scale_pages, const int32_t *block_table,
@@ -738,7 +821,7 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
                            float *out_val, void *stream, const flashtopk_options *opt)
 {
     if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
-    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 31))
+    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 30))
         return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (page_size < 1 || num_pages < 0) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (topk < 1 || topk > FLASHTOPK_MAX_TOPK) return FLASHTOPK_ERR_INVALID_ARGUMENT;
@@ -753,6 +836,10 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
     p.topk = topk;
     int st = resolve(p, opt);
     if (st) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    Workspace *w = get_ws(s, &st);
+    if (!w) return st;
+    std::lock_guard<std::mutex> lk(w->mu);
     if (p.validate) {
         // the pool may hold unused pages: q, weights, windows and page ids only
         const int64_t rb = dtype == FLASHTOPK_FP8_E4M3 ? kDim : 2 * kDim;
@@ -768,19 +855,16 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
         va.table = num_kv > 0 ? block_table : nullptr;
         va.ntable = num_kv > 0 ? (num_kv + page_size - 1) / page_size : 0;
         va.num_pages = num_pages;
-        if ((st = check_inputs((hipStream_t)stream, p, va))) return st;
+        if ((st = check_inputs(*w, s, p, va))) return st;
     }
-    if (num_kv == 0) return run(q, nullptr, nullptr, weights, ks, ke, out_idx, out_val, (hipStream_t)stream, p);
-    const hipStream_t s = (hipStream_t)stream;
-    if (num_q <= kFewRows && p.heads == 32) {
-        // few rows read their keys from the pages directly
+    if (num_kv == 0) return run(*w, q, nullptr, nullptr, weights, ks, ke, out_idx, out_val, s, p);
+    if (dense_path(p)) {
+        // the dense kernel reads each key from its page
         p.table = block_table;
         p.page_size = page_size;
         p.num_pages = num_pages;
-        return run(q, kv_pages, scale_pages, weights, ks, ke, out_idx, out_val, s, p);
+        return run_dense(*w, q, kv_pages, scale_pages, weights, ks, ke, out_idx, out_val, s, p);
     }
-    Workspace *w = get_ws(s, &st);
-    if (!w) return st;
     const bool fp8 = dtype == FLASHTOPK_FP8_E4M3;
     const int RB = fp8 ? 128 : 256;
     if ((st = ensure(*w, w->pkv, (size_t)num_kv * RB))) return st;
@@ -796,7 +880,7 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
                                                               page_size, num_pages, num_kv, (uint8_t *)w->pkv.ptr, sig);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_status(e);
-    return run(q, w->pkv.ptr, sig, weights, ks, ke, out_idx, out_val, s, p);
+    return run_fused(*w, q, w->pkv.ptr, sig, weights, ks, ke, out_idx, out_val, s, p);
 }
 
 int flashtopk_select(const void *q, const void *kv, const float *kv_scales, const float *weights,
@@ -822,92 +906,157 @@ int flashtopk_topk_rows(const void *x, int score_dtype, int64_t rows, int64_t co
     if (x && !aligned16(x)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (rows > 1 && (row_stride * esize) % 16 != 0) return FLASHTOPK_ERR_INVALID_ARGUMENT;
     if (out_flags & ~(FLASHTOPK_OUT_INDEX_ORDER | FLASHTOPK_OUT_INT64)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
-    RowsArgs a{x, rows, cols, row_stride, ends, topk, out_idx, out_val, nan_flag, out_flags};
+    RowsArgs a{};
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.stride = row_stride;
+    a.ends = ends;
+    a.topk = topk;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    a.nan_flag = nan_flag;
+    a.out_flags = out_flags;
     const hipStream_t s = (hipStream_t)stream;
-    const bool small = topk <= RowsSmall::maxk;
-    if (score_dtype == FLASHTOPK_SCORES_F32) {
-        if (small) launch_rows<float, RowsSmall>(a, s);
-        else launch_rows<float, RowsLarge>(a, s);
-    } else {
-        if (small) launch_rows<uint16_t, RowsSmall>(a, s);
-        else launch_rows<uint16_t, RowsLarge>(a, s);
+    // Few rows are split over several workgroups each, with per-row state in
+    // the stream's workspace.
+    const int parts = split_parts(rows, cols);
+    RowsSplit sp{};
+    std::unique_lock<std::mutex> lk;
+    if (parts > 1) {
+        int st = FLASHTOPK_OK;
+        Workspace *w = get_ws(s, &st);
+        if (!w) return st;
+        lk = std::unique_lock<std::mutex>(w->mu);
+        if ((st = ensure_split(*w, rows, parts, sp))) return st;
     }
+    if (score_dtype == FLASHTOPK_SCORES_F32) launch_rows_k<float>(a, s, true, &sp);
+    else launch_rows_k<uint16_t>(a, s, true, &sp);
     return hip_status(hipGetLastError());
 }
 
 int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream)
 {
     if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
-    if (max_q < 0 || max_kv < 0 || max_topk < 1 || max_topk > FLASHTOPK_MAX_TOPK)
+    if (max_q < 0 || max_kv < 0 || max_kv >= (int64_t(1) << 31) || max_q >= (int64_t(1) << 30) || max_topk < 1 ||
+        max_topk > FLASHTOPK_MAX_TOPK)
         return FLASHTOPK_ERR_INVALID_ARGUMENT;
     int st = FLASHTOPK_OK;
     Workspace *w = get_ws((hipStream_t)stream, &st);
     if (!w) return st;
-    const int64_t T = std::max<int64_t>(max_q, 1);
+    std::lock_guard<std::mutex> lk(w->mu);
+    // Everything a call of at most these sizes with default options (either
+    // head count, either path) grows the workspace to.
+    const int64_t T = std::max<int64_t>(max_q, 1), S = max_kv;
+    const int64_t TC = 2 * T;  // 64 heads: two tile columns per row
     const int cap = std::min(kMaxCap, std::max(4 * max_topk, max_topk));
+    Plan p{};
+    p.T = T;
+    p.S = S;
+    p.recover_budget = kDefaultRecoverBudget;
+    const int64_t stride = scratch_stride(S);
+    const int64_t rcap = batch_rows(p);
+    const int64_t nblocks = (S + kBlockKeys - 1) / kBlockKeys;
+    const int64_t ntiles = (T + kTileQ - 1) / kTileQ;
     if ((st = ensure(*w, w->tau, sizeof(float) * T))) return st;
     if ((st = ensure(*w, w->cnt, sizeof(uint32_t) * T))) return st;
     if ((st = ensure(*w, w->rowlist, sizeof(int32_t) * T))) return st;
+    if ((st = ensure(*w, w->wlen, sizeof(int32_t) * T))) return st;
     if ((st = ensure(*w, w->stats, sizeof(unsigned long long) * kStCount))) return st;
     if ((st = ensure(*w, w->cand, sizeof(uint64_t) * (size_t)T * cap))) return st;
     if ((st = ensure(*w, w->samp, sizeof(uint32_t) * (size_t)T * kDefaultSampleTarget))) return st;
-    if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(max_kv + 64)))) return st;
-    if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
-    if ((st = ensure_zeroed(*w, w->ticket, sizeof(uint32_t) * T))) return st;
+    if ((st = ensure(*w, w->sigh, sizeof(float) * (size_t)(S + 64)))) return st;
+    if ((st = ensure(*w, w->scratch, sizeof(float) * (size_t)rcap * stride))) return st;
     if (dtype == FLASHTOPK_FP8_E4M3) {
-        if ((st = ensure(*w, w->qbar, (size_t)T * kQbarParts * kDim))) return st;
-        if ((st = ensure(*w, w->qscale, sizeof(float) * T))) return st;
+        if ((st = ensure(*w, w->qbar, (size_t)TC * kQbarParts * kDim))) return st;
+        if ((st = ensure(*w, w->qscale, sizeof(float) * TC))) return st;
     }
-    if (max_kv > 0) {
-        const int64_t nblocks = (max_kv + kBlockKeys - 1) / kBlockKeys;
-        const int64_t ntiles = (T + kTileQ - 1) / kTileQ;
-        if ((st = ensure(*w, w->kb, (size_t)nblocks * 2 * (dtype == FLASHTOPK_FP8_E4M3 ? 128 : 256)))) return st;
-        if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)nblocks))) return st;
-        if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
-    }
+    if ((st = ensure(*w, w->kb, (size_t)std::max<int64_t>(nblocks, 1) * 2 * (dtype == FLASHTOPK_FP8_E4M3 ? 128 : 256))))
+        return st;
+    if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)std::max<int64_t>(nblocks, 1)))) return st;
+    if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
+    if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
+    // the dense path's split-row state: few rows, so at most about 2 CUs' worth
+    RowsSplit sp;
+    const int64_t brows = std::min(rcap, T);
+    if ((st = ensure_split(*w, brows, split_parts(brows, S), sp))) return st;
     return FLASHTOPK_OK;
 }
 
 int flashtopk_get_last_info(void *stream, flashtopk_info *out)
 {
     if (!out) return FLASHTOPK_ERR_INVALID_ARGUMENT;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_status(e);
-    std::lock_guard<std::mutex> lk(g_mu);
-    for (Workspace *w : g_ws) {
-        if (w->device == dev && w->stream == (hipStream_t)stream && w->has_last) {
-            if (w->last_pending) {
-                e = hipEventSynchronize(w->stats_ev);
-                if (e != hipSuccess) return hip_status(e);
-                fill_counts(*w);
-            }
-            *out = w->last;
-            return FLASHTOPK_OK;
-        }
-    }
     std::memset(out, 0, sizeof(*out));
-    return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    Workspace *w = find_ws((hipStream_t)stream);
+    if (!w) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lk(w->mu);
+    if (w->last_kind == kCallNone) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (w->last_kind != kCallFailed) {
+        hipError_t e = hipStreamSynchronize(w->stream);
+        if (e != hipSuccess) return hip_status(e);
+        int st = fill_counts(*w);
+        if (st) return st;
+    }
+    *out = w->last;
+    return FLASHTOPK_OK;
+}
+
+int flashtopk_get_last_recovered(void *stream, int32_t *rows, int64_t max_rows, int64_t *count)
+{
+    if (!count || max_rows < 0 || (max_rows > 0 && !rows)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    *count = 0;
+    Workspace *w = find_ws((hipStream_t)stream);
+    if (!w) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lk(w->mu);
+    if (w->last_kind == kCallNone) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (w->last_kind == kCallFailed) return FLASHTOPK_OK;
+    hipError_t e = hipStreamSynchronize(w->stream);
+    if (e != hipSuccess) return hip_status(e);
+    const int64_t T = w->last.rows;
+    if (w->last_kind == kCallDense) {
+        std::vector<int32_t> len((size_t)T);
+        e = hipMemcpy(len.data(), w->wlen.ptr, sizeof(int32_t) * (size_t)T, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_status(e);
+        int64_t n = 0;
+        for (int64_t t = 0; t < T; ++t)
+            if (len[t] > 0) {
+                if (n < max_rows) rows[n] = (int32_t)t;
+                ++n;
+            }
+        *count = n;
+        return FLASHTOPK_OK;
+    }
+    unsigned long long nf = 0;
+    e = hipMemcpy(&nf, (unsigned long long *)w->stats.ptr + kStFlagged, sizeof(nf), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && nf > 0 && max_rows > 0)
+        e = hipMemcpy(rows, w->rowlist.ptr, sizeof(int32_t) * (size_t)std::min<int64_t>((int64_t)nf, max_rows),
+                      hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    *count = (int64_t)nf;
+    return FLASHTOPK_OK;
 }
 
 void flashtopk_release(void)
 {
     std::lock_guard<std::mutex> lk(g_mu);
     for (Workspace *w : g_ws) {
-        int prev = 0;
-        (void)hipGetDevice(&prev);
-        (void)hipSetDevice(w->device);
-        (void)hipStreamSynchronize(w->stream);
-        DevBuf *bufs[] = {&w->tau, &w->cnt, &w->rowlist, &w->stats,
-                          &w->cand, &w->samp, &w->scratch, &w->qbar, &w->qscale, &w->sigh,
-                          &w->kb, &w->kmeta, &w->vplan, &w->q1, &w->ticket, &w->pkv, &w->psig, &w->vflag};
-        for (DevBuf *b : bufs)
-            if (b->ptr) (void)hipFree(b->ptr);
-        if (w->host_stats) (void)hipHostFree(w->host_stats);
-        for (hipEvent_t &ev : w->ev)
-            if (ev) (void)hipEventDestroy(ev);
-        if (w->stats_ev) (void)hipEventDestroy(w->stats_ev);
-        (void)hipSetDevice(prev);
+        {
+            std::lock_guard<std::mutex> wl(w->mu);
+            int prev = 0;
+            (void)hipGetDevice(&prev);
+            (void)hipSetDevice(w->device);
+            (void)hipStreamSynchronize(w->stream);
+            DevBuf *bufs[] = {&w->tau,   &w->cnt,   &w->rowlist, &w->stats,  &w->wlen, &w->cand,
+                              &w->samp,  &w->scratch, &w->qbar,  &w->qscale, &w->sigh, &w->kb,
+                              &w->kmeta, &w->vplan, &w->q1,      &w->scnt,   &w->sover, &w->sticket,
+                              &w->scand, &w->pkv,   &w->psig,    &w->vflag};
+            for (DevBuf *b : bufs)
+                if (b->ptr) (void)hipFree(b->ptr);
+            if (w->host_flag) (void)hipHostFree(w->host_flag);
+            for (hipEvent_t &ev : w->ev)
+                if (ev) (void)hipEventDestroy(ev);
+            (void)hipSetDevice(prev);
+        }
         delete w;
     }
     g_ws.clear();
@@ -925,6 +1074,6 @@ const char *flashtopk_status_string(int status)
     }
 }
 
-int flashtopk_version(void) { return 100; }
+int flashtopk_version(void) { return 200; }
 
 }  // extern "C"

@@ -92,4 +92,49 @@ __device__ __forceinline__ void qbar_rows(const uint8_t *q, const float *w, int6
     if (lane == 0) qscale[t] = ldexpf(1.0f, -k);
 }
 
+// The same parts for the 16 columns of a q tile staged in LDS (heads 0-31 in
+// the tile's slot layout: byte d of head h of column n at
+// ((2 h + (d / 16) % 2) * 64 + n + 16 (d / 32)) * 16 + d % 16), written to
+// heads 32-34 of the tile, and each column's 2^-e to s_qsc[n].  s_w[h * 16 +
+// n] holds the column's weights.  The sums, the scale and the truncations
+// are those of qbar_rows, in the same order, so the parts have the same bits
+// as the ones the preparation pass writes.  NT threads (the whole
+// workgroup); one wave per column, lane l owning dimensions 2l and 2l + 1.
+template <int NT>
+__device__ __forceinline__ void qbar_tile_lds(uint8_t *s_q, const float *s_w, float *s_qsc)
+{
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int d = 2 * lane;
+    const int off = ((d >> 4) & 1) * 64 * 16 + (d >> 5) * 16 * 16 + (d & 15);  // byte d's place within a head
+    for (int n = wave; n < 16; n += NW) {
+        uint32_t c[kHeads];
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) c[h] = *reinterpret_cast<const uint16_t *>(s_q + h * 2 * 64 * 16 + n * 16 + off);
+        float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) {
+            const float wv = s_w[h * 16 + n];
+            v0 = __builtin_fmaf(wv, e4m3_to_f32(c[h] & 0xFFu), v0);
+            v1 = __builtin_fmaf(wv, e4m3_to_f32(c[h] >> 8), v1);
+        }
+        float m = fmaxf(fabsf(v0), fabsf(v1));
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        int k = 0;
+        if (m > 0.0f) {
+            int E;
+            frexpf(m, &E);
+            k = 8 - E;
+        }
+        float r0 = ldexpf(v0, k), r1 = ldexpf(v1, k);
+        for (int p = 0; p < kQbarParts; ++p) {
+            const uint32_t c0 = f32_to_e4m3_trunc(r0), c1 = f32_to_e4m3_trunc(r1);
+            r0 -= e4m3_to_f32(c0);
+            r1 -= e4m3_to_f32(c1);
+            *reinterpret_cast<uint16_t *>(s_q + (kHeads + p) * 2 * 64 * 16 + n * 16 + off) = (uint16_t)(c0 | (c1 << 8));
+        }
+        if (lane == 0) s_qsc[n] = ldexpf(1.0f, -k);
+    }
+}
+
 }  // namespace ftk

@@ -54,16 +54,19 @@ struct RowsArgs {
     float *out_val;         // [rows, topk] or null
     int32_t *nan_flag;      // set to 1 when a row holds a NaN; or null
     int out_flags;          // OutFlag
-    // Mapped rows (dense recovery of the fused call), when rowmap is set:
-    // input row r is entry row_base + r of rowmap, present while that entry
-    // is below *nrows; its outputs go to row rowmap[row_base + r], its length
-    // is that row's window ke - ks (at most cols) and its indices are offset
-    // by the window start ks.
+    // Window rows (dense scores of the fused call), when ks is set: input
+    // row r is call row rowmap[row_base + r], present while row_base + r is
+    // below *nrows (dense recovery of flagged rows), or, with no rowmap, call
+    // row row_base + r, present while below rows_total (every row scored
+    // densely); its outputs go to that call row, its length is the row's
+    // window ke - ks (at most cols) and its indices are offset by the window
+    // start ks.
     const int32_t *rowmap;
     const unsigned long long *nrows;
     int64_t row_base;
     const int32_t *ks;
     const int32_t *ke;
+    int64_t rows_total;
 };
 
 // Output row, length and index offset of input row r (present = false: a
@@ -76,9 +79,14 @@ struct RowPlace {
 
 __device__ __forceinline__ RowPlace row_place(const RowsArgs &a, int64_t r)
 {
-    if (a.rowmap) {
-        if ((unsigned long long)(a.row_base + r) >= *a.nrows) return {0, 0, 0, false};
-        const int64_t t = a.rowmap[a.row_base + r];
+    if (a.ks) {
+        int64_t t = a.row_base + r;
+        if (a.rowmap) {
+            if ((unsigned long long)t >= *a.nrows) return {0, 0, 0, false};
+            t = a.rowmap[t];
+        } else if (t >= a.rows_total) {
+            return {0, 0, 0, false};
+        }
         const int64_t lo = a.ks[t], hi = max((int64_t)a.ke[t], lo);
         return {t, min(hi - lo, a.cols), (int32_t)lo, true};
     }
@@ -265,7 +273,7 @@ __device__ float rows_sample_tau(RowsLds<SH> &L, const v4i &raw, int64_t n, uint
 // the group with a select chain.  TAIL: the group may pass the row's end.
 template <typename T, typename SH, int U, bool TAIL>
 __device__ __forceinline__ void scan_group(RowsLds<SH> &L, const v4i (&raw)[U], int64_t g0, int64_t n, float tau,
-                                           bool &nan)
+                                           bool &nan, int64_t ibase)
 {
     constexpr int NT = SH::nt, V = 16 / sizeof(T), PER = sizeof(uint32_t) / sizeof(T);  // entries per word
     constexpr int E = U * V;
@@ -300,25 +308,27 @@ __device__ __forceinline__ void scan_group(RowsLds<SH> &L, const v4i (&raw)[U], 
         if (PER == 2) f = __uint_as_float((b & 1) ? (w & 0xFFFF0000u) : (w << 16));
         else f = __uint_as_float(w);
         const uint32_t li = (uint32_t)(((b / V) * NT + tid) * V + (b % V));
-        if (pos < (uint32_t)SH::cap) L.cand[pos] = raw_cand(f, (int32_t)(g0 + li));
+        if (pos < (uint32_t)SH::cap) L.cand[pos] = raw_cand(f, (int32_t)(ibase + g0 + li));
         ++pos;
     } while (mask);
 }
 
 template <typename T, typename SH, int U>
 __device__ __forceinline__ void scan_any(RowsLds<SH> &L, const v4i (&raw)[U], int64_t g0, int64_t n, float tau,
-                                         bool &nan)
+                                         bool &nan, int64_t ibase)
 {
-    if (n - g0 >= (int64_t)(SH::nt * U * (16 / sizeof(T)))) scan_group<T, SH, U, false>(L, raw, g0, n, tau, nan);
-    else scan_group<T, SH, U, true>(L, raw, g0, n, tau, nan);
+    if (n - g0 >= (int64_t)(SH::nt * U * (16 / sizeof(T)))) scan_group<T, SH, U, false>(L, raw, g0, n, tau, nan, ibase);
+    else scan_group<T, SH, U, true>(L, raw, g0, n, tau, nan, ibase);
 }
 
-// Gathers every valid entry >= tau (as raw candidates) into L.cand, the
-// first SH::cap of them, and returns how many there are.  `a` holds the
-// row's first group, already loaded.  Two register sets alternate, so one
-// group is in flight while the other is scanned.
+// Gathers every valid entry >= tau (as raw candidates, their positions
+// offset by ibase) into L.cand, the first SH::cap of them, and returns how
+// many there are.  `a` holds the row's first group, already loaded.  Two
+// register sets alternate, so one group is in flight while the other is
+// scanned.
 template <typename T, typename SH, int U>
-__device__ uint32_t rows_gather(RowsLds<SH> &L, v4i (&a)[U], const T *row, int64_t n, float tau, bool &nan)
+__device__ uint32_t rows_gather(RowsLds<SH> &L, v4i (&a)[U], const T *row, int64_t n, float tau, bool &nan,
+                                int64_t ibase = 0)
 {
     constexpr int64_t G = (int64_t)SH::nt * U * (16 / sizeof(T));
     if (threadIdx.x == 0) L.misc[3] = 0u;
@@ -327,11 +337,11 @@ __device__ uint32_t rows_gather(RowsLds<SH> &L, v4i (&a)[U], const T *row, int64
     for (int64_t g0 = 0; g0 < n; g0 += 2 * G) {
         load_group<T, SH::nt, U>(b, row, n, g0 + G);
         __builtin_amdgcn_sched_barrier(0);  // the loads go out before the scan
-        scan_any<T, SH, U>(L, a, g0, n, tau, nan);
+        scan_any<T, SH, U>(L, a, g0, n, tau, nan, ibase);
         if (g0 + G >= n) break;  // block-uniform
         load_group<T, SH::nt, U>(a, row, n, g0 + 2 * G);
         __builtin_amdgcn_sched_barrier(0);
-        scan_any<T, SH, U>(L, b, g0 + G, n, tau, nan);
+        scan_any<T, SH, U>(L, b, g0 + G, n, tau, nan, ibase);
     }
     __syncthreads();
     const uint32_t cnt = L.misc[3];
@@ -589,6 +599,111 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     } else {
         RowStream<T> el{row, n};
         select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags, pl.base);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Rows split over several workgroups (few rows: each row's latency-bound
+// stream is shared out).  Workgroup (row r, part p) computes the row's
+// threshold from the whole row's sample (every part gets the same value),
+// gathers the entries of its slice that reach it and appends them to the
+// row's candidate list in global memory; the row's last workgroup to finish
+// (a self-resetting ticket) selects from the list, or, when the parts
+// together kept fewer than k or more than the capacity, redoes the row
+// alone by the digit histogram.  Per-row state lives in a workspace that
+// reads zero between calls.
+struct RowsSplit {
+    uint32_t *cnt;     // [rows] candidates appended
+    uint32_t *over;    // [rows] a part held more than it could keep
+    uint32_t *ticket;  // [rows] parts finished
+    uint64_t *cand;    // [rows, cap] the row's candidates
+    int parts;         // workgroups per row
+};
+
+template <typename T, typename SH>
+__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows_split(RowsArgs a,
+                                                                                                   RowsSplit sp)
+{
+    constexpr int NT = SH::nt, U = kRowsUnroll, V = 16 / sizeof(T), CAP = SH::cap;
+    __shared__ RowsLds<SH> L;
+    __shared__ uint32_t s_base;
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x / sp.parts;
+    const int part = (int)(blockIdx.x - r * sp.parts);
+    const RowPlace pl = row_place(a, r);
+    if (!pl.present) return;  // block-uniform
+    const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
+    const int64_t n = pl.n;
+    const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
+    void *oi = out_row(a.out_idx, pl.out, a.topk, a.out_flags);
+    float *ov = a.out_val ? a.out_val + pl.out * a.topk : nullptr;
+    if (k == 0) {
+        if (part == 0)
+            for (int j = tid; j < a.topk; j += NT) {
+                if (a.out_flags & kOutInt64) ((int64_t *)oi)[j] = -1;
+                else ((int32_t *)oi)[j] = -1;
+                if (ov) ov[j] = -__builtin_inff();
+            }
+        return;  // every part of the row returns here
+    }
+    // This part's slice: whole 16-byte chunks.
+    const int64_t per = ((n + sp.parts - 1) / sp.parts + V - 1) / V * V;
+    const int64_t s0 = min((int64_t)part * per, n), s1 = min(s0 + per, n);
+    bool nan = false;
+    float tau = -__builtin_inff();
+    v4i first[U];
+    load_group<T, NT, U>(first, row + s0, s1 - s0, 0);  // in flight while the sample is read
+    if (n > CAP) {
+        const v4i smp = sample_load(row, n, tid);
+        tau = rows_sample_tau<T, SH>(L, smp, n, rows_target(k, CAP));
+    }
+    const uint32_t m = rows_gather<T, SH, U>(L, first, row + s0, s1 - s0, tau, nan, s0);
+    if (a.nan_flag && __any(nan) && (tid & 63) == 0) atomicOr(a.nan_flag, 1);
+    if (tid == 0) {
+        if (m > (uint32_t)CAP) {
+            atomicOr(sp.over + r, 1u);
+            s_base = (uint32_t)CAP;
+        } else {
+            s_base = m ? atomicAdd(sp.cnt + r, m) : 0u;
+        }
+    }
+    __syncthreads();
+    const uint32_t base = s_base;
+    if (m <= (uint32_t)CAP)
+        for (uint32_t i = tid; i < m; i += NT)
+            if (base + i < (uint32_t)CAP) sp.cand[r * CAP + base + i] = L.cand[i];
+    // The row's last part to finish selects.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(sp.ticket + r, 1u) == (uint32_t)(sp.parts - 1);
+    __syncthreads();
+    if (!s_last) return;  // block-uniform
+    __threadfence();
+    const uint32_t tot = __hip_atomic_load(sp.cnt + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t over = __hip_atomic_load(sp.over + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) {
+        sp.cnt[r] = 0u;
+        sp.over[r] = 0u;
+        sp.ticket[r] = 0u;
+    }
+    if (!over && tot >= k && tot <= (uint32_t)CAP) {
+        RowElems<SH::regs> el;
+        el.load(sp.cand + r * CAP, tot);
+        select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, tot, k, a.topk, oi, ov, a.out_flags, pl.base);
+    } else {
+        bool nan2 = false;
+        const uint32_t m2 = rows_digit_gather<T, SH>(L, row, n, k, nan2);
+        if (m2 <= (uint32_t)CAP) {
+            RowElems<SH::regs> el;
+            el.load(L.cand, m2);
+            __syncthreads();
+            select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m2, k, a.topk, oi, ov, a.out_flags, pl.base);
+        } else {
+            RowStream<T> el{row, n};
+            select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags, pl.base);
+        }
     }
 }
 

@@ -100,13 +100,21 @@ struct ScoreArgs {
     int sample_target;
     int sample_min_stride;     // power of two, see sample_stride
     int sample_split;          // workgroups per tile in sample mode
-    // dense mode
-    const int32_t *rowlist;    // flagged rows
+    // dense mode: batch entry e (e < row_limit) is entry row_base + e of the
+    // flagged-row list (present while below *nrows), or, with no list, row
+    // row_base + e (present while below nrows_direct)
+    const int32_t *rowlist;    // flagged rows, or null: every row
     const unsigned long long *nrows;  // device count of flagged rows
-    int row_base;              // first flagged entry of this batch
+    int nrows_direct;          // rows of the call (no list)
+    int row_base;              // first entry of this batch
     int row_limit;             // entries per batch
     float *scratch;            // [row_limit, scratch_stride] window scores (dense mode)
     int64_t scratch_stride;
+    int32_t *wlen;             // dense mode, or null: window length of each row scored
+    // dense mode without the per-call preparation pass: the FP8 query sums
+    // come from the staged q tile, the per-key factor from sigma (or the
+    // page pool's scales) as each step loads it
+    int own_prep;
     // score-bound pruning (sample and filter modes)
     int prune;                 // 0: off; 1: per tile, from its planner sample; 2: always
     const uint8_t *kb;         // [nblocks, 2, 128] block extremes
@@ -115,22 +123,18 @@ struct ScoreArgs {
     int nblocks;
     float *vplan;              // [ntiles, kPlanGroups, 16 blocks, 16 rows] planner sample
     unsigned long long *plan;  // PlanCounter slots
-    // sample mode: the threshold of each row is computed by the last
-    // workgroup to finish the samples of its row (k_score_few), or by the
-    // tile's workgroup when it is the only one (k_score, sample_split 1)
+    // sample mode: the threshold of each row is computed by the tile's
+    // workgroup when it is the only one (sample_split 1)
     int topk;
     float rank_scale;
     float *tau_w;              // [rows] written threshold
-    uint32_t *ticket;          // [rows] self-resetting finish counters (k_score_few)
-    unsigned long long *stats; // call statistics, cleared by workgroup 0
-    int nstats;
     // 64-head indexers: row t's heads 0-31 and 32-63 are the tile columns 2t
     // and 2t + 1 (q [num_q / 2, 64, 128] read as [num_q, 32, 128], weights
     // likewise, num_q counting columns); the two columns' head sums are
     // added before the threshold, and only even columns emit results, for
     // row column / 2.
     int pair;
-    // few-row kernels over a paged key cache: kv and sigma are the page pools
+    // dense mode over a paged key cache: kv and sigma are the page pools
     const int32_t *table;      // [ceil(num_kv / page_size)] page ids, or null (contiguous keys)
     int page_size;
     int64_t num_pages;
@@ -515,6 +519,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     __shared__ uint16_t s_skip[MODE == kModeFilter ? kMaxSteps / 16 + 1 : 1];  // per 16-block group
     __shared__ int s_wcnt[kWaves];
     __shared__ float s_tau[kTileQ], s_q1[kTileQ];
+    __shared__ float s_qsc[MODE == kModeDense ? kTileQ : 1];  // dense mode without the preparation pass: 2^-e
     __shared__ float s_l1[MODE == kModeSample ? kTileQ * kHeads : 1];
     __shared__ unsigned long long s_pp[2];  // planner sample: pairs, prunable pairs
     __shared__ int s_next;                  // sample mode: next unclaimed step
@@ -541,9 +546,16 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         int t = -1, slot = -1;  // t: the column's q row (row, or 2 row + half)
         if (MODE == kModeDense) {
             const int e = (tile * kTileQ + n) >> ps;
-            if (e < a.row_limit && (unsigned long long)(a.row_base + e) < *a.nrows) {
-                t = (a.rowlist[a.row_base + e] << ps) + (n & ps);
-                slot = e;
+            if (e < a.row_limit) {
+                if (a.rowlist) {
+                    if ((unsigned long long)(a.row_base + e) < *a.nrows) {
+                        t = (a.rowlist[a.row_base + e] << ps) + (n & ps);
+                        slot = e;
+                    }
+                } else if (a.row_base + e < a.nrows_direct) {
+                    t = ((a.row_base + e) << ps) + (n & ps);
+                    slot = e;
+                }
             }
         } else {
             const int64_t tt = (int64_t)tile * kTileQ + n;
@@ -564,6 +576,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                 lo = hi = 0;
             }
         }
+        if (MODE == kModeDense && a.wlen && t >= 0 && (n & ps) == 0 && chunk == 0) a.wlen[t >> ps] = hi - lo;
         s_row[n] = t;
         s_ks[n] = lo;
         s_ke[n] = hi;
@@ -631,13 +644,21 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         jhi = (int)((khi + kStepKeys - 1) / kStepKeys);
     }
 
-    stage_q_tile<DT, 64 * kWaves>(s_q, a, s_row);
+    // Without the preparation pass (dense mode only) the FP8 query sums are
+    // computed here from the staged heads.
+    const bool own_prep = MODE == kModeDense && a.own_prep;  // workgroup-uniform
+    if (DT == kFP8 && own_prep) stage_q_heads<DT, kHeads, 64 * kWaves>(s_q, a.q, a.qbar, s_row);
+    else stage_q_tile<DT, 64 * kWaves>(s_q, a, s_row);
     for (int i = threadIdx.x; i < kHeads * kTileQ; i += blockDim.x) {
         const int rn = i & (kTileQ - 1), h = i / kTileQ;
         const int rt = s_row[rn];
         s_w[i] = rt >= 0 ? a.w[(int64_t)rt * kHeads + h] : 0.0f;
     }
     __syncthreads();
+    if (DT == kFP8 && own_prep) {
+        qbar_tile_lds<64 * kWaves>(s_q, s_w, s_qsc);
+        __syncthreads();
+    }
 
     int nstep = jhi - jlo;
     bool use_skip = false;  // workgroup-uniform
@@ -791,7 +812,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     const int to = PAIR ? s_out[n] : t;  // the row this lane's results belong to, or -1
     const int rks = s_ks[n], rke = s_ke[n];
     const int S = a.num_kv;
-    const float qsc = (DT == kFP8 && t >= 0) ? a.qscale[t] : 1.0f;
+    const float qsc = (DT == kFP8 && t >= 0) ? (own_prep ? s_qsc[MODE == kModeDense ? n : 0] : a.qscale[t]) : 1.0f;
 
     float tau = __builtin_inff();
     if (MODE == kModeFilter && to >= 0) tau = a.tau[to];
@@ -821,7 +842,16 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             } else {
                 int p = (MODE == kModeSample) ? first_b + e * dmin : e;
                 p = min(p, S - 1);
-                load_kfrag(f[kt], a.kv, p, g);
+                if (MODE == kModeDense && a.table) {
+                    // paged keys: logical key p is row p % page_size of its
+                    // page (a page id out of range reads the pool's first row;
+                    // its scale factor is 0)
+                    const int64_t pg = a.table[p / a.page_size];
+                    const int64_t slot = (pg >= 0 && pg < a.num_pages) ? pg * a.page_size + p % a.page_size : 0;
+                    load_kfrag(f[kt], a.kv + slot * RB, 0, g);
+                } else {
+                    load_kfrag(f[kt], a.kv, p, g);
+                }
             }
         }
     };
@@ -850,6 +880,26 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         shv[kt][i] = a.sigh[min(first_b + (sb + 16 * kt + i) * dmin, S + kStepKeys - 1)];
+            } else if (own_prep) {
+                // the factor the preparation pass would store: sigma / 2
+                // (FP8) or sigma, 0 past the keys and for a page out of range
+#pragma unroll
+                for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int p = sb + 16 * kt + i;
+                        float sg = 0.0f;
+                        if (p < S) {
+                            if (a.table) {
+                                const int64_t pg = a.table[p / a.page_size];
+                                const bool ok = pg >= 0 && pg < a.num_pages;
+                                sg = !ok ? 0.0f : (a.sigma ? a.sigma[pg * a.page_size + p % a.page_size] : 1.0f);
+                            } else {
+                                sg = a.sigma ? a.sigma[p] : 1.0f;
+                            }
+                        }
+                        shv[kt][i] = DT == kFP8 ? sg * 0.5f : sg;
+                    }
             } else {
 #pragma unroll
                 for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);

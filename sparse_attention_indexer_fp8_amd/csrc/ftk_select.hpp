@@ -160,155 +160,23 @@ struct RowElems {
 };
 
 // ---------------------------------------------------------------------------
-// Call statistics, accumulated on the device (zeroed by the per-key pass at
-// the start of every call) and copied to the host once selection is done.
-// kStPruned / kStPruneOn are the scan's PlanCounter slots; kStFlagged is also
-// the length of the flagged-row list.
+// Call statistics kept on the device (zeroed by the preparation pass at the
+// start of every fused call): kStPruned / kStPruneOn are the scan's
+// PlanCounter slots; kStFlagged is the length of the flagged-row list.  The
+// row classes of flashtopk_info are counted on the host from each row's
+// window length and candidate count when the record is read.
 
-enum Stat {
-    kStEmpty = 0, kStTakeAll, kStSampled, kStUnder, kStOver, kStFlagged, kStMaxCand, kStWindow,
-    kStPruned, kStPruneOn, kStCount
-};
+enum Stat { kStFlagged = 0, kStPruned, kStPruneOn, kStCount };
 static_assert(kStPruneOn == kStPruned + kPlanItems, "the scan's counters live in the statistics");
 
 // Triage of one row (the pages' "recovery triage"): a row with a non-empty
 // window is rescored densely when its candidate count is below
 // min(topk, L) (its threshold was too high) or above the capacity (too low:
-// the list lost candidates), and every row on the recover-all path is.
-__device__ __forceinline__ bool row_flagged(int64_t len, uint32_t c, int topk, int cap, int recover_all)
+// the list lost candidates).
+__device__ __host__ __forceinline__ bool row_flagged(int64_t len, uint32_t c, int topk, int cap)
 {
     if (len <= 0) return false;
-    if (recover_all) return true;
-    return (int64_t)c < min((int64_t)topk, len) || (int64_t)c > cap;
-}
-
-struct TriageArgs {
-    const int32_t *ks;
-    const int32_t *ke;
-    int64_t num_q;
-    int topk;
-    int cap;
-    const uint32_t *cnt;
-    int recover_all;
-    int32_t *rowlist;
-    unsigned long long *stats;  // Stat
-};
-
-// Triage bookkeeping of one row by one thread (one atomic per statistic).
-__device__ __forceinline__ void triage_one(int64_t t, int64_t len, uint32_t c, int topk, int cap, int recover_all,
-                                           int32_t *rowlist, unsigned long long *stats)
-{
-    if (row_flagged(len, c, topk, cap, recover_all))
-        rowlist[atomicAdd(stats + kStFlagged, 1ull)] = (int32_t)t;
-    if (len == 0) {
-        atomicAdd(stats + kStEmpty, 1ull);
-    } else if (!recover_all) {
-        if ((int64_t)c < min((int64_t)topk, len)) atomicAdd(stats + kStUnder, 1ull);
-        if ((int64_t)c > cap) atomicAdd(stats + kStOver, 1ull);
-        if (len <= cap) {
-            atomicAdd(stats + kStTakeAll, 1ull);
-        } else {
-            atomicAdd(stats + kStSampled, 1ull);
-            atomicMax(stats + kStMaxCand, (unsigned long long)c);
-        }
-    }
-    if (len) atomicAdd(stats + kStWindow, (unsigned long long)len);
-}
-
-// RPT rows per thread (strided by the workgroup size, so loads coalesce);
-// statistics are summed per workgroup and added with one atomic per
-// workgroup and statistic (the counters are few and shared by every
-// workgroup, so per-wave atomics on them serialise).  Flagged rows are
-// appended with one atomic per wave and row round that holds any; the list
-// is in no particular order (each flagged row's result depends on that row
-// alone).  Calls of up to kTriageFewRows rows take one row per thread (more
-// workgroups, each short); larger ones 16 (fewer atomics).
-constexpr int kTriageThreads = 256;
-constexpr int kTriageFewRows = 16384;
-
-template <int RPT>
-__global__ __launch_bounds__(kTriageThreads) void k_triage(TriageArgs a)
-{
-    constexpr int NW = kTriageThreads / 64;
-    constexpr int kTriageRowsPerThread = RPT;
-    __shared__ unsigned long long s_sum[NW][7];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * (kTriageThreads * RPT) + threadIdx.x;
-    uint32_t n_empty = 0, n_take = 0, n_samp = 0, n_under = 0, n_over = 0, maxc = 0;
-    unsigned long long win = 0;
-    // Every row's loads are issued before the first is used (indices past
-    // the last row re-read it; their results are not counted).
-    int32_t rlo[kTriageRowsPerThread], rhi[kTriageRowsPerThread];
-    uint32_t rc[kTriageRowsPerThread];
-#pragma unroll
-    for (int r = 0; r < kTriageRowsPerThread; ++r) {
-        const int64_t t = min(t0 + (int64_t)r * kTriageThreads, a.num_q - 1);
-        rlo[r] = a.ks[t];
-        rhi[r] = a.ke[t];
-        rc[r] = a.cnt[t];
-    }
-#pragma unroll
-    for (int r = 0; r < kTriageRowsPerThread; ++r) {
-        const int64_t t = t0 + (int64_t)r * kTriageThreads;
-        bool flag = false;
-        if (t < a.num_q) {
-            const int64_t lo = rlo[r], hi = rhi[r];
-            const int64_t len = hi > lo ? hi - lo : 0;
-            const uint32_t c = rc[r];
-            flag = row_flagged(len, c, a.topk, a.cap, a.recover_all);
-            if (len == 0) {
-                ++n_empty;
-            } else if (!a.recover_all) {
-                n_under += (int64_t)c < min((int64_t)a.topk, len) ? 1u : 0u;
-                n_over += (int64_t)c > a.cap ? 1u : 0u;
-                if (len <= a.cap) {
-                    ++n_take;
-                } else {
-                    ++n_samp;
-                    maxc = max(maxc, c);
-                }
-            }
-            win += (unsigned long long)len;
-        }
-        const uint64_t bal = __ballot(flag);
-        if (bal) {  // wave-uniform
-            unsigned long long base = 0;
-            if (lane == 0) base = atomicAdd(a.stats + kStFlagged, (unsigned long long)__builtin_popcountll(bal));
-            base = __shfl(base, 0);
-            if (flag) a.rowlist[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (int32_t)t;
-        }
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-        n_empty += __shfl_xor(n_empty, off);
-        n_take += __shfl_xor(n_take, off);
-        n_samp += __shfl_xor(n_samp, off);
-        n_under += __shfl_xor(n_under, off);
-        n_over += __shfl_xor(n_over, off);
-        maxc = max(maxc, (uint32_t)__shfl_xor(maxc, off));
-        win += __shfl_xor(win, off);
-    }
-    if (lane == 0) {
-        s_sum[wave][0] = n_empty;
-        s_sum[wave][1] = n_take;
-        s_sum[wave][2] = n_samp;
-        s_sum[wave][3] = n_under;
-        s_sum[wave][4] = n_over;
-        s_sum[wave][5] = maxc;
-        s_sum[wave][6] = win;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long v[7] = {0, 0, 0, 0, 0, 0, 0};
-        for (int w = 0; w < NW; ++w)
-            for (int i = 0; i < 7; ++i) v[i] = i == 5 ? (s_sum[w][i] > v[i] ? s_sum[w][i] : v[i]) : v[i] + s_sum[w][i];
-        if (v[0]) atomicAdd(a.stats + kStEmpty, v[0]);
-        if (v[1]) atomicAdd(a.stats + kStTakeAll, v[1]);
-        if (v[2]) atomicAdd(a.stats + kStSampled, v[2]);
-        if (v[3]) atomicAdd(a.stats + kStUnder, v[3]);
-        if (v[4]) atomicAdd(a.stats + kStOver, v[4]);
-        if (v[5]) atomicMax(a.stats + kStMaxCand, v[5]);
-        if (v[6]) atomicAdd(a.stats + kStWindow, v[6]);
-    }
+    return (int64_t)c < (len < (int64_t)topk ? len : (int64_t)topk) || (int64_t)c > cap;
 }
 
 // ---------------------------------------------------------------------------
@@ -322,7 +190,6 @@ struct SelectArgs {
     const int32_t *ke;
     int topk;
     int cap;
-    int recover_all;
     // candidate rows
     const uint32_t *cnt;
     const uint64_t *cand;
@@ -330,12 +197,11 @@ struct SelectArgs {
     void *out_idx;       // int32 or int64 (kOutInt64)
     float *out_val;
     int out_flags;       // OutFlag
-    // candidate mode with triage: each row's workgroup also does the row's
-    // triage bookkeeping (statistics, flagged-row list) -- calls with few
-    // rows skip the separate triage pass
-    int triage;
-    int32_t *rowlist_w;
-    unsigned long long *stats_w;
+    // triage: each row's workgroup records the row's window length and
+    // appends a flagged row to the recovery list
+    int32_t *wlen;                 // [rows]
+    int32_t *rowlist;              // flagged rows, in no particular order
+    unsigned long long *nflagged;  // length of the list
 };
 
 // Bucketed selection.  The row's candidates are spread over NBKT buckets
@@ -403,8 +269,12 @@ __global__ __launch_bounds__(SH::nt, SH::minw > 0 ? SH::minw : 1) void k_select(
     const int64_t lo = a.ks[t], hi = a.ke[t];
     const int64_t len = hi > lo ? hi - lo : 0;
     const uint32_t c = a.cnt[t];
-    if (a.triage && threadIdx.x == 0) triage_one(t, len, c, a.topk, a.cap, a.recover_all, a.rowlist_w, a.stats_w);
-    if (row_flagged(len, c, a.topk, a.cap, a.recover_all)) return;  // block-uniform
+    const bool flagged = row_flagged(len, c, a.topk, a.cap);
+    if (threadIdx.x == 0) {
+        a.wlen[t] = (int32_t)len;
+        if (flagged) a.rowlist[atomicAdd(a.nflagged, 1ull)] = t;
+    }
+    if (flagged) return;  // block-uniform
     const uint64_t *src = a.cand + (int64_t)t * a.cap;
     const int64_t n = len > 0 ? min((int64_t)c, (int64_t)a.cap) : 0;  // a.cap <= NREG * NT
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);

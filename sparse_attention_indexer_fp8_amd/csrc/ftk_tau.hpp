@@ -180,74 +180,6 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
     }
 }
 
-// The same threshold computed by a whole workgroup of NT threads from n <=
-// kTauBuckets sample codes (at most kTauBuckets / NT per thread): the same
-// buckets and rule as wave_tau.  hist is kTauBuckets words of LDS, red 3 *
-// (NT / 64) + 1 words; every thread returns the threshold.
-template <int NT>
-__device__ float block_tau(const uint32_t *samp, int n, uint32_t r, uint32_t *hist, uint32_t *red)
-{
-    constexpr int NW = NT / 64, PER = kTauBuckets / NT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t c[PER];
-    uint32_t hic = 0, nloc = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) c[j] = samp[min(tid + NT * j, max(n, 1) - 1)];  // all loads in flight
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int i = tid + NT * j;
-        if (i >= n) c[j] = 0u;
-        if (i < n) {
-            hic = max(hic, c[j]);
-            nloc = max(nloc, ~c[j]);
-        }
-    }
-    hic = wave_max(hic);
-    nloc = wave_max(nloc);
-    if (lane == 0) {
-        red[wave] = hic;
-        red[NW + wave] = nloc;
-    }
-    for (int i = tid; i < kTauBuckets; i += NT) hist[i] = 0u;
-    __syncthreads();
-    for (int w = 0; w < NW; ++w) {
-        hic = max(hic, red[w]);
-        nloc = max(nloc, red[NW + w]);
-    }
-    const float vmin = float_of_ord(~nloc), vmax = float_of_ord(hic);
-    const float scale = (float)kTauBuckets / (vmax - vmin);
-    if (!(vmax > vmin) || !__builtin_isfinite(scale)) return vmin;  // all samples equal: admit them all
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (tid + NT * j < n) {
-            const float x = (vmax - float_of_ord(c[j])) * scale;
-            atomicAdd(&hist[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
-        }
-    }
-    __syncthreads();
-    // Thread t owns buckets [PER t, PER t + PER); exclusive prefix over threads.
-    uint32_t run = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        c[j] = hist[tid * PER + j];
-        run += c[j];
-    }
-    const uint32_t x = wave_incl_add(run);
-    if (lane == 63) red[2 * NW + wave] = x;
-    if (tid == 0) red[3 * NW] = 0u;
-    __syncthreads();
-    uint32_t base = x - run;
-    for (int w = 0; w < wave; ++w) base += red[2 * NW + w];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (base < r && r <= base + c[j]) red[3 * NW] = tid * PER + j;
-        base += c[j];
-    }
-    __syncthreads();
-    const uint32_t b = red[3 * NW];
-    return vmax - (float)(b + 2) / scale;
-}
-
 struct TauArgs {
     const int32_t *ks;
     const int32_t *ke;

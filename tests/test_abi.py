@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sparse_attention_indexer_fp8_amd as ftk
@@ -52,6 +53,7 @@ def test_header_constants_match_binding():
     assert int(consts["FLASHTOPK_BF16"]) == ftk.FLASHTOPK_BF16
     assert int(consts["FLASHTOPK_MAX_TOPK"]) == ftk.MAX_TOPK
     assert int(consts["FLASHTOPK_PATH_RECOVER"]) == ftk.PATH_RECOVER
+    assert int(consts["FLASHTOPK_PATH_FUSED"]) == ftk.PATH_FUSED
     assert int(consts["FLASHTOPK_SCORES_F32"]) == ftk.FLASHTOPK_SCORES_F32
     assert int(consts["FLASHTOPK_SCORES_BF16"]) == ftk.FLASHTOPK_SCORES_BF16
     assert int(consts["FLASHTOPK_OUT_INDEX_ORDER"]) == ftk.FLASHTOPK_OUT_INDEX_ORDER
@@ -113,6 +115,11 @@ def test_argument_errors_without_device(lib):
     assert _call(lib, num_q=3, topk=5) == 1                  # null required pointers
     assert lib.flashtopk_reserve(-1, 0, 1, 0, None) == 1
     assert lib.flashtopk_reserve(1, 1, 1, 3, None) == 2
+    assert lib.flashtopk_reserve(1, 1 << 31, 1, 0, None) == 1
+    assert lib.flashtopk_get_last_info(None, None) == 1
+    assert lib.flashtopk_get_last_recovered(None, None, 0, None) == 1     # no count pointer
+    n = ctypes.c_int64(0)
+    assert lib.flashtopk_get_last_recovered(None, None, 5, ctypes.byref(n)) == 1  # rows missing
 
 
 def test_misaligned_operands_rejected(lib):
@@ -171,3 +178,50 @@ def test_select_paged_argument_errors_without_device(lib):
     assert call(table=None) == 1               # keys without a block table
     assert call(num_pages=0) == 1              # keys without pages
     assert call(pages=ctypes.c_void_p(ok.value + 2)) == 1  # misaligned pool
+
+
+# ------------------------------------------------- windows_from_cu_seqlens ---
+
+def _windows_by_definition(cu_q, cu_k):
+    """Bottom-right aligned causal windows, row by row (README "Usage"
+    windows_from_cu_seqlens; query i of document j, Lq queries and Lk keys,
+    sees [cu_k[j], cu_k[j] + Lk - Lq + i + 1), clipped to the document)."""
+    ks, ke = [], []
+    for j in range(len(cu_q) - 1):
+        lq, lk = cu_q[j + 1] - cu_q[j], cu_k[j + 1] - cu_k[j]
+        for i in range(lq):
+            e = cu_k[j] + lk - lq + i + 1
+            ks.append(cu_k[j])
+            ke.append(min(max(e, cu_k[j]), cu_k[j + 1]))
+    return np.asarray(ks, np.int32), np.asarray(ke, np.int32)
+
+
+@pytest.mark.parametrize("cu_q,cu_k", [
+    ([0, 8192, 24576, 49152, 65536], [0, 8192, 24576, 49152, 65536]),   # the packed BF16 sequence
+    ([0, 2, 2, 5], [0, 4, 6, 9]),                                        # an empty document, Lq < Lk
+    ([0, 4], [0, 2]),                                                    # Lq > Lk: leading empty windows
+    ([0, 0, 3], [0, 5, 5]),                                              # a document without keys
+    ([0, 1, 2, 3], [0, 100, 200, 300]),                                  # decode: one query per document
+])
+def test_windows_from_cu_seqlens(cu_q, cu_k):
+    import torch
+
+    import workloads
+
+    ks, ke = ftk.windows_from_cu_seqlens(torch.tensor(cu_q, dtype=torch.int32), torch.tensor(cu_k, dtype=torch.int32))
+    assert ks.dtype == torch.int32 and ke.dtype == torch.int32
+    dks, dke = _windows_by_definition(cu_q, cu_k)
+    assert np.array_equal(ks.numpy(), dks) and np.array_equal(ke.numpy(), dke)
+    wks, wke = workloads.packed_windows(cu_q, cu_k)
+    assert np.array_equal(ks.numpy(), wks) and np.array_equal(ke.numpy(), wke)
+
+
+def test_windows_from_cu_seqlens_hand_values():
+    import torch
+
+    ks, ke = ftk.windows_from_cu_seqlens(torch.tensor([0, 2, 2, 5]), torch.tensor([0, 4, 6, 9]))
+    assert ks.tolist() == [0, 0, 6, 6, 6]
+    assert ke.tolist() == [3, 4, 7, 8, 9]
+    ks, ke = ftk.windows_from_cu_seqlens(torch.tensor([0, 4]), torch.tensor([0, 2]))
+    assert ks.tolist() == [0, 0, 0, 0]
+    assert ke.tolist() == [0, 0, 1, 2]

@@ -1,11 +1,14 @@
-"""Calls with at most four query rows (decode and a few speculative tokens),
-which score with the heads-on-M kernel in every mode.
+"""Calls of few query rows (decode, a few speculative tokens) and the
+independence of a row's results from the rest of the call.
 
-Integer data is compared with the oracle bit-exactly, Gaussian data within
-the tolerance rule; forced paths (dense recovery of every row, a capacity
-small enough to overflow, the prune option, which such calls ignore) must
-return the default path's bits, since every mode of the call shares the
-kernel's arithmetic.
+By default such calls take the dense path: every row's window scores are
+materialised and the row top-k kernels select from them, each row split
+over several workgroups.  Integer data is compared with the oracle
+bit-exactly, Gaussian data within the tolerance rule.  The fused path
+forced on the same call (sampled threshold, filter, selection, recovery of
+misjudged rows) and its forced variants must return the dense path's bits:
+every path scores a (row, key) pair with the same instructions.  For the
+same reason a row's bits must not depend on which other rows share its call.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ from gpu_util import opts, parity, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
-SCAN, PRUNE, RECOVER = 1, 2, 3
+SCAN, PRUNE, RECOVER, FUSED = 1, 2, 3, 4
 
 
 def _say(*a):
@@ -48,6 +51,17 @@ CASES = [
     (3, 50000, 2048, "bf16", "ragged"),
     (4, 65536, 1024, "bf16", "causal"),
     (4, 20001, 64, "fp8", "ragged"),
+    (16, 30000, 4096, "fp8", "ragged"),
+    (61, 9000, 100, "bf16", "ragged"),
+]
+
+FORCED = [
+    ("recover", dict(path=RECOVER)),
+    ("fused", dict(path=FUSED)),
+    ("prune", dict(path=PRUNE)),
+    ("scan_cap_topk", dict(path=SCAN, cand_capacity=4096)),
+    ("fused_underflow", dict(path=FUSED, sample_rank_scale=0.02)),
+    ("dense_small_budget", dict(path=RECOVER, recover_budget_bytes=4 << 20)),
 ]
 
 
@@ -60,12 +74,14 @@ def test_few_rows_integer_exact(case):
     got = run_gpu(wl, d)
     rep = parity(wl, got[0], got[1], "exact")
     assert rep["ok"], rep
-    # every forced path returns the same bits
-    for o in (opts(path=RECOVER), opts(path=PRUNE), opts(path=SCAN, cand_capacity=topk)):
-        assert _same(run_gpu(wl, d, options=o), got)
+    for label, kw in FORCED:
+        kw = dict(kw)
+        if "cand_capacity" in kw:
+            kw["cand_capacity"] = topk
+        assert _same(run_gpu(wl, d, options=opts(**kw)), got), label
 
 
-@pytest.mark.parametrize("T,dt", [(1, "bf16"), (3, "fp8")])
+@pytest.mark.parametrize("T,dt", [(1, "bf16"), (3, "fp8"), (64, "fp8")])
 def test_few_rows_gaussian_tolerance_and_paths(T, dt):
     _say("few gaussian", T, dt)
     wl = workloads.gaussian(T, 131072, 2048, dt, 980 + T)
@@ -73,8 +89,10 @@ def test_few_rows_gaussian_tolerance_and_paths(T, dt):
     got = run_gpu(wl, d)
     rep = parity(wl, got[0], got[1], "tolerance")
     assert rep["ok"], rep
-    assert _same(run_gpu(wl, d, options=opts(path=RECOVER)), got)
-    assert _same(run_gpu(wl, d, options=opts(sample_rank_scale=0.02)), got)  # threshold too high: recovery
+    for label, kw in FORCED:
+        if "cand_capacity" in kw:
+            continue
+        assert _same(run_gpu(wl, d, options=opts(**kw)), got), label
     assert _same(run_gpu(wl, d), got)  # repeatable
 
 
@@ -83,3 +101,33 @@ def test_few_rows_trained_shaped_decode():
     got = run_gpu(wl)
     rep = parity(wl, got[0], got[1], "tolerance")
     assert rep["ok"], rep
+
+
+def _rows_of(wl, rows):
+    """The workload restricted to the given rows (same keys)."""
+    out = dict(wl)
+    for k in ("q", "weights", "ks", "ke"):
+        out[k] = np.ascontiguousarray(wl[k][rows])
+    return out
+
+
+@pytest.mark.parametrize("dt,maker", [("fp8", "gaussian"), ("bf16", "gaussian"), ("fp8", "trained")])
+def test_row_bits_do_not_depend_on_the_call(dt, maker):
+    # The same rows scored in calls of 1, 5, 17 and 300 rows, on the dense and
+    # the fused path, give the same bits (Gaussian data: the scores are not
+    # exact, so this checks that every path runs the same arithmetic).
+    _say("batch invariance", dt, maker)
+    T, S, topk = 300, 20000, 256
+    if maker == "gaussian":
+        wl = _windows(workloads.gaussian(T, S, topk, dt, 995), "ragged", 996)
+    else:
+        wl = _windows(workloads.trained_shaped(T, S, topk, dt, 997), "ragged", 998)
+    big = run_gpu(wl, options=opts(path=FUSED))
+    big_dense = run_gpu(wl, options=opts(path=RECOVER))
+    assert _same(big, big_dense)
+    for rows in ([123], [0, 7, 150, 298, 299], list(range(40, 57))):
+        sub = _rows_of(wl, np.asarray(rows))
+        for path in (0, FUSED, RECOVER):
+            got = run_gpu(sub, options=opts(path=path))
+            assert np.array_equal(got[0], big[0][rows]), (rows, path)
+            assert np.array_equal(got[1].view(np.uint32), big[1][rows].view(np.uint32)), (rows, path)

@@ -52,7 +52,8 @@ def test_64_heads_integer_exact_and_paths(case):
     got = run_gpu(wl, d)
     rep = parity(wl, got[0], got[1], "exact")
     assert rep["ok"], rep
-    for o in (opts(path=3), opts(path=2), opts(cand_capacity=topk), opts(sample_rank_scale=0.02)):
+    for o in (opts(path=3), opts(path=2), opts(path=4), opts(path=4, cand_capacity=topk),
+              opts(path=4, sample_rank_scale=0.02)):
         assert _same(run_gpu(wl, d, options=o), got)
 
 
@@ -64,11 +65,16 @@ def test_64_heads_gaussian(dt):
     assert rep["ok"], rep
 
 
-def test_64_heads_full_size_sampled_rows():
-    from gpu_util import sample_rows
+def test_64_heads_full_size_parity():
+    # every 16th row, the first and last 64 and every rescored row
+    import sparse_attention_indexer_fp8_amd as ftk
 
     wl = workloads.config(9)
     got = run_gpu(wl)
-    rows = sample_rows(wl["q"].shape[0], n_mid=16, edge=4, seed=9)
+    recovered = ftk.flashtopk_get_last_recovered()
+    T = wl["q"].shape[0]
+    rows = np.unique(np.concatenate([np.arange(0, T, 16), np.arange(64), np.arange(T - 64, T),
+                                     recovered.astype(np.int64)])).astype(np.int64)
+    print("oracle rows", len(rows), "recovered", len(recovered), flush=True)
     rep = parity(wl, got[0], got[1], "tolerance", rows=rows)
     assert rep["ok"], rep

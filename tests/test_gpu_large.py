@@ -1,32 +1,40 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py times,
-checked against the oracle on sampled rows (MI355X only).
+checked against the oracle (MI355X only).
 
 * 4096 queries x 128K FP8 keys, causal, topk 4096 (flat Gaussian rows) and
   topk 2048 (heavy-tailed rows);
 * 64K x 64K BF16 packed sequence of four documents, topk 512, rows shorter
   than topk padded;
 * decode shapes: one and 64 query rows over the whole 128K context, topk 2048
-  (the launch configuration splits each tile's sample over many workgroups);
-* the integer-valued twins of all five, checked bit-exact.
-Sampled rows: the first and last rows, random rows, and (packed) rows at
-every document start and in the short-window region.
+  (the dense path: every row's scores materialised, each row's selection
+  split over several workgroups), and the 64-row shape forced through the
+  fused path (each tile's sample split over many workgroups);
+* the integer-valued twins of all of them, checked bit-exact.
+Rows checked against the oracle: every 16th row, the first and the last 64
+rows, every row the call rescored densely, and (packed) the rows around
+every document start and the short-window boundaries; decode shapes on
+every row.  The structure of every row (count, uniqueness, windows,
+padding, order) is checked on all rows.
 """
 import numpy as np
 import pytest
 
 import workloads
 
-from gpu_util import parity, run_gpu, sample_rows
+from gpu_util import parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
 
-def _rows(wl, extra=()):
+def _rows(wl, extra=(), recovered=()):
+    """Every 16th row, the first and last 64, the rows the call rescored and
+    the extra rows (all rows when there are at most 64)."""
     T = wl["q"].shape[0]
     if T <= 64:
-        return np.arange(0, T, 4 if T > 16 else 1, dtype=np.int64)
-    rows = sample_rows(T, n_mid=20, edge=6, seed=T)
-    return np.unique(np.concatenate([rows, np.asarray(extra, np.int64)])).astype(np.int64)
+        return np.arange(T, dtype=np.int64)
+    rows = np.concatenate([np.arange(0, T, 16), np.arange(min(64, T)), np.arange(max(0, T - 64), T),
+                           np.asarray(recovered, np.int64), np.asarray(extra, np.int64)])
+    return np.unique(rows[(rows >= 0) & (rows < T)]).astype(np.int64)
 
 
 def _packed_extra():
@@ -61,28 +69,35 @@ CASES = [
     ("decode_fp8_64x131072", 8, False, "tolerance"),
     ("decode_int_fp8_1x131072", 7, True, "exact"),
     ("decode_int_fp8_64x131072", 8, True, "exact"),
+    ("decode_fused_fp8_64x131072", 8, False, "tolerance"),
+    ("decode_fused_int_fp8_64x131072", 8, True, "exact"),
 ]
 
 
 @pytest.mark.parametrize("name,n,twin,mode", CASES, ids=[c[0] for c in CASES])
-def test_full_size_sampled_rows(name, n, twin, mode):
+def test_full_size_parity(name, n, twin, mode):
     import sparse_attention_indexer_fp8_amd as ftk
+
+    from gpu_util import opts
 
     print("case", name, flush=True)
     wl = workloads.config(n, integer_twin=twin)
-    idx, val = run_gpu(wl)
+    idx, val = run_gpu(wl, options=opts(path=4) if "fused" in name else None)
     info = ftk.flashtopk_get_last_info()
-    print("info", info, flush=True)
+    recovered = ftk.flashtopk_get_last_recovered()
+    print("info", info, "recovered", recovered[:20], flush=True)
+    assert len(recovered) == info["rows_recovered"]
     if n in (3, 4, 5):
         _check_row_classes(wl, info)
-    rows = _rows(wl, _packed_extra() if n == 5 else ())
+    rows = _rows(wl, _packed_extra() if n == 5 else (), recovered)
+    print("oracle rows", len(rows), flush=True)
     rep = parity(wl, idx, val, mode, rows=rows)
     assert rep["ok"], rep
-    # every row, sampled or not, has the right structure
+    # every row has the right structure
     import checker
 
     T = wl["q"].shape[0]
-    for t in range(0, T, max(1, T // 512)):
+    for t in range(T):
         assert not checker.structure_failures(idx[t], val[t], wl["ks"][t], wl["ke"][t], wl["topk"]), t
     if n == 5:
         short = (wl["ke"] - wl["ks"]) < wl["topk"]

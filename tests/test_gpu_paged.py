@@ -3,8 +3,9 @@
 A workload's keys are scattered over a shuffled page pool with garbage in
 the unused pages; the paged call must return the contiguous call's bits,
 and the oracle's result on the logical keys (bit-exact on integer data).
-Calls with many rows gather the keys first; calls with at most four rows
-read them from the pages in every mode (forced recovery included).
+The fused path gathers the keys first; the dense path (the default for
+calls of few (row, key) pairs, and forced recovery) reads each key from its
+page.  Both are run on every case.
 """
 import numpy as np
 import pytest
@@ -81,9 +82,9 @@ def test_paged_matches_contiguous_and_oracle(name, make, page_size, mode):
     assert np.array_equal(got[1].view(np.uint32), ref[1].view(np.uint32))
     rep = parity(wl, got[0], got[1], mode)
     assert rep["ok"], rep
-    if wl["q"].shape[0] <= 4:
-        from gpu_util import opts
+    from gpu_util import opts
 
-        rec = _run_paged(wl, page_size, 1010, options=opts(path=3))
-        assert np.array_equal(rec[0], got[0])
-        assert np.array_equal(rec[1].view(np.uint32), got[1].view(np.uint32))
+    for path in (3, 4):  # dense (pages read in place), fused (pages gathered)
+        other = _run_paged(wl, page_size, 1010, options=opts(path=path))
+        assert np.array_equal(other[0], got[0]), path
+        assert np.array_equal(other[1].view(np.uint32), got[1].view(np.uint32)), path

@@ -94,15 +94,23 @@ def path_case():
     return wl, d, base
 
 
+FUSED, RECOVER = 4, 3
+
+
 @pytest.mark.parametrize("label,kw", [
-    ("recover_all", dict(path=3)),
-    ("tiny_capacity_overflow", dict(cand_capacity=256)),
-    ("high_threshold_underflow", dict(sample_rank_scale=0.02)),
-    ("low_threshold", dict(sample_rank_scale=1.7)),
-    ("small_sample", dict(sample_target=64)),
-    ("tiny_recover_budget", dict(cand_capacity=256, recover_budget_bytes=1)),
+    ("recover_all", dict(path=RECOVER)),
+    ("fused", dict(path=FUSED)),
+    ("fused_scan", dict(path=1)),
+    ("tiny_capacity_overflow", dict(path=FUSED, cand_capacity=256)),
+    ("high_threshold_underflow", dict(path=FUSED, sample_rank_scale=0.02)),
+    ("low_threshold", dict(path=FUSED, sample_rank_scale=1.7)),
+    ("small_sample", dict(path=FUSED, sample_target=64)),
+    ("tiny_recover_budget", dict(path=FUSED, cand_capacity=256, recover_budget_bytes=1)),
+    ("dense_tiny_budget", dict(path=RECOVER, recover_budget_bytes=1)),
 ])
 def test_paths_give_identical_bits(path_case, label, kw):
+    # The default path of this call (dense: few (row, key) pairs) against the
+    # fused path and every forced variant of either.
     import sparse_attention_indexer_fp8_amd as ftk
 
     wl, d, base = path_case
@@ -111,15 +119,19 @@ def test_paths_give_identical_bits(path_case, label, kw):
     assert np.array_equal(idx, base[0])
     assert np.array_equal(val.view(np.uint32), base[1].view(np.uint32))
     info = ftk.flashtopk_get_last_info()
-    if label in ("recover_all", "tiny_capacity_overflow", "high_threshold_underflow", "tiny_recover_budget"):
+    if label in ("recover_all", "tiny_capacity_overflow", "high_threshold_underflow", "tiny_recover_budget",
+                 "dense_tiny_budget"):
         assert info["rows_recovered"] > 0, info
+    if label in ("tiny_capacity_overflow", "high_threshold_underflow", "tiny_recover_budget"):
+        # the rows counted as recovered are the ones that under- or overflowed
+        assert info["rows_recovered"] == info["rows_underflow"] + info["rows_overflow"], info
 
 
 def test_default_path_recovers_nothing_on_random_rows(path_case):
     import sparse_attention_indexer_fp8_amd as ftk
 
     wl, d, base = path_case
-    run_gpu(wl, d)
+    run_gpu(wl, d, options=opts(path=FUSED))
     info = ftk.flashtopk_get_last_info()
     assert info["rows_recovered"] == 0, info
     assert info["rows_sampled"] == 64
@@ -127,15 +139,16 @@ def test_default_path_recovers_nothing_on_random_rows(path_case):
 
 def test_repeat_runs_identical(path_case):
     wl, d, base = path_case
-    for _ in range(5):
-        idx, val = run_gpu(wl, d)
-        assert np.array_equal(idx, base[0])
-        assert np.array_equal(val.view(np.uint32), base[1].view(np.uint32))
+    for path in (0, FUSED):
+        for _ in range(10):
+            idx, val = run_gpu(wl, d, options=opts(path=path))
+            assert np.array_equal(idx, base[0])
+            assert np.array_equal(val.view(np.uint32), base[1].view(np.uint32))
 
 
 def test_recovered_rows_match_oracle(path_case):
     wl, d, base = path_case
-    idx, val = run_gpu(wl, d, options=opts(path=3))
+    idx, val = run_gpu(wl, d, options=opts(path=FUSED, cand_capacity=256))
     rep = parity(wl, idx, val, "tolerance")
     assert rep["ok"], rep
 

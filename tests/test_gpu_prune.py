@@ -15,7 +15,7 @@ from gpu_util import opts, parity, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
-SCAN, PRUNE = 1, 2
+SCAN, PRUNE, FUSED = 1, 2, 4
 
 
 def _say(*a):
@@ -54,6 +54,8 @@ def test_forced_prune_matches_scan_and_oracle(name, make, mode):
     assert _same(pr, scan)
     auto = run_gpu(wl, d)
     assert _same(auto, scan)
+    planned = run_gpu(wl, d, options=opts(path=FUSED))
+    assert _same(planned, scan)
     rep = parity(wl, pr[0], pr[1], mode)
     assert rep["ok"], rep
 
@@ -62,7 +64,7 @@ def test_planner_prunes_block_local_keys():
     wl = workloads.blocky(256, 65536, 512, "fp8", 505)
     d = to_device(wl)
     scan = run_gpu(wl, d, options=opts(path=SCAN))
-    auto = run_gpu(wl, d)
+    auto = run_gpu(wl, d, options=opts(path=FUSED))
     info = _info()
     _say("auto", info)
     assert info["path"] == PRUNE, info
@@ -75,7 +77,7 @@ def test_planner_scans_untrained_keys(dtype):
     wl = workloads.gaussian(128, 32768, 256, dtype, 506)
     d = to_device(wl)
     scan = run_gpu(wl, d, options=opts(path=SCAN))
-    auto = run_gpu(wl, d)
+    auto = run_gpu(wl, d, options=opts(path=FUSED))
     info = _info()
     assert info["path"] == SCAN, info
     assert info["pruned_keys"] == 0, info
