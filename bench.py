@@ -301,6 +301,7 @@ def main():
         "path_taken": m["path_taken"],
         "rows_recovered": m["rows_recovered"],
         "max_candidates": m["max_candidates"],
+        "mean_candidates": m["mean_candidates"],
         "kernels_ms": m["kernels_ms"],
         "roofline": {"bound": "mfma", "kernel": m["roofline_kernel"], "achieved": m["achieved_tflops"],
                      "peak": peak, "unit": "TFLOP/s", "frac": round(m["achieved_tflops"] / peak, 4),
@@ -313,8 +314,8 @@ def main():
         owl = workloads.config(n)
         om = measure(owl, args, full=False)
         others[owl["name"]] = {k: om[k] for k in ("ms", "pct_mfma_peak", "dense_equiv_tflops", "path_taken",
-                                                  "rows_recovered", "kernels_ms", "achieved_tflops",
-                                                  "roofline_kernel")}
+                                                  "rows_recovered", "mean_candidates", "kernels_ms",
+                                                  "achieved_tflops", "roofline_kernel")}
         others[owl["name"]]["ms"] = round(om["ms"], 4)
         others[owl["name"]]["roofline_frac"] = round(om["achieved_tflops"] / PEAK_TFLOPS[om["dtype"]], 4)
         others[owl["name"]]["peak_tflops"] = PEAK_TFLOPS[om["dtype"]]
@@ -454,6 +455,7 @@ def measure(wl, args, full):
         "path_taken": {1: "scan", 2: "prune", 3: "dense"}.get(info["path"], "?"),
         "rows_recovered": info["rows_recovered"],
         "max_candidates": info["max_candidates"],
+        "mean_candidates": round(info["candidates"] / max(1, info["rows_sampled"]), 1),
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "achieved_tflops": round(achieved, 1),
         "flops": flops,

@@ -78,7 +78,7 @@ extern "C" {
 
 /* Execution paths.  Every path returns bit-identical results; they differ only
  * in speed.  Used by tests and benchmarks to force a path.
- *   AUTO     calls of at most 16M (row, key) pairs (num_q * num_kv) take the
+ *   AUTO     calls of at most 8M (row, key) pairs (num_q * num_kv) take the
  *            dense path, larger ones the fused path with the per-tile prune
  *            decision
  *   SCAN     fused: sampled threshold + full filtering scan, no pruning
@@ -114,7 +114,7 @@ typedef struct flashtopk_options {
     int sample_target;        /* most keys sampled per row for the
                                  threshold; 0 = 2048, at most 2048 (the
                                  lattice stride is also at least topk / 32) */
-    int64_t recover_budget_bytes; /* scratch for dense scores; 0 = 1 GiB.  The
+    int64_t recover_budget_bytes; /* scratch for dense scores; 0 = 2 GiB.  The
                                  fused path reserves it for the rescoring it
                                  launches up front; rows are rescored in
                                  batches of budget / (4 * num_kv) rows (at
@@ -180,6 +180,8 @@ typedef struct flashtopk_info {
      * whole call). */
     float ms_sample, ms_tau, ms_filter, ms_triage, ms_select, ms_recover;
     int32_t invalid;            /* FLASHTOPK_INVALID_* bits found by options.validate, else 0 */
+    int64_t candidates;         /* fused path: candidates of the sampled rows, summed (the
+                                   threshold aims at 2 * topk per row) */
 } flashtopk_info;
 
 /* Exact top-k of the indexer score for every query row (see the file comment
@@ -260,7 +262,7 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
  * drain the stream.  Calls whose options raise the capacity, the sample size
  * or the budget may still grow it.  The workspace holds about
  * max_q * (8 * min(16384, 4 * max_topk) + 8 KiB) bytes plus the recovery
- * scratch (up to 1 GiB by default). */
+ * scratch (up to 2 GiB by default). */
 int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, void *stream);
 
 /* Record of the last call issued on `stream` from this process.  Synchronises

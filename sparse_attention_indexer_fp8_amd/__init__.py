@@ -82,6 +82,7 @@ class Info(ctypes.Structure):
         ("ms_select", ctypes.c_float),
         ("ms_recover", ctypes.c_float),
         ("invalid", ctypes.c_int32),
+        ("candidates", ctypes.c_int64),
     ]
 
     def as_dict(self):

@@ -55,11 +55,11 @@ namespace {
 
 constexpr int kMaxCap = 16384;
 constexpr int kDefaultSampleTarget = 2048;
-constexpr int64_t kDefaultRecoverBudget = int64_t(1) << 30;
+constexpr int64_t kDefaultRecoverBudget = int64_t(2) << 30;
 // The auto path scores every row densely when the call's (row, key) pairs
 // are at most this many: materialising the scores then costs less than the
 // fused path's fixed passes (preparation, sample, thresholds, selection).
-constexpr int64_t kDensePairs = int64_t(16) << 20;
+constexpr int64_t kDensePairs = int64_t(8) << 20;
 // Smallest key chunk of a dense-mode work item.
 constexpr int kMinDenseChunk = 512;
 // Split-row top-k: at most this many workgroups per row, each streaming at
@@ -83,7 +83,7 @@ struct Workspace {
     std::mutex mu;  // held while a call is enqueued or its record read
     DevBuf tau, cnt, rowlist, stats, wlen, cand, samp, scratch, qbar, qscale, sigh;
     DevBuf kb, kmeta, vplan, q1;                 // score-bound pruning
-    DevBuf scnt, sover, sticket, scand;          // split-row top-k (kept zero between calls)
+    DevBuf scnt, sover, scand;                   // split-row top-k (counters read zero between calls)
     DevBuf pkv, psig;                            // keys and scales gathered from a paged cache
     DevBuf vflag;                                // precondition flags (options.validate)
     unsigned *host_flag = nullptr;               // pinned: the precondition flags
@@ -259,17 +259,23 @@ int split_parts(int64_t rows, int64_t cols)
     return parts;
 }
 
+// kModeDenseLoop: dense mode with workgroups looping over the work items.
+constexpr int kModeDenseLoop = 3;
+
 template <int DT>
 void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
 {
+    constexpr int WD = 64 * ScoreCfg<DT, kModeDense>::waves;
     if (a.pair) {
         if (mode == kModeFilter) k_score<DT, kModeFilter, true><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
         else if (mode == kModeSample) k_score<DT, kModeSample, true><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
-        else k_score<DT, kModeDense, true><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
+        else if (mode == kModeDense) k_score<DT, kModeDense, true><<<grid, WD, 0, st>>>(a);
+        else k_score<DT, kModeDense, true, true><<<grid, WD, 0, st>>>(a);
     } else {
         if (mode == kModeFilter) k_score<DT, kModeFilter, false><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
         else if (mode == kModeSample) k_score<DT, kModeSample, false><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
-        else k_score<DT, kModeDense, false><<<grid, 64 * ScoreCfg<DT, kModeDense>::waves, 0, st>>>(a);
+        else if (mode == kModeDense) k_score<DT, kModeDense, false><<<grid, WD, 0, st>>>(a);
+        else k_score<DT, kModeDense, false, true><<<grid, WD, 0, st>>>(a);
     }
 }
 
@@ -311,8 +317,9 @@ template <typename T, typename SH>
 void launch_rows(const RowsArgs &a, hipStream_t s, bool pre_tau, const RowsSplit *split)
 {
     if (split && split->parts > 1) {
-        hipLaunchKernelGGL((k_topk_rows_split<T, SH>), dim3((unsigned)(a.rows * split->parts)), dim3(SH::nt), 0, s, a,
+        hipLaunchKernelGGL((k_topk_rows_part<T, SH>), dim3((unsigned)(a.rows * split->parts)), dim3(SH::nt), 0, s, a,
                            *split);
+        hipLaunchKernelGGL((k_topk_rows_merge<T, SH>), dim3((unsigned)a.rows), dim3(SH::nt), 0, s, a, *split);
         return;
     }
     static int per_cu = 0;
@@ -323,13 +330,18 @@ void launch_rows(const RowsArgs &a, hipStream_t s, bool pre_tau, const RowsSplit
             b = 1;
         per_cu = b;
     }
-    const dim3 grid((unsigned)a.rows);
-    if (pre_tau && a.rows > (int64_t)per_cu * num_cu()) {
+    const int64_t resident = (int64_t)per_cu * num_cu();
+    if (a.rowmap) {
+        // flagged rows, counted on the device: the rows loop over at most the
+        // resident workgroups
+        hipLaunchKernelGGL((k_topk_rows<T, SH, false, true>), dim3((unsigned)std::min(a.rows, resident)),
+                           dim3(SH::nt), 0, s, a);
+    } else if (pre_tau && a.rows > resident) {
         const dim3 tgrid((unsigned)((a.rows + kRowsTauWaves - 1) / kRowsTauWaves));
         hipLaunchKernelGGL((k_rows_tau<T, SH>), tgrid, dim3(64 * kRowsTauWaves), 0, s, a);
-        hipLaunchKernelGGL((k_topk_rows<T, SH, true>), grid, dim3(SH::nt), 0, s, a);
+        hipLaunchKernelGGL((k_topk_rows<T, SH, true>), dim3((unsigned)a.rows), dim3(SH::nt), 0, s, a);
     } else {
-        hipLaunchKernelGGL((k_topk_rows<T, SH, false>), grid, dim3(SH::nt), 0, s, a);
+        hipLaunchKernelGGL((k_topk_rows<T, SH, false>), dim3((unsigned)a.rows), dim3(SH::nt), 0, s, a);
     }
 }
 
@@ -350,11 +362,9 @@ int ensure_split(Workspace &w, int64_t rows, int parts, RowsSplit &sp)
     int st;
     if ((st = ensure_zeroed(w, w.scnt, sizeof(uint32_t) * (size_t)rows))) return st;
     if ((st = ensure_zeroed(w, w.sover, sizeof(uint32_t) * (size_t)rows))) return st;
-    if ((st = ensure_zeroed(w, w.sticket, sizeof(uint32_t) * (size_t)rows))) return st;
     if ((st = ensure(w, w.scand, sizeof(uint64_t) * (size_t)rows * RowsLarge::cap))) return st;
     sp.cnt = (uint32_t *)w.scnt.ptr;
     sp.over = (uint32_t *)w.sover.ptr;
-    sp.ticket = (uint32_t *)w.sticket.ptr;
     sp.cand = (uint64_t *)w.scand.ptr;
     return FLASHTOPK_OK;
 }
@@ -627,8 +637,10 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
         sa.scratch_stride = stride;
         sa.ntiles = (int)((rcap << ps) / kTileQ);
         sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves);
-        const int rchunks = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
-        launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * rchunks)), stream, sa);
+        // the work items loop over two workgroups per compute unit: a
+        // batch with nothing flagged costs one short launch
+        const int64_t items = (int64_t)sa.ntiles * std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
+        launch_score_dt(p.dtype, kModeDenseLoop, dim3((unsigned)std::min<int64_t>(items, 2 * num_cu())), stream, sa);
         // Exact top k of each batch row's window scores: the row top-k
         // kernels in mapped-row mode (outputs to the flagged row, indices
         // offset by its window start; entries past the list exit).
@@ -718,7 +730,7 @@ int fill_counts(Workspace &w)
     hipError_t e = hipMemcpy(len.data(), w.wlen.ptr, sizeof(int32_t) * (size_t)T, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_status(e);
     info.rows_empty = info.rows_take_all = info.rows_sampled = info.rows_underflow = info.rows_overflow = 0;
-    info.rows_recovered = info.max_candidates = info.window_keys = info.pruned_keys = 0;
+    info.rows_recovered = info.max_candidates = info.window_keys = info.pruned_keys = info.candidates = 0;
     if (w.last_kind == kCallDense) {
         for (int64_t t = 0; t < T; ++t) {
             info.window_keys += len[t];
@@ -749,6 +761,7 @@ int fill_counts(Workspace &w)
         } else {
             ++info.rows_sampled;
             info.max_candidates = std::max<int64_t>(info.max_candidates, c);
+            info.candidates += c;
         }
     }
     info.pruned_keys = (int64_t)stats[kStPruned];
@@ -1048,8 +1061,7 @@ void flashtopk_release(void)
             (void)hipStreamSynchronize(w->stream);
             DevBuf *bufs[] = {&w->tau,   &w->cnt,   &w->rowlist, &w->stats,  &w->wlen, &w->cand,
                               &w->samp,  &w->scratch, &w->qbar,  &w->qscale, &w->sigh, &w->kb,
-                              &w->kmeta, &w->vplan, &w->q1,      &w->scnt,   &w->sover, &w->sticket,
-                              &w->scand, &w->pkv,   &w->psig,    &w->vflag};
+                              &w->kmeta, &w->vplan, &w->q1,      &w->scnt,   &w->sover, &w->scand, &w->pkv,   &w->psig,    &w->vflag};
             for (DevBuf *b : bufs)
                 if (b->ptr) (void)hipFree(b->ptr);
             if (w->host_flag) (void)hipHostFree(w->host_flag);

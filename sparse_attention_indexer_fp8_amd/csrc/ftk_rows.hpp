@@ -557,13 +557,27 @@ __global__ __launch_bounds__(64 * kRowsTauWaves) void k_rows_tau(RowsArgs a)
 // k_rows_tau and parked in the first 4 bytes of the row's output indices
 // (the outputs are written last); otherwise the workgroup reads the sample itself, with
 // its first group of the row already in flight.
-template <typename T, typename SH, bool PRE_TAU>
-__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows(RowsArgs a)
+// Rows present in the call: all of them, or for rows mapped through the
+// flagged-row list, those below its device-side length.
+__device__ __forceinline__ int64_t rows_present(const RowsArgs &a)
+{
+    if (a.ks && a.rowmap) return min(a.rows, max((int64_t)*a.nrows - a.row_base, (int64_t)0));
+    return a.rows;
+}
+
+// One workgroup per row; with LOOP the workgroups loop over the rows
+// (grid-stride), so a batch of flagged rows whose count only the device
+// knows costs one launch of at most the resident workgroups (the one-row
+// form keeps the register allocation of the plain body).
+template <typename T, typename SH, bool PRE_TAU, bool LOOP = false>
+__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(LOOP ? 4 : 8))) void k_topk_rows(RowsArgs a)
 {
     constexpr int NT = SH::nt, U = kRowsUnroll;
     __shared__ RowsLds<SH> L;
     const int tid = threadIdx.x;
-    const int64_t r = blockIdx.x;
+    const int64_t nrow = LOOP ? rows_present(a) : a.rows;
+    for (int64_t r = blockIdx.x; r < nrow; r += gridDim.x) {
+    auto body = [&]() {
     const RowPlace pl = row_place(a, r);
     if (!pl.present) return;  // block-uniform
     const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
@@ -600,34 +614,40 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
         RowStream<T> el{row, n};
         select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags, pl.base);
     }
+    };  // body
+    body();
+    if (!LOOP) break;
+    __syncthreads();  // the next row reuses the LDS
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Rows split over several workgroups (few rows: each row's latency-bound
-// stream is shared out).  Workgroup (row r, part p) computes the row's
-// threshold from the whole row's sample (every part gets the same value),
-// gathers the entries of its slice that reach it and appends them to the
-// row's candidate list in global memory; the row's last workgroup to finish
-// (a self-resetting ticket) selects from the list, or, when the parts
-// together kept fewer than k or more than the capacity, redoes the row
-// alone by the digit histogram.  Per-row state lives in a workspace that
-// reads zero between calls.
+// stream is shared out), in two launches.  k_topk_rows_part: workgroup (row
+// r, part p) computes the row's threshold from the whole row's sample (every
+// part gets the same value), gathers the entries of its slice that reach it
+// and appends them to the row's candidate list in global memory.
+// k_topk_rows_merge: one workgroup per row selects from the list, or, when
+// the parts together kept fewer than k or more than the capacity, redoes the
+// row alone by the digit histogram; it then clears the row's state, so the
+// state reads zero between calls.  The launch boundary orders the parts'
+// writes before the merge's reads (no fence inside either kernel: a
+// device-scope fence writes back and invalidates the L2, which is slow when
+// hundreds of workgroups do it).
 struct RowsSplit {
     uint32_t *cnt;     // [rows] candidates appended
     uint32_t *over;    // [rows] a part held more than it could keep
-    uint32_t *ticket;  // [rows] parts finished
     uint64_t *cand;    // [rows, cap] the row's candidates
     int parts;         // workgroups per row
 };
 
 template <typename T, typename SH>
-__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows_split(RowsArgs a,
-                                                                                                   RowsSplit sp)
+__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows_part(RowsArgs a,
+                                                                                                  RowsSplit sp)
 {
     constexpr int NT = SH::nt, U = kRowsUnroll, V = 16 / sizeof(T), CAP = SH::cap;
     __shared__ RowsLds<SH> L;
     __shared__ uint32_t s_base;
-    __shared__ int s_last;
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x / sp.parts;
     const int part = (int)(blockIdx.x - r * sp.parts);
@@ -636,17 +656,7 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
     const int64_t n = pl.n;
     const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
-    void *oi = out_row(a.out_idx, pl.out, a.topk, a.out_flags);
-    float *ov = a.out_val ? a.out_val + pl.out * a.topk : nullptr;
-    if (k == 0) {
-        if (part == 0)
-            for (int j = tid; j < a.topk; j += NT) {
-                if (a.out_flags & kOutInt64) ((int64_t *)oi)[j] = -1;
-                else ((int32_t *)oi)[j] = -1;
-                if (ov) ov[j] = -__builtin_inff();
-            }
-        return;  // every part of the row returns here
-    }
+    if (k == 0) return;
     // This part's slice: whole 16-byte chunks.
     const int64_t per = ((n + sp.parts - 1) / sp.parts + V - 1) / V * V;
     const int64_t s0 = min((int64_t)part * per, n), s1 = min(s0 + per, n);
@@ -673,33 +683,49 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     if (m <= (uint32_t)CAP)
         for (uint32_t i = tid; i < m; i += NT)
             if (base + i < (uint32_t)CAP) sp.cand[r * CAP + base + i] = L.cand[i];
-    // The row's last part to finish selects.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(sp.ticket + r, 1u) == (uint32_t)(sp.parts - 1);
-    __syncthreads();
-    if (!s_last) return;  // block-uniform
-    __threadfence();
-    const uint32_t tot = __hip_atomic_load(sp.cnt + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t over = __hip_atomic_load(sp.over + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+}
+
+template <typename T, typename SH>
+__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows_merge(RowsArgs a,
+                                                                                                   RowsSplit sp)
+{
+    constexpr int NT = SH::nt, CAP = SH::cap;
+    __shared__ RowsLds<SH> L;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const RowPlace pl = row_place(a, r);
+    if (!pl.present) return;  // block-uniform
+    const T *row = reinterpret_cast<const T *>(a.x) + r * a.stride;
+    const int64_t n = pl.n;
+    const uint32_t k = (uint32_t)min((int64_t)a.topk, n);
+    void *oi = out_row(a.out_idx, pl.out, a.topk, a.out_flags);
+    float *ov = a.out_val ? a.out_val + pl.out * a.topk : nullptr;
+    const uint32_t tot = sp.cnt[r], over = sp.over[r];
+    __syncthreads();  // every thread has read the state before it is cleared
     if (tid == 0) {
         sp.cnt[r] = 0u;
         sp.over[r] = 0u;
-        sp.ticket[r] = 0u;
+    }
+    if (k == 0) {
+        for (int j = tid; j < a.topk; j += NT) {
+            if (a.out_flags & kOutInt64) ((int64_t *)oi)[j] = -1;
+            else ((int32_t *)oi)[j] = -1;
+            if (ov) ov[j] = -__builtin_inff();
+        }
+        return;
     }
     if (!over && tot >= k && tot <= (uint32_t)CAP) {
         RowElems<SH::regs> el;
         el.load(sp.cand + r * CAP, tot);
         select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, tot, k, a.topk, oi, ov, a.out_flags, pl.base);
     } else {
-        bool nan2 = false;
-        const uint32_t m2 = rows_digit_gather<T, SH>(L, row, n, k, nan2);
-        if (m2 <= (uint32_t)CAP) {
+        bool nan = false;  // the parts have reported NaN already
+        const uint32_t m = rows_digit_gather<T, SH>(L, row, n, k, nan);
+        if (m <= (uint32_t)CAP) {
             RowElems<SH::regs> el;
-            el.load(L.cand, m2);
+            el.load(L.cand, m);
             __syncthreads();
-            select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m2, k, a.topk, oi, ov, a.out_flags, pl.base);
+            select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, m, k, a.topk, oi, ov, a.out_flags, pl.base);
         } else {
             RowStream<T> el{row, n};
             select_core<NT, SH::nbkt, SH::maxk>(L.sel, el, n, k, a.topk, oi, ov, a.out_flags, pl.base);

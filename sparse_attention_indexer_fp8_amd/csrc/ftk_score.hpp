@@ -489,10 +489,15 @@ __device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t 
         }
 }
 
-// PAIR: 64-head rows, two tile columns each (see ScoreArgs::pair).
-template <int DT, int MODE, bool PAIR>
+// PAIR: 64-head rows, two tile columns each (see ScoreArgs::pair).  LOOP
+// (dense mode only): each workgroup loops over work items, for a grid
+// smaller than the work (the recovery batches, whose row count only the
+// device knows); without it a workgroup scores one item, which keeps the
+// register allocation of the one-item body.
+template <int DT, int MODE, bool PAIR, bool LOOP = false>
 __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(ScoreArgs a)
 {
+    static_assert(!LOOP || MODE == kModeDense, "only dense mode loops");
     using Cfg = ScoreCfg<DT, MODE>;
     constexpr int kWaves = Cfg::waves;
     constexpr int RB = RowBytes<DT>::value;
@@ -527,10 +532,22 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
     uint8_t *s_q = smem + WB;
     uint64_t *s_ring = reinterpret_cast<uint64_t *>(smem + WB + QB);
 
+    // Dense mode loops over its work items (a grid smaller than the work, or
+    // a batch whose row count is only known on the device): the tiles that
+    // hold present entries times the key chunks.
+    int ntiles = a.ntiles, nitems = 1;
+    if constexpr (LOOP) {
+        int64_t ent = a.rowlist ? (int64_t)*a.nrows - a.row_base : (int64_t)a.nrows_direct - a.row_base;
+        ent = min(max(ent, (int64_t)0), (int64_t)a.row_limit);
+        ntiles = (int)(((ent << (PAIR ? 1 : 0)) + kTileQ - 1) / kTileQ);
+        nitems = ntiles * max(1, (a.num_kv + a.chunk - 1) / a.chunk);
+    }
+    for (int item = blockIdx.x; !LOOP || item < nitems; item += gridDim.x) {
+    auto body = [&]() {
     // Work item: tile (fast index) x chunk; in sample mode the "chunk" is the
     // part of the tile's sample lattice (sample_split parts).
-    const int chunk = blockIdx.x / a.ntiles;
-    const int tile = blockIdx.x - chunk * a.ntiles;
+    const int chunk = item / ntiles;
+    const int tile = item - chunk * ntiles;
     // Sample mode: every workgroup, with or without work, ends here; with
     // one workgroup per tile it sets the tile's thresholds (the q tile's LDS
     // is free by then and holds the histograms).
@@ -1082,6 +1099,11 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
         if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, to, a.cnt, a.cand, a.cap);
     }
     finish();
+    };  // body
+    body();
+    if (!LOOP) break;
+    __syncthreads();  // the next item reuses the LDS
+    }
 }
 
 }  // namespace ftk

@@ -2,14 +2,16 @@
 // "Highlights": the threshold comes from a strided sample of the row's own
 // window).
 //
-// The threshold needs no exact rank -- only the candidate count it admits
-// matters, and triage catches any row it misjudges -- so the sample is
-// bucketed linearly in score (kTauBuckets buckets between the sample's
-// minimum and maximum, highest first) and the threshold is one bucket below
-// the lower edge of the bucket that holds the r-th largest sample: at least r
-// samples reach it, whatever the rounding of the bucket arithmetic.  With
-// r = ceil(2 * topk * n / L) for n samples of an L-key window, about 2 topk
-// keys of the window are expected to reach it.
+// The threshold is the r-th largest sample score, r = ceil(2 * topk * n / L)
+// for n samples of an L-key window, so about 2 topk keys of the window are
+// expected to reach it.  The sample is bucketed linearly in score
+// (kTauBuckets buckets between its minimum and maximum, highest first); the
+// bucket that holds the r-th largest sample is found from the histogram, and
+// when it holds at most 64 samples (the usual case) the r-th largest is
+// picked from them exactly.  A denser bucket gives the threshold one bucket
+// below its lower edge instead: at least r samples reach it, whatever the
+// rounding of the bucket arithmetic.  No threshold changes results -- triage
+// catches any row it misjudges -- only the candidate count.
 #pragma once
 
 #include "ftk_common.hpp"
@@ -17,6 +19,52 @@
 namespace ftk {
 
 constexpr int kTauBuckets = 2048;
+constexpr int kTauExactMax = 64;  // largest bucket searched for the exact r-th sample
+
+// The r-th largest of the wave's samples, given the bucket b that holds it:
+// v holds the lane's PER samples (NaN: absent), `above` the samples of the
+// buckets before b and cb those of b (cb <= kTauExactMax), with the same
+// bucket arithmetic (vmax, scale) as the histogram.  buf: kTauExactMax words
+// of LDS private to the wave.  Every lane returns the value.
+template <int PER>
+__device__ __forceinline__ float tau_exact_in_bucket(const float (&v)[PER], float vmax, float scale, int b,
+                                                     uint32_t above, uint32_t cb, uint32_t r, uint32_t *buf,
+                                                     int lane)
+{
+    auto in_b = [&](float x) {
+        if (!(x == x)) return false;
+        const float y = (vmax - x) * scale;
+        const int bb = y < (float)(kTauBuckets - 1) ? (int)(uint32_t)y : kTauBuckets - 1;
+        return bb == b;
+    };
+    // the bucket's samples, compacted into buf
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) mine += in_b(v[q]) ? 1u : 0u;
+    uint32_t pos = wave_incl_add(mine) - mine;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        if (in_b(v[q])) buf[pos++] = __float_as_uint(v[q]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // lane j < cb: the rank of its sample among the bucket's (larger values
+    // first, equal ones by position); the one of rank r - above - 1 wins
+    const uint32_t want = r - above - 1;
+    float e = 0.0f;
+    uint32_t rank = 0xFFFFFFFFu;
+    if ((uint32_t)lane < cb) {
+        e = __uint_as_float(buf[lane]);
+        rank = 0;
+        for (uint32_t i = 0; i < cb; ++i) {
+            const float f = __uint_as_float(buf[i]);
+            rank += (f > e || (f == e && i < (uint32_t)lane)) ? 1u : 0u;
+        }
+    }
+    const uint64_t hit = __ballot(rank == want);
+    const float t = __shfl(e, hit ? __builtin_ctzll(hit) : 0);
+    __builtin_amdgcn_wave_barrier();  // every lane has read buf before the caller reuses the LDS
+    return t;
+}
 
 // Rank of the threshold in a sample of n keys of an L-key window.
 __device__ __forceinline__ uint32_t tau_rank(int topk, int64_t n, int64_t len, float rank_scale)
@@ -91,13 +139,25 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
     }
     uint32_t base = x - run;
     int b = -1;
+    uint32_t above = 0, cb = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-        if (base < r && r <= base + c[q]) b = lane * PER + q;
+        if (base < r && r <= base + c[q]) {
+            b = lane * PER + q;
+            above = base;
+            cb = c[q];
+        }
         base += c[q];
     }
     const uint64_t hit = __ballot(b >= 0);
-    b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
+    const int src = hit ? __builtin_ctzll(hit) : 0;
+    b = __shfl(b, src);
+    above = __shfl(above, src);
+    cb = __shfl(cb, src);
+    if (n <= CHUNK && cb <= (uint32_t)kTauExactMax) {
+        __builtin_amdgcn_wave_barrier();  // every lane has read its counts before hist is reused
+        return tau_exact_in_bucket<PERL>(v, vmax, scale, b, above, cb, r, hist, lane);
+    }
     return vmax - (float)(b + 2) / scale;
 }
 
@@ -168,15 +228,25 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
         }
         uint32_t base = wave_incl_add(run) - run;
         int b = -1;
+        uint32_t above = 0, cb = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            if (base < r[k] && r[k] <= base + c[q]) b = lane * PER + q;
+            if (base < r[k] && r[k] <= base + c[q]) {
+                b = lane * PER + q;
+                above = base;
+                cb = c[q];
+            }
             base += c[q];
         }
         const uint64_t hit = __ballot(b >= 0);
-        b = __shfl(b, hit ? __builtin_ctzll(hit) : 0);
-        tv[k] = vmax[k] - (float)(b + 2) / scale;
-        __builtin_amdgcn_wave_barrier();  // every lane has read the counts before the next row clears them
+        const int src = hit ? __builtin_ctzll(hit) : 0;
+        b = __shfl(b, src);
+        above = __shfl(above, src);
+        cb = __shfl(cb, src);
+        __builtin_amdgcn_wave_barrier();  // every lane has read the counts before hist is reused
+        if (cb <= (uint32_t)kTauExactMax) tv[k] = tau_exact_in_bucket<PER>(v[k], vmax[k], scale, b, above, cb, r[k], hist, lane);
+        else tv[k] = vmax[k] - (float)(b + 2) / scale;
+        __builtin_amdgcn_wave_barrier();
     }
 }
 

@@ -65,7 +65,7 @@ def test_header_constants_match_binding():
 def test_options_and_info_layout_match_header():
     # sizes of the C structs as laid out by the platform ABI
     assert ctypes.sizeof(ftk.Options) == 40
-    assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4 + 6 * 4 + 4 + 4  # invalid, padding
+    assert ctypes.sizeof(ftk.Info) == 4 + 4 + 8 * 10 + 4 + 4 + 6 * 4 + 4 + 4 + 8  # invalid, padding, candidates
 
 
 def test_struct_layout_matches_the_c_compiler(tmp_path):
