@@ -75,6 +75,8 @@ extern "C" {
 #define FLASHTOPK_ERR_UNSUPPORTED 2      /* dtype other than FP8 E4M3 / BF16 */
 #define FLASHTOPK_ERR_OUT_OF_MEMORY 3    /* workspace allocation failed */
 #define FLASHTOPK_ERR_HIP 4              /* a HIP runtime or launch error */
+#define FLASHTOPK_ERR_WORKSPACE_LIMIT 5  /* flashtopk_select_noalloc: the call needs more
+                                            scratch than its fixed array holds */
 
 /* Execution paths.  Every path returns bit-identical results; they differ only
  * in speed.  Used by tests and benchmarks to force a path.
@@ -279,6 +281,28 @@ int flashtopk_get_last_info(void *stream, flashtopk_info *out);
  * Like flashtopk_get_last_info it must be read before the next call on the
  * stream.  rows may be NULL when max_rows is 0. */
 int flashtopk_get_last_recovered(void *stream, int32_t *rows, int64_t max_rows, int64_t *count);
+
+/* flashtopk_select for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results bit-identical to
+ * flashtopk_select's, and no hipMalloc, hipFree or other allocating call.
+ * Its scratch is one fixed array of FLASHTOPK_NOALLOC_SCRATCH_BYTES in the
+ * library's device code object: every GPU the library is loaded on holds
+ * its own copy until the process ends.  A call whose workspace does not fit
+ * (roughly: num_q * (min(16384, 4 * topk) * 8 + 8192) bytes for calls above
+ * 8M (row, key) pairs, num_q * num_kv * 4 bytes of window scores below;
+ * dense rescoring takes at most 32 MiB of it) returns
+ * FLASHTOPK_ERR_WORKSPACE_LIMIT before any work is enqueued.  Default
+ * options only.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (from several host threads, or on several streams whose
+ * work runs concurrently) race on it and must be serialised by the caller;
+ * successive calls on one stream are safe.  It keeps no record for
+ * flashtopk_get_last_info. */
+#define FLASHTOPK_NOALLOC_SCRATCH_BYTES (128ll << 20)
+int flashtopk_select_noalloc(const void *q, const void *kv, const float *kv_scales,
+                             const float *weights, const int32_t *ks, const int32_t *ke,
+                             int64_t num_q, int64_t num_kv, int dtype, int topk,
+                             void *out_idx, float *out_val, void *stream);
 
 /* Frees every cached workspace.  No call may be in flight. */
 void flashtopk_release(void);

@@ -36,7 +36,9 @@ FLASHTOPK_INVALID_PAGE = 32
 PATH_AUTO, PATH_SCAN, PATH_PRUNE, PATH_RECOVER, PATH_FUSED = 0, 1, 2, 3, 4
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "out of device memory",
-          4: "HIP runtime error"}
+          4: "HIP runtime error", 5: "call too large for the fixed scratch array"}
+FLASHTOPK_ERR_WORKSPACE_LIMIT = 5
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class FlashTopKError(RuntimeError):
@@ -90,9 +92,9 @@ class Info(ctypes.Structure):
 
 
 # Every symbol include/flashtopk.h declares.
-EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_select_paged", "flashtopk_topk_rows",
-           "flashtopk_reserve", "flashtopk_get_last_info", "flashtopk_get_last_recovered", "flashtopk_release",
-           "flashtopk_status_string", "flashtopk_version")
+EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_select_paged", "flashtopk_select_noalloc",
+           "flashtopk_topk_rows", "flashtopk_reserve", "flashtopk_get_last_info", "flashtopk_get_last_recovered",
+           "flashtopk_release", "flashtopk_status_string", "flashtopk_version")
 
 _lib = None
 
@@ -111,6 +113,8 @@ def load_library():
     lib.flashtopk_select.restype = I
     lib.flashtopk_select_ex.argtypes = sel + [ctypes.POINTER(Options)]
     lib.flashtopk_select_ex.restype = I
+    lib.flashtopk_select_noalloc.argtypes = sel
+    lib.flashtopk_select_noalloc.restype = I
     lib.flashtopk_select_paged.argtypes = [P, P, P, P, I, I64, P, P, P, I64, I64, I, I, P, P, P,
                                            ctypes.POINTER(Options)]
     lib.flashtopk_select_paged.restype = I
@@ -249,6 +253,33 @@ def flashtopk_select_paged(q, kv_pages, scale_pages, block_table, num_kv, weight
 
 def flashtopk_select(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=None, stream=None) -> None:
     flashtopk_select_ex(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val, stream, None)
+
+
+def flashtopk_select_noalloc(q, kv, kv_scales, weights, ks, ke, topk, out_idx, out_val=None, stream=None) -> None:
+    """flashtopk_select with no device allocation: its scratch is the library's
+    fixed array (NOALLOC_SCRATCH_BYTES per GPU); a call that does not fit
+    raises FlashTopKError with status FLASHTOPK_ERR_WORKSPACE_LIMIT."""
+    torch = _torch()
+    lib = load_library()
+    T, S = q.shape[0], kv.shape[0]
+    code = _dtype_code(q)
+    if _dtype_code(kv) != code:
+        raise TypeError("q and kv must have the same dtype")
+    if tuple(q.shape[1:]) != (HEADS, DIM) or tuple(kv.shape[1:]) != (DIM,):
+        raise ValueError("q must be [T, 32, 128] and kv [S, 128]")
+    _check_dev("q", q)
+    _check_dev("kv", kv)
+    _check_dev("kv_scales", kv_scales, (torch.float32,), (S,))
+    _check_dev("weights", weights, (torch.float32,), (T, HEADS))
+    _check_dev("ks", ks, (torch.int32,), (T,))
+    _check_dev("ke", ke, (torch.int32,), (T,))
+    _check_dev("out_idx", out_idx, (torch.int32,), (T, topk))
+    _check_dev("out_val", out_val, (torch.float32,), (T, topk))
+    st = lib.flashtopk_select_noalloc(_ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(weights), _ptr(ks), _ptr(ke),
+                                      T, S, code, int(topk), _ptr(out_idx), _ptr(out_val),
+                                      ctypes.c_void_p(_stream_handle(stream)))
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_select_noalloc")
 
 
 def flashtopk_topk_rows(x, topk, out_idx, out_val=None, ends=None, nan_flag=None, stream=None,

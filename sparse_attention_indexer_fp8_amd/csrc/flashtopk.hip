@@ -67,10 +67,12 @@ constexpr int kMinDenseChunk = 512;
 constexpr int kMaxSplit = 64;
 constexpr int64_t kMinSplitEntries = 4096;
 
-// Grow-only device buffer.
+// Grow-only device buffer.  zero: it must read zero when handed to a call
+// (recorded by the sizing pass of the allocation-free entry point).
 struct DevBuf {
     void *ptr = nullptr;
     size_t bytes = 0;
+    bool zero = false;
 };
 
 // Record of the last call on a stream; its counts are computed from the
@@ -91,10 +93,30 @@ struct Workspace {
     int last_kind = kCallNone;
     flashtopk_info last{};                       // status, sizes, timings of the last call
     int last_topk = 0;
+    // The allocation-free entry point's workspace: first a sizing pass
+    // (ensure records the sizes a call needs), then the buffers are carved
+    // from a fixed array and ensure only checks them.
+    bool sizing = false;
+    bool fixed = false;
 };
 
 std::mutex g_mu;
 std::vector<Workspace *> g_ws;
+
+// Scratch of the allocation-free entry point.  In host code `scratch` only
+// names the symbol: its device address comes from hipGetSymbolAddress, once
+// per device (each device holds its own copy).
+constexpr size_t kNoAllocBytes = (size_t)FLASHTOPK_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kNoAllocRecoverBudget = int64_t(32) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+struct NoAllocDevice {
+    std::mutex mu;       // held for the whole call: calls from several host threads take turns
+    uint8_t *base = nullptr;  // the device address of `scratch`
+    Workspace ws;        // buffers carved from it
+};
+NoAllocDevice g_na[kNoAllocMaxDevices];
 
 int hip_status(hipError_t e)
 {
@@ -107,7 +129,12 @@ int hip_status(hipError_t e)
 // no pending kernel still uses the old buffer.
 int ensure(Workspace &w, DevBuf &b, size_t bytes)
 {
+    if (w.sizing) {
+        b.bytes = std::max(b.bytes, bytes);
+        return FLASHTOPK_OK;
+    }
     if (b.bytes >= bytes && b.ptr) return FLASHTOPK_OK;
+    if (w.fixed) return FLASHTOPK_ERR_WORKSPACE_LIMIT;
     size_t want = std::max(bytes, b.bytes + b.bytes / 4);
     if (b.ptr) {
         hipError_t e = hipStreamSynchronize(w.stream);
@@ -129,7 +156,8 @@ int ensure(Workspace &w, DevBuf &b, size_t bytes)
 // ensure() for a buffer that must read zero when (re)allocated.
 int ensure_zeroed(Workspace &w, DevBuf &b, size_t bytes)
 {
-    if (b.bytes >= bytes && b.ptr) return FLASHTOPK_OK;
+    if (w.sizing) b.zero = true;
+    if (w.sizing || w.fixed || (b.bytes >= bytes && b.ptr)) return ensure(w, b, bytes);
     int st = ensure(w, b, bytes);
     if (st) return st;
     return hip_status(hipMemset(b.ptr, 0, b.bytes));
@@ -393,6 +421,17 @@ void begin_record(Workspace &w, const Plan &p, int kind)
     w.last_topk = p.topk;
 }
 
+// Workspace of a dense call.
+int prepare_dense(Workspace &w, const Plan &p, RowsSplit &sp)
+{
+    int st = FLASHTOPK_OK;
+    const int64_t rcap = batch_rows(p);
+    const int64_t brows = std::min(rcap, p.T);
+    if ((st = ensure(w, w.scratch, sizeof(float) * (size_t)rcap * scratch_stride(p.S)))) return st;
+    if ((st = ensure(w, w.wlen, sizeof(int32_t) * (size_t)p.T))) return st;
+    return ensure_split(w, brows, split_parts(brows, p.S), sp);
+}
+
 // Every row scored densely: window scores in scratch, then the row top-k.
 int run_dense(Workspace &w, const void *q, const void *kv, const float *kv_scales, const float *weights,
               const int32_t *ks, const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
@@ -402,11 +441,8 @@ int run_dense(Workspace &w, const void *q, const void *kv, const float *kv_scale
     const int ps = p.heads == 64 ? 1 : 0;
     const int64_t stride = scratch_stride(S);
     const int64_t rcap = batch_rows(p);
-    const int64_t brows = std::min(rcap, T);
-    if ((st = ensure(w, w.scratch, sizeof(float) * (size_t)rcap * stride))) return st;
-    if ((st = ensure(w, w.wlen, sizeof(int32_t) * (size_t)T))) return st;
     RowsSplit sp;
-    if ((st = ensure_split(w, brows, split_parts(brows, S), sp))) return st;
+    if ((st = prepare_dense(w, p, sp))) return st;
 
     mark(w, p, 0, stream);
     for (int64_t rb = 0; rb < T; rb += rcap) {
@@ -467,22 +503,25 @@ int run_dense(Workspace &w, const void *q, const void *kv, const float *kv_scale
     return FLASHTOPK_OK;
 }
 
-// The fused path: sampled thresholds, the filtering scan, selection, and
-// dense recovery of the rows the threshold misjudged.
-int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scales, const float *weights,
-              const int32_t *ks, const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+// Score-bound pruning: on the auto / fused path (each scan work item decides
+// from its tile's planner sample) and the forced prune path; not for 64
+// heads.
+bool bounds_on(const Plan &p) { return p.heads == 32 && p.S > 0 && p.path != FLASHTOPK_PATH_SCAN; }
+
+// Workspace of a fused call.
+int prepare_fused(Workspace &w, const Plan &p)
 {
     int st = FLASHTOPK_OK;
     const int64_t T = p.T, S = p.S;
+    const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
+    const int64_t TC = T << (p.heads == 64 ? 1 : 0);
+    const int ntiles = (int)((TC + kTileQ - 1) / kTileQ);
+    const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
     if ((st = ensure(w, w.tau, sizeof(float) * T))) return st;
     if ((st = ensure(w, w.cnt, sizeof(uint32_t) * T))) return st;
     if ((st = ensure(w, w.rowlist, sizeof(int32_t) * T))) return st;
     if ((st = ensure(w, w.wlen, sizeof(int32_t) * T))) return st;
     if ((st = ensure(w, w.stats, sizeof(unsigned long long) * kStCount))) return st;
-    const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
-    // 64 heads: row t's two 32-head halves are tile columns 2t and 2t + 1.
-    const int ps = p.heads == 64 ? 1 : 0;
-    const int64_t TC = T << ps;  // tile columns
     if (fp8) {
         if ((st = ensure(w, w.qbar, (size_t)TC * kQbarParts * kDim))) return st;
         if ((st = ensure(w, w.qscale, sizeof(float) * TC))) return st;
@@ -490,22 +529,33 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
     if ((st = ensure(w, w.sigh, sizeof(float) * (size_t)(S + 64)))) return st;
     if ((st = ensure(w, w.cand, sizeof(uint64_t) * (size_t)T * p.cap))) return st;
     if ((st = ensure(w, w.samp, sizeof(uint32_t) * (size_t)T * p.sample_target))) return st;
-
-    const int ntiles = (int)((TC + kTileQ - 1) / kTileQ);
-    // Score-bound pruning: on the auto path (each scan work item decides from
-    // its tile's planner sample) and the forced prune path; not for 64 heads.
-    const bool bounds = !ps && S > 0 && p.path != FLASHTOPK_PATH_SCAN;
-    const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
-    if (bounds) {
+    if (bounds_on(p)) {
         if ((st = ensure(w, w.kb, (size_t)nblocks * 2 * (fp8 ? 128 : 256)))) return st;
         if ((st = ensure(w, w.kmeta, sizeof(float2) * (size_t)nblocks))) return st;
         if ((st = ensure(w, w.vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
         if ((st = ensure(w, w.q1, sizeof(float) * (size_t)T))) return st;
     }
     // Recovery batches: rows of scratch that fit the budget.
+    return ensure(w, w.scratch, sizeof(float) * (size_t)batch_rows(p) * scratch_stride(S));
+}
+
+// The fused path: sampled thresholds, the filtering scan, selection, and
+// dense recovery of the rows the threshold misjudged.
+int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scales, const float *weights,
+              const int32_t *ks, const int32_t *ke, void *out_idx, float *out_val, hipStream_t stream, const Plan &p)
+{
+    int st = FLASHTOPK_OK;
+    const int64_t T = p.T, S = p.S;
+    if ((st = prepare_fused(w, p))) return st;
+    const bool fp8 = p.dtype == FLASHTOPK_FP8_E4M3;
+    // 64 heads: row t's two 32-head halves are tile columns 2t and 2t + 1.
+    const int ps = p.heads == 64 ? 1 : 0;
+    const int64_t TC = T << ps;  // tile columns
+    const int ntiles = (int)((TC + kTileQ - 1) / kTileQ);
+    const bool bounds = bounds_on(p);
+    const int nblocks = (int)((S + kBlockKeys - 1) / kBlockKeys);
     const int64_t stride = scratch_stride(S);
     const int64_t rcap = batch_rows(p);
-    if ((st = ensure(w, w.scratch, sizeof(float) * (size_t)rcap * stride))) return st;
 
     const int chunk = chunk_keys(ntiles, S, fp8 ? ScoreCfg<kFP8, kModeFilter>::waves : ScoreCfg<kBF16, kModeFilter>::waves);
     const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
@@ -694,6 +744,37 @@ int run(Workspace &w, const void *q, const void *kv, const float *kv_scales, con
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Zero fill of n words (clears what the allocation-free entry point hands to
+// a call as zero; a kernel, so the call can be captured in a graph).
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Lays the buffers a call needs (the sizing pass's sizes) out in the fixed
+// array and clears the ones that must read zero.  Returns
+// FLASHTOPK_ERR_WORKSPACE_LIMIT when they do not fit.
+int carve(Workspace &w, uint8_t *base, hipStream_t s)
+{
+    DevBuf *bufs[] = {&w.tau,   &w.cnt,     &w.rowlist, &w.stats, &w.wlen, &w.cand,  &w.samp,
+                      &w.scratch, &w.qbar,  &w.qscale,  &w.sigh,  &w.kb,   &w.kmeta, &w.vplan,
+                      &w.q1,    &w.scnt,    &w.sover,   &w.scand};
+    size_t off = 0;
+    for (DevBuf *b : bufs) {
+        if (!b->bytes) continue;
+        const size_t len = (b->bytes + 255) / 256 * 256;
+        if (len > kNoAllocBytes - off) return FLASHTOPK_ERR_WORKSPACE_LIMIT;
+        b->ptr = base + off;
+        off += len;
+    }
+    for (DevBuf *b : bufs)
+        if (b->bytes && b->zero) {
+            const int64_t n = (int64_t)(b->bytes + 3) / 4;
+            k_fill_zero<<<(unsigned)std::min<int64_t>(1024, (n + 255) / 256), 256, 0, s>>>((uint32_t *)b->ptr, n);
+        }
+    return hip_status(hipGetLastError());
+}
 
 // options.validate: runs k_validate on the call's inputs, waits for its flags
 // (p.invalid) and, when it found any, fails the call before a scoring kernel
@@ -896,6 +977,65 @@ int flashtopk_select_paged(const void *q, const void *kv_pages, const float *sca
     return run_fused(*w, q, w->pkv.ptr, sig, weights, ks, ke, out_idx, out_val, s, p);
 }
 
+int flashtopk_select_noalloc(const void *q, const void *kv, const float *kv_scales, const float *weights,
+                             const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype,
+                             int topk, void *out_idx, float *out_val, void *stream)
+{
+    if (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16) return FLASHTOPK_ERR_UNSUPPORTED;
+    if (num_q < 0 || num_kv < 0 || num_kv >= (int64_t(1) << 31) || num_q >= (int64_t(1) << 30))
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (topk < 1 || topk > FLASHTOPK_MAX_TOPK) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (num_q == 0) return FLASHTOPK_OK;
+    if (!q || !weights || !ks || !ke || !out_idx || (!kv && num_kv > 0)) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || (kv && !aligned16(kv))) return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    Plan p{};
+    p.T = num_q;
+    p.S = num_kv;
+    p.dtype = dtype;
+    p.topk = topk;
+    int st = resolve(p, nullptr);
+    if (st) return st;
+    p.recover_budget = kNoAllocRecoverBudget;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return FLASHTOPK_ERR_HIP;
+    NoAllocDevice &na = g_na[dev];
+    std::lock_guard<std::mutex> lk(na.mu);
+    if (!na.base) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return FLASHTOPK_ERR_HIP;
+        }
+        na.base = (uint8_t *)ptr;
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    Workspace &w = na.ws;
+    w.device = dev;
+    w.stream = s;
+    DevBuf *bufs[] = {&w.tau,   &w.cnt,     &w.rowlist, &w.stats, &w.wlen, &w.cand,  &w.samp,
+                      &w.scratch, &w.qbar,  &w.qscale,  &w.sigh,  &w.kb,   &w.kmeta, &w.vplan,
+                      &w.q1,    &w.scnt,    &w.sover,   &w.scand, &w.pkv,  &w.psig,  &w.vflag};
+    for (DevBuf *b : bufs) *b = DevBuf{};
+    // sizing pass, then the buffers in the fixed array, then the call
+    const bool dense = dense_path(p);
+    w.fixed = false;
+    w.sizing = true;
+    RowsSplit sp;
+    st = dense ? prepare_dense(w, p, sp) : prepare_fused(w, p);
+    w.sizing = false;
+    if (st) return st;
+    w.fixed = true;
+    st = carve(w, na.base, s);
+    if (st == FLASHTOPK_OK)
+        st = dense ? run_dense(w, q, kv, kv_scales, weights, ks, ke, out_idx, out_val, s, p)
+                   : run_fused(w, q, kv, kv_scales, weights, ks, ke, out_idx, out_val, s, p);
+    w.fixed = false;
+    return st;
+}
+
 int flashtopk_select(const void *q, const void *kv, const float *kv_scales, const float *weights,
                      const int32_t *ks, const int32_t *ke, int64_t num_q, int64_t num_kv, int dtype, int topk,
                      void *out_idx, float *out_val, void *stream)
@@ -1082,6 +1222,7 @@ const char *flashtopk_status_string(int status)
     case FLASHTOPK_ERR_UNSUPPORTED: return "unsupported dtype";
     case FLASHTOPK_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FLASHTOPK_ERR_HIP: return "HIP runtime error";
+    case FLASHTOPK_ERR_WORKSPACE_LIMIT: return "call too large for the fixed scratch array";
     default: return "unknown status";
     }
 }
