@@ -293,17 +293,17 @@ constexpr int kModeDenseLoop = 3;
 template <int DT>
 void launch_score(int mode, dim3 grid, hipStream_t st, const ScoreArgs &a)
 {
-    constexpr int WD = 64 * ScoreCfg<DT, kModeDense>::waves;
+    constexpr int WD = 64 * ScoreCfg<DT, kModeDense>::waves, WL = 64 * ScoreCfg<DT, kModeDense, true>::waves;
     if (a.pair) {
         if (mode == kModeFilter) k_score<DT, kModeFilter, true><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
         else if (mode == kModeSample) k_score<DT, kModeSample, true><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
         else if (mode == kModeDense) k_score<DT, kModeDense, true><<<grid, WD, 0, st>>>(a);
-        else k_score<DT, kModeDense, true, true><<<grid, WD, 0, st>>>(a);
+        else k_score<DT, kModeDense, true, true><<<grid, WL, 0, st>>>(a);
     } else {
         if (mode == kModeFilter) k_score<DT, kModeFilter, false><<<grid, 64 * ScoreCfg<DT, kModeFilter>::waves, 0, st>>>(a);
         else if (mode == kModeSample) k_score<DT, kModeSample, false><<<grid, 64 * ScoreCfg<DT, kModeSample>::waves, 0, st>>>(a);
         else if (mode == kModeDense) k_score<DT, kModeDense, false><<<grid, WD, 0, st>>>(a);
-        else k_score<DT, kModeDense, false, true><<<grid, WD, 0, st>>>(a);
+        else k_score<DT, kModeDense, false, true><<<grid, WL, 0, st>>>(a);
     }
 }
 
@@ -687,10 +687,10 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
         sa.scratch_stride = stride;
         sa.ntiles = (int)((rcap << ps) / kTileQ);
         sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves);
-        // the work items loop over two workgroups per compute unit: a
-        // batch with nothing flagged costs one short launch
+        // the work items loop over one workgroup per compute unit: a batch
+        // with nothing flagged costs one short launch
         const int64_t items = (int64_t)sa.ntiles * std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
-        launch_score_dt(p.dtype, kModeDenseLoop, dim3((unsigned)std::min<int64_t>(items, 2 * num_cu())), stream, sa);
+        launch_score_dt(p.dtype, kModeDenseLoop, dim3((unsigned)std::min<int64_t>(items, num_cu())), stream, sa);
         // Exact top k of each batch row's window scores: the row top-k
         // kernels in mapped-row mode (outputs to the flagged row, indices
         // offset by its window start; entries past the list exit).
@@ -744,6 +744,21 @@ int run(Workspace &w, const void *q, const void *kv, const float *kv_scales, con
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Run once by flashtopk_reserve on its stream: the first launch of a kernel
+// of this library loads its code object, and a kernel that keeps values in
+// private (scratch) memory makes the runtime size the stream's private-memory
+// area for it.  This kernel holds kWarmWords words per lane there, more than
+// any kernel of the library spills, so both happen here and not in a later
+// call.
+constexpr int kWarmWords = 96;
+__global__ __launch_bounds__(64) void k_warm(float *out, int n)
+{
+    float buf[kWarmWords];
+    for (int i = 0; i < kWarmWords; ++i) buf[(i * 7 + (int)threadIdx.x) % kWarmWords] = (float)(i + n);
+    const float v = buf[(n + (int)threadIdx.x) % kWarmWords];
+    if (out && n > 0) out[threadIdx.x] = v;
+}
 
 // Zero fill of n words (clears what the allocation-free entry point hands to
 // a call as zero; a kernel, so the call can be captured in a graph).
@@ -1129,11 +1144,16 @@ int flashtopk_reserve(int64_t max_q, int64_t max_kv, int max_topk, int dtype, vo
     if ((st = ensure(*w, w->kmeta, sizeof(float2) * (size_t)std::max<int64_t>(nblocks, 1)))) return st;
     if ((st = ensure(*w, w->vplan, sizeof(float) * (size_t)ntiles * kPlanGroups * 256))) return st;
     if ((st = ensure(*w, w->q1, sizeof(float) * (size_t)T))) return st;
-    // the dense path's split-row state: few rows, so at most about 2 CUs' worth
+    // split-row state (dense path and row top-k of at most one row per compute
+    // unit): its size depends on the rows only
     RowsSplit sp;
-    const int64_t brows = std::min(rcap, T);
-    if ((st = ensure_split(*w, brows, split_parts(brows, S), sp))) return st;
-    return FLASHTOPK_OK;
+    const int64_t srows = std::min<int64_t>(T, num_cu());
+    if ((st = ensure_split(*w, srows, split_parts(1, S), sp))) return st;
+    // the code object and the private-memory area, see k_warm
+    k_warm<<<1, 64, 0, (hipStream_t)stream>>>(nullptr, 0);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    return hip_status(e);
 }
 
 int flashtopk_get_last_info(void *stream, flashtopk_info *out)

@@ -67,11 +67,14 @@ template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? k
 // so the rings start on distinct LDS banks.
 //   Sample and dense modes (no candidate rings, more bookkeeping registers)
 //   use the 8-wave prefetching shape for both dtypes.
-template <int DT, int MODE> struct ScoreCfg {
+//   The looping dense form (recovery, LOOP) runs 4 waves, so each may hold
+//   512 registers (the loop's state pushed the 8-wave form past 256 into
+//   scratch memory), with one fragment set.
+template <int DT, int MODE, bool LOOP = false> struct ScoreCfg {
     static constexpr bool wide = DT == kFP8 && MODE == 0;  // 0: filter mode
-    static constexpr int waves = wide ? 16 : 8;
+    static constexpr int waves = wide ? 16 : (LOOP ? 4 : 8);
     static constexpr int ring = DT == kFP8 ? 40 : 24;
-    static constexpr bool prefetch = !wide;
+    static constexpr bool prefetch = !wide && !LOOP;
 };
 template <int DT> struct RingEntries { static constexpr int value = ScoreCfg<DT, 0>::ring; };
 template <int DT> struct RingStride { static constexpr int value = RingEntries<DT>::value + 1; };
@@ -495,10 +498,10 @@ __device__ __forceinline__ void tile_tau(const ScoreArgs &a, int tile, uint32_t 
 // device knows); without it a workgroup scores one item, which keeps the
 // register allocation of the one-item body.
 template <int DT, int MODE, bool PAIR, bool LOOP = false>
-__global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(ScoreArgs a)
+__global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_score(ScoreArgs a)
 {
     static_assert(!LOOP || MODE == kModeDense, "only dense mode loops");
-    using Cfg = ScoreCfg<DT, MODE>;
+    using Cfg = ScoreCfg<DT, MODE, LOOP>;
     constexpr int kWaves = Cfg::waves;
     constexpr int RB = RowBytes<DT>::value;
     constexpr int TH = TileHeads<DT>::value;
@@ -593,7 +596,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
                 lo = hi = 0;
             }
         }
-        if (MODE == kModeDense && a.wlen && t >= 0 && (n & ps) == 0 && chunk == 0) a.wlen[t >> ps] = hi - lo;
+        if (MODE == kModeDense && !LOOP && a.wlen && t >= 0 && (n & ps) == 0 && chunk == 0) a.wlen[t >> ps] = hi - lo;
         s_row[n] = t;
         s_ks[n] = lo;
         s_ke[n] = hi;
@@ -663,7 +666,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
 
     // Without the preparation pass (dense mode only) the FP8 query sums are
     // computed here from the staged heads.
-    const bool own_prep = MODE == kModeDense && a.own_prep;  // workgroup-uniform
+    const bool own_prep = MODE == kModeDense && !LOOP && a.own_prep;  // workgroup-uniform; recovery (LOOP) reads the prep pass
     if (DT == kFP8 && own_prep) stage_q_heads<DT, kHeads, 64 * kWaves>(s_q, a.q, a.qbar, s_row);
     else stage_q_tile<DT, 64 * kWaves>(s_q, a, s_row);
     for (int i = threadIdx.x; i < kHeads * kTileQ; i += blockDim.x) {
@@ -859,7 +862,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE>::waves)) void k_score(Scor
             } else {
                 int p = (MODE == kModeSample) ? first_b + e * dmin : e;
                 p = min(p, S - 1);
-                if (MODE == kModeDense && a.table) {
+                if (MODE == kModeDense && !LOOP && a.table) {
                     // paged keys: logical key p is row p % page_size of its
                     // page (a page id out of range reads the pool's first row;
                     // its scale factor is 0)
