@@ -266,8 +266,9 @@ __device__ __forceinline__ v4f bound_group(const uint8_t *kb, int nblocks, int c
     const int n = lane & 15, g = lane >> 4;
     KFrag<DT> kx, kn;
     const int bb = min(c * 16 + n, nblocks - 1);  // A row n = block 16 c + n
-    load_kfrag(kx, kb, 2 * bb, g);
-    load_kfrag(kn, kb, 2 * bb + 1, g);
+    constexpr int RB = RowBytes<DT>::value;  // the 16x16 MFMA slices: lane group g holds [RB g / 4, RB (g + 1) / 4)
+    load_kfrag_at(kx, kb + (int64_t)(2 * bb) * RB + (RB / 4) * g);
+    load_kfrag_at(kn, kb + (int64_t)(2 * bb + 1) * RB + (RB / 4) * g);
     v4f u = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll UNR
     for (int h = 0; h < kHeads; ++h) {

@@ -17,17 +17,44 @@ template <int DT> struct KFrag;
 template <> struct KFrag<kFP8> { v8i a; };
 template <> struct KFrag<kBF16> { v4i a[4]; };
 
-// Key row p, lane group g: dimensions [32g, 32g+32).
-__device__ __forceinline__ void load_kfrag(KFrag<kFP8> &f, const uint8_t *kv, int p, int g)
+// Where the key fragments of a 64-key step come from and where the step's
+// scores land, per dtype.  A lane's fragment kt (kt < 4) holds the slice of
+// key frag_key(kt) of the step that starts frag_byte(kt) bytes into the key
+// row (32 bytes FP8, 64 bytes BF16); after the head sum the lane holds the
+// score of key out_base + KSTR kt + i for output element (kt, i).
+//   FP8, 16x16x128 MFMAs, four 16-key subtiles: lane (n, g) = (lane % 16,
+//   lane / 16) loads key 16 kt + n, dimensions [32 g, 32 g + 32), and ends
+//   with keys 4 g + 16 kt + i of query n.
+//   BF16, 32x32x16 MFMAs, two 32-key subtiles: lane l loads key
+//   32 (kt / 2) + l % 32, dimensions [64 (l / 32) + 32 (kt % 2), +32) (the
+//   K steps 4 (kt % 2) .. +3 of its subtile); the MFMA leaves it keys
+//   8 (r / 4) + 4 (l / 32) + r % 4 (r < 16) of both subtiles, and the head
+//   halves' swap leaves lanes of half (l / 16) % 2 with subtile half's keys.
+template <int DT> struct StepLayout;
+template <> struct StepLayout<kFP8> {
+    static constexpr int KSTR = 16;
+    __device__ static __forceinline__ int frag_key(int kt, int lane) { return 16 * kt + (lane & 15); }
+    __device__ static __forceinline__ int frag_byte(int, int lane) { return 32 * (lane >> 4); }
+    __device__ static __forceinline__ int out_base(int lane) { return 4 * (lane >> 4); }
+};
+template <> struct StepLayout<kBF16> {
+    static constexpr int KSTR = 8;
+    __device__ static __forceinline__ int frag_key(int kt, int lane) { return 32 * (kt >> 1) + (lane & 31); }
+    __device__ static __forceinline__ int frag_byte(int kt, int lane) { return 128 * (lane >> 5) + 64 * (kt & 1); }
+    __device__ static __forceinline__ int out_base(int lane) { return 32 * ((lane >> 4) & 1) + 4 * (lane >> 5); }
+};
+
+// A key fragment from its slice (p: first byte).
+__device__ __forceinline__ void load_kfrag_at(KFrag<kFP8> &f, const uint8_t *p)
 {
-    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 128 + 32 * g);
+    const v4i *src = reinterpret_cast<const v4i *>(p);
     const v4i lo = src[0], hi = src[1];
     f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ void load_kfrag(KFrag<kBF16> &f, const uint8_t *kv, int p, int g)
+__device__ __forceinline__ void load_kfrag_at(KFrag<kBF16> &f, const uint8_t *p)
 {
-    const v4i *src = reinterpret_cast<const v4i *>(kv + (int64_t)p * 256 + 64 * g);
+    const v4i *src = reinterpret_cast<const v4i *>(p);
 #pragma unroll
     for (int m = 0; m < 4; ++m) f.a[m] = src[m];
 }

@@ -74,7 +74,7 @@ template <int DT, int MODE, bool LOOP = false> struct ScoreCfg {
     static constexpr bool wide = DT == kFP8 && MODE == 0;  // 0: filter mode
     static constexpr int waves = wide ? 16 : (LOOP ? 4 : 8);
     static constexpr int ring = DT == kFP8 ? 40 : 24;
-    static constexpr bool prefetch = !wide && !LOOP;
+    static constexpr bool prefetch = !wide && !LOOP && DT == kFP8;
 };
 template <int DT> struct RingEntries { static constexpr int value = ScoreCfg<DT, 0>::ring; };
 template <int DT> struct RingStride { static constexpr int value = RingEntries<DT>::value + 1; };
@@ -340,69 +340,97 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     epi_abs(o.acc, xb, wp[kTileQ]);
 }
 
-__device__ __forceinline__ v4f mfma_bf16_d128(const KFrag<kBF16> &k, const v4i (&qf)[4])
+// BF16: v_mfma_f32_32x32x16_bf16, A = 32 keys x 16 dimensions (the lane's
+// fragments), B = 16 dimensions x 32 columns from the q tile.  The 32
+// columns are the tile's 16 queries for head hp (columns 0-15) and for head
+// hp + 16 (columns 16-31), so one chain of 8 MFMAs (K = 128) scores 32 keys
+// x 16 queries x 2 heads; the step's two 32-key subtiles interleave their
+// chains.  A lane (column l % 32: query l % 16, head half (l / 16) % 2)
+// sums ReLU of its half's 16 heads in order, weighted, for 16 keys of each
+// subtile; then lanes l and l ^ 16 exchange one subtile's sums (one row
+// swap), so that each lane adds the other head half to the subtile it keeps
+// (half 0: subtile 0, half 1: subtile 1).  Every score is (heads 0-15) +
+// (heads 16-31), each half summed in head order.
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// B fragment of K step s of a head: lane (column n = l % 32, k group
+// kb = l / 32) takes dimensions [64 kb + 8 s, +8) of its column's head row,
+// piece c = 8 kb + s of the q tile's slot layout (lane group c / 4, sub c % 4).
+// qp points at the lane's slot of head 0 of its half: s_q + half * 16 * HB +
+// (l % 16 + 32 kb) * 16.
+__device__ __forceinline__ v4i bfrag_bf16(const uint8_t *qp, int s)
 {
-    v4f x = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, k.a[m]), __builtin_bit_cast(v8bf, qf[m]),
-                                                    x, 0, 0, 0);
-    return x;
+    return *reinterpret_cast<const v4i *>(qp + (s & 3) * 1024 + (s >> 2) * 256);
 }
 
-// qp points at the lane's slot of head 0 (s_q + lane * 16); head h adds h * 4 KiB.
-__device__ __forceinline__ void mfma_bf16_head(v4f (&x)[kSub], const KFrag<kBF16> (&kf)[kSub], const uint8_t *qp)
+__device__ __forceinline__ void mfma_bf16_pair(v16f (&x)[2], const KFrag<kBF16> (&kf)[kSub], const uint8_t *qp)
 {
-    v4i qf[4];
+    const v16f z = {};
+    v4i qa = bfrag_bf16(qp, 0), qb;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) qf[m] = *reinterpret_cast<const v4i *>(qp + m * 1024);
+    for (int st = 0; st < 8; st += 2) {
+        qb = bfrag_bf16(qp, st + 1);
 #pragma unroll
-    for (int kt = 0; kt < kSub; ++kt) x[kt] = mfma_bf16_d128(kf[kt], qf);
+        for (int u = 0; u < 2; ++u)
+            x[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kf[2 * u + (st >> 2)].a[st & 3]),
+                                                          __builtin_bit_cast(v8bf, qa), st ? x[u] : z, 0, 0, 0);
+        if (st + 2 < 8) qa = bfrag_bf16(qp, st + 2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            x[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(v8bf, kf[2 * u + ((st + 1) >> 2)].a[(st + 1) & 3]), __builtin_bit_cast(v8bf, qb), x[u],
+                0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void epi_relu16(float (&acc)[2][16], const v16f (&x)[2], float w)
+{
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(w, relu_bits(x[u][r]), acc[u][r]);
 }
 
 template <typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[kSub], const uint8_t *s_q,
                                            const float *s_w, int lane, float /*qsc*/, AfterMfma after_mfma)
 {
-    // One head is 16 MFMAs here, so a one-head lag already covers the MFMA
-    // latency and two result sets suffice (the key fragments take 128
-    // registers on this path).
-    constexpr int HB = 4096;
+    constexpr int HB = 4096;  // LDS bytes per head of the q tile
+    const int half = (lane >> 4) & 1;
+    const uint8_t *qp = s_q + half * 16 * HB + ((lane & 15) + 32 * (lane >> 5)) * 16;
+    const float *wp = s_w + half * 16 * kTileQ + (lane & 15);  // head hp + 16 half: wp[hp * kTileQ]
+    float acc[2][16];
 #pragma unroll
-    for (int kt = 0; kt < kSub; ++kt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o.acc[kt][i] = 0.0f;
-    const uint8_t *qp = s_q + lane * 16;
-    const float *wp = s_w + (lane & 15);
-    v4f xa[kSub], xb[kSub];
+        for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
+    v16f xa[2], xb[2];
     __builtin_amdgcn_s_setprio(1);  // as on the FP8 path
-    mfma_bf16_head(xa, kf, qp);
+    mfma_bf16_pair(xa, kf, qp);
 #pragma unroll 1
-    for (int h = 1; h < kHeads - 1; h += 2) {
+    for (int hp = 1; hp < 15; hp += 2) {
         const float w0 = wp[0], w1 = wp[kTileQ];
-        mfma_bf16_head(xb, kf, qp + HB);
-        epi_relu(o.acc, xa, w0);
-        mfma_bf16_head(xa, kf, qp + 2 * HB);
-        epi_relu(o.acc, xb, w1);
+        mfma_bf16_pair(xb, kf, qp + HB);
+        epi_relu16(acc, xa, w0);
+        mfma_bf16_pair(xa, kf, qp + 2 * HB);
+        epi_relu16(acc, xb, w1);
         qp += 2 * HB;
         wp += 2 * kTileQ;
-        // Issue order: one MFMA, then two epilogue instructions (max, fma);
-        // each head's four LDS reads go out first.
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-            }
-        }
     }
-    mfma_bf16_head(xb, kf, qp + HB);
+    mfma_bf16_pair(xb, kf, qp + HB);
     __builtin_amdgcn_s_setprio(0);
     after_mfma();
-    epi_relu(o.acc, xa, wp[0]);
-    epi_relu(o.acc, xb, wp[kTileQ]);
+    epi_relu16(acc, xa, wp[0]);
+    epi_relu16(acc, xb, wp[kTileQ]);
+    // Lane l keeps subtile (l / 16) % 2: the swap hands lane l ^ 16 the
+    // subtile it keeps and brings back this lane's.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0][r]), __float_as_uint(acc[1][r]), false,
+                                                         false);
+        o.acc[r >> 2][r & 3] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
 }
 
 // The score of output element (kt, i) from the step accumulators; sh is the
@@ -851,14 +879,19 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     const int kspan = min(S - kbase, a.chunk + kStepKeys);
     const __amdgpu_buffer_rsrc_t kvr = make_rsrc(a.kv + (int64_t)kbase * RB, (uint32_t)kspan * RB);
     const __amdgpu_buffer_rsrc_t shr = make_rsrc(a.sigh + kbase, (uint32_t)(kspan + kStepKeys) * 4u);
-    const uint32_t klane = (uint32_t)(n * RB + (RB / 4) * g);  // lane's slice in a 16-key subtile
+    using LY = StepLayout<DT>;
+    constexpr int KSTR = LY::KSTR;
+    // the lane's slice of its fragment-0 key (fragment kt adds a constant)
+    const uint32_t klane = (uint32_t)(LY::frag_key(0, lane) * RB + LY::frag_byte(0, lane));
     auto load_step = [&](KFrag<DT>(&f)[kSub], int j) {
 #pragma unroll
         for (int kt = 0; kt < kSub; ++kt) {
-            const int e = j * kStepKeys + 16 * kt + n;
+            const int e = j * kStepKeys + LY::frag_key(kt, lane);
             if (MODE == kModeFilter) {
                 const uint32_t soff = (uint32_t)(j * kStepKeys - kbase) * RB;
-                load_kfrag_buf(f[kt], kvr, klane + (uint32_t)(16 * kt * RB), soff);
+                const uint32_t kofs = (uint32_t)((LY::frag_key(kt, 0) - LY::frag_key(0, 0)) * RB +
+                                                 (LY::frag_byte(kt, 0) - LY::frag_byte(0, 0)));  // compile-time
+                load_kfrag_buf(f[kt], kvr, klane + kofs, soff);
             } else {
                 int p = (MODE == kModeSample) ? first_b + e * dmin : e;
                 p = min(p, S - 1);
@@ -868,9 +901,9 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                     // its scale factor is 0)
                     const int64_t pg = a.table[p / a.page_size];
                     const int64_t slot = (pg >= 0 && pg < a.num_pages) ? pg * a.page_size + p % a.page_size : 0;
-                    load_kfrag(f[kt], a.kv + slot * RB, 0, g);
+                    load_kfrag_at(f[kt], a.kv + slot * RB + LY::frag_byte(kt, lane));
                 } else {
-                    load_kfrag(f[kt], a.kv, p, g);
+                    load_kfrag_at(f[kt], a.kv + (int64_t)p * RB + LY::frag_byte(kt, lane));
                 }
             }
         }
@@ -880,7 +913,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     // `next` runs as soon as the step's MFMAs no longer need the key
     // fragments (it issues the next step's key loads).
     auto process = [&](KFrag<DT>(&kf)[kSub], int j, auto next) {
-        const int sb = j * kStepKeys + 4 * g;  // key of element (kt, i) is sb + 16 kt + i
+        const int sb = j * kStepKeys + LY::out_base(lane);  // key of element (kt, i) is sb + KSTR kt + i
         // Scale factors of the step's outputs (4 consecutive keys per
         // subtile).  With the prefetching (2-wave) shape they load before the
         // MFMA work so their latency hides; with 4 waves per SIMD other waves
@@ -891,7 +924,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 const uint32_t soff = (uint32_t)(j * kStepKeys - kbase) * 4u;
 #pragma unroll
                 for (int kt = 0; kt < kSub; ++kt)
-                    shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(16 * g + 64 * kt), soff));
+                    shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(4 * LY::out_base(lane) + 4 * KSTR * kt), soff));
             } else if (MODE == kModeSample) {
                 // Lattice keys first_b + e * dmin: a strided gather from the
                 // padded factors (entries past the end are never used).
@@ -899,7 +932,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        shv[kt][i] = a.sigh[min(first_b + (sb + 16 * kt + i) * dmin, S + kStepKeys - 1)];
+                        shv[kt][i] = a.sigh[min(first_b + (sb + KSTR * kt + i) * dmin, S + kStepKeys - 1)];
             } else if (own_prep) {
                 // the factor the preparation pass would store: sigma / 2
                 // (FP8) or sigma, 0 past the keys and for a page out of range
@@ -907,7 +940,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int p = sb + 16 * kt + i;
+                        const int p = sb + KSTR * kt + i;
                         float sg = 0.0f;
                         if (p < S) {
                             if (a.table) {
@@ -922,7 +955,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                     }
             } else {
 #pragma unroll
-                for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + 16 * kt);
+                for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + sb + KSTR * kt);
             }
         };
         // The factors load before the MFMA work where registers allow (their
@@ -959,7 +992,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             if (__builtin_expect(!inside, 0)) {
 #pragma unroll
                 for (int b = 0; b < kSub * 4; ++b) {
-                    const int s = sb + 16 * (b >> 2) + (b & 3);
+                    const int s = sb + KSTR * (b >> 2) + (b & 3);
                     if (s < rks || s >= rke) sc[b] = __builtin_nanf("");
                 }
             }
@@ -988,7 +1021,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                     for (int b = 0; b < kSub * 4; ++b) {
                         if (sc[b] >= tau) {
                             if (pos < (uint32_t)a.cap)
-                                a.cand[(int64_t)to * a.cap + pos] = raw_cand(sc[b], sb + 16 * (b >> 2) + (b & 3));
+                                a.cand[(int64_t)to * a.cap + pos] = raw_cand(sc[b], sb + KSTR * (b >> 2) + (b & 3));
                             ++pos;
                         }
                     }
@@ -999,7 +1032,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
 #pragma unroll
                 for (int b = 0; b < kSub * 4; ++b) {
                     if (sc[b] >= tau) {
-                        *rp = raw_cand(sc[b], sb + 16 * (b >> 2) + (b & 3));
+                        *rp = raw_cand(sc[b], sb + KSTR * (b >> 2) + (b & 3));
                         ++rp;
                     }
                 }
@@ -1012,7 +1045,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             uint32_t *srow = a.samp + (int64_t)(to < 0 ? 0 : to) * a.sample_target;
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt) {
-                const int e0 = sb + 16 * kt;
+                const int e0 = sb + KSTR * kt;
                 const int p0 = first_b + e0 * dmin, p3 = p0 + 3 * dmin;
                 const int idx0 = (p0 - first_n) >> dsh;
                 if (to >= 0 && dn == dmin && e0 + 3 < nlat && p0 >= rks && p3 < rke && (idx0 & 3) == 0) {
@@ -1037,7 +1070,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             for (int kt = 0; kt < kSub; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int s = sb + 16 * kt + i;
+                    const int s = sb + KSTR * kt + i;
                     if (slot < 0 || s < rks || s >= rke) continue;
                     a.scratch[(int64_t)slot * a.scratch_stride + (s - rks)] = score_of<DT>(o, kt, i, shv[kt][i]);
                 }
@@ -1058,18 +1091,34 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             if (lane == 0) v = atomicAdd(&s_next, 1);
             return __builtin_amdgcn_readfirstlane(__shfl(v, 0));
         };
-        KFrag<DT> ka[kSub], kb[kSub];
-        int i = claim();
-        if (i < nstep) load_step(ka, step_of(i));
-        while (i < nstep) {
-            const int i2 = claim();
-            if (i2 < nstep) load_step(kb, step_of(i2));
-            process(ka, step_of(i), nop);
-            if (i2 >= nstep) break;
-            const int i3 = claim();
-            if (i3 < nstep) load_step(ka, step_of(i3));
-            process(kb, step_of(i2), nop);
-            i = i3;
+        if constexpr (DT == kFP8) {
+            KFrag<DT> ka[kSub], kb[kSub];
+            int i = claim();
+            if (i < nstep) load_step(ka, step_of(i));
+            while (i < nstep) {
+                const int i2 = claim();
+                if (i2 < nstep) load_step(kb, step_of(i2));
+                process(ka, step_of(i), nop);
+                if (i2 >= nstep) break;
+                const int i3 = claim();
+                if (i3 < nstep) load_step(ka, step_of(i3));
+                process(kb, step_of(i2), nop);
+                i = i3;
+            }
+        } else {
+            // one fragment set (BF16's 32x32 step needs the registers): the
+            // next claimed step's keys load as soon as this step's last MFMA
+            // has issued
+            KFrag<DT> kf[kSub];
+            int i = claim();
+            if (i < nstep) load_step(kf, step_of(i));
+            while (i < nstep) {
+                const int i2 = claim();
+                process(kf, step_of(i), [&]() {
+                    if (i2 < nstep) load_step(kf, step_of(i2));
+                });
+                i = i2;
+            }
         }
     } else if (Cfg::prefetch) {
         // Two fragment sets alternate so the next step's keys load while this
