@@ -23,23 +23,26 @@ namespace ftk {
 
 constexpr int kQbarParts = 3;
 
-// OCP E4M3 ("fn") code -> binary32, exact.
+// OCP E4M3 ("fn") code -> binary32, exact.  The 7 magnitude bits placed at
+// bits 26..20 of a binary32 read as 2^(e - 127) (1 + m / 8), or as the
+// subnormal (m / 8) 2^-126 when e = 0; times 2^120 both are the E4M3 value
+// (binary32 subnormals are kept: the kernels run with f32 denormals on).
+// Branch-free: three instructions.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c)
 {
-    const uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 0xFu, m = c & 0x7u;
-    if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));  // m * 2^-9
-    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+    const float mag = __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
+    return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
-// binary32 with |v| <= 448 -> E4M3 code, truncating toward zero.
+// binary32 with |v| <= 448 -> E4M3 code, truncating toward zero (selects,
+// no branches).
 __device__ __forceinline__ uint32_t f32_to_e4m3_trunc(float v)
 {
     const uint32_t b = __float_as_uint(v), s = (b >> 24) & 0x80u;
-    const float a = fabsf(v);
-    if (a < 0.001953125f) return s;                        // below the smallest subnormal
     const int E = (int)((b >> 23) & 0xFFu) - 127;
-    if (E < -6) return s | (uint32_t)(a * 512.0f);         // subnormal: trunc(a / 2^-9)
-    return s | ((uint32_t)(E + 7) << 3) | ((b >> 20) & 7u);  // normal: top 3 mantissa bits
+    const uint32_t sub = (uint32_t)(fabsf(v) * 512.0f);                   // below 2^-6: trunc(|v| / 2^-9), 0 below 2^-9
+    const uint32_t nrm = ((uint32_t)(E + 7) << 3) | ((b >> 20) & 7u);   // normal: top 3 mantissa bits
+    return s | (E < -6 ? sub : nrm);
 }
 
 // Rows 4 blk .. 4 blk + 3, one wave per query row (a 256-thread

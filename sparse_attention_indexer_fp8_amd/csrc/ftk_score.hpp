@@ -151,7 +151,10 @@ struct ScoreArgs {
 // path heads 32..34 hold the qbar parts.
 // NT threads (the whole workgroup) stage NH heads; each thread's global loads
 // are issued in batches of up to 8 before their LDS stores, so the latency
-// of the tile's reads is paid a few times, not once per piece.
+// of the tile's reads is paid a few times, not once per piece.  The loads
+// are unconditional (a column without a row reads row 0 and stores zeros,
+// a piece past the tile re-reads the last piece and stores nothing): a load
+// under a branch would be waited for inside that branch.
 template <int DT, int NH, int NT>
 __device__ __forceinline__ void stage_q_heads(uint8_t *s_q, const uint8_t *q, const uint8_t *qbar, const int *s_row)
 {
@@ -164,21 +167,19 @@ __device__ __forceinline__ void stage_q_heads(uint8_t *s_q, const uint8_t *q, co
 #pragma unroll
     for (int base = 0; base < ITER; base += BATCH) {
         v4i v[BATCH];
+        bool live[BATCH];
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const int id = threadIdx.x + (base + u) * NT;
-            v[u] = (v4i){0, 0, 0, 0};
-            if (base + u < ITER && id < NCH) {
-                const int n = id / (NH * CPR);
-                const int h = (id / CPR) % NH;
-                const int c = id % CPR;
-                const int t = s_row[n];
-                if (t >= 0) {
-                    const uint8_t *src = (h < kHeads) ? q + ((int64_t)t * kHeads + h) * RB
-                                                      : qbar + ((int64_t)t * kQbarParts + (h - kHeads)) * RB;
-                    v[u] = *reinterpret_cast<const v4i *>(src + c * 16);
-                }
-            }
+            const int id = min(threadIdx.x + (base + u) * NT, NCH - 1);
+            const int n = id / (NH * CPR);
+            const int h = (id / CPR) % NH;
+            const int c = id % CPR;
+            const int t = s_row[n];
+            live[u] = t >= 0;
+            const int64_t tt = max(t, 0);
+            const uint8_t *src = (h < kHeads) ? q + (tt * kHeads + h) * RB
+                                              : qbar + (tt * kQbarParts + (h - kHeads)) * RB;
+            v[u] = *reinterpret_cast<const v4i *>(src + c * 16);
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -188,7 +189,8 @@ __device__ __forceinline__ void stage_q_heads(uint8_t *s_q, const uint8_t *q, co
                 const int h = (id / CPR) % NH;
                 const int c = id % CPR;
                 const int sub = c % SUB, g = c / SUB;
-                *reinterpret_cast<v4i *>(s_q + ((h * SUB + sub) * 64 + n + 16 * g) * 16) = v[u];
+                *reinterpret_cast<v4i *>(s_q + ((h * SUB + sub) * 64 + n + 16 * g) * 16) =
+                    live[u] ? v[u] : (v4i){0, 0, 0, 0};
             }
         }
     }
