@@ -89,23 +89,38 @@ __device__ __forceinline__ float relu_bits(float x)
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// Stride of the row's strided sample: the smallest power of two d >=
-// min_stride with len <= target * d, so the sample holds at most `target`
-// keys.  (min_stride keeps the sample no denser than the threshold needs.)
+// The row's strided sample is a lattice of 64-key runs: the keys p with
+// p mod (64 d) < 64 for a power of two d, i.e. every d-th aligned 64-key
+// block of the window.  A sample step then reads 64 consecutive keys, like
+// a scan step.
+constexpr int kRunKeys = 64;
+
+// Stride of the row's sample: the smallest power of two d >= min_stride
+// with len <= (target - 128) d, which keeps the sample (at most len / d +
+// 128 keys: two partial runs) within `target` keys; tiny targets, below 192,
+// use a floor of 64 keys per stride and keep only the first `target`
+// samples.  (min_stride keeps the sample no denser than the threshold
+// needs.)
 __device__ __host__ __forceinline__ int sample_stride(int64_t len, int target, int min_stride)
 {
+    const int64_t room = target - 2 * kRunKeys > kRunKeys ? target - 2 * kRunKeys : kRunKeys;
     int d = min_stride;
-    while (len > (int64_t)target * d) d <<= 1;
+    while (len > room * d) d <<= 1;
     return d;
 }
 
-// Number of multiples of d (a power of two) in [lo, hi).
+// Lattice keys of stride d in [0, x): whole periods of 64 d keys hold 64.
+__device__ __host__ __forceinline__ int64_t lattice_prefix(int64_t x, int d)
+{
+    const int64_t period = (int64_t)kRunKeys * d, r = x % period;
+    return x / period * kRunKeys + (r < kRunKeys ? r : kRunKeys);
+}
+
+// Lattice keys of stride d in [lo, hi).
 __device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi, int d)
 {
     if (hi <= lo) return 0;
-    int64_t first = (lo + d - 1) / d * d;
-    if (first >= hi) return 0;
-    return (hi - 1 - first) / d + 1;
+    return lattice_prefix(hi, d) - lattice_prefix(lo, d);
 }
 
 // ---------------------------------------------------------------------------

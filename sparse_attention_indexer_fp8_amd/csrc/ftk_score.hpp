@@ -150,8 +150,8 @@ struct ScoreArgs {
 // head reads 1 KiB of consecutive LDS, free of bank conflicts.  On the FP8
 // path heads 32..34 hold the qbar parts.
 // NT threads (the whole workgroup) stage NH heads; each thread's global loads
-// are issued in batches of up to 8 before their LDS stores, so the latency
-// of the tile's reads is paid a few times, not once per piece.  The loads
+// (at most 16, else batches of 8) are all issued before their LDS stores, so
+// the latency of the tile's reads is paid once or twice, not once per piece.  The loads
 // are unconditional (a column without a row reads row 0 and stores zeros,
 // a piece past the tile re-reads the last piece and stores nothing): a load
 // under a branch would be waited for inside that branch.
@@ -163,7 +163,7 @@ __device__ __forceinline__ void stage_q_heads(uint8_t *s_q, const uint8_t *q, co
     constexpr int SUB = CPR / 4;    // pieces per lane group
     constexpr int NCH = kTileQ * NH * CPR;
     constexpr int ITER = (NCH + NT - 1) / NT;
-    constexpr int BATCH = ITER < 8 ? ITER : 8;
+    constexpr int BATCH = ITER <= 16 ? ITER : 8;
 #pragma unroll
     for (int base = 0; base < ITER; base += BATCH) {
         v4i v[BATCH];
@@ -620,7 +620,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         if (MODE == kModeSample) {
             if (t >= 0 && hi - lo > a.cap) {
                 d = sample_stride(hi - lo, a.sample_target, a.sample_min_stride);
-                s_nl[n] = (int)lattice_count(lo, hi, d);
+                s_nl[n] = (int)min(lattice_count(lo, hi, d), (int64_t)a.sample_target);
             } else {
                 t = -1;
                 lo = hi = 0;
@@ -669,16 +669,19 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         return;
     }
 
-    // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode the
-    // steps index the lattice first_b + e * dmin, e < nlat.
-    int jlo, jhi, first_b = 0, nlat = 0;
+    // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode
+    // step j is the run of the tile's lattice (stride dmin) that starts at
+    // key (run0 + j) * 64 * dmin: the runs that meet the union of the
+    // windows.
+    int jlo, jhi, run0 = 0, rsh = 0;
     if (MODE == kModeSample) {
-        const int msh = __builtin_ctz((unsigned)dmin);  // power of two
-        first_b = ((lo + dmin - 1) >> msh) << msh;
-        nlat = (int)lattice_count(lo, hi, dmin);
+        rsh = 6 + __builtin_ctz((unsigned)dmin);  // log2 of the run period 64 dmin
+        static_assert(kRunKeys == 64 && kStepKeys == 64, "one run per step");
+        run0 = lo >> rsh;
+        if ((lo & ((1 << rsh) - 1)) >= kRunKeys) ++run0;  // lo falls between runs
+        const int nsteps = max(0, ((hi - 1) >> rsh) - run0 + 1);
         // With few tiles the lattice is split over a.sample_split workgroups
         // (the chunk index is the part).
-        const int nsteps = (nlat + kStepKeys - 1) / kStepKeys;
         const int per = (nsteps + a.sample_split - 1) / a.sample_split;
         jlo = chunk * per;
         jhi = min(nsteps, jlo + per);
@@ -697,12 +700,21 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     // Without the preparation pass (dense mode only) the FP8 query sums are
     // computed here from the staged heads.
     const bool own_prep = MODE == kModeDense && !LOOP && a.own_prep;  // workgroup-uniform; recovery (LOOP) reads the prep pass
+    // The weights load first so their latency overlaps the q tile's.
+    constexpr int WR = (kHeads * kTileQ + 64 * kWaves - 1) / (64 * kWaves);
+    float wv[WR];
+#pragma unroll
+    for (int u = 0; u < WR; ++u) {
+        const int i = min((int)threadIdx.x + u * 64 * kWaves, kHeads * kTileQ - 1);
+        const int rt = s_row[i & (kTileQ - 1)];
+        wv[u] = a.w[(int64_t)max(rt, 0) * kHeads + i / kTileQ];
+    }
     if (DT == kFP8 && own_prep) stage_q_heads<DT, kHeads, 64 * kWaves>(s_q, a.q, a.qbar, s_row);
     else stage_q_tile<DT, 64 * kWaves>(s_q, a, s_row);
-    for (int i = threadIdx.x; i < kHeads * kTileQ; i += blockDim.x) {
-        const int rn = i & (kTileQ - 1), h = i / kTileQ;
-        const int rt = s_row[rn];
-        s_w[i] = rt >= 0 ? a.w[(int64_t)rt * kHeads + h] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < WR; ++u) {
+        const int i = threadIdx.x + u * 64 * kWaves;
+        if (i < kHeads * kTileQ) s_w[i] = s_row[i & (kTileQ - 1)] >= 0 ? wv[u] : 0.0f;
     }
     __syncthreads();
     if (DT == kFP8 && own_prep) {
@@ -866,9 +878,11 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
 
     float tau = __builtin_inff();
     if (MODE == kModeFilter && to >= 0) tau = a.tau[to];
+    // Sample mode: the row's lattice (stride dn, a multiple of dmin) holds
+    // the tile's runs whose step index is a multiple of dn; a key's slot in
+    // the row's sample is its lattice rank within the window.
     const int dn = s_d[n];                       // power of two
-    const int dsh = __builtin_ctz((unsigned)dn);
-    const int first_n = ((rks + dn - 1) >> dsh) << dsh;
+    const int64_t rank0 = MODE == kModeSample ? lattice_prefix(rks, dn) : 0;
     uint64_t *ring = s_ring + (MODE == kModeFilter ? wave * kTileQ * RS : 0);
     uint32_t ring_cnt = 0;
 
@@ -895,7 +909,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                                                  (LY::frag_byte(kt, 0) - LY::frag_byte(0, 0)));  // compile-time
                 load_kfrag_buf(f[kt], kvr, klane + kofs, soff);
             } else {
-                int p = (MODE == kModeSample) ? first_b + e * dmin : e;
+                int p = (MODE == kModeSample) ? ((run0 + j) << rsh) + LY::frag_key(kt, lane) : e;
                 p = min(p, S - 1);
                 if (MODE == kModeDense && !LOOP && a.table) {
                     // paged keys: logical key p is row p % page_size of its
@@ -928,13 +942,12 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 for (int kt = 0; kt < kSub; ++kt)
                     shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(4 * LY::out_base(lane) + 4 * KSTR * kt), soff));
             } else if (MODE == kModeSample) {
-                // Lattice keys first_b + e * dmin: a strided gather from the
-                // padded factors (entries past the end are never used).
+                // The run's keys are consecutive: the factors load like a
+                // scan step's (the run starts below num_kv; the padded
+                // factors cover its last 64 keys).
+                const int rb = ((run0 + j) << rsh) + LY::out_base(lane);
 #pragma unroll
-                for (int kt = 0; kt < kSub; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        shv[kt][i] = a.sigh[min(first_b + (sb + KSTR * kt + i) * dmin, S + kStepKeys - 1)];
+                for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + rb + KSTR * kt);
             } else if (own_prep) {
                 // the factor the preparation pass would store: sigma / 2
                 // (FP8) or sigma, 0 past the keys and for a page out of range
@@ -1041,28 +1054,30 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             }
             ring_cnt += direct ? 0u : tot;
         } else if (MODE == kModeSample) {
-            // The lane's 4 outputs of a subtile are consecutive lattice keys;
-            // when the row samples on the tile's lattice they are consecutive
-            // sample slots and go out as one 16-byte store.
+            // The lane's 4 outputs of a subtile are consecutive keys of the
+            // run; when the run is on the row's lattice and inside its window
+            // they take consecutive sample slots and go out as one 16-byte
+            // store where aligned.
             uint32_t *srow = a.samp + (int64_t)(to < 0 ? 0 : to) * a.sample_target;
+            const int rbase = (run0 + j) << rsh;
+            const bool on_row = to >= 0 && (((rbase >> 6) & (dn - 1)) == 0);
+            const int64_t slot0 = lattice_prefix(rbase, dn) - rank0;  // slot of the run's first key
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt) {
-                const int e0 = sb + KSTR * kt;
-                const int p0 = first_b + e0 * dmin, p3 = p0 + 3 * dmin;
-                const int idx0 = (p0 - first_n) >> dsh;
-                if (to >= 0 && dn == dmin && e0 + 3 < nlat && p0 >= rks && p3 < rke && (idx0 & 3) == 0) {
+                const int e0 = LY::out_base(lane) + KSTR * kt;  // key rbase + e0 .. + 3
+                const int p0 = rbase + e0;
+                const int64_t idx0 = slot0 + e0;
+                if (on_row && p0 >= rks && p0 + 3 < rke && (idx0 & 3) == 0 && idx0 + 3 < a.sample_target) {
                     v4i v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = (int)ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
                     *reinterpret_cast<v4i *>(srow + idx0) = v;
-                } else {
+                } else if (on_row) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int e = e0 + i;
-                        if (to < 0 || e >= nlat) continue;
-                        const int p = first_b + e * dmin;
-                        if (p < rks || p >= rke || (p & (dn - 1)) != 0) continue;
-                        srow[(p - first_n) >> dsh] = ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
+                        const int p = p0 + i;
+                        if (p < rks || p >= rke || idx0 + i >= a.sample_target) continue;
+                        srow[idx0 + i] = ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
                     }
                 }
             }

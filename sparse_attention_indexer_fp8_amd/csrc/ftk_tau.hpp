@@ -48,18 +48,19 @@ __device__ __forceinline__ float tau_exact_in_bucket(const float (&v)[PER], floa
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // lane j < cb: the rank of its sample among the bucket's (larger values
-    // first, equal ones by position); the one of rank r - above - 1 wins
+    // first, equal ones by position); the one of rank r - above - 1 wins.
+    // Lane i's sample reaches the others through readlane (no LDS round
+    // trip per comparison).
     const uint32_t want = r - above - 1;
-    float e = 0.0f;
-    uint32_t rank = 0xFFFFFFFFu;
-    if ((uint32_t)lane < cb) {
-        e = __uint_as_float(buf[lane]);
-        rank = 0;
-        for (uint32_t i = 0; i < cb; ++i) {
-            const float f = __uint_as_float(buf[i]);
-            rank += (f > e || (f == e && i < (uint32_t)lane)) ? 1u : 0u;
-        }
+    const bool mine_ok = (uint32_t)lane < cb;
+    const uint32_t eb = mine_ok ? buf[lane] : 0u;
+    const float e = __uint_as_float(eb);
+    uint32_t rank = 0;
+    for (uint32_t i = 0; i < cb; ++i) {
+        const float f = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)eb, (int)i));
+        rank += (f > e || (f == e && i < (uint32_t)lane)) ? 1u : 0u;
     }
+    if (!mine_ok) rank = 0xFFFFFFFFu;
     const uint64_t hit = __ballot(rank == want);
     const float t = __shfl(e, hit ? __builtin_ctzll(hit) : 0);
     __builtin_amdgcn_wave_barrier();  // every lane has read buf before the caller reuses the LDS
@@ -164,7 +165,7 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
 // wave_tau for K rows, each of n[k] <= 2048 samples: the same buckets and
 // rule, with the K rows' sample loads and range reductions interleaved so
 // their latencies overlap; the histogram passes then take the rows in turn.
-// hist: kTauBuckets words of LDS private to the wave.  Every lane gets the
+// hist: kTauBuckets words of LDS private to the wave, 16-byte aligned.  Every lane gets the
 // K thresholds.
 template <int K>
 __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], const int (&n)[K],
@@ -207,7 +208,7 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
             continue;
         }
 #pragma unroll
-        for (int q = 0; q < PER; ++q) hist[lane + 64 * q] = 0u;
+        for (int q = 0; q < PER / 4; ++q) reinterpret_cast<v4i *>(hist)[lane + 64 * q] = (v4i){0, 0, 0, 0};
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land before any lane adds
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(64 * kTauWaves) void k_tau(TauArgs a)
     float tv = -__builtin_inff();
     if (len > a.cap) {
         const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
-        const int ns = (int)lattice_count(lo, hi, d);
+        const int ns = (int)min(lattice_count(lo, hi, d), (int64_t)a.sample_target);
         tv = wave_tau(a.samp + t * a.sample_target, ns, tau_rank(a.topk, ns, len, a.rank_scale), s_hist[wave], lane);
     }
     if (lane == 0) a.tau[t] = tv;
