@@ -103,14 +103,17 @@ __device__ __forceinline__ void qbar_rows(const uint8_t *q, const float *w, int6
 // are those of qbar_rows, in the same order, so the parts have the same bits
 // as the ones the preparation pass writes.  NT threads (the whole
 // workgroup); one wave per column, lane l owning dimensions 2l and 2l + 1.
+// Columns without a row (s_row[n] < 0) are skipped: their scores are never
+// kept, whatever their parts hold.
 template <int NT>
-__device__ __forceinline__ void qbar_tile_lds(uint8_t *s_q, const float *s_w, float *s_qsc)
+__device__ __forceinline__ void qbar_tile_lds(uint8_t *s_q, const float *s_w, float *s_qsc, const int *s_row)
 {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int d = 2 * lane;
     const int off = ((d >> 4) & 1) * 64 * 16 + (d >> 5) * 16 * 16 + (d & 15);  // byte d's place within a head
     for (int n = wave; n < 16; n += NW) {
+        if (s_row[n] < 0) continue;  // wave-uniform
         uint32_t c[kHeads];
 #pragma unroll
         for (int h = 0; h < kHeads; ++h) c[h] = *reinterpret_cast<const uint16_t *>(s_q + h * 2 * 64 * 16 + n * 16 + off);

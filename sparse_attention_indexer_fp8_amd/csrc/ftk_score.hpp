@@ -718,7 +718,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     }
     __syncthreads();
     if (DT == kFP8 && own_prep) {
-        qbar_tile_lds<64 * kWaves>(s_q, s_w, s_qsc);
+        qbar_tile_lds<64 * kWaves>(s_q, s_w, s_qsc, s_row);
         __syncthreads();
     }
 
