@@ -127,8 +127,8 @@ typedef struct flashtopk_options {
                                  flashtopk_info); adds a few microseconds */
     int out_flags;            /* FLASHTOPK_OUT_* bits; 0 = score order, int32 */
     int heads;                /* indexer heads: 0 or 32, or 64 (README
-                                 "Roadmap": other head counts such as the 64
-                                 of DeepSeek-V3.2); q is [num_q, heads, 128]
+                                 "Roadmap": head counts besides 32, with 64
+                                 as the named case); q is [num_q, heads, 128]
                                  and weights [num_q, heads].  64-head calls
                                  take the scan path (no score-bound pruning) */
     int validate;             /* nonzero: check the data preconditions on the

@@ -4,8 +4,9 @@ An independent restatement of the same definition for tiny inputs, written
 without the C code: operand decode from the OCP E4M3FN / bfloat16 bit layouts
 with numpy integer arithmetic, the indexer score in binary64 (FlashTopK
 README, "Quick start", indexer-score equation), and selection with
-``numpy.lexsort`` on (key index, -score) -- README "What you can do": ties at
-the k-th score keep the smallest key indices.  Short windows pad with -1 /
+``numpy.lexsort`` on (key index, -score), so an equal score at the k-th
+place goes to the lower key index (tie rule of the FlashTopK README, "What
+you can do").  Short windows pad with -1 /
 -inf (DeepSelect README, "Variable-length rows").
 """
 from __future__ import annotations

@@ -215,7 +215,7 @@ static int select_row(const void *q, int dtype, int heads, const float *kv_scale
 /* Exact top-k for a list of rows.
  *   q        [num_q, heads, 128]  FP8 E4M3FN bytes or BF16 codes (heads = 32 for
  *            oracle_select; the head count is a parameter of oracle_select_h, for
- *            indexers with other head counts such as 64: README "Roadmap")
+ *            head counts besides 32, e.g. 64: README "Roadmap")
  *   kv       [num_kv, 128]     same dtype
  *   kv_scales[num_kv] fp32 or NULL (all ones)
  *   weights  [num_q, heads] fp32

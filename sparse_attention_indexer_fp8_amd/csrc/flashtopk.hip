@@ -643,6 +643,7 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
         ta.samp = (const uint32_t *)w.samp.ptr;
         ta.sample_target = p.sample_target;
         ta.sample_min_stride = p.sample_min_stride;
+        ta.pair = p.heads == 64 ? 1 : 0;
         ta.rank_scale = p.rank_scale;
         ta.tau = (float *)w.tau.ptr;
         ta.cnt = (uint32_t *)w.cnt.ptr;

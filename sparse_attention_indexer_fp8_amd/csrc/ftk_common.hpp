@@ -50,9 +50,10 @@ __device__ __forceinline__ float float_of_ord(uint32_t u)
 
 // 64-bit selection key: score code in the high word, the complement of the
 // key index in the low word.  Ordering keys descending gives score
-// descending and, among equal scores, the smaller key index first -- the tie
-// rule of the README ("What you can do": ties at the k-th score keep the
-// smallest key indices).  Keys of distinct indices are distinct.
+// descending and, among equal scores, the smaller key index first: the
+// tie rule of the FlashTopK README, "What you can do" (an equal score at
+// the k-th place goes to the lower index).  Keys of distinct indices are
+// distinct.
 __device__ __forceinline__ uint64_t sel_key(float score, int32_t s)
 {
     return ((uint64_t)ord_of(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
@@ -89,38 +90,69 @@ __device__ __forceinline__ float relu_bits(float x)
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// The row's strided sample is a lattice of 64-key runs: the keys p with
-// p mod (64 d) < 64 for a power of two d, i.e. every d-th aligned 64-key
-// block of the window.  A sample step then reads 64 consecutive keys, like
-// a scan step.
-constexpr int kRunKeys = 64;
+// The row's strided sample is a lattice of short runs: the keys p with
+// p mod (kRunKeys d) < kRunKeys, for a power of two d.  Runs of 4 keys let a
+// lane's four outputs of a subtile (four consecutive lattice keys) share one
+// scale-factor load and one sample store, while a 2048-key sample still
+// spans 512 places of the window (keys with block structure need many
+// independent places; 64-key runs gave 32 and misjudged such rows).
+constexpr int kRunKeys = 4;
+constexpr int kRunShift = 2;
 
 // Stride of the row's sample: the smallest power of two d >= min_stride
-// with len <= (target - 128) d, which keeps the sample (at most len / d +
-// 128 keys: two partial runs) within `target` keys; tiny targets, below 192,
-// use a floor of 64 keys per stride and keep only the first `target`
-// samples.  (min_stride keeps the sample no denser than the threshold
-// needs.)
+// with len <= target * d.  The window then holds at most target + 2
+// kRunKeys lattice keys (two partial runs); the kernels keep the first
+// `target` of them.  (min_stride keeps the sample no denser than the
+// threshold needs.)
 __device__ __host__ __forceinline__ int sample_stride(int64_t len, int target, int min_stride)
 {
-    const int64_t room = target - 2 * kRunKeys > kRunKeys ? target - 2 * kRunKeys : kRunKeys;
     int d = min_stride;
-    while (len > room * d) d <<= 1;
+    while (len > (int64_t)target * d) d <<= 1;
     return d;
 }
 
-// Lattice keys of stride d in [0, x): whole periods of 64 d keys hold 64.
-__device__ __host__ __forceinline__ int64_t lattice_prefix(int64_t x, int d)
+// Which run of each period a lattice uses: slot sl of stride d holds the
+// keys p with (p / kRunKeys) mod d == sl.  The slot comes from a hash of the
+// 16-row tile that scores the row's sample, taken mod d: rows of one tile
+// then share their keys (a row of stride dn >= dmin uses slot h mod dn,
+// whose runs lie on the tile's lattice, slot h mod dmin), while different
+// tiles sample different keys, so no single choice of keys biases every
+// row's threshold the same way.
+__device__ __host__ __forceinline__ uint32_t lattice_hash(int64_t tile)
 {
-    const int64_t period = (int64_t)kRunKeys * d, r = x % period;
-    return x / period * kRunKeys + (r < kRunKeys ? r : kRunKeys);
+    uint32_t x = (uint32_t)tile * 0x9E3779B1u;
+    x ^= x >> 15;
+    x *= 0x85EBCA77u;
+    x ^= x >> 13;
+    return x;
 }
 
-// Lattice keys of stride d in [lo, hi).
-__device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi, int d)
+// Lattice keys (stride 2^dsh, slot sl) in [0, x).
+__device__ __host__ __forceinline__ int64_t lattice_prefix_sh(int64_t x, int dsh, int sl)
+{
+    const int64_t y = x - (int64_t)sl * kRunKeys;
+    if (y <= 0) return 0;
+    const int64_t r = y & (((int64_t)kRunKeys << dsh) - 1);
+    return ((y >> (kRunShift + dsh)) << kRunShift) + (r < kRunKeys ? r : kRunKeys);
+}
+
+// Key of lattice index e (stride 2^dsh, slot sl; index 0 is the slot's first key).
+__device__ __host__ __forceinline__ int64_t lattice_key(int64_t e, int dsh, int sl)
+{
+    return (int64_t)sl * kRunKeys + ((e >> kRunShift) << (kRunShift + dsh)) + (e & (kRunKeys - 1));
+}
+
+// Lattice keys (stride d = 2^dsh, slot sl) in [lo, hi).
+__device__ __host__ __forceinline__ int64_t lattice_count(int64_t lo, int64_t hi, int dsh, int sl)
 {
     if (hi <= lo) return 0;
-    return lattice_prefix(hi, d) - lattice_prefix(lo, d);
+    return lattice_prefix_sh(hi, dsh, sl) - lattice_prefix_sh(lo, dsh, sl);
+}
+
+// Slot of stride 2^dsh for the rows of tile `tile`.
+__device__ __host__ __forceinline__ int lattice_slot(int64_t tile, int dsh)
+{
+    return (int)(lattice_hash(tile) & ((1u << dsh) - 1u));
 }
 
 // ---------------------------------------------------------------------------

@@ -1,5 +1,5 @@
-// Keys in a paged cache (FlashTopK README, "Roadmap": paged KV cache; today
-// the keys must be contiguous).  Logical key s of a call lives in page
+// Keys in a paged cache (FlashTopK README, "Roadmap": a paged KV cache, where
+// the released kernel needs one contiguous key array).  Logical key s of a call lives in page
 // block_table[s / page_size] at slot s % page_size of a page pool
 // [num_pages, page_size, 128] (its scale in a pool [num_pages, page_size]).
 //

@@ -620,7 +620,8 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         if (MODE == kModeSample) {
             if (t >= 0 && hi - lo > a.cap) {
                 d = sample_stride(hi - lo, a.sample_target, a.sample_min_stride);
-                s_nl[n] = (int)min(lattice_count(lo, hi, d), (int64_t)a.sample_target);
+                const int dsh = __builtin_ctz((unsigned)d);
+                s_nl[n] = (int)min(lattice_count(lo, hi, dsh, lattice_slot(tile, dsh)), (int64_t)a.sample_target);
             } else {
                 t = -1;
                 lo = hi = 0;
@@ -669,17 +670,18 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         return;
     }
 
-    // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode
-    // step j is the run of the tile's lattice (stride dmin) that starts at
-    // key (run0 + j) * 64 * dmin: the runs that meet the union of the
-    // windows.
-    int jlo, jhi, run0 = 0, rsh = 0;
+    // Keys of this work item, in 64-key steps [jlo, jhi).  In sample mode the
+    // steps index the tile's lattice (stride dmin): step j holds lattice
+    // indices e_first + 64 j + [0, 64), e_first the multiple of 64 at or
+    // below the index of the first lattice key at or after lo.
+    int jlo, jhi, msh = 0, msl = 0;
+    int64_t e_first = 0;
     if (MODE == kModeSample) {
-        rsh = 6 + __builtin_ctz((unsigned)dmin);  // log2 of the run period 64 dmin
-        static_assert(kRunKeys == 64 && kStepKeys == 64, "one run per step");
-        run0 = lo >> rsh;
-        if ((lo & ((1 << rsh) - 1)) >= kRunKeys) ++run0;  // lo falls between runs
-        const int nsteps = max(0, ((hi - 1) >> rsh) - run0 + 1);
+        msh = __builtin_ctz((unsigned)dmin);  // power of two
+        msl = lattice_slot(tile, msh);
+        static_assert(kRunKeys >= 4 && kStepKeys % kRunKeys == 0, "a lane's 4 outputs share a run");
+        e_first = lattice_prefix_sh(lo, msh, msl) & ~(int64_t)(kStepKeys - 1);
+        const int nsteps = (int)((lattice_prefix_sh(hi, msh, msl) - e_first + kStepKeys - 1) / kStepKeys);
         // With few tiles the lattice is split over a.sample_split workgroups
         // (the chunk index is the part).
         const int per = (nsteps + a.sample_split - 1) / a.sample_split;
@@ -882,7 +884,9 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     // the tile's runs whose step index is a multiple of dn; a key's slot in
     // the row's sample is its lattice rank within the window.
     const int dn = s_d[n];                       // power of two
-    const int64_t rank0 = MODE == kModeSample ? lattice_prefix(rks, dn) : 0;
+    const int dsh = __builtin_ctz((unsigned)dn);
+    const int rsl = MODE == kModeSample ? lattice_slot(tile, dsh) : 0;
+    const int64_t rank0 = MODE == kModeSample ? lattice_prefix_sh(rks, dsh, rsl) : 0;
     uint64_t *ring = s_ring + (MODE == kModeFilter ? wave * kTileQ * RS : 0);
     uint32_t ring_cnt = 0;
 
@@ -909,7 +913,9 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                                                  (LY::frag_byte(kt, 0) - LY::frag_byte(0, 0)));  // compile-time
                 load_kfrag_buf(f[kt], kvr, klane + kofs, soff);
             } else {
-                int p = (MODE == kModeSample) ? ((run0 + j) << rsh) + LY::frag_key(kt, lane) : e;
+                int p = e;
+                if (MODE == kModeSample)
+                    p = (int)min(lattice_key(e_first + e, msh, msl), (int64_t)S - 1);
                 p = min(p, S - 1);
                 if (MODE == kModeDense && !LOOP && a.table) {
                     // paged keys: logical key p is row p % page_size of its
@@ -942,12 +948,16 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 for (int kt = 0; kt < kSub; ++kt)
                     shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(4 * LY::out_base(lane) + 4 * KSTR * kt), soff));
             } else if (MODE == kModeSample) {
-                // The run's keys are consecutive: the factors load like a
-                // scan step's (the run starts below num_kv; the padded
-                // factors cover its last 64 keys).
-                const int rb = ((run0 + j) << rsh) + LY::out_base(lane);
+                // A lane's 4 outputs of a subtile are one run of 4
+                // consecutive keys: one aligned load of the padded factors
+                // (runs past the keys read the padding; their scores are
+                // never kept).
+                const int64_t sal = ((int64_t)S + 3) & ~(int64_t)3;
 #pragma unroll
-                for (int kt = 0; kt < kSub; ++kt) shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + rb + KSTR * kt);
+                for (int kt = 0; kt < kSub; ++kt) {
+                    const int64_t p0 = lattice_key(e_first + sb + KSTR * kt, msh, msl);
+                    shv[kt] = *reinterpret_cast<const v4f *>(a.sigh + min(p0, sal));
+                }
             } else if (own_prep) {
                 // the factor the preparation pass would store: sigma / 2
                 // (FP8) or sigma, 0 past the keys and for a page out of range
@@ -1054,28 +1064,26 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             }
             ring_cnt += direct ? 0u : tot;
         } else if (MODE == kModeSample) {
-            // The lane's 4 outputs of a subtile are consecutive keys of the
-            // run; when the run is on the row's lattice and inside its window
-            // they take consecutive sample slots and go out as one 16-byte
-            // store where aligned.
+            // The lane's 4 outputs of a subtile are one run of the tile's
+            // lattice; when the run is on the row's lattice and inside its
+            // window they take consecutive sample slots and go out as one
+            // 16-byte store where aligned.
             uint32_t *srow = a.samp + (int64_t)(to < 0 ? 0 : to) * a.sample_target;
-            const int rbase = (run0 + j) << rsh;
-            const bool on_row = to >= 0 && (((rbase >> 6) & (dn - 1)) == 0);
-            const int64_t slot0 = lattice_prefix(rbase, dn) - rank0;  // slot of the run's first key
 #pragma unroll
             for (int kt = 0; kt < kSub; ++kt) {
-                const int e0 = LY::out_base(lane) + KSTR * kt;  // key rbase + e0 .. + 3
-                const int p0 = rbase + e0;
-                const int64_t idx0 = slot0 + e0;
-                if (on_row && p0 >= rks && p0 + 3 < rke && (idx0 & 3) == 0 && idx0 + 3 < a.sample_target) {
+                const int64_t p0 = lattice_key(e_first + sb + KSTR * kt, msh, msl);
+                const bool on_row = to >= 0 && ((p0 >> kRunShift) & (dn - 1)) == rsl;
+                if (!on_row) continue;
+                const int64_t idx0 = lattice_prefix_sh(p0, dsh, rsl) - rank0;
+                if (p0 >= rks && p0 + 3 < rke && (idx0 & 3) == 0 && idx0 + 3 < a.sample_target) {
                     v4i v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = (int)ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
                     *reinterpret_cast<v4i *>(srow + idx0) = v;
-                } else if (on_row) {
+                } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int p = p0 + i;
+                        const int64_t p = p0 + i;
                         if (p < rks || p >= rke || idx0 + i >= a.sample_target) continue;
                         srow[idx0 + i] = ord_of(score_of<DT>(o, kt, i, shv[kt][i]));
                     }

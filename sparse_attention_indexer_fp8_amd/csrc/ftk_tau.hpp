@@ -260,6 +260,7 @@ struct TauArgs {
     const uint32_t *samp;      // [num_q, sample_target] sample score codes
     int sample_target;
     int sample_min_stride;
+    int pair;                  // 64-head rows: two tile columns per row
     float rank_scale;          // multiplies the rank of the threshold
     float *tau;                // [num_q]
     uint32_t *cnt;             // [num_q] candidate counters, reset here
@@ -283,7 +284,9 @@ __global__ __launch_bounds__(64 * kTauWaves) void k_tau(TauArgs a)
     float tv = -__builtin_inff();
     if (len > a.cap) {
         const int d = sample_stride(len, a.sample_target, a.sample_min_stride);
-        const int ns = (int)min(lattice_count(lo, hi, d), (int64_t)a.sample_target);
+        const int dsh = __builtin_ctz((unsigned)d);
+        const int64_t tile = (t << a.pair) / 16;  // the sample kernel's tile of the row's first column
+        const int ns = (int)min(lattice_count(lo, hi, dsh, lattice_slot(tile, dsh)), (int64_t)a.sample_target);
         tv = wave_tau(a.samp + t * a.sample_target, ns, tau_rank(a.topk, ns, len, a.rank_scale), s_hist[wave], lane);
     }
     if (lane == 0) a.tau[t] = tv;

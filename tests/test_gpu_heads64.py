@@ -1,5 +1,5 @@
-"""Indexers with 64 heads (FlashTopK README, "Roadmap": other head counts,
-such as the 64 heads of DeepSeek-V3.2).  Each row's two 32-head halves are
+"""Indexers with 64 heads (FlashTopK README, "Roadmap": head counts besides
+32, with 64 as the named case).  Each row's two 32-head halves are
 neighbouring tile columns whose head sums are added before the threshold.
 
 Integer data bit-exact against the oracle (which takes the head count from

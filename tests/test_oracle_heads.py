@@ -1,6 +1,7 @@
 """Pins of the oracle for indexers with 64 heads (FlashTopK README,
-"Roadmap": other head counts, such as the 64 heads of DeepSeek-V3.2; the
-score keeps its definition with the head sum running over all heads).
+"Roadmap": indexers with a head count other than 32, 64 being the case
+named there; the score keeps its definition with the head sum running over
+all heads).
 
 * The numpy twin (an independent formulation whose head count comes from
   the operand shapes) agrees on random 64-head inputs.
