@@ -42,6 +42,7 @@
 
 #include "flashtopk.h"
 #include "ftk_bound.hpp"
+#include "ftk_dec.hpp"
 #include "ftk_paged.hpp"
 #include "ftk_rows.hpp"
 #include "ftk_score.hpp"
@@ -471,7 +472,14 @@ int run_dense(Workspace &w, const void *q, const void *kv, const float *kv_scale
         sa.ntiles = (int)(((nb << ps) + kTileQ - 1) / kTileQ);
         sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves, kMinDenseChunk);
         const int nch = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
-        launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * nch)), stream, sa);
+        if (nb <= kDecRows && !ps && !p.table) {
+            // A few rows: their heads on the MFMA's N dimension (same bits).
+            const unsigned grid = (unsigned)std::max<int64_t>(1, ((S + kStepKeys - 1) / kStepKeys + kDecWaves - 1) / kDecWaves);
+            if (p.dtype == FLASHTOPK_FP8_E4M3) k_score_dec<kFP8><<<grid, 64 * kDecWaves, 0, stream>>>(sa);
+            else k_score_dec<kBF16><<<grid, 64 * kDecWaves, 0, stream>>>(sa);
+        } else {
+            launch_score_dt(p.dtype, kModeDense, dim3((unsigned)(sa.ntiles * nch)), stream, sa);
+        }
 
         RowsArgs ra{};
         ra.x = w.scratch.ptr;
