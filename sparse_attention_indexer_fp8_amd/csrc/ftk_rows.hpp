@@ -156,13 +156,19 @@ __device__ __forceinline__ void load_group(v4i (&raw)[U], const T *row, int64_t 
 // sample extremes, largest first; tau is one bucket below the lower edge of
 // the bucket holding the r-th largest sample, so at least r samples reach
 // it whatever the rounding.  r = ceil(target * samples / n).
-// About three times topk entries should reach the threshold, but no more
-// than halfway from topk to the LDS capacity: a sample rank of a few dozen
-// then misses both bounds (fewer than topk, more than the capacity) only in
-// rows far from independent values, and those take the slower exact path.
-__device__ __forceinline__ uint32_t rows_target(uint32_t k, uint32_t cap)
+// The count of entries reaching the r-th largest of ns samples of n entries
+// is about r n / ns, with a relative spread of about 1 / sqrt(r) for
+// independent values; the target t keeps topk four spreads below it
+// (t - 4 sqrt(t n / ns) >= topk), but at most three times topk and no more
+// than halfway from topk to the LDS capacity: rows far from independent
+// values that miss both bounds (fewer than topk, more than the capacity)
+// take the slower exact path.
+__device__ __forceinline__ uint32_t rows_target(uint32_t k, uint32_t cap, uint32_t ns, int64_t n)
 {
-    return min(3u * k, k + (cap - k) / 2u);
+    const float m = ns > 0 ? (float)n / (float)ns : 1.0f;
+    const float s = 2.0f * sqrtf(m) + sqrtf(4.0f * m + (float)k);
+    const uint32_t t = (uint32_t)fminf(s * s + 1.0f, 4.0e9f);
+    return min(min(max(t, k + 1u), 3u * k), k + (cap - k) / 2u);
 }
 
 // The sample: 64 runs of 128 bytes, run j starting at line floor(j lines / 64)
@@ -188,7 +194,7 @@ __device__ __forceinline__ v4i sample_load(const T *row, int64_t n, int t)
 }
 
 template <typename T, typename SH>
-__device__ float rows_sample_tau(RowsLds<SH> &L, const v4i &raw, int64_t n, uint32_t target)
+__device__ float rows_sample_tau(RowsLds<SH> &L, const v4i &raw, int64_t n, uint32_t k)
 {
     constexpr int NT = SH::nt, V = 16 / sizeof(T), NW = NT / 64;
     constexpr int BPT = kRowsTauBuckets / NT;
@@ -239,6 +245,7 @@ __device__ float rows_sample_tau(RowsLds<SH> &L, const v4i &raw, int64_t n, uint
     const bool spread = any && hi > lo && __builtin_isfinite(scale) && scale > 0.0f;
     __syncthreads();  // the reductions are read before the prefix reuses redu
     if (!spread) return any && !(hi > lo) ? lo : -__builtin_inff();  // degenerate sample: let the count decide
+    const uint32_t target = rows_target(k, SH::cap, ns, n);
     const uint32_t r = (uint32_t)min(max(ceil((double)target * (double)ns / (double)n), 1.0), (double)ns);
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(64 * kRowsTauWaves) void k_rows_tau(RowsArgs a)
     if (!(any && hi > lo && __builtin_isfinite(scale) && scale > 0.0f)) {
         tau = any && !(hi > lo) ? lo : -__builtin_inff();
     } else {
-        const uint32_t rk = (uint32_t)min(max(ceil((double)rows_target(k, SH::cap) * (double)ns / (double)n), 1.0),
+        const uint32_t rk = (uint32_t)min(max(ceil((double)rows_target(k, SH::cap, ns, n) * (double)ns / (double)n), 1.0),
                                           (double)ns);
 #pragma unroll
         for (int q = 0; q < PER; ++q) hist[lane + 64 * q] = 0u;
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(LOOP ? 4
     load_group<T, NT, U>(first, row, n, 0);  // in flight while the sample is read
     if (!PRE_TAU && n > SH::cap) {
         const v4i smp = sample_load(row, n, tid);
-        tau = rows_sample_tau<T, SH>(L, smp, n, rows_target(k, SH::cap));
+        tau = rows_sample_tau<T, SH>(L, smp, n, k);
     }
     uint32_t m = rows_gather<T, SH, U>(L, first, row, n, tau, nan);
     if (m < k || m > (uint32_t)SH::cap) m = rows_digit_gather<T, SH>(L, row, n, k, nan);
@@ -666,7 +673,7 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
     load_group<T, NT, U>(first, row + s0, s1 - s0, 0);  // in flight while the sample is read
     if (n > CAP) {
         const v4i smp = sample_load(row, n, tid);
-        tau = rows_sample_tau<T, SH>(L, smp, n, rows_target(k, CAP));
+        tau = rows_sample_tau<T, SH>(L, smp, n, k);
     }
     const uint32_t m = rows_gather<T, SH, U>(L, first, row + s0, s1 - s0, tau, nan, s0);
     if (a.nan_flag && __any(nan) && (tid & 63) == 0) atomicOr(a.nan_flag, 1);
