@@ -692,8 +692,10 @@ __global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) voi
             if (base + i < (uint32_t)CAP) sp.cand[r * CAP + base + i] = L.cand[i];
 }
 
+// One workgroup per row and few rows: occupancy does not matter, so the
+// merge keeps its registers (no spill to scratch).
 template <typename T, typename SH>
-__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(8))) void k_topk_rows_merge(RowsArgs a,
+__global__ __launch_bounds__(SH::nt) __attribute__((amdgpu_waves_per_eu(SH::nt / 256))) void k_topk_rows_merge(RowsArgs a,
                                                                                                    RowsSplit sp)
 {
     constexpr int NT = SH::nt, CAP = SH::cap;
