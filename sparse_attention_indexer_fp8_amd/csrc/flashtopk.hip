@@ -602,8 +602,12 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
     }
 
     // The sample kernel sets the thresholds itself when each row's samples
-    // come from one workgroup per tile; otherwise k_tau follows it.
-    const bool fused_tau = sa.sample_split == 1;
+    // come from one workgroup per tile and the tiles fit one round of
+    // workgroups (the thresholds then add to the one round's span only);
+    // with more tiles, k_tau follows it, so that each round of sample
+    // workgroups ends without the thresholds on its critical path.
+    const bool fused_tau = sa.sample_split == 1 && (int64_t)ntiles * sa.sample_split <= num_cu();
+    sa.tau_in_sample = fused_tau ? 1 : 0;
     sa.topk = p.topk;
     sa.rank_scale = p.rank_scale;
     sa.tau_w = (float *)w.tau.ptr;

@@ -103,6 +103,7 @@ struct ScoreArgs {
     int sample_target;
     int sample_min_stride;     // power of two, see sample_stride
     int sample_split;          // workgroups per tile in sample mode
+    int tau_in_sample;         // sample mode, one workgroup per tile: it also sets the thresholds
     // dense mode: batch entry e (e < row_limit) is entry row_base + e of the
     // flagged-row list (present while below *nrows), or, with no list, row
     // row_base + e (present while below nrows_direct)
@@ -592,7 +593,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     static_assert(MODE != kModeSample || QB >= kWaves * kTauBuckets * 4, "histograms fit the q tile");
     auto finish = [&]() {
         if constexpr (MODE == kModeSample)
-            if (a.sample_split == 1) tile_tau<kWaves, PAIR>(a, tile, reinterpret_cast<uint32_t *>(s_q), s_row, s_ks, s_ke, s_nl);
+            if (a.tau_in_sample) tile_tau<kWaves, PAIR>(a, tile, reinterpret_cast<uint32_t *>(s_q), s_row, s_ks, s_ke, s_nl);
     };
 
     if (threadIdx.x < kTileQ) {

@@ -268,8 +268,9 @@ struct TauArgs {
 
 // One wave per row: resets the row's candidate counter and sets its
 // threshold (-inf for rows that take their whole window).  Used when the
-// sample scores of a tile come from several workgroups (with one, the
-// sample kernel sets the thresholds itself).
+// sample scores of a tile come from several workgroups, or when the tiles
+// take more than one round of sample workgroups (otherwise the sample
+// kernel sets the thresholds itself).
 constexpr int kTauWaves = 4;
 
 __global__ __launch_bounds__(64 * kTauWaves) void k_tau(TauArgs a)
