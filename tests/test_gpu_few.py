@@ -113,7 +113,7 @@ def _rows_of(wl, rows):
 
 @pytest.mark.parametrize("dt,maker", [("fp8", "gaussian"), ("bf16", "gaussian"), ("fp8", "trained")])
 def test_row_bits_do_not_depend_on_the_call(dt, maker):
-    # The same rows scored in calls of 1, 5, 17 and 300 rows, on the dense and
+    # The same rows scored in calls of 1, 3, 4, 5, 17 and 300 rows, on the dense and
     # the fused path, give the same bits (Gaussian data: the scores are not
     # exact, so this checks that every path runs the same arithmetic).
     _say("batch invariance", dt, maker)
@@ -125,7 +125,7 @@ def test_row_bits_do_not_depend_on_the_call(dt, maker):
     big = run_gpu(wl, options=opts(path=FUSED))
     big_dense = run_gpu(wl, options=opts(path=RECOVER))
     assert _same(big, big_dense)
-    for rows in ([123], [0, 7, 150, 298, 299], list(range(40, 57))):
+    for rows in ([123], [2, 150, 299], [10, 11, 12, 13], [0, 7, 150, 298, 299], list(range(40, 57))):
         sub = _rows_of(wl, np.asarray(rows))
         for path in (0, FUSED, RECOVER):
             got = run_gpu(sub, options=opts(path=path))
