@@ -21,7 +21,7 @@ constexpr int kTileQ = 16;
 constexpr int kSub = 4;
 constexpr int kStepKeys = 16 * kSub;      // 64 keys per wave step
 constexpr int kMinChunk = 1024;
-constexpr int kMaxChunk = 32768;
+constexpr int kMaxChunk = 131072;
 
 constexpr int kFP8 = 0;
 constexpr int kBF16 = 1;

@@ -553,7 +553,6 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     // Filter mode with pruning: offsets (from jlo) of the steps whose block
     // is not skipped, in order.
     constexpr int kMaxSteps = kMaxChunk / kStepKeys;
-    static_assert(MODE != kModeFilter || 64 * kWaves >= kMaxSteps, "one thread per step");
     __shared__ uint16_t s_steps[MODE == kModeFilter ? kMaxSteps : 1];
     __shared__ uint16_t s_skip[MODE == kModeFilter ? kMaxSteps / 16 + 1 : 1];  // per 16-block group
     __shared__ int s_wcnt[kWaves];
@@ -856,24 +855,28 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         if (ln == 0 && pr) atomicAdd(a.plan + kPlanPruned, pr);
         if (threadIdx.x == 0) atomicAdd(a.plan + kPlanItems, 1ull);
         __syncthreads();
-        // Order-preserving compaction of the steps that are not skipped.
-        const int i = threadIdx.x;
-        bool keep = false;
-        if (i < nstep) {
-            const int j = jlo + i;
-            keep = !((s_skip[(j >> 4) - c0] >> (j & 15)) & 1u);
+        // Order-preserving compaction of the steps that are not skipped, one
+        // step per thread and round.
+        int total = 0;
+        for (int r0 = 0; r0 < nstep; r0 += 64 * kWaves) {
+            const int i = r0 + threadIdx.x;
+            bool keep = false;
+            if (i < nstep) {
+                const int j = jlo + i;
+                keep = !((s_skip[(j >> 4) - c0] >> (j & 15)) & 1u);
+            }
+            const unsigned long long bal = __ballot(keep);
+            if (ln == 0) s_wcnt[wv] = __popcll(bal);
+            __syncthreads();
+            int base = total;
+            for (int v = 0; v < kWaves; ++v) {
+                base += v < wv ? s_wcnt[v] : 0;
+                total += s_wcnt[v];
+            }
+            if (keep) s_steps[base + __popcll(bal & ((1ull << ln) - 1ull))] = (uint16_t)i;
+            __syncthreads();  // s_wcnt is read before the next round writes it
         }
-        const unsigned long long bal = __ballot(keep);
-        if (ln == 0) s_wcnt[wv] = __popcll(bal);
-        __syncthreads();
-        int base = 0, total = 0;
-        for (int v = 0; v < kWaves; ++v) {
-            base += v < wv ? s_wcnt[v] : 0;
-            total += s_wcnt[v];
-        }
-        if (keep) s_steps[base + __popcll(bal & ((1ull << ln) - 1ull))] = (uint16_t)i;
         nstep = __builtin_amdgcn_readfirstlane(total);
-        __syncthreads();
     }
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
