@@ -9,7 +9,9 @@ checked against the oracle (MI355X only).
   (the dense path: every row's scores materialised, each row's selection
   split over several workgroups), and the 64-row shape forced through the
   fused path (each tile's sample split over many workgroups);
-* the integer-valued twins of all of them, checked bit-exact.
+* the integer-valued twins of all of them, checked bit-exact;
+* block-local integer keys at the headline's size on the pruned scan (FP8
+  auto, BF16 forced), bit-exact.
 Rows checked against the oracle: every 16th row, the first and the last 64
 rows, every row the call rescored densely, and (packed) the rows around
 every document start and the short-window boundaries; decode shapes on
@@ -129,3 +131,33 @@ def test_many_rows_mixed_windows():
                                      rng.choice(20001, size=24, replace=False)])).astype(np.int64)
     rep = parity(wl, idx, val, "exact", rows=rows)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("dt", ["fp8", "bf16"])
+def test_full_size_block_local_parity(dt):
+    # Block-local integer keys at the headline's size: the scan's work items
+    # hold whole windows (up to 2048 key steps), so the step-list compaction
+    # of the pruned scan runs several rounds per thread.  FP8 takes the auto
+    # path (its planner picks pruning), BF16 is forced onto it.
+    import sparse_attention_indexer_fp8_amd as ftk
+
+    from gpu_util import opts
+
+    name = f"blocky_int_{dt}_4096x131072_k2048"
+    print("case", name, flush=True)
+    wl = workloads.blocky(4096, 131072, 2048, dt, 610 if dt == "fp8" else 611, exact=True, name=name)
+    idx, val = run_gpu(wl, options=None if dt == "fp8" else opts(path=2))
+    info = ftk.flashtopk_get_last_info()
+    recovered = ftk.flashtopk_get_last_recovered()
+    print("info", info, flush=True)
+    assert info["path"] == ftk.PATH_PRUNE, info
+    assert info["pruned_keys"] > info["window_keys"] // 4, info
+    _check_row_classes(wl, info)
+    rows = _rows(wl, (), recovered)
+    print("oracle rows", len(rows), flush=True)
+    rep = parity(wl, idx, val, "exact", rows=rows)
+    assert rep["ok"], rep
+    import checker
+
+    for t in range(wl["q"].shape[0]):
+        assert not checker.structure_failures(idx[t], val[t], wl["ks"][t], wl["ke"][t], wl["topk"]), t
