@@ -10,9 +10,11 @@
 //                       and (FP8) head-weighted query sums split into FP8
 //                       parts, in one launch; clears the call's counters
 //   1. k_score<sample>  strided-sample scores of every long row     (MFMA);
-//                       with one workgroup per tile it also sets the
-//                       tile's per-row thresholds from those samples
-//   2. k_tau            (several workgroups per tile) the thresholds
+//                       with one workgroup per tile and at most one round
+//                       of workgroups it also sets the tile's per-row
+//                       thresholds from those samples
+//   2. k_tau            the thresholds otherwise (several workgroups per
+//                       tile, or more tiles than compute units)
 //   3. k_score<filter>  fused score (+ bound) + threshold filter -> candidates (MFMA, hot)
 //   4. k_select         triage (flagged rows go to a list on the device) and
 //                       the exact top-k of every other row
@@ -22,8 +24,9 @@
 //                       rows past the list's device-side length exit)
 //
 // Dense path (calls of few rows, and the forced recover-all path): every
-// row's window scores are materialised (k_score<dense>, computing its own
-// query sums and scale factors) and the row top-k kernels select from them;
+// row's window scores are materialised (k_score_dec for at most 4 rows,
+// otherwise k_score<dense>; both compute their own query sums and scale
+// factors) and the row top-k kernels select from them;
 // with few rows each row is split over several workgroups.
 //
 // Both paths score a (row, key) pair with the same instruction sequence, so

@@ -477,10 +477,11 @@ __device__ __forceinline__ void ring_flush(const uint64_t *ring, uint32_t ring_c
 
 // ---------------------------------------------------------------------------
 
-// Sample mode with one workgroup per tile (sample_split == 1), after the
-// workgroup's samples are written: it sets the threshold of each of the
-// tile's rows from the row's samples, one wave per row (wave_tau), and
-// resets the row's candidate counter.  The samples were written by this
+// Sample mode with one workgroup per tile (sample_split == 1) and the
+// thresholds asked of it (tau_in_sample), after the workgroup's samples are
+// written: it sets the threshold of each of the tile's rows from the row's
+// samples, each wave taking its rows together (wave_tau_rows), and resets
+// the row's candidate counter.  The samples were written by this
 // workgroup's own waves, so workgroup-scope ordering is all it needs (an
 // agent-scope fence would write back and invalidate the L2 and cost more
 // than the thresholds).  hist: NW * kTauBuckets words of LDS that nothing
