@@ -53,6 +53,12 @@ namespace ftk {
 
 constexpr int kBlockKeys = kStepKeys;   // keys per bound block
 constexpr int kPlanGroups = 2;          // 16-block groups of each tile in the planner sample
+// The auto path evaluates the planner sample only for tiles whose sampled
+// rows' windows span at least this many keys: the sample costs the same for
+// every tile, while what pruning can save grows with the window, and below
+// about eight times the sample's 2048 keys a tile's scan is cheap anyway.
+// Other tiles are scanned (their planner entries read as not prunable).
+constexpr int kPlanMinKeys = 16384;
 
 // ---------------------------------------------------------------------------
 // Per-key pass: the scale factor of the scoring kernels (sigh, see sigh_of)

@@ -732,7 +732,9 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
 
     int nstep = jhi - jlo;
     bool use_skip = false;  // workgroup-uniform
-    if (MODE == kModeSample && DT == kBF16 && a.prune) {
+    // Auto path: does this tile evaluate the planner sample (sample mode)?
+    const bool plan = MODE == kModeSample && a.prune == 1 && hi > lo && hi - lo >= kPlanMinKeys;
+    if (MODE == kModeSample && DT == kBF16 && (a.prune == 2 || plan)) {
         // Q1[t] = sum_h |w[t,h]| ||q[t,h,:]||_1 of the sampled rows (the
         // bound's rounding margin), from the q tile in LDS: one (row, head)
         // per thread, then one thread per row.
@@ -766,7 +768,14 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         }
         __syncthreads();
     }
-    if (MODE == kModeSample && a.prune == 1 && threadIdx.x < 64 * kPlanGroups) {
+    if (MODE == kModeSample && a.prune == 1 && !plan && threadIdx.x < 64 * kPlanGroups) {
+        // a tile of short windows: its entries read as not prunable
+        const int ln = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int n = ln & 15, g = ln >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.vplan[(((int64_t)tile * kPlanGroups + wv) * 16 + 4 * g + i) * 16 + n] = __builtin_inff();
+    }
+    if (MODE == kModeSample && plan && threadIdx.x < 64 * kPlanGroups) {
         // Planner sample: the skip test's left side for kPlanGroups groups
         // spread over the union of ALL the tile's windows (take-all rows
         // included: they can never be skipped, value +inf).
