@@ -126,29 +126,23 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // Lane l owns buckets [PER l, PER l + PER); exclusive prefix over lanes.
-    uint32_t c[PER], run = 0;
+    // The counts are read twice from LDS rather than held in registers (more
+    // waves fit per SIMD).
+    uint32_t run = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        c[q] = hist[lane * PER + q];
-        run += c[q];
-    }
-    uint32_t x = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    uint32_t base = x - run;
+    for (int q = 0; q < PER; ++q) run += hist[lane * PER + q];
+    uint32_t base = wave_incl_add(run) - run;
     int b = -1;
     uint32_t above = 0, cb = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-        if (base < r && r <= base + c[q]) {
+        const uint32_t cq = hist[lane * PER + q];
+        if (base < r && r <= base + cq) {
             b = lane * PER + q;
             above = base;
-            cb = c[q];
+            cb = cq;
         }
-        base += c[q];
+        base += cq;
     }
     const uint64_t hit = __ballot(b >= 0);
     const int src = hit ? __builtin_ctzll(hit) : 0;
@@ -273,7 +267,7 @@ struct TauArgs {
 // kernel sets the thresholds itself).
 constexpr int kTauWaves = 4;
 
-__global__ __launch_bounds__(64 * kTauWaves) void k_tau(TauArgs a)
+__global__ __launch_bounds__(64 * kTauWaves) __attribute__((amdgpu_waves_per_eu(5))) void k_tau(TauArgs a)
 {
     __shared__ uint32_t s_hist[kTauWaves][kTauBuckets];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
