@@ -261,8 +261,11 @@ int chunk_keys(int ntiles, int64_t S, int waves, int min_chunk = kMinChunk)
     for (int chunk = kMaxChunk; chunk >= min_chunk; chunk >>= 1) {
         const int64_t items = (int64_t)ntiles * ((S + chunk - 1) / chunk);
         const int64_t rounds = (items + n_cu - 1) / n_cu;
-        const int64_t steps = (chunk / kStepKeys + waves - 1) / waves;
-        const int64_t cost = rounds * (1 + steps);
+        // in 1 / waves of a wave step (the fixed part is `waves` of them):
+        // an item's steps count exactly, not rounded up to whole steps per
+        // wave, so of two chunks that both give each wave at most one step
+        // the smaller one, on twice the compute units, wins
+        const int64_t cost = rounds * (waves + chunk / kStepKeys);
         if (cost < best_cost) {
             best_cost = cost;
             best = chunk;
@@ -473,7 +476,10 @@ int run_dense(Workspace &w, const void *q, const void *kv, const float *kv_scale
         sa.wlen = (int32_t *)w.wlen.ptr;
         sa.own_prep = 1;
         sa.ntiles = (int)(((nb << ps) + kTileQ - 1) / kTileQ);
-        sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves, kMinDenseChunk);
+        sa.chunk = chunk_keys(sa.ntiles, S,
+                              p.dtype == FLASHTOPK_FP8_E4M3 ? ScoreCfg<kFP8, kModeDense>::waves
+                                                            : ScoreCfg<kBF16, kModeDense>::waves,
+                              kMinDenseChunk);
         const int nch = (int)std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
         if (nb <= kDecRows && !ps && !p.table) {
             // A few rows: their heads on the MFMA's N dimension (same bits).
@@ -702,7 +708,7 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
         sa.scratch = (float *)w.scratch.ptr;
         sa.scratch_stride = stride;
         sa.ntiles = (int)((rcap << ps) / kTileQ);
-        sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense>::waves);
+        sa.chunk = chunk_keys(sa.ntiles, S, ScoreCfg<kFP8, kModeDense, true>::waves);
         // the work items loop over one workgroup per compute unit: a batch
         // with nothing flagged costs one short launch
         const int64_t items = (int64_t)sa.ntiles * std::max<int64_t>(1, (S + sa.chunk - 1) / sa.chunk);
