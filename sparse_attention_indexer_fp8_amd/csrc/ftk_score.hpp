@@ -70,12 +70,15 @@ template <int DT> struct TileHeads { static constexpr int value = DT == kFP8 ? k
 //   scan's 16-wave shape (122 VGPRs, no candidate rings): 4 waves per SIMD
 //   instead of 2 scored the 64-row decode call 10 % faster and the
 //   recover-all path of the 4096 x 131072 chunk in 2.4 ms instead of 4.3.
-//   The looping dense form (recovery, LOOP) runs 4 waves, so each may hold
-//   512 registers (the loop's state pushed the 8-wave form past 256 into
-//   scratch memory, and the 16-wave form past 128), with one fragment set.
+//   The looping dense form (recovery, LOOP) runs 8 waves with one fragment
+//   set.  For FP8 the loop's state pushes it 36 bytes per lane past 256
+//   registers into scratch memory, and it still recovered every row of the
+//   4096 x 131072 chunk in 4.2 ms against 5.6 ms with 4 waves of 512
+//   registers; BF16 fits (a packed 65536-row sequence with 57344 rows
+//   recovered: 12.5 against 14.2 ms).  The 16-wave form spills 172 bytes.
 template <int DT, int MODE, bool LOOP = false> struct ScoreCfg {
     static constexpr bool wide = DT == kFP8 && (MODE == 0 || (MODE == 2 && !LOOP));  // 0: filter, 2: dense
-    static constexpr int waves = wide ? 16 : (LOOP ? 4 : 8);
+    static constexpr int waves = wide ? 16 : 8;
     static constexpr int ring = DT == kFP8 ? 40 : 24;
     static constexpr bool prefetch = !wide && !LOOP && DT == kFP8;
 };
