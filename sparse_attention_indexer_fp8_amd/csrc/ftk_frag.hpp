@@ -76,10 +76,11 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 }
 
 // Key fragment through a buffer resource: voff is the lane's byte offset of
-// its slice within the key row block, soff the wave's.
+// its slice within the key row block, soff the wave's (plus any offset that
+// is the same for every lane, so the lane offset needs no vector add).
 __device__ __forceinline__ void load_kfrag_buf(KFrag<kFP8> &f, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    const v4i lo = buf_load16(r, voff, soff), hi = buf_load16(r, voff + 16, soff);
+    const v4i lo = buf_load16(r, voff, soff), hi = buf_load16(r, voff, soff + 16);
     f.a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -87,7 +88,7 @@ __device__ __forceinline__ void load_kfrag_buf(KFrag<kBF16> &f, __amdgpu_buffer_
                                                uint32_t soff)
 {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) f.a[m] = buf_load16(r, voff + 16 * m, soff);
+    for (int m = 0; m < 4; ++m) f.a[m] = buf_load16(r, voff, soff + 16 * m);
 }
 
 template <int DT> struct BFrag;

@@ -315,8 +315,9 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     qp += 2 * HB;
     wp += 2 * kTileQ;
     // Loop invariant: qa holds head h's fragment, xa head h-1's results.
-#pragma unroll 1
+#pragma unroll 2
     for (int h = 3; h < kHeads - 1; h += 2) {
+        __builtin_amdgcn_sched_barrier(0);
         const float w0 = wp[0], w1 = wp[kTileQ];
         qb = load_qfrag_fp8(qp + 2 * HB);  // head h + 1
         mfma_fp8_head(xb, kf, qa, z);      // head h
@@ -342,6 +343,7 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     mfma_fp8_head(xb, kf, qa, z);  // head 31
     __builtin_amdgcn_s_setprio(0);
     after_mfma();  // the key fragments are free from here on
@@ -936,7 +938,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 const uint32_t soff = (uint32_t)(j * kStepKeys - kbase) * RB;
                 const uint32_t kofs = (uint32_t)((LY::frag_key(kt, 0) - LY::frag_key(0, 0)) * RB +
                                                  (LY::frag_byte(kt, 0) - LY::frag_byte(0, 0)));  // compile-time
-                load_kfrag_buf(f[kt], kvr, klane + kofs, soff);
+                load_kfrag_buf(f[kt], kvr, klane, soff + kofs);
             } else {
                 int p = e;
                 if (MODE == kModeSample)
@@ -971,7 +973,7 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
                 const uint32_t soff = (uint32_t)(j * kStepKeys - kbase) * 4u;
 #pragma unroll
                 for (int kt = 0; kt < kSub; ++kt)
-                    shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(4 * LY::out_base(lane) + 4 * KSTR * kt), soff));
+                    shv[kt] = __builtin_bit_cast(v4f, buf_load16(shr, (uint32_t)(4 * LY::out_base(lane)), soff + 4u * KSTR * kt));
             } else if (MODE == kModeSample) {
                 // A lane's 4 outputs of a subtile are one run of 4
                 // consecutive keys: one aligned load of the padded factors
