@@ -8,7 +8,11 @@
 // (kTauBuckets buckets between its minimum and maximum, highest first); the
 // bucket that holds the r-th largest sample is found from the histogram, and
 // when it holds at most 64 samples (the usual case) the r-th largest is
-// picked from them exactly.  A denser bucket gives the threshold one bucket
+// picked from them exactly.  When every lane holds a sample and r <= 64, the
+// smallest of the 64 lanes' largest samples is a floor: at least 64 samples
+// reach it, so the r-th largest does too, and only the samples at or above
+// it are bucketed (between it and the maximum), which leaves most samples
+// out of the histogram and spreads the top of the row over all buckets.  A denser bucket gives the threshold one bucket
 // below its lower edge instead: at least r samples reach it, whatever the
 // rounding of the bucket arithmetic.  No threshold changes results -- triage
 // catches any row it misjudges -- only the candidate count.
@@ -24,15 +28,15 @@ constexpr int kTauExactMax = 64;  // largest bucket searched for the exact r-th 
 // The r-th largest of the wave's samples, given the bucket b that holds it:
 // v holds the lane's PER samples (NaN: absent), `above` the samples of the
 // buckets before b and cb those of b (cb <= kTauExactMax), with the same
-// bucket arithmetic (vmax, scale) as the histogram.  buf: kTauExactMax words
+// bucket arithmetic (lo, vmax, scale) as the histogram.  buf: kTauExactMax words
 // of LDS private to the wave.  Every lane returns the value.
 template <int PER>
-__device__ __forceinline__ float tau_exact_in_bucket(const float (&v)[PER], float vmax, float scale, int b,
-                                                     uint32_t above, uint32_t cb, uint32_t r, uint32_t *buf,
+__device__ __forceinline__ float tau_exact_in_bucket(const float (&v)[PER], float lo, float vmax, float scale,
+                                                     int b, uint32_t above, uint32_t cb, uint32_t r, uint32_t *buf,
                                                      int lane)
 {
     auto in_b = [&](float x) {
-        if (!(x == x)) return false;
+        if (!(x >= lo)) return false;  // below the bucketed range (or NaN: absent)
         const float y = (vmax - x) * scale;
         const int bb = y < (float)(kTauBuckets - 1) ? (int)(uint32_t)y : kTauBuckets - 1;
         return bb == b;
@@ -103,12 +107,13 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
             vmax = fmaxf(vmax, v[q]);
         }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-        vmin = fminf(vmin, __shfl_xor(vmin, off));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-    }
-    const float scale = (float)kTauBuckets / (vmax - vmin);
-    if (!(vmax > vmin) || !__builtin_isfinite(scale)) return vmin;  // all samples equal: admit them all
+    // wave extremes through DPP on the order codes (lanes with no sample hold +-inf)
+    const float lmin = float_of_ord(~wave_max(~ord_of(vmax)));  // smallest lane maximum
+    vmax = float_of_ord(wave_max(ord_of(vmax)));
+    vmin = float_of_ord(~wave_max(~ord_of(vmin)));
+    const float lo = (n >= 64 && r <= 64u) ? lmin : vmin;  // floor of the bucketed range
+    const float scale = (float)kTauBuckets / (vmax - lo);
+    if (!(vmax > lo) || !__builtin_isfinite(scale)) return lo;  // samples at the floor equal: admit them all
 #pragma unroll
     for (int q = 0; q < PER; ++q) hist[lane + 64 * q] = 0u;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros land before any lane adds
@@ -117,7 +122,7 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
         if (n > CHUNK) load_chunk(base);  // a single chunk is still in registers
 #pragma unroll
         for (int q = 0; q < PERL; ++q) {
-            if (base + lane + 64 * q < n) {
+            if (v[q] >= lo) {  // NaN fill fails
                 const float x = (vmax - v[q]) * scale;
                 atomicAdd(&hist[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
             }
@@ -151,7 +156,7 @@ __device__ __forceinline__ float wave_tau(const uint32_t *samp, int n, uint32_t 
     cb = __shfl(cb, src);
     if (n <= CHUNK && cb <= (uint32_t)kTauExactMax) {
         __builtin_amdgcn_wave_barrier();  // every lane has read its counts before hist is reused
-        return tau_exact_in_bucket<PERL>(v, vmax, scale, b, above, cb, r, hist, lane);
+        return tau_exact_in_bucket<PERL>(v, lo, vmax, scale, b, above, cb, r, hist, lane);
     }
     return vmax - (float)(b + 2) / scale;
 }
@@ -178,7 +183,7 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
 #pragma unroll
             for (int q = 0; q < PER; ++q) v[k][q] = lane + 64 * q < n[k] ? float_of_ord(u[k][q]) : __builtin_nanf("");
     }
-    float vmin[K], vmax[K];
+    float vmin[K], vmax[K], lo[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         vmin[k] = __builtin_inff();
@@ -191,14 +196,16 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {  // wave extremes through DPP on the order codes (lanes with no sample hold +-inf)
+        const float lmin = float_of_ord(~wave_max(~ord_of(vmax[k])));  // smallest lane maximum
         vmax[k] = float_of_ord(wave_max(ord_of(vmax[k])));
         vmin[k] = float_of_ord(~wave_max(~ord_of(vmin[k])));
+        lo[k] = (n[k] >= 64 && r[k] <= 64u) ? lmin : vmin[k];  // floor of the bucketed range
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const float scale = (float)kTauBuckets / (vmax[k] - vmin[k]);
-        if (!(vmax[k] > vmin[k]) || !__builtin_isfinite(scale)) {  // all samples equal: admit them all
-            tv[k] = vmin[k];
+        const float scale = (float)kTauBuckets / (vmax[k] - lo[k]);
+        if (!(vmax[k] > lo[k]) || !__builtin_isfinite(scale)) {  // samples at the floor equal: admit them all
+            tv[k] = lo[k];
             continue;
         }
 #pragma unroll
@@ -207,7 +214,7 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            if (lane + 64 * q < n[k]) {
+            if (v[k][q] >= lo[k]) {  // NaN fill fails
                 const float x = (vmax[k] - v[k][q]) * scale;
                 atomicAdd(&hist[x < (float)(kTauBuckets - 1) ? (uint32_t)x : (uint32_t)(kTauBuckets - 1)], 1u);
             }
@@ -239,7 +246,7 @@ __device__ __forceinline__ void wave_tau_rows(const uint32_t *const (&samp)[K], 
         above = __shfl(above, src);
         cb = __shfl(cb, src);
         __builtin_amdgcn_wave_barrier();  // every lane has read the counts before hist is reused
-        if (cb <= (uint32_t)kTauExactMax) tv[k] = tau_exact_in_bucket<PER>(v[k], vmax[k], scale, b, above, cb, r[k], hist, lane);
+        if (cb <= (uint32_t)kTauExactMax) tv[k] = tau_exact_in_bucket<PER>(v[k], lo[k], vmax[k], scale, b, above, cb, r[k], hist, lane);
         else tv[k] = vmax[k] - (float)(b + 2) / scale;
         __builtin_amdgcn_wave_barrier();
     }
@@ -270,8 +277,8 @@ constexpr int kTauWaves = 4;
 __global__ __launch_bounds__(64 * kTauWaves) __attribute__((amdgpu_waves_per_eu(5))) void k_tau(TauArgs a)
 {
     __shared__ uint32_t s_hist[kTauWaves][kTauBuckets];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * kTauWaves + wave;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kTauWaves + wave;  // wave-uniform: scalar registers
     if (t >= a.num_q) return;
     const int64_t lo = a.ks[t], hi = a.ke[t];
     const int64_t len = hi > lo ? hi - lo : 0;
