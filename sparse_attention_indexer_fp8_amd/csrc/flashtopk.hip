@@ -576,10 +576,6 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
 
     const int chunk = chunk_keys(ntiles, S, fp8 ? ScoreCfg<kFP8, kModeFilter>::waves : ScoreCfg<kBF16, kModeFilter>::waves);
     const int nchunks = (int)std::max<int64_t>(1, (S + chunk - 1) / chunk);
-    // One long item per tile and between half and one round of tiles: two
-    // half-tile items each (see k_score), which balances the units' work
-    // when the tiles' windows differ in length.
-    const bool halves = nchunks == 1 && S >= kHalvesMinKeys && ntiles <= num_cu() && 2 * (int64_t)ntiles > num_cu();
 
     ScoreArgs sa{};
     sa.q = (const uint8_t *)q;
@@ -596,7 +592,6 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
     sa.qscale = (const float *)w.qscale.ptr;
     sa.ntiles = ntiles;
     sa.chunk = chunk;
-    sa.halves = halves ? 1 : 0;
     sa.cap = p.cap;
     sa.tau = (const float *)w.tau.ptr;
     sa.cnt = (uint32_t *)w.cnt.ptr;
@@ -677,7 +672,7 @@ int run_fused(Workspace &w, const void *q, const void *kv, const float *kv_scale
     }
     mark(w, p, 2, stream);
 
-    launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * (sa.halves ? 2 : nchunks))), stream, sa);
+    launch_score_dt(p.dtype, kModeFilter, dim3((unsigned)(ntiles * nchunks)), stream, sa);
     mark(w, p, 3, stream);
 
     SelectArgs se{};

@@ -22,7 +22,6 @@ constexpr int kSub = 4;
 constexpr int kStepKeys = 16 * kSub;      // 64 keys per wave step
 constexpr int kMinChunk = 1024;
 constexpr int kMaxChunk = 131072;
-constexpr int kHalvesMinKeys = 32768;  // shortest key set split into half-tile items
 
 constexpr int kFP8 = 0;
 constexpr int kBF16 = 1;

@@ -148,7 +148,6 @@ struct ScoreArgs {
     const int32_t *table;      // [ceil(num_kv / page_size)] page ids, or null (contiguous keys)
     int page_size;
     int64_t num_pages;
-    int halves;                // filter mode: each tile's steps split at their midpoint into two items
 };
 
 // LDS layout of the q tile: for head h, the 64 lanes' fragments are stored as
@@ -706,18 +705,6 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             finish();
             return;
         }
-    } else if (MODE == kModeFilter && a.halves) {
-        // Two items per tile, each half of its steps: the grid's first round
-        // runs one half of every tile (longest tiles first), and the compute
-        // unit that finishes first takes the longest remaining half, so each
-        // unit's two halves add up to about the mean tile (causal windows
-        // grow row by row: whole tiles would leave the units of the shorter
-        // tiles idle while the longest finishes).
-        const int j0 = lo / kStepKeys, j1 = (hi + kStepKeys - 1) / kStepKeys;
-        const int jm = j0 + (j1 - j0) / 2;
-        jlo = chunk == 0 ? j0 : jm;
-        jhi = chunk == 0 ? jm : j1;
-        if (jhi <= jlo) return;
     } else {
         const int64_t c0 = (int64_t)chunk * a.chunk;
         const int64_t klo = max((int64_t)lo, c0), khi = min((int64_t)hi, c0 + a.chunk);
