@@ -310,6 +310,19 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": round(m["achieved_tflops"] / peak, 4),
                      "traffic": traffic, "flops_per_launch": m["flops"]},
     }
+    # The attainable rate of the same instruction on this GPU: a register-only
+    # MFMA throughput kernel (flashtopk_probe_mfma), timed after the steps.
+    probes = {}
+
+    def attainable(dtype):
+        if dtype not in probes:
+            probes[dtype] = ftk.flashtopk_probe_mfma(ftk.FLASHTOPK_FP8_E4M3 if dtype == "fp8" else ftk.FLASHTOPK_BF16,
+                                                     PROBE_ITERS)
+        return probes[dtype]
+
+    att = attainable(dt)
+    out["roofline"]["attainable"] = round(att, 1)
+    out["roofline"]["frac_of_attainable"] = round(m["achieved_tflops"] / att, 4) if att > 0 else None
     others = {}
     for n in [int(x) for x in args.also.split(",") if x.strip()]:
         if n == args.workload:
@@ -322,6 +335,7 @@ def main():
         others[owl["name"]]["ms"] = round(om["ms"], 4)
         others[owl["name"]]["roofline_frac"] = round(om["achieved_tflops"] / PEAK_TFLOPS[om["dtype"]], 4)
         others[owl["name"]]["peak_tflops"] = PEAK_TFLOPS[om["dtype"]]
+        others[owl["name"]]["attainable_tflops"] = round(attainable(om["dtype"]), 1)
         del owl
     if others:
         out["other_workloads"] = others
@@ -332,6 +346,7 @@ def main():
 
 
 PATH_NAMES = {0: "auto", 1: "scan", 2: "prune", 3: "dense", 4: "fused"}
+PROBE_ITERS = 400000  # about 0.1 s of matrix-core work per probe launch
 
 
 def measure(wl, args, full):

@@ -304,6 +304,20 @@ int flashtopk_select_noalloc(const void *q, const void *kv, const float *kv_scal
                              int64_t num_q, int64_t num_kv, int dtype, int topk,
                              void *out_idx, float *out_val, void *stream);
 
+/* Diagnostic: the attainable throughput of the scan's matrix-core
+ * instruction on the stream's device under sustained load, in TFLOP/s
+ * (dense, 2 FLOPs per multiply-add), written to *tflops.  dtype picks the
+ * instruction: FLASHTOPK_FP8_E4M3, v_mfma_f32_16x16x128_f8f6f4 on E4M3
+ * operands; FLASHTOPK_BF16, v_mfma_f32_32x32x16_bf16.  Four workgroups of
+ * four waves per compute unit each issue iters rounds of four independent
+ * accumulation chains on register operands (fixed per-lane pseudo-random
+ * finite codes), with no memory traffic; one warm-up launch of iters / 8
+ * rounds precedes the timed launch, which is timed with HIP events on
+ * `stream`.  Synchronises the stream; allocates no device memory.
+ * FLASHTOPK_ERR_INVALID_ARGUMENT for a NULL tflops, iters <= 0 or another
+ * dtype. */
+int flashtopk_probe_mfma(int dtype, int iters, void *stream, double *tflops);
+
 /* Frees every cached workspace.  No call may be in flight. */
 void flashtopk_release(void);
 

@@ -94,7 +94,7 @@ class Info(ctypes.Structure):
 # Every symbol include/flashtopk.h declares.
 EXPORTS = ("flashtopk_select", "flashtopk_select_ex", "flashtopk_select_paged", "flashtopk_select_noalloc",
            "flashtopk_topk_rows", "flashtopk_reserve", "flashtopk_get_last_info", "flashtopk_get_last_recovered",
-           "flashtopk_release", "flashtopk_status_string", "flashtopk_version")
+           "flashtopk_release", "flashtopk_status_string", "flashtopk_version", "flashtopk_probe_mfma")
 
 _lib = None
 
@@ -106,6 +106,9 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+    # torch first: the library then binds to the HIP runtime torch has loaded,
+    # so the process holds one runtime whichever call comes first.
+    _torch()
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sel = [P, P, P, P, P, P, I64, I64, I, I, P, P, P]
@@ -132,6 +135,8 @@ def load_library():
     lib.flashtopk_status_string.restype = ctypes.c_char_p
     lib.flashtopk_version.argtypes = []
     lib.flashtopk_version.restype = I
+    lib.flashtopk_probe_mfma.argtypes = [I, I, P, ctypes.POINTER(ctypes.c_double)]
+    lib.flashtopk_probe_mfma.restype = I
     _lib = lib
     return lib
 
@@ -372,6 +377,18 @@ def flashtopk_status_string(status: int) -> str:
 
 def flashtopk_version() -> int:
     return int(load_library().flashtopk_version())
+
+
+def flashtopk_probe_mfma(dtype: int, iters: int, stream=None) -> float:
+    """Attainable TFLOP/s of the scan's MFMA instruction (FP8 16x16x128 or
+    BF16 32x32x16) on the current device, from a register-only throughput
+    kernel timed on `stream` (synchronises it)."""
+    out = ctypes.c_double(0.0)
+    st = load_library().flashtopk_probe_mfma(int(dtype), int(iters), ctypes.c_void_p(_stream_handle(stream)),
+                                             ctypes.byref(out))
+    if st != 0:
+        raise FlashTopKError(st, "flashtopk_probe_mfma")
+    return float(out.value)
 
 
 def select(q, kv, weights, ks, ke, kv_scales=None, topk=2048, return_scores=False, options=None, stream=None,

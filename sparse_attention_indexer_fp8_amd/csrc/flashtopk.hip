@@ -38,6 +38,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -47,6 +48,7 @@
 #include "ftk_bound.hpp"
 #include "ftk_dec.hpp"
 #include "ftk_paged.hpp"
+#include "ftk_probe.hpp"
 #include "ftk_rows.hpp"
 #include "ftk_score.hpp"
 #include "ftk_select.hpp"
@@ -1267,6 +1269,48 @@ const char *flashtopk_status_string(int status)
     case FLASHTOPK_ERR_WORKSPACE_LIMIT: return "call too large for the fixed scratch array";
     default: return "unknown status";
     }
+}
+
+int flashtopk_probe_mfma(int dtype, int iters, void *stream, double *tflops)
+{
+    if (!tflops || iters <= 0 || (dtype != FLASHTOPK_FP8_E4M3 && dtype != FLASHTOPK_BF16))
+        return FLASHTOPK_ERR_INVALID_ARGUMENT;
+    *tflops = 0.0;
+    (void)hipGetLastError();  // a stale error of an earlier call is not this call's
+    hipStream_t s = (hipStream_t)stream;
+    const unsigned grid = (unsigned)(4 * num_cu());  // four workgroups of four waves per compute unit
+    const float never = __builtin_nanf("");
+    auto launch = [&](int n) {
+        if (dtype == FLASHTOPK_FP8_E4M3) k_probe_mfma<kFP8><<<grid, kProbeThreads, 0, s>>>(n, never);
+        else k_probe_mfma<kBF16><<<grid, kProbeThreads, 0, s>>>(n, never);
+    };
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) {
+        launch(std::max(1, iters / 8));  // warm-up: code object loaded, clocks up
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    if (e == hipSuccess) {
+        launch(iters);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (e != hipSuccess) {
+        std::fprintf(stderr, "flashtopk_probe_mfma: %s\n", hipGetErrorString(e));
+        (void)hipGetLastError();
+        return hip_status(e);
+    }
+    const double per_mfma = dtype == FLASHTOPK_FP8_E4M3 ? 2.0 * 16 * 16 * 128 : 2.0 * 32 * 32 * 16;
+    const double flops = (double)grid * (kProbeThreads / 64) * (double)iters * kProbeChains * per_mfma;
+    *tflops = ms > 0.0f ? flops / ((double)ms * 1e-3) / 1e12 : 0.0;
+    return FLASHTOPK_OK;
 }
 
 int flashtopk_version(void) { return 200; }

@@ -120,6 +120,10 @@ def test_argument_errors_without_device(lib):
     assert lib.flashtopk_get_last_recovered(None, None, 0, None) == 1     # no count pointer
     n = ctypes.c_int64(0)
     assert lib.flashtopk_get_last_recovered(None, None, 5, ctypes.byref(n)) == 1  # rows missing
+    tf = ctypes.c_double(1.0)
+    assert lib.flashtopk_probe_mfma(7, 10, None, ctypes.byref(tf)) == 1          # no such dtype
+    assert lib.flashtopk_probe_mfma(0, 0, None, ctypes.byref(tf)) == 1           # no rounds
+    assert lib.flashtopk_probe_mfma(0, 10, None, None) == 1                      # no output
 
 
 def test_misaligned_operands_rejected(lib):
