@@ -8,14 +8,15 @@
 // (kTauBuckets buckets between its minimum and maximum, highest first); the
 // bucket that holds the r-th largest sample is found from the histogram, and
 // when it holds at most 64 samples (the usual case) the r-th largest is
-// picked from them exactly.  When every lane holds a sample and r <= 64, the
-// smallest of the 64 lanes' largest samples is a floor: at least 64 samples
-// reach it, so the r-th largest does too, and only the samples at or above
-// it are bucketed (between it and the maximum), which leaves most samples
-// out of the histogram and spreads the top of the row over all buckets.  A denser bucket gives the threshold one bucket
+// picked from them exactly.  A denser bucket gives the threshold one bucket
 // below its lower edge instead: at least r samples reach it, whatever the
-// rounding of the bucket arithmetic.  No threshold changes results -- triage
-// catches any row it misjudges -- only the candidate count.
+// rounding of the bucket arithmetic.  When every lane holds a sample and
+// r <= 64, the smallest of the 64 lanes' largest samples is a floor: at
+// least 64 samples reach it, so the r-th largest does too, and only the
+// samples at or above it are bucketed (between it and the maximum), which
+// leaves most samples out of the histogram and spreads the top of the row
+// over all buckets.  No threshold changes results -- triage catches any row
+// it misjudges -- only the candidate count.
 #pragma once
 
 #include "ftk_common.hpp"
