@@ -26,6 +26,26 @@ constexpr int kMaxChunk = 131072;
 constexpr int kFP8 = 0;
 constexpr int kBF16 = 1;
 
+// FP8 rows whose window holds at most this many keys are scored in the plain
+// form sigma * sum_h w ReLU(x_h); longer rows through the linear identity.
+// The identity's error is absolute (set by the query sum's truncation), while
+// the score tolerance scales with the row's largest score, and on a short
+// window that can be as small as one key's score.  The form depends only on
+// the row's own window, so every path and batch gives a row the same bits.
+constexpr int kPlainKeys = 4096;
+
+__device__ __forceinline__ bool plain_row(int ks, int ke)
+{
+    return ke > ks && ke - ks <= kPlainKeys;
+}
+
+// 2 ReLU(x) for p = 1 and |x| for p = 0, exactly (one FMA, |x| as a source
+// modifier): x + |x| is 2x or +0, and |x| + (+-0) is |x|.
+__device__ __forceinline__ float relu2_or_abs(float p, float x)
+{
+    return __builtin_fmaf(p, x, __builtin_fabsf(x));
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));

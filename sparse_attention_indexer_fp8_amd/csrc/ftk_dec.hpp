@@ -150,10 +150,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_score_dec(ScoreArgs a)
                 __builtin_amdgcn_wave_barrier();
                 const float *xr = xs + lane * kDecLd;
                 const float *wr = s_w + e * kHeads;
-                float acc = __builtin_fmaf(wr[0], __builtin_fabsf(xr[0]), s_lin[wave][lane]);
-#pragma unroll
-                for (int h = 1; h < kHeads; ++h) acc = __builtin_fmaf(wr[h], __builtin_fabsf(xr[h]), acc);
                 const int rks = s_ks[e], rke = s_ke[e];
+                // the row's form, as in the tile kernel: plain rows sum
+                // w 2 ReLU(x) from zero, identity rows w |x| from the linear half
+                const bool plain = plain_row(rks, rke);
+                const float pl = plain ? 1.0f : 0.0f;
+                float acc = __builtin_fmaf(wr[0], relu2_or_abs(pl, xr[0]), plain ? 0.0f : s_lin[wave][lane]);
+#pragma unroll
+                for (int h = 1; h < kHeads; ++h) acc = __builtin_fmaf(wr[h], relu2_or_abs(pl, xr[h]), acc);
                 if (key >= rks && key < rke)
                     a.scratch[(int64_t)e * a.scratch_stride + (key - rks)] = acc * sh;
                 __builtin_amdgcn_wave_barrier();  // every lane has read before the next row overwrites

@@ -26,7 +26,9 @@
 //   ftk_qbar.hpp), one vector FMA per (row, head, key) plus three MFMAs per
 //   (row, key) on the FP8 parts of qbar, staged in LDS as three extra heads.
 //   FP8 MFMAs are fast enough that the vector ALUs would otherwise bound the
-//   loop.
+//   loop.  Rows with short windows (kPlainKeys) take the plain form instead;
+//   a tile that holds one runs the step with a per-lane choice of form, at
+//   one more vector op per (row, head, key).
 //   BF16 (v_mfma_f32_16x16x32_bf16, four chained MFMAs per dot product): the
 //   matrix cores are the bound, so the plain form sigma * sum_h w ReLU(x_h)
 //   is kept (ReLU as an integer max on the bit pattern, then an FMA).
@@ -275,10 +277,42 @@ __device__ __forceinline__ void epi_abs_lin(float (&acc)[kSub][4], const v4f (&x
         for (int i = 0; i < 4; ++i) acc[kt][i] = __builtin_fmaf(w, __builtin_fabsf(x[kt][i]), lin[kt][i]);
 }
 
-template <typename AfterMfma>
-__device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[kSub], const uint8_t *s_q,
-                                           const float *s_w, int lane, float qsc, AfterMfma after_mfma)
+// Tiles that hold a plain-form row (kPlainKeys): each lane scores its own
+// row's form.  pl = 1 (plain) sums w 2 ReLU(x) from zero; pl = 0 (identity)
+// sums w |x| from the linear half, the same bits as epi_abs / epi_abs_lin.
+__device__ __forceinline__ void epi_mixed(float (&acc)[kSub][4], const v4f (&x)[kSub], float w, float pl)
 {
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[kt][i] = __builtin_fmaf(w, relu2_or_abs(pl, x[kt][i]), acc[kt][i]);
+}
+
+__device__ __forceinline__ void epi_mixed_lin(float (&acc)[kSub][4], const v4f (&x)[kSub], float w, float pl,
+                                              const v4f (&lin)[kSub])
+{
+#pragma unroll
+    for (int kt = 0; kt < kSub; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[kt][i] = __builtin_fmaf(w, relu2_or_abs(pl, x[kt][i]), pl != 0.0f ? 0.0f : lin[kt][i]);
+}
+
+// One epilogue of the FP8 step, in the tile's variant.
+template <bool MIXED>
+__device__ __forceinline__ void epi_fp8(float (&acc)[kSub][4], const v4f (&x)[kSub], float w, float pl)
+{
+    if constexpr (MIXED) epi_mixed(acc, x, w, pl);
+    else epi_abs(acc, x, w);
+}
+
+// MIXED: the tile holds a plain-form row; pl is the lane's row form (1
+// plain, 0 identity).
+template <bool MIXED, typename AfterMfma>
+__device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[kSub], const uint8_t *s_q,
+                                           const float *s_w, int lane, float qsc, float pl, AfterMfma after_mfma)
+{
+    constexpr int EV = MIXED ? 8 : 4;  // epilogue VALU ops per MFMA
     constexpr int HB = 2048;  // LDS bytes per head of the q tile
     const v4f z[kSub] = {};
     const uint8_t *qp = s_q + lane * 16;
@@ -308,10 +342,11 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
     mfma_lin(lin, kf, qb, lin, sb);         // part 2
     qb = load_qfrag_fp8(qp + 2 * HB);
     mfma_fp8_head(xb, kf, qa, z);  // head 1
-    epi_abs_lin(o.acc, xa, wp[0], lin);
+    if constexpr (MIXED) epi_mixed_lin(o.acc, xa, wp[0], pl, lin);
+    else epi_abs_lin(o.acc, xa, wp[0], lin);
     qa = load_qfrag_fp8(qp + 3 * HB);
     mfma_fp8_head(xa, kf, qb, z);  // head 2
-    epi_abs(o.acc, xb, wp[kTileQ]);
+    epi_fp8<MIXED>(o.acc, xb, wp[kTileQ], pl);
     qp += 2 * HB;
     wp += 2 * kTileQ;
     // Loop invariant: qa holds head h's fragment, xa head h-1's results.
@@ -321,10 +356,10 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
         const float w0 = wp[0], w1 = wp[kTileQ];
         qb = load_qfrag_fp8(qp + 2 * HB);  // head h + 1
         mfma_fp8_head(xb, kf, qa, z);      // head h
-        epi_abs(o.acc, xa, w0);            // head h - 1
+        epi_fp8<MIXED>(o.acc, xa, w0, pl); // head h - 1
         qa = load_qfrag_fp8(qp + 3 * HB);  // head h + 2 (at most head 31)
         mfma_fp8_head(xa, kf, qb, z);      // head h + 1
-        epi_abs(o.acc, xb, w1);            // head h
+        epi_fp8<MIXED>(o.acc, xb, w1, pl); // head h
         qp += 2 * HB;
         wp += 2 * kTileQ;
         // Issue order: one MFMA, then four epilogue FMAs, so each wave keeps
@@ -334,21 +369,21 @@ __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kFP8> (&kf)[k
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, EV, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, EV, 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     mfma_fp8_head(xb, kf, qa, z);  // head 31
     __builtin_amdgcn_s_setprio(0);
     after_mfma();  // the key fragments are free from here on
-    epi_abs(o.acc, xa, wp[0]);
-    epi_abs(o.acc, xb, wp[kTileQ]);
+    epi_fp8<MIXED>(o.acc, xa, wp[0], pl);
+    epi_fp8<MIXED>(o.acc, xb, wp[kTileQ], pl);
 }
 
 // BF16: v_mfma_f32_32x32x16_bf16, A = 32 keys x 16 dimensions (the lane's
@@ -403,9 +438,11 @@ __device__ __forceinline__ void epi_relu16(float (&acc)[2][16], const v16f (&x)[
         for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(w, relu_bits(x[u][r]), acc[u][r]);
 }
 
-template <typename AfterMfma>
+// BF16 rows always take the plain form: MIXED and pl are unused.
+template <bool MIXED, typename AfterMfma>
 __device__ __forceinline__ void score_step(StepOut &o, const KFrag<kBF16> (&kf)[kSub], const uint8_t *s_q,
-                                           const float *s_w, int lane, float /*qsc*/, AfterMfma after_mfma)
+                                           const float *s_w, int lane, float /*qsc*/, float /*pl*/,
+                                           AfterMfma after_mfma)
 {
     constexpr int HB = 4096;  // LDS bytes per head of the q tile
     const int half = (lane >> 4) & 1;
@@ -904,6 +941,17 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     const int rks = s_ks[n], rke = s_ke[n];
     const int S = a.num_kv;
     const float qsc = (DT == kFP8 && t >= 0) ? (own_prep ? s_qsc[MODE == kModeDense ? n : 0] : a.qscale[t]) : 1.0f;
+    // FP8 row forms: the lane's (1 plain, 0 identity) and whether the tile
+    // holds any plain row (workgroup-uniform).  Sample scores only steer the
+    // threshold, so sampling keeps the identity for every row.
+    bool mixed = false;
+    float pl = 0.0f;
+    if constexpr (DT == kFP8 && MODE != kModeSample) {
+#pragma unroll
+        for (int c = 0; c < kTileQ; ++c) mixed |= s_row[c] >= 0 && plain_row(s_ks[c], s_ke[c]);
+        mixed = __builtin_amdgcn_readfirstlane(mixed ? 1 : 0) != 0;
+        pl = t >= 0 && plain_row(rks, rke) ? 1.0f : 0.0f;
+    }
 
     float tau = __builtin_inff();
     if (MODE == kModeFilter && to >= 0) tau = a.tau[to];
@@ -961,7 +1009,8 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
     // Scores one step and hands its 16 outputs per lane to the mode's sink;
     // `next` runs as soon as the step's MFMAs no longer need the key
     // fragments (it issues the next step's key loads).
-    auto process = [&](KFrag<DT>(&kf)[kSub], int j, auto next) {
+    // mx: std::true_type for the tile variant with plain-form rows (FP8).
+    auto process = [&](KFrag<DT>(&kf)[kSub], int j, auto next, auto mx) {
         const int sb = j * kStepKeys + LY::out_base(lane);  // key of element (kt, i) is sb + KSTR kt + i
         // Scale factors of the step's outputs (4 consecutive keys per
         // subtile).  With the prefetching (2-wave) shape they load before the
@@ -1018,10 +1067,11 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
         constexpr bool early = Cfg::prefetch && !(DT == kBF16 && MODE == kModeSample);
         if (early) load_sh();
         StepOut o;
-        score_step(o, kf, s_q, s_w, lane, qsc, [&]() {
+        auto after_mfma = [&]() {
             if (!early) load_sh();
             next();
-        });
+        };
+        score_step<decltype(mx)::value>(o, kf, s_q, s_w, lane, qsc, pl, after_mfma);
         if (PAIR) {
             // a row's two columns are neighbouring lanes: add their head sums
 #pragma unroll
@@ -1150,11 +1200,11 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             while (i < nstep) {
                 const int i2 = claim();
                 if (i2 < nstep) load_step(kb, step_of(i2));
-                process(ka, step_of(i), nop);
+                process(ka, step_of(i), nop, std::false_type{});
                 if (i2 >= nstep) break;
                 const int i3 = claim();
                 if (i3 < nstep) load_step(ka, step_of(i3));
-                process(kb, step_of(i2), nop);
+                process(kb, step_of(i2), nop, std::false_type{});
                 i = i3;
             }
         } else {
@@ -1166,38 +1216,48 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             if (i < nstep) load_step(kf, step_of(i));
             while (i < nstep) {
                 const int i2 = claim();
-                process(kf, step_of(i), [&]() {
-                    if (i2 < nstep) load_step(kf, step_of(i2));
-                });
+                process(
+                    kf, step_of(i), [&]() {
+                        if (i2 < nstep) load_step(kf, step_of(i2));
+                    },
+                    std::false_type{});
                 i = i2;
             }
         }
-    } else if (Cfg::prefetch) {
-        // Two fragment sets alternate so the next step's keys load while this
-        // step computes.
-        KFrag<DT> ka[kSub], kb[kSub];
-        int i = wave;
-        if (i < nstep) load_step(ka, step_of(i));
-        for (; i < nstep; i += 2 * kWaves) {
-            if (i + kWaves < nstep) load_step(kb, step_of(i + kWaves));
-            process(ka, step_of(i), nop);
-            if (i + kWaves >= nstep) break;
-            if (i + 2 * kWaves < nstep) load_step(ka, step_of(i + 2 * kWaves));
-            process(kb, step_of(i + kWaves), nop);
-        }
     } else {
-        // One fragment set: the next step's keys load into it as soon as this
-        // step's last MFMA is issued, so the sink hides their latency.
-        // The load is unconditional (the last step re-reads its own keys) so
-        // the code after it has one path and the wait for the scale factors
-        // never covers these loads.
-        KFrag<DT> kf[kSub];
-        int i = wave;
-        if (i < nstep) load_step(kf, step_of(i));
-        for (; i < nstep; i += kWaves) {
-            const int in = min(i + kWaves, nstep - 1);
-            process(kf, step_of(i), [&]() { load_step(kf, step_of(in)); });
+      // Filter and dense modes: one copy of the step loop per tile variant,
+      // so each keeps its own register allocation.
+      auto scan = [&](auto mx) {
+        if constexpr (Cfg::prefetch) {
+            // Two fragment sets alternate so the next step's keys load while
+            // this step computes.
+            KFrag<DT> ka[kSub], kb[kSub];
+            int i = wave;
+            if (i < nstep) load_step(ka, step_of(i));
+            for (; i < nstep; i += 2 * kWaves) {
+                if (i + kWaves < nstep) load_step(kb, step_of(i + kWaves));
+                process(ka, step_of(i), nop, mx);
+                if (i + kWaves >= nstep) break;
+                if (i + 2 * kWaves < nstep) load_step(ka, step_of(i + 2 * kWaves));
+                process(kb, step_of(i + kWaves), nop, mx);
+            }
+        } else {
+            // One fragment set: the next step's keys load into it as soon as
+            // this step's last MFMA is issued, so the sink hides their
+            // latency.  The load is unconditional (the last step re-reads its
+            // own keys) so the code after it has one path and the wait for
+            // the scale factors never covers these loads.
+            KFrag<DT> kf[kSub];
+            int i = wave;
+            if (i < nstep) load_step(kf, step_of(i));
+            for (; i < nstep; i += kWaves) {
+                const int in = min(i + kWaves, nstep - 1);
+                process(kf, step_of(i), [&]() { load_step(kf, step_of(in)); }, mx);
+            }
         }
+      };
+      if (DT == kFP8 && mixed) scan(std::true_type{});
+      else scan(std::false_type{});
     }
     if (MODE == kModeFilter) {
         if (__any(ring_cnt > 0)) ring_flush<RS>(ring, ring_cnt, n, g, to, a.cnt, a.cand, a.cap);

@@ -59,15 +59,16 @@ def exact_row(idx, val, o_idx, o_val):
     return f
 
 
-def tolerance_row(idx, val, o_idx, o_score, all_scores, ks, ke, topk, rel_tol=1e-3):
-    """Returns (failures, precision p)."""
+def tolerance_row(idx, val, o_idx, o_score, all_scores, ks, ke, topk, rel_tol=1e-3, floor=0.0):
+    """Returns (failures, precision p).  ``floor``: an absolute lower limit
+    of the row's tolerance (the arithmetic's own error bound), or 0."""
     f = []
     L = max(0, int(ke) - int(ks))
     k = min(int(topk), L)
     if k == 0:
         return f, 1.0
     win = all_scores[int(ks):int(ke)]
-    tol = rel_tol * float(np.max(np.abs(win)))
+    tol = max(rel_tol * float(np.max(np.abs(win))), float(floor))
     sel = np.asarray(idx[:k], dtype=np.int64)
     osel = np.asarray(o_idx[:k], dtype=np.int64)
     if np.any(sel < ks) or np.any(sel >= ke):
@@ -90,11 +91,12 @@ def tolerance_row(idx, val, o_idx, o_score, all_scores, ks, ke, topk, rel_tol=1e
 
 
 def check(idx, val, ks, ke, topk, *, o_idx, o_val=None, o_score=None, all_scores=None,
-          rows=None, mode="exact", rel_tol=1e-3, max_report=5):
+          rows=None, mode="exact", rel_tol=1e-3, floor=None, max_report=5):
     """Check a [n, topk] selection against oracle outputs for the same rows.
 
     ``rows`` maps each output row to its query index (for ks/ke); None means
-    rows 0..n-1.  Returns a report dict with failures (first few), the number
+    rows 0..n-1.  ``floor`` (tolerance mode, indexed like ``rows``): per-row
+    absolute lower limits of the tolerance, or None.  Returns a report dict with failures (first few), the number
     of failing rows, the mean precision and the bit-identical row fraction.
     """
     idx = np.asarray(idx)
@@ -110,7 +112,7 @@ def check(idx, val, ks, ke, topk, *, o_idx, o_val=None, o_score=None, all_scores
             p = 1.0 if not fr else np.intersect1d(idx[r][idx[r] >= 0], o_idx[r][o_idx[r] >= 0]).size / max(1, min(topk, int(ke[t]) - int(ks[t])))
         else:
             ft, p = tolerance_row(idx[r], val[r], o_idx[r], o_score[r], all_scores[r], ks[t], ke[t],
-                                  topk, rel_tol)
+                                  topk, rel_tol, 0.0 if floor is None else floor[r])
             fr += ft
         if o_val is not None and np.array_equal(idx[r], o_idx[r]) and np.array_equal(
                 val[r].view(np.uint32), np.asarray(o_val[r], np.float32).view(np.uint32)):
