@@ -165,3 +165,27 @@ def test_rows_misleading_sample_falls_back(level):
     lines[:, ::32, :] += level
     wl["x"] = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     _check(wl, _run(wl))
+
+
+def _random_rows_case(seed):
+    rng = np.random.default_rng(7700 + seed)
+    rows = int(rng.choice([1, 2, 5, 17, 64, 130, 300]))
+    cols = int(rng.integers(1, 70000)) if rows <= 64 else int(rng.integers(1, 20000))
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    kind = ["normal", "skewed", "ties", "special"][seed % 4]
+    topk = int(rng.choice([1, 5, 64, 300, 512, 1024, 2048, 4096]))
+    ends = [None, "ragged", "causal"][seed % 3]
+    stride = None if rows == 1 or seed % 5 else cols + int(rng.integers(0, 3)) * 8 + (-cols) % 8
+    return rows, cols, dtype, kind, topk, ends, stride
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_rows_random_shapes(seed):
+    """Seeded random row counts, lengths, strides, ends, topk and value kinds
+    (including the split-row form for few rows), bit-exact."""
+    rows, cols, dtype, kind, topk, ends, stride = _random_rows_case(seed)
+    _say("random rows", seed, rows, cols, dtype, kind, topk, ends, stride)
+    if rows > 1 and stride is None and cols % 8:
+        stride = cols + (-cols) % 8  # rows start 16-byte aligned
+    wl = workloads.score_rows(rows, cols, dtype, 7800 + seed, kind=kind, topk=topk, ends=ends, stride=stride)
+    _check(wl, _run(wl))
