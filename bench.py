@@ -70,14 +70,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_score_filter_fp8_trained_4096x1
 
 
 def kernel_digest():
-    """SHA-256 of the fused filter kernel's sources (the traffic figure is
-    only valid for the sources it was measured on)."""
+    """SHA-256 of the fused filter kernel's sources with comments and blank
+    lines removed (the traffic figure is only valid for the code it was
+    measured on; a comment edit does not change the code)."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_attention_indexer_fp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_attention_indexer_fp8_amd", "csrc", f)) as fh:
+            t = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        t = re.sub(r"//[^\n]*", "", t)
+        h.update("\n".join(ln.rstrip() for ln in t.split("\n") if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

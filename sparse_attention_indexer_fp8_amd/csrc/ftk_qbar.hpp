@@ -14,7 +14,8 @@
 // sum_p part_p . kv[s] and the kernel multiplies by 2^-e.  Three parts carry
 // 12 significant bits of every component: exact whenever qbar's components
 // have at most 12 (integer-valued operands with dyadic weights), and about
-// 2^-12 relative to the row's largest component otherwise.
+// 2^-12 relative to the row's largest component otherwise.  Rows with short
+// windows (kPlainKeys) are scored without it.
 #pragma once
 
 #include "ftk_common.hpp"
