@@ -1101,11 +1101,16 @@ __global__ __launch_bounds__((64 * ScoreCfg<DT, MODE, LOOP>::waves)) void k_scor
             uint32_t m = 0;
 #pragma unroll
             for (int b = 0; b < kSub * 4; ++b) m += (sc[b] >= tau) ? 1u : 0u;
-            // Survivors of the 4 lanes that hold query n: total and this lane's offset.
-            const uint32_t c0 = __shfl(m, n), c1 = __shfl(m, n + 16), c2 = __shfl(m, n + 32),
-                           c3 = __shfl(m, n + 48);
-            uint32_t tot = c0 + c1 + c2 + c3;
-            const uint32_t pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+            // Survivors of the 4 lanes that hold query n (lanes n + 16 g'):
+            // total and this lane's offset, by two row swaps in the VALU (no
+            // LDS round trip).  A swap returns the lane's own value in one
+            // output and its partner's in the other, so their sum is the
+            // pair's: p16 = counts of g and g ^ 1, tot = all four.
+            const auto s16 = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+            const uint32_t p16 = s16[0] + s16[1];
+            const auto s32 = __builtin_amdgcn_permlane32_swap(p16, p16, false, false);
+            uint32_t tot = s32[0] + s32[1];
+            const uint32_t pre = ((g & 2) ? tot - p16 : 0u) + ((g & 1) ? p16 - m : 0u);
             if (__builtin_expect(__any(ring_cnt + tot > (uint32_t)RING), 0)) {
                 ring_flush<RS>(ring, ring_cnt, n, g, to, a.cnt, a.cand, a.cap);
                 ring_cnt = 0;
