@@ -44,6 +44,15 @@
  * from several host threads are serialised by a lock on the stream's
  * workspace; calls on different streams run concurrently.
  *
+ * Precision: scores are binary32, and a (row, key) pair's score has the same
+ * bits on every path and in every batch (the selection is exact with respect
+ * to these scores).  BF16 dot products round like binary32 sums.  The FP8
+ * matrix cores' dot products err by up to about 2^-16 of sum_d |q_d kv_d|;
+ * FP8 rows whose window holds more than 4096 keys also evaluate the head sum
+ * through (sum_h w|x_h| + qbar . kv) / 2 with the query sum qbar carried to
+ * 12 significant bits, which adds at most 2^-12 * sigma * max_d |kv_d| *
+ * sum_h |w_h| ||q_h||_1; shorter rows use the plain ReLU form.
+ *
  * Errors: every entry point returns 0 (FLASHTOPK_OK) or a positive status;
  * nothing is thrown across the ABI and nothing is printed.  Preconditions
  * that cost a device read (window bounds inside [0, num_kv], finite operands)
